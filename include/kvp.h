@@ -1,0 +1,223 @@
+/*
+ * kvp.h -- paged KV cache and paged decode attention for AMD MI355X (gfx950).
+ *
+ * The method ("KV-Cache Optimization Techniques", section "PagedAttention",
+ * eq. 1; "Understanding KV-Cache Optimization in Modern LLM Serving", section
+ * "PagedAttention Solution"): the K/V rows of every sequence live in
+ * fixed-size physical pages of P tokens; a per-sequence block table maps the
+ * sequence's logical block i (tokens i*P .. i*P+P-1) to a physical page id.
+ * Decode attention gathers the pages in logical order and computes
+ *     out_j = softmax(scale * q_j . [K_page1; ...; K_pagen]^T) [V_page1; ...; V_pagen]
+ * for every query head j of the one new query token of each sequence.
+ *
+ * ---------------------------------------------------------------------------
+ * Symbols
+ *   P      page size in tokens (16 or 32)
+ *   H_kv   KV heads, H_q query heads, g = H_q / H_kv query heads per KV head
+ *   D      head dimension (64 or 128)
+ *   B      sequences in a call
+ * Query head j reads KV head j / g: consecutive query heads share a KV head
+ * ("KV-Cache Optimization Techniques", section "Multi-Query and Grouped-Query
+ * Caching", eq. 7; MQA is H_kv = 1).
+ *
+ * ---------------------------------------------------------------------------
+ * Memory layout (one layer).  All arrays are dense, row-major, no padding.
+ *   K pool, element type T (bfloat16 bits, or int8 code):
+ *       K[page][h][t][d]      at element ((page*H_kv + h)*P + t)*D + d
+ *   V pool, element type T, stored transposed inside each (page, head) tile:
+ *       V[page][h][t][d]      at element ((page*H_kv + h)*D + d)*P + t
+ *   INT8 metadata, one (scale, zero) float16 pair per token per KV head, the
+ *   same layout for K and for V:
+ *       scale of row (page,h,t)  at float16 element ((page*H_kv + h)*P + t)*2 + 0
+ *       zero  of row (page,h,t)  at float16 element ((page*H_kv + h)*P + t)*2 + 1
+ *     and the stored value of element d of that row is
+ *       float(scale) * code[d] + float(zero)
+ *   A pool of num_pages pages spans num_pages*H_kv*P*D elements per K or V
+ *   array (kvp_pool_bytes).  One page id names the same page in every layer's
+ *   pool, so one block table serves all layers.
+ *   q, out:         [B][H_q][D] bfloat16 bits.
+ *   block_tables:   [B][max_blocks] int32; entry (b, i) is the page holding
+ *                   tokens i*P .. i*P+P-1 of sequence b.  Entries at
+ *                   i >= ceil(ctx_b / P) are never read.
+ *   context_lens:   [B] int32, tokens each sequence attends over.
+ * Token position pos of sequence b sits in page block_tables[b][pos / P] at
+ * in-page row pos % P.  Rows of a page beyond a sequence's length, and pages
+ * no table names, are never read by decode and may hold anything (NaN too).
+ *
+ * INT8 rows ("KV-Cache Optimization Techniques", section "KV-Cache
+ * Quantization", eq. 3, per-token calibration): each (token, KV head) row x of
+ * D bfloat16 values is stored as
+ *     mn = min x, mx = max x                          (float32, exact)
+ *     z  = f16( (mx + mn) * 0.5f )                    (float32 ops, RNE to f16)
+ *     s  = f16( (mx - mn) / 254.0f ); s = 1.0 if s == 0
+ *     code[d] = clamp( rint_even( (x[d] - float(z)) / float(s) ), -128, 127 )
+ * with every float32 operation IEEE round-to-nearest-even.  Inputs need
+ * |x| <= 65504 so that z is finite in float16.
+ *
+ * ---------------------------------------------------------------------------
+ * Ownership.  The caller owns every device buffer (pools, metadata, q, out,
+ * tables, lengths, workspace) and keeps it alive until the work queued on the
+ * stream has finished.  The library owns the host pool object: the page
+ * free-list and per-page reference counts.  The library never allocates or
+ * frees device memory.
+ *
+ * Errors.  Every call returns kvp_status.  A host call that fails leaves all
+ * state unchanged.  Device work is queued asynchronously on the given stream
+ * (NULL = the default stream); a failed launch returns KVP_E_HIP.  Device data
+ * the host cannot see is handled without faulting: a page id outside
+ * [0, num_pages) makes the tokens of that block count as absent (decode) or
+ * the row is not written (append); context_lens are clamped to
+ * [0, min(max_context_len, max_blocks*P)].  Such inputs are caller errors
+ * with no other guarantee about the result.
+ *
+ * Threads.  A pool object is not thread safe; the caller serializes calls on
+ * one pool.  Device calls on one stream run in order.
+ */
+#ifndef KVP_H
+#define KVP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t; NULL means the default stream. */
+struct ihipStream_t;
+typedef struct ihipStream_t* kvp_stream_t;
+
+typedef enum {
+  KVP_OK = 0,
+  KVP_E_INVAL = 1,        /* bad argument, or a state violation (double free ...) */
+  KVP_E_NOPAGES = 2,      /* not enough free pages; nothing was allocated */
+  KVP_E_UNSUPPORTED = 3,  /* shape or dtype with no kernel (P, D, g, dtype) */
+  KVP_E_HIP = 4           /* a HIP runtime call failed */
+} kvp_status;
+
+typedef enum { KVP_BF16 = 0, KVP_INT8 = 1 } kvp_kv_dtype;
+
+typedef struct {
+  int32_t num_pages;     /* pages in the pool, > 0 */
+  int32_t page_size;     /* P: 16 or 32 */
+  int32_t num_kv_heads;  /* H_kv, > 0 */
+  int32_t head_dim;      /* D: 64 or 128 */
+  kvp_kv_dtype dtype;
+} kvp_pool_desc;
+
+typedef struct kvp_pool kvp_pool; /* opaque; host memory owned by the library */
+
+/* Text for a status code (static storage). */
+const char* kvp_status_string(kvp_status s);
+
+/* ---- Pool and page allocation (host only; "KV-Cache Optimization
+ * Techniques", section "PagedAttention": pages allocated on demand and freed
+ * when the request completes; section "Prefix Caching": pages shared by
+ * requests with a common prefix). -------------------------------------- */
+
+/* Bytes of one layer's K (or V) array, and of its INT8 metadata array (0 for
+ * bfloat16).  Either output pointer may be NULL. */
+kvp_status kvp_pool_bytes(const kvp_pool_desc* desc, size_t* kv_bytes, size_t* meta_bytes);
+
+/* Create a pool object: every page free, reference count 0.  *out receives a
+ * new object the caller releases with kvp_pool_destroy. */
+kvp_status kvp_pool_create(const kvp_pool_desc* desc, kvp_pool** out);
+void kvp_pool_destroy(kvp_pool* pool);                 /* NULL is a no-op */
+kvp_status kvp_pool_get_desc(const kvp_pool* pool, kvp_pool_desc* out);
+int32_t kvp_pool_free_count(const kvp_pool* pool);     /* -1 if pool is NULL */
+/* Reference count of one page (0 = free), or -1 if the id is out of range. */
+int32_t kvp_pool_refcount(const kvp_pool* pool, int32_t page);
+
+/* Take n pages from the free-list (last freed, first taken) and write their
+ * ids to out_ids[0..n-1]; each gets reference count 1.  All or nothing:
+ * KVP_E_NOPAGES if fewer than n are free. */
+kvp_status kvp_pages_alloc(kvp_pool* pool, int32_t n, int32_t* out_ids);
+/* Add one reference to each listed page (sharing it with one more sequence).
+ * Every page must be in use (count >= 1); KVP_E_INVAL otherwise. */
+kvp_status kvp_pages_ref(kvp_pool* pool, int32_t n, const int32_t* ids);
+/* Drop one reference from each listed page; a page whose count reaches 0
+ * returns to the free-list.  A listed page must hold at least as many
+ * references as times it is listed; KVP_E_INVAL otherwise. */
+kvp_status kvp_pages_free(kvp_pool* pool, int32_t n, const int32_t* ids);
+
+/* Block-table row helpers (host memory).  kvp_seq_grow makes row cover
+ * new_len tokens: blocks ceil(cur_len/P) .. ceil(new_len/P)-1 get freshly
+ * allocated pages; earlier entries are kept.  All or nothing. */
+kvp_status kvp_seq_grow(kvp_pool* pool, int32_t* row, int32_t max_blocks,
+                        int32_t cur_len, int32_t new_len);
+/* Point blocks 0..n_blocks-1 of dst_row at the pages of src_row and add a
+ * reference to each (a shared prefix of whole pages). */
+kvp_status kvp_seq_share(kvp_pool* pool, const int32_t* src_row, int32_t* dst_row,
+                         int32_t n_blocks);
+/* Drop the references of blocks 0..n_blocks-1 of row and set them to -1
+ * (the request completed). */
+kvp_status kvp_seq_release(kvp_pool* pool, int32_t* row, int32_t n_blocks);
+
+/* ---- Append (device) ------------------------------------------------------
+ * For each of n_tokens new tokens i: sequence seq_idx[i], position pos[i];
+ * write k_new[i][h][:] and v_new[i][h][:] (bfloat16 [n_tokens][H_kv][D]) into
+ * row pos[i] % P of page block_tables[seq_idx[i]][pos[i] / P], for every KV
+ * head h; INT8 pools quantize each row as described above and write its code
+ * row and (scale, zero).  k_meta/v_meta must be NULL for bfloat16 pools.
+ * All pointers are device pointers.  Rows whose seq_idx is outside
+ * [0, num_seqs), whose pos is outside [0, max_blocks*P) or whose page id is
+ * outside [0, num_pages) are not written.  Two tokens naming the same row
+ * race.  A page shared by several sequences must not be appended into. */
+kvp_status kvp_kv_append(const kvp_pool* pool, void* k_pool, void* v_pool,
+                         void* k_meta, void* v_meta,
+                         const void* k_new, const void* v_new,
+                         const int32_t* seq_idx, const int32_t* pos, int32_t n_tokens,
+                         const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks,
+                         kvp_stream_t stream);
+
+/* ---- Decode plan (host, pure) -----------------------------------------------
+ * Work is split into B * H_kv * num_splits workgroups: each covers one
+ * (sequence, KV head) pair and one range of pages_per_split logical blocks,
+ * handled by waves_per_group wavefronts that each stream a share of the pages
+ * and merge their softmax partials in LDS.  With num_splits > 1 the partials
+ * go to the workspace and a second kernel merges them by log-sum-exp.
+ * num_splits_req <= 0 picks a split count from max_context_len and num_cus.
+ */
+typedef struct {
+  int32_t num_splits;
+  int32_t pages_per_split;
+  int32_t waves_per_group;
+  int32_t use_mfma;          /* 1: matrix-core kernel (g >= 4); 0: vector ALU kernel */
+  size_t workspace_bytes;    /* device workspace decode needs (0 when num_splits == 1) */
+} kvp_decode_plan_t;
+
+kvp_status kvp_decode_plan(const kvp_pool_desc* desc, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t max_context_len, int32_t num_splits_req, int32_t num_cus,
+                           kvp_decode_plan_t* out);
+
+/* Workspace bytes kvp_paged_attention_decode needs on the current device. */
+kvp_status kvp_decode_workspace_bytes(const kvp_pool* pool, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t max_context_len,
+                                      int32_t num_splits_req, size_t* bytes);
+
+/* ---- Decode (device) --------------------------------------------------------
+ * out[b][j][:] = attention of q[b][j][:] over tokens 0 .. ctx_b-1 of sequence
+ * b (ctx_b = context_lens[b]) through KV head j/g, as eq. 1 above, scores
+ * multiplied by `scale` (normally 1/sqrt(D)).  Scores, softmax and the
+ * weighted sum are accumulated in float32; out is rounded to bfloat16 (RNE).
+ * ctx_b == 0 gives out = 0.  max_context_len is a host-side upper bound of
+ * context_lens (1 .. max_blocks*P), used to plan the split.  workspace must
+ * be a device buffer of at least kvp_decode_workspace_bytes (may be NULL when
+ * that is 0).  All array pointers are device pointers.  Output rows depend
+ * only on the pages' contents in logical order, so relabelling physical pages
+ * leaves the result bit-identical. */
+kvp_status kvp_paged_attention_decode(const kvp_pool* pool, const void* q,
+                                      const void* k_pool, const void* v_pool,
+                                      const void* k_meta, const void* v_meta,
+                                      const int32_t* block_tables, int32_t max_blocks,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t max_context_len,
+                                      float scale, void* out, int32_t num_splits_req,
+                                      void* workspace, size_t workspace_bytes,
+                                      kvp_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVP_H */

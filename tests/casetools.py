@@ -1,0 +1,73 @@
+"""Test-side helpers: assemble a case's logical rows, build oracle pools,
+compare outputs to the tolerance the workloads are held to."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from workloads import POISON_BF16, POISON_F16, POISON_I8, DecodeCase
+
+# Attention outputs (bfloat16, float32 accumulation) against the float64 oracle.
+MAX_ABS_TOL = 1e-2
+REL_L2_TOL = 5e-3
+
+
+def layout_of(case: DecodeCase) -> oracle.PoolLayout:
+    c = case.cfg
+    return oracle.PoolLayout(case.num_pages, c.page_size, c.num_kv_heads, c.head_dim, c.kv_dtype)
+
+
+def logical_rows(case: DecodeCase, b: int):
+    """K and V rows of sequence b in position order: uint16 [ctx, H_kv, D]."""
+    c = case.cfg
+    n = int(case.ctx[b])
+    K = np.zeros((n, c.num_kv_heads, c.head_dim), dtype=np.uint16)
+    V = np.zeros_like(K)
+    filled = np.zeros(n, dtype=bool)
+    src = [b] if not c.shared_prefix or b == 0 else [0, b]
+    for s in src:
+        sel = np.nonzero(case.hist_seq == s)[0]
+        p = case.hist_pos[sel]
+        keep = p < n - 1 if s == b else p < c.shared_prefix
+        K[p[keep]] = case.hist_k[sel[keep]]
+        V[p[keep]] = case.hist_v[sel[keep]]
+        filled[p[keep]] = True
+    K[n - 1] = case.new_k[b]
+    V[n - 1] = case.new_v[b]
+    filled[n - 1] = True
+    assert filled.all()
+    return K, V
+
+
+def oracle_pools(case: DecodeCase, with_new: bool = True):
+    """Poisoned pools with every history row (and the new rows) appended by the oracle."""
+    lay = layout_of(case)
+    fill = POISON_BF16 if lay.dtype == "bf16" else POISON_I8
+    k, v, km, vm = lay.empty_pools(fill, POISON_F16)
+    oracle.append(lay, k, v, km, vm, case.hist_k, case.hist_v, case.hist_seq, case.hist_pos,
+                  case.block_tables)
+    if with_new:
+        oracle.append(lay, k, v, km, vm, case.new_k, case.new_v,
+                      np.arange(case.B, dtype=np.int32), case.new_pos, case.block_tables)
+    return k, v, km, vm
+
+
+def compare_outputs(out_bf16_bits: np.ndarray, ref_f64: np.ndarray):
+    """(max_abs, rel_l2, worst index) of bfloat16 outputs against float64."""
+    got = (np.asarray(out_bf16_bits, dtype=np.uint16).astype(np.uint32) << 16) \
+        .view(np.float32).astype(np.float64)
+    d = got - ref_f64
+    if not np.isfinite(got).all():
+        return float("inf"), float("inf"), None
+    max_abs = float(np.abs(d).max()) if d.size else 0.0
+    den = float(np.linalg.norm(ref_f64))
+    rel = float(np.linalg.norm(d) / den) if den > 0 else float(np.linalg.norm(d))
+    worst = np.unravel_index(int(np.abs(d).argmax()), d.shape) if d.size else None
+    return max_abs, rel, worst
+
+
+def assert_close(out_bf16_bits, ref_f64, what=""):
+    max_abs, rel, worst = compare_outputs(out_bf16_bits, ref_f64)
+    assert max_abs <= MAX_ABS_TOL and rel <= REL_L2_TOL, \
+        f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} worst={worst}"
+    return max_abs, rel

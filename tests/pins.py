@@ -1,0 +1,296 @@
+"""Checks that pin the CPU oracle to the pages and to mathematics.
+
+Each ``pin_*`` raises AssertionError when the oracle disagrees with something
+fixed outside it: values the pages print, a library routine that computes the
+same definition, exact-rational arithmetic, closed forms and invariants.
+test_oracle_pins runs them on the oracle; test_oracle_mutations plants
+plausible mistakes in the oracle and checks that some pin catches each one.
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import paged_attention as opa
+from oracle import quantize as oq
+from workloads import TINY, f32_to_bf16_bits, make_case, variant
+
+from .casetools import layout_of, logical_rows, oracle_pools
+from .exact_ieee import quantize_row_exact
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _bf16_f64(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32) \
+        .astype(np.float64)
+
+
+# Small cases: the tiny workload and its MHA (g=1), g=2, H_kv=2 and peaky variants.
+def small_cases():
+    return [
+        TINY,
+        variant(TINY, name="tiny_g1", num_q_heads=2, num_kv_heads=2, pool_pages=32),
+        variant(TINY, name="tiny_g2", num_q_heads=4, num_kv_heads=2, pool_pages=32),
+        variant(TINY, name="tiny_h2g4", num_q_heads=8, num_kv_heads=2, pool_pages=32,
+                head_dim=128),
+        variant(TINY, name="tiny_peaky", q_gain=4.0),
+        variant(TINY, name="tiny_p32_int8", page_size=32, kv_dtype="int8", num_q_heads=8,
+                num_kv_heads=2, head_dim=128, pool_pages=16, outlier_channels=3,
+                outlier_gain=8.0),
+    ]
+
+
+# ---------------------------------------------------------------- layout / gather
+def loop_scatter(case):
+    """Pools written one element at a time from the header's index formulas."""
+    lay = layout_of(case)
+    c = case.cfg
+    P, H, D = c.page_size, c.num_kv_heads, c.head_dim
+    assert c.kv_dtype == "bf16"
+    k = np.full(lay.elems, 0x7FC0, dtype=np.uint16)
+    v = np.full(lay.elems, 0x7FC0, dtype=np.uint16)
+    for b in range(case.B):
+        K, V = logical_rows(case, b)
+        for pos in range(int(case.ctx[b])):
+            page = int(case.block_tables[b][pos // P])
+            t = pos % P
+            for h in range(H):
+                for d in range(D):
+                    k[((page * H + h) * P + t) * D + d] = K[pos, h, d]
+                    v[((page * H + h) * D + d) * P + t] = V[pos, h, d]
+    return k, v
+
+
+def pin_block_table_worked_example():
+    g = _golden("block_table_p2.json")
+    row = np.array(g["block_table"], dtype=np.int32)
+    for c in g["cases"]:
+        assert oracle.slot(row, c["pos"], c["page_size"]) == (c["page"], c["row"]), c
+
+
+def pin_append_and_gather_layout(case):
+    """oracle.append writes what the element loop writes; gather returns the rows."""
+    k_loop, v_loop = loop_scatter(case)
+    k, v, _, _ = oracle_pools(case)
+    assert np.array_equal(k, k_loop), "K pool differs from the header layout"
+    assert np.array_equal(v, v_loop), "V pool differs from the header layout"
+    lay = layout_of(case)
+    for b in range(case.B):
+        K, V = logical_rows(case, b)
+        Kg, Vg = oracle.gather_sequence(lay, k, v, None, None, case.block_tables[b],
+                                        int(case.ctx[b]))
+        assert np.array_equal(Kg, _bf16_f64(K).transpose(1, 0, 2)), f"K gather seq {b}"
+        assert np.array_equal(Vg, _bf16_f64(V).transpose(1, 0, 2)), f"V gather seq {b}"
+
+
+# ---------------------------------------------------------------- attention
+def _sdpa(q, K, V, scale):
+    """torch's scaled_dot_product_attention in float64 on the CPU (GQA: query
+    head j reads KV head j // g)."""
+    qt = torch.from_numpy(q)[None, :, None, :]
+    kt = torch.from_numpy(np.ascontiguousarray(K.transpose(1, 0, 2)))[None]
+    vt = torch.from_numpy(np.ascontiguousarray(V.transpose(1, 0, 2)))[None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale,
+                                                         enable_gqa=True)
+    return o[0, :, 0, :].numpy()
+
+
+def pin_attention_vs_sdpa(case, tol=1e-12):
+    k, v, km, vm = oracle_pools(case)
+    lay = layout_of(case)
+    out = oracle.paged_decode(lay, case.q, k, v, km, vm, case.block_tables, case.ctx,
+                              case.scale)
+    for b in range(case.B):
+        K, V = logical_rows(case, b)
+        if case.cfg.kv_dtype == "int8":
+            # the library routine sees the dequantized rows of the row contract
+            Kf = np.stack([_dequant_exact(K[t]) for t in range(K.shape[0])])
+            Vf = np.stack([_dequant_exact(V[t]) for t in range(V.shape[0])])
+        else:
+            Kf, Vf = _bf16_f64(K), _bf16_f64(V)
+        ref = _sdpa(_bf16_f64(case.q[b]), Kf, Vf, float(np.float32(case.scale)))
+        err = np.abs(out[b] - ref).max()
+        assert err <= tol, f"seq {b}: oracle vs sdpa {err:.3e}"
+
+
+def _dequant_exact(rows_bits):
+    """[H, D] bfloat16 rows -> float64 values after the exact-rational row contract."""
+    xs = _bf16_f64(rows_bits)
+    res = np.zeros_like(xs)
+    for h in range(xs.shape[0]):
+        codes, s, z = quantize_row_exact(xs[h].tolist())
+        res[h] = [float(s * c + z) for c in codes]
+    return res
+
+
+def pin_special_cases():
+    rng = np.random.default_rng(7)
+    D, n = 64, 21
+    V = rng.standard_normal((1, n, D))
+    K = rng.standard_normal((1, n, D))
+    q = rng.standard_normal((2, D))
+    # one token: the output is that token's V row, exactly
+    o = oracle.attend(q, K[:, :1], V[:, :1], 0.125)
+    assert np.array_equal(o, np.repeat(V[:, 0], 2, axis=0))
+    # zero query or identical keys: uniform weights, the mean of V
+    o = oracle.attend(np.zeros((2, D)), K, V, 0.125)
+    assert np.allclose(o, V[0].mean(axis=0), rtol=0, atol=1e-14)
+    Keq = np.repeat(K[:, :1], n, axis=1)
+    o = oracle.attend(q, Keq, V, 0.125)
+    assert np.allclose(o, V[0].mean(axis=0), rtol=0, atol=1e-14)
+    # empty context: zero
+    o = oracle.attend(q, K[:, :0], V[:, :0], 0.125)
+    assert np.array_equal(o, np.zeros((2, D)))
+
+
+def pin_page_relabel_invariance(case, seed=11):
+    """Relabelling physical pages leaves every output bit unchanged."""
+    lay = layout_of(case)
+    k, v, km, vm = oracle_pools(case)
+    out = oracle.paged_decode(lay, case.q, k, v, km, vm, case.block_tables, case.ctx,
+                              case.scale)
+    perm = np.random.default_rng(seed).permutation(case.num_pages)
+    c = case.cfg
+    per_page = c.num_kv_heads * c.page_size * c.head_dim
+
+    def relabel(a, n):
+        if a is None:
+            return None
+        src = a.reshape(case.num_pages, n)
+        dst = np.empty_like(src)
+        dst[perm] = src
+        return dst.reshape(-1)
+
+    bt = np.where(case.block_tables >= 0, perm[np.maximum(case.block_tables, 0)], -1)
+    meta_n = c.num_kv_heads * c.page_size * 2
+    out2 = oracle.paged_decode(lay, case.q, relabel(k, per_page), relabel(v, per_page),
+                               relabel(km, meta_n), relabel(vm, meta_n), bt, case.ctx,
+                               case.scale)
+    assert np.array_equal(out, out2)
+
+
+# ---------------------------------------------------------------- quantization
+def _quant_rows_for_pins():
+    rng = np.random.default_rng(3)
+    rows = [rng.standard_normal(64).astype(np.float32) for _ in range(40)]
+    x = rng.standard_normal(64).astype(np.float32)
+    x[[3, 17]] *= 8
+    rows.append(x)
+    rows.append(np.full(64, 0.375, np.float32))               # constant row
+    rows.append(np.linspace(-1e-6, 1e-6, 64).astype(np.float32))  # tiny range
+    rows.append((rng.standard_normal(64) * 300).astype(np.float32))  # wide range
+    rows.append((rng.standard_normal(64) + 40).astype(np.float32))   # offset row
+    return [f32_to_bf16_bits(r) for r in rows]
+
+
+def pin_quantize_exact_rational():
+    """The float32/float16 pipeline equals the exact-rational IEEE model, bit for bit."""
+    for bits in _quant_rows_for_pins():
+        codes, s16, z16 = oq.quantize_rows(bits[None, :])
+        xs = [Fraction(float(v)) for v in _bf16_f64(bits)]
+        ecodes, es, ez = quantize_row_exact(xs)
+        assert codes[0].tolist() == ecodes
+        assert Fraction(float(s16.view(np.float16)[0])) == es
+        assert Fraction(float(z16.view(np.float16)[0])) == ez
+
+
+def pin_quantize_ties_and_grid():
+    # mn = -127, mx = 127: z = 0, s = 1, codes = x rounded half to even
+    x = np.zeros(16, np.float32)
+    x[:8] = [-127, 127, 2.5, 3.5, -2.5, -0.5, 0.5, 1.5]
+    codes, s16, z16 = oq.quantize_rows(f32_to_bf16_bits(x)[None])
+    assert s16.view(np.float16)[0] == 1.0 and z16.view(np.float16)[0] == 0.0
+    assert codes[0, :8].tolist() == [-127, 127, 2, 4, -2, 0, 0, 2]
+    # a row already on the grid of its own scale comes back exactly
+    grid = np.arange(-127, 128, 17, dtype=np.float32)
+    grid = np.concatenate([grid, [-127.0, 127.0]]).astype(np.float32)
+    codes, s16, z16 = oq.quantize_rows(f32_to_bf16_bits(grid)[None])
+    back = oq.dequantize(codes, s16, z16)[0]
+    assert np.array_equal(back, grid.astype(np.float64))
+    # a constant row: codes 0, value recovered exactly
+    c = np.full(32, -0.71875, np.float32)
+    codes, s16, z16 = oq.quantize_rows(f32_to_bf16_bits(c)[None])
+    assert (codes == 0).all()
+    assert np.array_equal(oq.dequantize(codes, s16, z16)[0], c.astype(np.float64))
+
+
+def pin_quantize_round_trip(rows_bits):
+    """|x - (s*code + z)| <= s * (1/2 + 2^-15) on normal-like rows (so no code clamps)."""
+    codes, s16, z16 = oq.quantize_rows(rows_bits)
+    x = _bf16_f64(rows_bits)
+    back = oq.dequantize(codes, s16, z16)
+    s = s16.view(np.float16).astype(np.float64)[..., None]
+    assert (np.abs(x - back) <= s * (0.5 + 2.0 ** -15)).all()
+
+
+# ---------------------------------------------------------------- closed forms
+def pin_memory_closed_forms():
+    g = _golden("memory_closed_forms.json")
+    e = g["llama3_70b"]
+    one = oracle.kv_bytes(e["layers"], e["kv_heads"], e["head_dim"], e["tokens"],
+                          e["elem_bytes"])
+    assert one == e["bytes_printed"]
+    assert one * e["batch"] == 85_899_345_920
+    # the printed 85.7 GB is 2.68 GB (rounded first) x 32 = 85.76, cut to one decimal
+    assert int(round(one / 1e9, 2) * e["batch"] * 10) / 10 == e["batch_gb_printed"]
+    q = g["gqa_llama2_70b"]
+    assert 1 / oracle.gqa_ratio(q["kv_groups"], q["q_heads"]) == q["reduction_printed"]
+    assert q["reduction_printed"] * q["int4_reduction_printed"] == q["int4_times_gqa_printed"]
+    x3 = g["exercise3"]
+    L, H, D, T = x3["layers"], x3["heads"], x3["head_dim"], x3["tokens"]
+    assert oracle.kv_bytes(L, H, D, T, 2) == x3["fp16_bytes"]
+    assert oracle.kv_bytes(L, H, D, T, 1) == x3["int8_bytes"]
+    assert oracle.kv_bytes(L, 4, D, T, 0.5) == x3["int4_gqa4_bytes"]
+    assert oracle.kv_bytes(L, H, D, T, 2) / oracle.kv_bytes(L, H, D, T, 1) == \
+        q["int8_reduction_printed"]
+    p = g["prefix_l81"]
+    c = 1.0
+    saved = oracle.paged_bytes(p["requests"], 2500, c) - \
+        oracle.prefix_cached_bytes(p["requests"], 2500, p["shared"], c)
+    assert saved == (p["requests"] - 1) * p["shared"] * c
+    assert saved + p["shared"] * c == p["savings_printed_in_units_of_c"]
+    x1 = g["exercise1"]
+    worst = max(oracle.waste(n, x1["page_size"]) for n in range(1, 4 * x1["page_size"] + 1))
+    assert worst == x1["max_waste_tokens"]
+    assert x1["static_max_tokens"] - 1 == x1["static_max_waste_tokens"]
+
+
+def pin_waste_bound(case):
+    """Paging wastes at most P-1 slots per sequence ("PagedAttention" section)."""
+    P = case.cfg.page_size
+    for n in case.ctx:
+        n = int(n)
+        a = oracle.alloc_tokens(n, P)
+        assert a % P == 0 and a >= n and a - P < n
+        w = oracle.waste(n, P)
+        assert 0 <= w <= P - 1 and (n + w) % P == 0
+
+
+def pin_shared_prefix_memory():
+    """Unique bytes of the shared-prefix workload equal eq. 2's prefix-cached value."""
+    from workloads import SHARED_PREFIX_MQA as cfg
+    case = make_case(cfg, with_data=False)
+    c = oracle.bytes_per_token(1, cfg.num_kv_heads, cfg.head_dim, 2)
+    assert c == 512
+    pages = np.unique(case.block_tables[case.block_tables >= 0])
+    assert pages.size == 125 + 100 * 32 == 3325
+    unique_tokens = cfg.shared_prefix + int((case.ctx - cfg.shared_prefix).sum())
+    assert unique_tokens * c == oracle.prefix_cached_bytes(cfg.batch, 2500, cfg.shared_prefix, c) \
+        == 26_624_000
+    saved = oracle.paged_bytes(cfg.batch, 2500, c) - unique_tokens * c
+    assert saved == 101_376_000
+    slots = pages.size * cfg.page_size
+    assert slots - unique_tokens == 1200
+    # only each sequence's own last page has empty slots
+    assert sum(oracle.waste(int(n), cfg.page_size) for n in case.ctx) == 1200
