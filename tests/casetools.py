@@ -53,21 +53,33 @@ def oracle_pools(case: DecodeCase, with_new: bool = True):
 
 
 def compare_outputs(out_bf16_bits: np.ndarray, ref_f64: np.ndarray):
-    """(max_abs, rel_l2, worst index) of bfloat16 outputs against float64."""
+    """(max_abs, rel_l2, worst index, max_ulps_big) of bfloat16 outputs against float64.
+
+    bfloat16 keeps 8 significant bits, so an output of magnitude >= 4 is stored
+    with a rounding step of at least 1/32: no bfloat16 result can be within
+    1e-2 of it in general.  max_abs is therefore taken over outputs with
+    |ref| < 4, and outputs with |ref| >= 4 are measured in bfloat16 ulps of
+    their magnitude (max_ulps_big).  rel_l2 covers every output."""
     got = (np.asarray(out_bf16_bits, dtype=np.uint16).astype(np.uint32) << 16) \
         .view(np.float32).astype(np.float64)
-    d = got - ref_f64
     if not np.isfinite(got).all():
-        return float("inf"), float("inf"), None
-    max_abs = float(np.abs(d).max()) if d.size else 0.0
+        return float("inf"), float("inf"), None, float("inf")
+    d = np.abs(got - ref_f64)
+    big = np.abs(ref_f64) >= 4.0
+    small_d = np.where(big, 0.0, d)
+    max_abs = float(small_d.max()) if d.size else 0.0
     den = float(np.linalg.norm(ref_f64))
-    rel = float(np.linalg.norm(d) / den) if den > 0 else float(np.linalg.norm(d))
-    worst = np.unravel_index(int(np.abs(d).argmax()), d.shape) if d.size else None
-    return max_abs, rel, worst
+    rel = float(np.linalg.norm(got - ref_f64) / den) if den > 0 else float(np.linalg.norm(d))
+    worst = np.unravel_index(int(small_d.argmax()), d.shape) if d.size else None
+    max_ulps = 0.0
+    if big.any():
+        ulp = np.exp2(np.floor(np.log2(np.abs(ref_f64[big]))) - 7)
+        max_ulps = float((d[big] / ulp).max())
+    return max_abs, rel, worst, max_ulps
 
 
 def assert_close(out_bf16_bits, ref_f64, what=""):
-    max_abs, rel, worst = compare_outputs(out_bf16_bits, ref_f64)
-    assert max_abs <= MAX_ABS_TOL and rel <= REL_L2_TOL, \
-        f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} worst={worst}"
+    max_abs, rel, worst, ulps = compare_outputs(out_bf16_bits, ref_f64)
+    assert max_abs <= MAX_ABS_TOL and rel <= REL_L2_TOL and ulps <= 1.0, \
+        f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} worst={worst} big_ulps={ulps:.2f}"
     return max_abs, rel
