@@ -1,0 +1,235 @@
+"""Paged KV cache and paged decode attention for AMD MI355X (gfx950).
+
+A thin Python binding over libkvp.so, whose C ABI (include/kvp.h) holds the
+whole path: the host page pool, kv_append and paged_attention_decode with
+their HIP kernels.  The functions below carry the C entry points' names and
+only marshal arguments: torch tensors supply device pointers and the current
+HIP stream.  There is no fallback: if libkvp.so is missing, import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+
+from . import _lib
+from ._lib import DecodePlan, PoolDesc
+
+_L = _lib.load()
+
+KVP_OK, KVP_E_INVAL, KVP_E_NOPAGES, KVP_E_UNSUPPORTED, KVP_E_HIP = range(5)
+KVP_BF16, KVP_INT8 = 0, 1
+_DTYPES = {"bf16": KVP_BF16, "int8": KVP_INT8}
+
+
+class KvpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {kvp_status_string(status)} (status {status})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != KVP_OK:
+        raise KvpError(status, where)
+
+
+def kvp_status_string(status: int) -> str:
+    return _L.kvp_status_string(status).decode()
+
+
+def make_desc(num_pages: int, page_size: int, num_kv_heads: int, head_dim: int,
+              dtype="bf16") -> PoolDesc:
+    return PoolDesc(num_pages, page_size, num_kv_heads, head_dim,
+                    _DTYPES.get(dtype, dtype) if isinstance(dtype, str) else int(dtype))
+
+
+class Pool:
+    """Owner of one host pool object (kvp_pool_create / kvp_pool_destroy)."""
+
+    def __init__(self, handle: int, desc: PoolDesc):
+        self.handle = ctypes.c_void_p(handle)
+        self.desc = desc
+
+    @property
+    def dtype(self) -> str:
+        return "int8" if self.desc.dtype == KVP_INT8 else "bf16"
+
+    def close(self) -> None:
+        if self.handle:
+            _L.kvp_pool_destroy(self.handle)
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---- host pool ------------------------------------------------------------------
+def kvp_pool_bytes(desc: PoolDesc):
+    kv, meta = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(_L.kvp_pool_bytes(ctypes.byref(desc), ctypes.byref(kv), ctypes.byref(meta)),
+           "kvp_pool_bytes")
+    return kv.value, meta.value
+
+
+def kvp_pool_create(desc: PoolDesc) -> Pool:
+    h = ctypes.c_void_p()
+    _check(_L.kvp_pool_create(ctypes.byref(desc), ctypes.byref(h)), "kvp_pool_create")
+    return Pool(h.value, desc)
+
+
+def kvp_pool_destroy(pool: Pool) -> None:
+    pool.close()
+
+
+def kvp_pool_get_desc(pool: Pool) -> PoolDesc:
+    d = PoolDesc()
+    _check(_L.kvp_pool_get_desc(pool.handle, ctypes.byref(d)), "kvp_pool_get_desc")
+    return d
+
+
+def kvp_pool_free_count(pool: Pool) -> int:
+    return int(_L.kvp_pool_free_count(pool.handle))
+
+
+def kvp_pool_refcount(pool: Pool, page: int) -> int:
+    return int(_L.kvp_pool_refcount(pool.handle, int(page)))
+
+
+def _i32(a) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype != np.int32 or not a.flags.c_contiguous:
+        raise ValueError("expected a C-contiguous int32 array")
+    return a
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_lib.P_int32)
+
+
+def kvp_pages_alloc(pool: Pool, n: int) -> np.ndarray:
+    out = np.empty(int(n), dtype=np.int32)
+    _check(_L.kvp_pages_alloc(pool.handle, int(n), _ptr(out)), "kvp_pages_alloc")
+    return out
+
+
+def kvp_pages_ref(pool: Pool, ids) -> None:
+    ids = _i32(np.ascontiguousarray(ids, dtype=np.int32))
+    _check(_L.kvp_pages_ref(pool.handle, ids.size, _ptr(ids)), "kvp_pages_ref")
+
+
+def kvp_pages_free(pool: Pool, ids) -> None:
+    ids = _i32(np.ascontiguousarray(ids, dtype=np.int32))
+    _check(_L.kvp_pages_free(pool.handle, ids.size, _ptr(ids)), "kvp_pages_free")
+
+
+def kvp_seq_grow(pool: Pool, row: np.ndarray, cur_len: int, new_len: int) -> None:
+    """Allocate pages so that ``row`` (int32 host array, edited in place) covers new_len."""
+    row = _i32(row)
+    _check(_L.kvp_seq_grow(pool.handle, _ptr(row), row.size, int(cur_len), int(new_len)),
+           "kvp_seq_grow")
+
+
+def kvp_seq_share(pool: Pool, src_row: np.ndarray, dst_row: np.ndarray, n_blocks: int) -> None:
+    src_row, dst_row = _i32(src_row), _i32(dst_row)
+    if n_blocks > min(src_row.size, dst_row.size):
+        raise ValueError("n_blocks exceeds a row")
+    _check(_L.kvp_seq_share(pool.handle, _ptr(src_row), _ptr(dst_row), int(n_blocks)),
+           "kvp_seq_share")
+
+
+def kvp_seq_release(pool: Pool, row: np.ndarray, n_blocks: int) -> None:
+    row = _i32(row)
+    if n_blocks > row.size:
+        raise ValueError("n_blocks exceeds the row")
+    _check(_L.kvp_seq_release(pool.handle, _ptr(row), int(n_blocks)), "kvp_seq_release")
+
+
+def kvp_decode_plan(desc: PoolDesc, num_seqs: int, num_q_heads: int, max_context_len: int,
+                    num_splits_req: int = 0, num_cus: int = 256) -> dict:
+    p = DecodePlan()
+    _check(_L.kvp_decode_plan(ctypes.byref(desc), int(num_seqs), int(num_q_heads),
+                              int(max_context_len), int(num_splits_req), int(num_cus),
+                              ctypes.byref(p)), "kvp_decode_plan")
+    return {"num_splits": p.num_splits, "pages_per_split": p.pages_per_split,
+            "waves_per_group": p.waves_per_group, "use_mfma": bool(p.use_mfma),
+            "workspace_bytes": int(p.workspace_bytes)}
+
+
+# ---- device entry points ------------------------------------------------------------
+def _dev(t, name, elem_size=None):
+    """Device pointer of a contiguous CUDA/HIP tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if elem_size is not None and t.element_size() != elem_size:
+        raise ValueError(f"{name} must have {elem_size}-byte elements")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def kvp_kv_append(pool: Pool, k_pool, v_pool, k_meta, v_meta, k_new, v_new, seq_idx, pos,
+                  block_tables, stream=None) -> None:
+    """Write k_new/v_new [N, H_kv, D] (bf16) into the slots the tables name."""
+    eb = 1 if pool.desc.dtype == KVP_INT8 else 2
+    n = int(seq_idx.numel())
+    if pos.numel() != n or k_new.shape[0] != n or v_new.shape[0] != n:
+        raise ValueError("seq_idx, pos, k_new and v_new must agree in length")
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [num_seqs, max_blocks]")
+    _check(_L.kvp_kv_append(pool.handle, _dev(k_pool, "k_pool", eb), _dev(v_pool, "v_pool", eb),
+                            _dev(k_meta, "k_meta", 2), _dev(v_meta, "v_meta", 2),
+                            _dev(k_new, "k_new", 2), _dev(v_new, "v_new", 2),
+                            _dev(seq_idx, "seq_idx", 4), _dev(pos, "pos", 4), n,
+                            _dev(block_tables, "block_tables", 4), int(block_tables.shape[0]),
+                            int(block_tables.shape[1]), _stream(stream)), "kvp_kv_append")
+
+
+def kvp_decode_workspace_bytes(pool: Pool, num_seqs: int, num_q_heads: int,
+                               max_context_len: int, num_splits_req: int = 0) -> int:
+    b = ctypes.c_size_t()
+    _check(_L.kvp_decode_workspace_bytes(pool.handle, int(num_seqs), int(num_q_heads),
+                                         int(max_context_len), int(num_splits_req),
+                                         ctypes.byref(b)), "kvp_decode_workspace_bytes")
+    return int(b.value)
+
+
+def kvp_paged_attention_decode(pool: Pool, q, k_pool, v_pool, k_meta, v_meta, block_tables,
+                               context_lens, max_context_len: int, scale: float, out,
+                               num_splits_req: int = 0, workspace=None,
+                               stream=None) -> None:
+    """out[b, j] = softmax(scale * q[b, j] K_b^T) V_b over the sequence's pages."""
+    eb = 1 if pool.desc.dtype == KVP_INT8 else 2
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables/context_lens must cover the batch")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_L.kvp_paged_attention_decode(
+        pool.handle, _dev(q, "q", 2), _dev(k_pool, "k_pool", eb), _dev(v_pool, "v_pool", eb),
+        _dev(k_meta, "k_meta", 2), _dev(v_meta, "v_meta", 2), _dev(block_tables, "block_tables", 4),
+        int(block_tables.shape[1]), _dev(context_lens, "context_lens", 4), B, Hq,
+        int(max_context_len), float(scale), _dev(out, "out", 2), int(num_splits_req),
+        _dev(workspace, "workspace"), ws_bytes, _stream(stream)), "kvp_paged_attention_decode")
+
+
+__all__ = [
+    "KVP_OK", "KVP_E_INVAL", "KVP_E_NOPAGES", "KVP_E_UNSUPPORTED", "KVP_E_HIP", "KVP_BF16",
+    "KVP_INT8", "KvpError", "Pool", "PoolDesc", "make_desc", "kvp_status_string",
+    "kvp_pool_bytes", "kvp_pool_create", "kvp_pool_destroy", "kvp_pool_get_desc",
+    "kvp_pool_free_count", "kvp_pool_refcount", "kvp_pages_alloc", "kvp_pages_ref",
+    "kvp_pages_free", "kvp_seq_grow", "kvp_seq_share", "kvp_seq_release", "kvp_decode_plan",
+    "kvp_kv_append", "kvp_decode_workspace_bytes", "kvp_paged_attention_decode",
+]

@@ -1,0 +1,74 @@
+"""ctypes loader and prototypes for libkvp.so (the C ABI in include/kvp.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvp.so")
+
+c_int32 = ctypes.c_int32
+c_size_t = ctypes.c_size_t
+c_void_p = ctypes.c_void_p
+c_float = ctypes.c_float
+P_int32 = ctypes.POINTER(ctypes.c_int32)
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("num_pages", c_int32), ("page_size", c_int32), ("num_kv_heads", c_int32),
+                ("head_dim", c_int32), ("dtype", c_int32)]
+
+
+class DecodePlan(ctypes.Structure):
+    _fields_ = [("num_splits", c_int32), ("pages_per_split", c_int32),
+                ("waves_per_group", c_int32), ("use_mfma", c_int32),
+                ("workspace_bytes", c_size_t)]
+
+
+# name -> (restype, argtypes); every symbol include/kvp.h declares
+PROTOTYPES = {
+    "kvp_status_string": (ctypes.c_char_p, [c_int32]),
+    "kvp_pool_bytes": (c_int32, [ctypes.POINTER(PoolDesc), ctypes.POINTER(c_size_t),
+                                 ctypes.POINTER(c_size_t)]),
+    "kvp_pool_create": (c_int32, [ctypes.POINTER(PoolDesc), ctypes.POINTER(c_void_p)]),
+    "kvp_pool_destroy": (None, [c_void_p]),
+    "kvp_pool_get_desc": (c_int32, [c_void_p, ctypes.POINTER(PoolDesc)]),
+    "kvp_pool_free_count": (c_int32, [c_void_p]),
+    "kvp_pool_refcount": (c_int32, [c_void_p, c_int32]),
+    "kvp_pages_alloc": (c_int32, [c_void_p, c_int32, P_int32]),
+    "kvp_pages_ref": (c_int32, [c_void_p, c_int32, P_int32]),
+    "kvp_pages_free": (c_int32, [c_void_p, c_int32, P_int32]),
+    "kvp_seq_grow": (c_int32, [c_void_p, P_int32, c_int32, c_int32, c_int32]),
+    "kvp_seq_share": (c_int32, [c_void_p, P_int32, P_int32, c_int32]),
+    "kvp_seq_release": (c_int32, [c_void_p, P_int32, c_int32]),
+    "kvp_kv_append": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32,
+                                c_void_p]),
+    "kvp_decode_plan": (c_int32, [ctypes.POINTER(PoolDesc), c_int32, c_int32, c_int32, c_int32,
+                                  c_int32, ctypes.POINTER(DecodePlan)]),
+    "kvp_decode_workspace_bytes": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                             ctypes.POINTER(c_size_t)]),
+    "kvp_paged_attention_decode": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                             c_void_p, c_void_p, c_int32, c_void_p, c_int32,
+                                             c_int32, c_int32, c_float, c_void_p, c_int32,
+                                             c_void_p, c_size_t, c_void_p]),
+}
+
+_lib = None
+
+
+def load():
+    """Load libkvp.so once; raise if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing; build it with "
+                          "`python -m paged_kv_cache_465_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in PROTOTYPES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib

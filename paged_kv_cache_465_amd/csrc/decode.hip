@@ -1,0 +1,855 @@
+// Paged decode attention for gfx950.
+//
+// "KV-Cache Optimization Techniques", section "PagedAttention", eq. 1: the new
+// query token of a sequence attends over the K/V rows of its pages, gathered
+// in logical order through the sequence's page table:
+//   out_j = softmax(scale * q_j K^T) V,  query head j reading KV head j / g
+// (section "Multi-Query and Grouped-Query Caching", eq. 7).  INT8 pools hold
+// codes with a per-token scale and zero point (section "KV-Cache
+// Quantization", eq. 3), dequantized here: q.k = s*(q.c) + z*sum(q) and
+// sum_t p_t v_t = sum_t (p_t s_t) c_t + sum_t p_t z_t.
+//
+// Work decomposition.  A workgroup owns one (sequence, KV head) pair and one
+// range of logical blocks (a split); its W wavefronts each stream a
+// contiguous share of those pages with a register ring of DEPTH pages in
+// flight, keep an online softmax in float32 (running max m, running sum l,
+// rescaled accumulator), and merge in LDS at the end.  With several splits
+// the merged partials (o, m, l) go to a workspace and merge_kernel combines
+// them by log-sum-exp.  Scores live in log2 units (scale * log2 e folded in)
+// so every exponential is one v_exp_f32.
+//
+// Matrix-core path (g >= 4): per 16-token sub-tile, S^T = K q^T on
+// v_mfma_f32_16x16x32 (K rows are the A operand, loaded straight from HBM
+// with 16-byte loads: each lane holds 8 channels of one token), then
+// O^T += V^T P^T on v_mfma_f32_16x16x16 (P = 16) or 16x16x32 (P = 32).  The
+// S^T accumulator layout (lane: head l%16, tokens 4*(l/16)..+3) is exactly the
+// B-operand layout P^T needs, and the O^T accumulator keeps head l%16 in the
+// same lane, so the whole online softmax is lane-local except the max over
+// tokens (two cross-lane steps).  V is stored transposed per (page, head) so
+// each lane's V^T operand is one contiguous load.  Query heads are padded to
+// 16 per tile; NT tiles cover g up to 16*NT.
+//
+// Vector-ALU path (g < 4): four lanes per token row split the channels for
+// the dot products; probabilities are broadcast through LDS for P.V.
+#include <algorithm>
+#include <cmath>
+#include <type_traits>
+
+#include "device_common.h"
+#include "kvp.h"
+
+namespace kvp {
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const void* k_pool;
+  const void* v_pool;
+  const uint16_t* k_meta;
+  const uint16_t* v_meta;
+  const int32_t* bt;
+  const int32_t* ctx_lens;
+  uint16_t* out;
+  float* part_o;
+  float* part_ml;
+  int32_t max_blocks, num_kv_heads, num_q_heads, group, num_pages, num_splits, pages_per_split;
+  int32_t ctx_cap;
+  float scale_log2;  // scale * log2(e)
+};
+
+struct WorkRange {
+  int b, h, s, ctx, kb0, cnt;
+};
+
+// Which (sequence, KV head, split) this workgroup owns and which contiguous
+// run of logical blocks [kb0, kb0 + cnt) wave `wave` streams.
+template <int P>
+__device__ __forceinline__ WorkRange work_range(const DecodeArgs& a, int wave, int W) {
+  WorkRange w;
+  int item = blockIdx.x;
+  w.s = item % a.num_splits;
+  item /= a.num_splits;
+  w.h = item % a.num_kv_heads;
+  w.b = item / a.num_kv_heads;
+  int ctx = a.ctx_lens[w.b];
+  ctx = min(max(ctx, 0), a.ctx_cap);
+  w.ctx = ctx;
+  const int nblk = (ctx + P - 1) / P;
+  const int blk0 = w.s * a.pages_per_split;
+  const int blk1 = min(blk0 + a.pages_per_split, nblk);
+  const int n = max(blk1 - blk0, 0);
+  const int cw = (n + W - 1) / W;
+  w.kb0 = blk0 + wave * cw;
+  w.cnt = max(0, min(cw, blk1 - w.kb0));
+  return w;
+}
+
+// Merge the W wavefronts' (m, l, o) partials held in LDS and store either the
+// final bfloat16 output (one split) or this split's normalized partial.
+template <int D>
+__device__ __forceinline__ void combine_and_store(const DecodeArgs& a, const WorkRange& wr,
+                                                  const float* sm_o, const float* sm_m,
+                                                  const float* sm_l, int W, int HP) {
+  const int g = a.group;
+  for (int e = threadIdx.x; e < g * D; e += blockDim.x) {
+    const int j = e / D, d = e - j * D;
+    float M = -INFINITY;
+    for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w * HP + j]);
+    float L = 0.0f, O = 0.0f;
+    if (M != -INFINITY) {
+      for (int w = 0; w < W; ++w) {
+        const float mw = sm_m[w * HP + j];
+        if (mw != -INFINITY) {
+          const float f = fast_exp2(mw - M);
+          L += sm_l[w * HP + j] * f;
+          O += sm_o[(w * g + j) * D + d] * f;
+        }
+      }
+    }
+    const float res = L > 0.0f ? O / L : 0.0f;
+    const int64_t row = int64_t(wr.b) * a.num_q_heads + int64_t(wr.h) * g + j;
+    if (a.num_splits == 1) {
+      a.out[row * D + d] = f32_to_bf16_rne(res);
+    } else {
+      const int64_t pr = row * a.num_splits + wr.s;
+      a.part_o[pr * D + d] = res;
+      if (d == 0) {
+        a.part_ml[pr * 2] = M;
+        a.part_ml[pr * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core kernel.
+template <bool INT8, int P, int D>
+struct MfmaShape {
+  static constexpr int T = P / 16;          // 16-token sub-tiles per page
+  static constexpr int KK = D / 32;         // 16x16x32 steps over the head dim
+  static constexpr int NC = D / 16;         // 16-channel output chunks
+  static constexpr int EV = 4 * T;          // tokens per lane in P.V
+  static constexpr int EB = INT8 ? 1 : 2;   // bytes per stored element
+  static constexpr int KL = INT8 ? D / 64 : KK;  // 16-byte K loads per lane per sub-tile
+  static constexpr int VB = EV * EB;        // bytes per lane per V^T chunk
+};
+
+template <int BYTES> struct LoadT;
+template <> struct LoadT<4> { using type = uint32_t; };
+template <> struct LoadT<8> { using type = uint2; };
+template <> struct LoadT<16> { using type = uint4; };
+
+template <bool INT8, int P, int D>
+struct PageRegs {
+  using S = MfmaShape<INT8, P, D>;
+  uint4 k[S::T][S::KL];
+  typename LoadT<S::VB>::type v[S::NC];
+  uint4 km[INT8 ? S::T : 1];
+  uint4 vm[INT8 ? S::T : 1];
+  int phys;  // page id, -1 when the table entry is out of range
+};
+
+// Largest workgroup each instance is compiled for.  Instances whose live
+// registers exceed what two waves per SIMD allow are built for 256 threads
+// (one wave per SIMD, the full register file); kvp_decode_plan applies the
+// same rule when it picks waves_per_group.
+constexpr int mfma_max_threads(int P, int D, int NT) {
+  return (NT == 4 || (NT == 2 && P == 32 && D == 128)) ? 256 : 512;
+}
+constexpr int valu_max_threads(int P, int D, int G) {
+  return (G == 3 && P == 32 && D == 128) ? 256 : 512;
+}
+
+template <bool INT8, int P, int D, int NT, int DEPTH>
+__global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel(DecodeArgs a) {
+  using S = MfmaShape<INT8, P, D>;
+  constexpr int T = S::T, KK = S::KK, NC = S::NC, EV = S::EV, EB = S::EB, KL = S::KL;
+  constexpr int HP = NT * 16;
+  using OpA = typename std::conditional<INT8, f16x8_t, bf16x8_t>::type;
+  using OpPV = typename std::conditional<
+      T == 1, typename std::conditional<INT8, f16x4_t, bf16x4_t>::type, OpA>::type;
+  using VLoad = typename LoadT<S::VB>::type;
+  extern __shared__ float smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
+  const int r = lane & 15, gq = lane >> 4;
+  const WorkRange wr = work_range<P>(a, wave, W);
+  const int g = a.group;
+  const int H = a.num_kv_heads;
+
+  // q^T as the B operand of S^T = K q^T: lane holds head nt*16 + r, 8 channels.
+  OpA qop[NT][KK];
+  float qsum[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int jj = nt * 16 + r;
+    const bool live = jj < g;
+    const uint16_t* qrow =
+        a.q + (int64_t(wr.b) * a.num_q_heads + int64_t(wr.h) * g + (live ? jj : 0)) * D;
+    float qs = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int d0 = INT8 ? (D / 4) * gq + 8 * kk : 32 * kk + 8 * gq;
+      uint4 raw = live ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
+      if constexpr (!INT8) {
+        qop[nt][kk] = __builtin_bit_cast(bf16x8_t, raw);
+      } else {
+        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+        f16x8_t v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = bf16_to_f32((w4[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+          v[e] = (_Float16)f;
+          qs += f;
+        }
+        qop[nt][kk] = v;
+      }
+    }
+    qsum[nt] = INT8 ? group4_sum(qs) : 0.0f;
+  }
+
+  // Per-lane byte offsets inside a (page, head) tile.
+  int koff[T];
+#pragma unroll
+  for (int st = 0; st < T; ++st) {
+    // sub-tile st, MFMA row r -> token; with two sub-tiles the rows are
+    // interleaved so a lane's eight P.V tokens are contiguous.
+    const int tok = (T == 1) ? r : 8 * (r >> 2) + 4 * st + (r & 3);
+    koff[st] = (tok * D + (INT8 ? (D / 4) * gq : 8 * gq)) * EB;
+  }
+  const int voff = (r * P + EV * gq) * EB;
+  const int moff = EV * gq * 4;
+
+  const size_t tile_bytes = size_t(P) * D * EB;
+  const char* kbase = static_cast<const char*>(a.k_pool);
+  const char* vbase = static_cast<const char*>(a.v_pool);
+  const int32_t* btrow = a.bt + int64_t(wr.b) * a.max_blocks;
+
+  auto issue = [&](PageRegs<INT8, P, D>& R, int k) {
+    int phys = btrow[wr.kb0 + k];
+    const bool ok = unsigned(phys) < unsigned(a.num_pages);
+    R.phys = ok ? phys : -1;
+    const int64_t tile = int64_t(ok ? phys : 0) * H + wr.h;
+    const char* kp = kbase + tile * tile_bytes;
+    const char* vp = vbase + tile * tile_bytes;
+#pragma unroll
+    for (int st = 0; st < T; ++st)
+#pragma unroll
+      for (int i = 0; i < KL; ++i)
+        R.k[st][i] = *reinterpret_cast<const uint4*>(kp + koff[st] + i * (INT8 ? 16 : 64));
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc)
+      R.v[nc] = *reinterpret_cast<const VLoad*>(vp + voff + nc * 16 * P * EB);
+    if constexpr (INT8) {
+      const char* km = reinterpret_cast<const char*>(a.k_meta) + tile * (P * 4);
+      const char* vm = reinterpret_cast<const char*>(a.v_meta) + tile * (P * 4);
+#pragma unroll
+      for (int st = 0; st < T; ++st) {
+        R.km[st] = *reinterpret_cast<const uint4*>(km + moff + st * 16);
+        R.vm[st] = *reinterpret_cast<const uint4*>(vm + moff + st * 16);
+      }
+    }
+  };
+
+  float m[NT], lsum[NT], zacc[NT];
+  f32x4_t acc[NT][NC];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m[nt] = -INFINITY;
+    lsum[nt] = 0.0f;
+    zacc[nt] = 0.0f;
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc) acc[nt][nc] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  auto compute = [&](const PageRegs<INT8, P, D>& R, int k) {
+    if (R.phys < 0) return;  // absent page: its tokens do not take part
+    const int rem = wr.ctx - (wr.kb0 + k) * P;  // valid rows in this page (>= 1)
+    const bool tail = rem < P;
+
+    // K operands for all sub-tiles (shared by every head tile).
+    OpA kop[T][KK];
+#pragma unroll
+    for (int st = 0; st < T; ++st) {
+      if constexpr (!INT8) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kop[st][kk] = __builtin_bit_cast(bf16x8_t, R.k[st][kk]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < KL; ++i) {
+          const uint32_t w4[4] = {R.k[st][i].x, R.k[st][i].y, R.k[st][i].z, R.k[st][i].w};
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            f16x2_t a0, a1, b0, b1;
+            i8x4_to_f16x4(w4[2 * half], a0, a1);
+            i8x4_to_f16x4(w4[2 * half + 1], b0, b1);
+            kop[st][2 * i + half] = f16x8_t{a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
+          }
+        }
+      }
+    }
+    // V^T operands.
+    OpPV vop[NC];
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc) {
+      if constexpr (!INT8) {
+        VLoad raw = R.v[nc];
+        if (tail) {
+          // rows past the sequence may hold anything (NaN): zero them so 0*x stays 0
+          uint32_t wv[EV / 2];
+          __builtin_memcpy(wv, &raw, sizeof(raw));
+#pragma unroll
+          for (int e = 0; e < EV; ++e) {
+            if (EV * gq + e >= rem) wv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          }
+          __builtin_memcpy(&raw, wv, sizeof(raw));
+        }
+        vop[nc] = __builtin_bit_cast(OpPV, raw);
+      } else {
+        uint32_t wv[EV / 4];
+        __builtin_memcpy(wv, &R.v[nc], sizeof(R.v[nc]));
+        OpPV v;
+#pragma unroll
+        for (int i = 0; i < EV / 4; ++i) {
+          f16x2_t lo, hi;
+          i8x4_to_f16x4(wv[i], lo, hi);
+          v[4 * i + 0] = lo[0];
+          v[4 * i + 1] = lo[1];
+          v[4 * i + 2] = hi[0];
+          v[4 * i + 3] = hi[1];
+        }
+        vop[nc] = v;
+      }
+    }
+    // Per-token scale/zero of this lane's rows (INT8).
+    float ks[T][4], kz[T][4], vs[T][4], vz[T][4];
+    if constexpr (INT8) {
+#pragma unroll
+      for (int st = 0; st < T; ++st) {
+        const uint32_t kw[4] = {R.km[st].x, R.km[st].y, R.km[st].z, R.km[st].w};
+        const uint32_t vw[4] = {R.vm[st].x, R.vm[st].y, R.vm[st].z, R.vm[st].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ks[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] & 0xffffu));
+          kz[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] >> 16));
+          vs[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(vw[i] & 0xffffu));
+          vz[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(vw[i] >> 16));
+        }
+      }
+    }
+
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float x[T][4];
+#pragma unroll
+      for (int st = 0; st < T; ++st) {
+        f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) sc = mfma_16x16x32(kop[st][kk], qop[nt][kk], sc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[st][i] = INT8 ? (ks[st][i] * sc[i] + kz[st][i] * qsum[nt]) * a.scale_log2
+                          : sc[i] * a.scale_log2;
+        }
+      }
+      if (tail) {
+#pragma unroll
+        for (int st = 0; st < T; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (EV * gq + 4 * st + i >= rem) x[st][i] = -INFINITY;
+      }
+      float mloc = x[0][0];
+#pragma unroll
+      for (int st = 0; st < T; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, x[st][i]);
+      mloc = group4_max(mloc);
+      const float mnew = fmaxf(m[nt], mloc);
+      const float al = fast_exp2(m[nt] - mnew);
+      m[nt] = mnew;
+      float p[T][4];
+      float ps = 0.0f;
+#pragma unroll
+      for (int st = 0; st < T; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[st][i] = fast_exp2(x[st][i] - mnew);
+          ps += p[st][i];
+        }
+      lsum[nt] = lsum[nt] * al + ps;
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc) acc[nt][nc] *= al;
+      OpPV pop;
+      if constexpr (INT8) {
+        float zs = 0.0f;
+#pragma unroll
+        for (int st = 0; st < T; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool valid = !tail || (EV * gq + 4 * st + i < rem);
+            const float pv = valid ? p[st][i] * vs[st][i] : 0.0f;
+            zs += valid ? p[st][i] * vz[st][i] : 0.0f;
+            pop[4 * st + i] = (_Float16)pv;
+          }
+        zacc[nt] = zacc[nt] * al + zs;
+      } else {
+#pragma unroll
+        for (int st = 0; st < T; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pop[4 * st + i] = (__bf16)p[st][i];
+      }
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc) {
+        if constexpr (T == 1)
+          acc[nt][nc] = mfma_16x16x16(vop[nc], pop, acc[nt][nc]);
+        else
+          acc[nt][nc] = mfma_16x16x32(vop[nc], pop, acc[nt][nc]);
+      }
+    }
+  };
+
+  if (wr.cnt > 0) {
+    PageRegs<INT8, P, D> ring[DEPTH];
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) issue(ring[s], min(s, wr.cnt - 1));
+    for (int k0 = 0; k0 < wr.cnt; k0 += DEPTH) {
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s) {
+        const int k = k0 + s;
+        if (k < wr.cnt) compute(ring[s], k);
+        // always refill (clamped to the last page: a cache hit, no HBM traffic)
+        // so the in-order load counter stays a compile-time pattern
+        issue(ring[s], min(k + DEPTH, wr.cnt - 1));
+      }
+    }
+  }
+
+  // Wavefront partials -> LDS.
+  float* sm_o = smem;                 // [W][g][D]
+  float* sm_m = smem + W * g * D;     // [W][HP]
+  float* sm_l = sm_m + W * HP;        // [W][HP]
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float lt = group4_sum(lsum[nt]);
+    const float zt = INT8 ? group4_sum(zacc[nt]) : 0.0f;
+    const int jj = nt * 16 + r;
+    if (jj < g) {
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc) {
+        f32x4_t v = acc[nt][nc];
+        if constexpr (INT8) v += zt;
+        *reinterpret_cast<f32x4_t*>(sm_o + (wave * g + jj) * D + 16 * nc + 4 * gq) = v;
+      }
+      if (gq == 0) {
+        sm_m[wave * HP + jj] = m[nt];
+        sm_l[wave * HP + jj] = lt;
+      }
+    }
+  }
+  __syncthreads();
+  combine_and_store<D>(a, wr, sm_o, sm_m, sm_l, W, HP);
+}
+
+// ---------------------------------------------------------------------------
+// Vector-ALU kernel for g < 4.  Lane l: token row tr = l/4 (+16 per extra
+// sub-tile), channel quarter c = l%4 for q.k; output channels l*D/64.. for P.V.
+template <bool INT8, int P, int D, int G, int DEPTH>
+__global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(DecodeArgs a) {
+  constexpr int TPL = P / 16;             // token rows per lane
+  constexpr int DQ = D / 4;               // channels per lane for q.k
+  constexpr int DV = D / 64;              // output channels per lane
+  constexpr int EB = INT8 ? 1 : 2;
+  constexpr int KL = DQ * EB / 16;        // 16-byte K loads per token row
+  constexpr int VL = DV * P * EB / 16;    // 16-byte V^T loads per lane
+  extern __shared__ float smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
+  const int tr = lane >> 2, c = lane & 3;
+  const WorkRange wr = work_range<P>(a, wave, W);
+  const int H = a.num_kv_heads;
+  float* sm_o = smem;                  // [W][G][D]
+  float* sm_m = smem + W * G * D;      // [W][G]
+  float* sm_l = sm_m + W * G;          // [W][G]
+  float* pbuf = sm_l + W * G + wave * G * P;  // this wave's [G][P] probabilities
+
+  float qf[G][DQ];
+  float qsum[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const uint16_t* qrow = a.q + (int64_t(wr.b) * a.num_q_heads + int64_t(wr.h) * G + j) * D;
+    float qs = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) {
+      qf[j][e] = bf16_to_f32(qrow[c * DQ + e]);
+      qs += qf[j][e];
+    }
+    qs += __shfl_xor(qs, 1);
+    qs += __shfl_xor(qs, 2);
+    qsum[j] = qs;
+  }
+
+  struct Regs {
+    uint4 k[TPL][KL];
+    uint4 v[VL];
+    uint32_t km[TPL], vm[TPL];
+    int phys;
+  };
+  const size_t tile_bytes = size_t(P) * D * EB;
+  const char* kbase = static_cast<const char*>(a.k_pool);
+  const char* vbase = static_cast<const char*>(a.v_pool);
+  const int32_t* btrow = a.bt + int64_t(wr.b) * a.max_blocks;
+
+  auto issue = [&](Regs& R, int k) {
+    int phys = btrow[wr.kb0 + k];
+    const bool ok = unsigned(phys) < unsigned(a.num_pages);
+    R.phys = ok ? phys : -1;
+    const int64_t tile = int64_t(ok ? phys : 0) * H + wr.h;
+    const char* kp = kbase + tile * tile_bytes;
+    const char* vp = vbase + tile * tile_bytes;
+#pragma unroll
+    for (int u = 0; u < TPL; ++u)
+#pragma unroll
+      for (int i = 0; i < KL; ++i)
+        R.k[u][i] = *reinterpret_cast<const uint4*>(kp + ((tr + 16 * u) * D + c * DQ) * EB + 16 * i);
+#pragma unroll
+    for (int i = 0; i < VL; ++i)
+      R.v[i] = *reinterpret_cast<const uint4*>(vp + (lane * DV * P) * EB + 16 * i);
+    if constexpr (INT8) {
+      const uint32_t* km = reinterpret_cast<const uint32_t*>(a.k_meta) + tile * P;
+      const uint32_t* vm = reinterpret_cast<const uint32_t*>(a.v_meta) + tile * P;
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        R.km[u] = km[tr + 16 * u];
+        R.vm[u] = vm[tr + 16 * u];
+      }
+    }
+  };
+
+  float m[G], lsum[G], zacc[G], acc[G][DV];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = -INFINITY;
+    lsum[j] = 0.0f;
+    zacc[j] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DV; ++e) acc[j][e] = 0.0f;
+  }
+
+  auto compute = [&](const Regs& R, int k) {
+    if (R.phys < 0) return;
+    const int rem = wr.ctx - (wr.kb0 + k) * P;
+    const bool tail = rem < P;
+    float x[TPL][G];
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) {
+      float kv[DQ];
+#pragma unroll
+      for (int i = 0; i < KL; ++i) {
+        const uint32_t w4[4] = {R.k[u][i].x, R.k[u][i].y, R.k[u][i].z, R.k[u][i].w};
+        if constexpr (!INT8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kv[8 * i + e] = bf16_to_f32((w4[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            kv[16 * i + e] = float(int8_t((w4[e >> 2] >> (8 * (e & 3))) & 0xffu));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float dsum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < DQ; ++e) dsum += qf[j][e] * kv[e];
+        dsum += __shfl_xor(dsum, 1);
+        dsum += __shfl_xor(dsum, 2);
+        float sc = dsum;
+        if constexpr (INT8) {
+          const float s = (float)__builtin_bit_cast(_Float16, uint16_t(R.km[u] & 0xffffu));
+          const float z = (float)__builtin_bit_cast(_Float16, uint16_t(R.km[u] >> 16));
+          sc = s * dsum + z * qsum[j];
+        }
+        x[u][j] = sc * a.scale_log2;
+        if (tail && tr + 16 * u >= rem) x[u][j] = -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float mloc = x[0][j];
+#pragma unroll
+      for (int u = 1; u < TPL; ++u) mloc = fmaxf(mloc, x[u][j]);
+      mloc = wave_max(mloc);
+      const float mnew = fmaxf(m[j], mloc);
+      const float al = fast_exp2(m[j] - mnew);
+      m[j] = mnew;
+      float ps = 0.0f, zs = 0.0f;
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        const float p = fast_exp2(x[u][j] - mnew);
+        const bool valid = !tail || tr + 16 * u < rem;
+        float pv = p;
+        if constexpr (INT8) {
+          const float vs = (float)__builtin_bit_cast(_Float16, uint16_t(R.vm[u] & 0xffffu));
+          const float vz = (float)__builtin_bit_cast(_Float16, uint16_t(R.vm[u] >> 16));
+          pv = valid ? p * vs : 0.0f;
+          zs += valid ? p * vz : 0.0f;
+        }
+        ps += p;
+        if (c == 0) pbuf[j * P + tr + 16 * u] = pv;
+      }
+      lsum[j] = lsum[j] * al + (c == 0 ? ps : 0.0f);
+      zacc[j] = zacc[j] * al + (c == 0 ? zs : 0.0f);
+#pragma unroll
+      for (int e = 0; e < DV; ++e) acc[j][e] *= al;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // P.V: this lane's output channels d = lane*DV + e over all P tokens.
+    float vv[DV][P];
+    {
+      uint32_t wv[VL * 4];
+      __builtin_memcpy(wv, R.v, sizeof(R.v));
+#pragma unroll
+      for (int e = 0; e < DV; ++e)
+#pragma unroll
+        for (int t = 0; t < P; ++t) {
+          const int idx = e * P + t;
+          float f;
+          if constexpr (!INT8)
+            f = bf16_to_f32((wv[idx >> 1] >> (16 * (idx & 1))) & 0xffffu);
+          else
+            f = float(int8_t((wv[idx >> 2] >> (8 * (idx & 3))) & 0xffu));
+          if (!INT8 && tail && t >= rem) f = 0.0f;
+          vv[e][t] = f;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+      for (int t4 = 0; t4 < P / 4; ++t4) {
+        const float4 pp = *reinterpret_cast<const float4*>(pbuf + j * P + 4 * t4);
+#pragma unroll
+        for (int e = 0; e < DV; ++e) {
+          acc[j][e] += pp.x * vv[e][4 * t4] + pp.y * vv[e][4 * t4 + 1] +
+                       pp.z * vv[e][4 * t4 + 2] + pp.w * vv[e][4 * t4 + 3];
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  if (wr.cnt > 0) {
+    Regs ring[DEPTH];
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) issue(ring[s], min(s, wr.cnt - 1));
+    for (int k0 = 0; k0 < wr.cnt; k0 += DEPTH) {
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s) {
+        const int k = k0 + s;
+        if (k < wr.cnt) compute(ring[s], k);
+        issue(ring[s], min(k + DEPTH, wr.cnt - 1));
+      }
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float lt = wave_sum_f(lsum[j]);
+    const float zt = INT8 ? wave_sum_f(zacc[j]) : 0.0f;
+#pragma unroll
+    for (int e = 0; e < DV; ++e) sm_o[(wave * G + j) * D + lane * DV + e] = acc[j][e] + zt;
+    if (lane == 0) {
+      sm_m[wave * G + j] = m[j];
+      sm_l[wave * G + j] = lt;
+    }
+  }
+  __syncthreads();
+  combine_and_store<D>(a, wr, sm_o, sm_m, sm_l, W, G);
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of the split partials: one wavefront per (sequence, query
+// head).  M = max_s m_s; w_s = l_s 2^(m_s - M); out = sum_s w_s o_s / sum_s w_s.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_ml,
+                                                    uint16_t* __restrict__ out, int rows, int S) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* ml = part_ml + int64_t(row) * S * 2;
+  float M = -INFINITY;
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
+  M = wave_max(M);
+  float o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.0f;
+  float L = 0.0f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < S; ++s) {
+      const float ms = ml[2 * s], ls = ml[2 * s + 1];
+      if (ls > 0.0f) {
+        const float w = ls * fast_exp2(ms - M);
+        L += w;
+        const float* po = part_o + (int64_t(row) * S + s) * D + lane * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] += w * po[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    out[int64_t(row) * D + lane * E + e] = f32_to_bf16_rne(L > 0.0f ? o[e] / L : 0.0f);
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+constexpr int kDepth = 2;
+
+int cu_count_current_device() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return -1;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
+template <bool INT8, int P, int D>
+hipError_t launch_decode_pd(const DecodeArgs& a, bool mfma, int g, dim3 grid, dim3 block,
+                            size_t lds, hipStream_t s) {
+  const int nt = g <= 16 ? 1 : g <= 32 ? 2 : 4;
+  const int max_threads = mfma ? mfma_max_threads(P, D, nt) : valu_max_threads(P, D, g);
+  if (int(block.x) > max_threads) return hipErrorInvalidConfiguration;
+  if (mfma) {
+    if (g <= 16)
+      hipLaunchKernelGGL((decode_mfma_kernel<INT8, P, D, 1, kDepth>), grid, block, lds, s, a);
+    else if (g <= 32)
+      hipLaunchKernelGGL((decode_mfma_kernel<INT8, P, D, 2, kDepth>), grid, block, lds, s, a);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<INT8, P, D, 4, kDepth>), grid, block, lds, s, a);
+  } else {
+    if (g == 1)
+      hipLaunchKernelGGL((decode_valu_kernel<INT8, P, D, 1, kDepth>), grid, block, lds, s, a);
+    else if (g == 2)
+      hipLaunchKernelGGL((decode_valu_kernel<INT8, P, D, 2, kDepth>), grid, block, lds, s, a);
+    else
+      hipLaunchKernelGGL((decode_valu_kernel<INT8, P, D, 3, kDepth>), grid, block, lds, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvp
+
+extern "C" kvp_status kvp_decode_workspace_bytes(const kvp_pool* pool, int32_t num_seqs,
+                                                 int32_t num_q_heads, int32_t max_context_len,
+                                                 int32_t num_splits_req, size_t* bytes) {
+  kvp_pool_desc d;
+  if (!bytes || kvp_pool_get_desc(pool, &d) != KVP_OK) return KVP_E_INVAL;
+  const int cus = kvp::cu_count_current_device();
+  if (cus <= 0) return KVP_E_HIP;
+  kvp_decode_plan_t plan;
+  const kvp_status st =
+      kvp_decode_plan(&d, num_seqs, num_q_heads, max_context_len, num_splits_req, cus, &plan);
+  if (st != KVP_OK) return st;
+  *bytes = plan.workspace_bytes;
+  return KVP_OK;
+}
+
+extern "C" kvp_status kvp_paged_attention_decode(
+    const kvp_pool* pool, const void* q, const void* k_pool, const void* v_pool,
+    const void* k_meta, const void* v_meta, const int32_t* block_tables, int32_t max_blocks,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    float scale, void* out, int32_t num_splits_req, void* workspace, size_t workspace_bytes,
+    kvp_stream_t stream) {
+  using namespace kvp;
+  kvp_pool_desc d;
+  if (kvp_pool_get_desc(pool, &d) != KVP_OK) return KVP_E_INVAL;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks <= 0) return KVP_E_INVAL;
+  if (num_q_heads % d.num_kv_heads) return KVP_E_INVAL;
+  if (int64_t(max_blocks) * d.page_size > 0x7fffffff) return KVP_E_INVAL;
+  if (max_context_len < 0 || int64_t(max_context_len) > int64_t(max_blocks) * d.page_size)
+    return KVP_E_INVAL;
+  if (!std::isfinite(scale)) return KVP_E_INVAL;
+  if (num_seqs == 0) return KVP_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return KVP_E_INVAL;
+  const bool int8 = d.dtype == KVP_INT8;
+  if (int8 != (k_meta != nullptr) || int8 != (v_meta != nullptr)) return KVP_E_INVAL;
+  const int g = num_q_heads / d.num_kv_heads;
+  const int cus = cu_count_current_device();
+  if (cus <= 0) return KVP_E_HIP;
+  kvp_decode_plan_t plan;
+  kvp_status st =
+      kvp_decode_plan(&d, num_seqs, num_q_heads, max_context_len, num_splits_req, cus, &plan);
+  if (st != KVP_OK) return st;
+  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    return KVP_E_INVAL;
+  const int64_t wgs = int64_t(num_seqs) * d.num_kv_heads * plan.num_splits;
+  if (wgs > 0x7fffffff) return KVP_E_UNSUPPORTED;
+
+  DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_meta = static_cast<const uint16_t*>(k_meta);
+  a.v_meta = static_cast<const uint16_t*>(v_meta);
+  a.bt = block_tables;
+  a.ctx_lens = context_lens;
+  a.out = static_cast<uint16_t*>(out);
+  const size_t parts = size_t(num_seqs) * num_q_heads * plan.num_splits;
+  const size_t o_bytes = (parts * d.head_dim * sizeof(float) + 255) & ~size_t(255);
+  a.part_o = plan.num_splits > 1 ? static_cast<float*>(workspace) : nullptr;
+  a.part_ml = plan.num_splits > 1
+                  ? reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes)
+                  : nullptr;
+  a.max_blocks = max_blocks;
+  a.num_kv_heads = d.num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.group = g;
+  a.num_pages = d.num_pages;
+  a.num_splits = plan.num_splits;
+  a.pages_per_split = plan.pages_per_split;
+  a.ctx_cap = max_context_len;
+  a.scale_log2 = scale * kLog2e;
+
+  const int W = plan.waves_per_group;
+  const int HP = plan.use_mfma ? ((g + 15) / 16) * 16 : g;
+  size_t lds = size_t(W) * (size_t(g) * d.head_dim + 2 * HP) * sizeof(float);
+  if (!plan.use_mfma) lds += size_t(W) * g * d.page_size * sizeof(float);
+  const dim3 grid(static_cast<unsigned>(wgs)), block(static_cast<unsigned>(W * 64));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  const int key = (d.page_size == 32) * 4 + (d.head_dim == 128) * 2 + int8;
+  switch (key) {
+    case 0: e = launch_decode_pd<false, 16, 64>(a, plan.use_mfma, g, grid, block, lds, s); break;
+    case 1: e = launch_decode_pd<true, 16, 64>(a, plan.use_mfma, g, grid, block, lds, s); break;
+    case 2: e = launch_decode_pd<false, 16, 128>(a, plan.use_mfma, g, grid, block, lds, s); break;
+    case 3: e = launch_decode_pd<true, 16, 128>(a, plan.use_mfma, g, grid, block, lds, s); break;
+    case 4: e = launch_decode_pd<false, 32, 64>(a, plan.use_mfma, g, grid, block, lds, s); break;
+    case 5: e = launch_decode_pd<true, 32, 64>(a, plan.use_mfma, g, grid, block, lds, s); break;
+    case 6: e = launch_decode_pd<false, 32, 128>(a, plan.use_mfma, g, grid, block, lds, s); break;
+    default: e = launch_decode_pd<true, 32, 128>(a, plan.use_mfma, g, grid, block, lds, s); break;
+  }
+  if (e != hipSuccess) return KVP_E_HIP;
+  if (plan.num_splits > 1) {
+    const int rows = num_seqs * num_q_heads;
+    const dim3 mg(static_cast<unsigned>((rows + 3) / 4));
+    if (d.head_dim == 128)
+      hipLaunchKernelGGL((merge_kernel<128>), mg, dim3(256), 0, s, a.part_o, a.part_ml, a.out,
+                         rows, plan.num_splits);
+    else
+      hipLaunchKernelGGL((merge_kernel<64>), mg, dim3(256), 0, s, a.part_o, a.part_ml, a.out,
+                         rows, plan.num_splits);
+    if (hipGetLastError() != hipSuccess) return KVP_E_HIP;
+  }
+  return KVP_OK;
+}
