@@ -1,0 +1,399 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark for paged decode attention on one MI355X.
+
+One step = one new token for every sequence, through every layer: kv_append of
+the token's K/V row into the page its block table names, then paged decode
+attention (split kernel + log-sum-exp merge) over all of the sequence's pages.
+The default workload is the Llama-3-70B-shaped full cache: 80 layers, 32
+sequences of 8,192 tokens, 64 query / 8 KV heads, head_dim 128, pages of 16
+tokens, bfloat16 K/V (85,899,345,920 bytes, "Understanding KV-Cache
+Optimization in Modern LLM Serving", section "Concrete Example"), every page
+resident in HBM when the timed region starts.
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value       KV-read GB/s: algorithmic bytes of a step / wall time of a step
+  roofline    the split kernel's algorithmic bytes per launch / its mean
+              duration from HIP events inside the timed region, against 8 TB/s
+  cpu_baseline  the float64 CPU oracle on a bounded sample of the same data
+  parity      sampled outputs of the timed step against the oracle
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+    python bench.py --copy-calibration   # plain copy kernel for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD's published figure
+MALL_FLUSH_BYTES = 1 << 30      # > 256 MB Infinity Cache
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="llama3_70b_full_cache")
+    p.add_argument("--splits", type=int, default=0, help="forced split count (0 = planner)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target CPU time of the oracle sample")
+    p.add_argument("--no-parity", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain device copy of known size (for counter scaling)")
+    return p.parse_args(argv)
+
+
+# ---- algorithmic bytes -----------------------------------------------------------
+def step_bytes(cfg, ctx: np.ndarray) -> dict:
+    """Bytes a step must move at minimum, per term, summed over sequences and layers.
+
+    Per sequence of n tokens and per layer: K and V rows n*H_kv*D elements each
+    (plus one float16 (scale, zero) pair per row for INT8), the query and output
+    rows H_q*D bfloat16 each, the used block-table entries and the context
+    length (int32), and the appended row (read once, written once, K and V).
+    """
+    eb = 1 if cfg.kv_dtype == "int8" else 2
+    n = ctx.astype(np.int64)
+    Hkv, Hq, D, P, L = cfg.num_kv_heads, cfg.num_q_heads, cfg.head_dim, cfg.page_size, cfg.layers
+    kv = int((n * Hkv * 2 * D * eb).sum())
+    if cfg.kv_dtype == "int8":
+        kv += int((n * Hkv * 2 * 4).sum())
+    B = int(n.shape[0])
+    q_out = B * Hq * D * 2 * 2
+    table = int((-(-n // P) * 4).sum()) + B * 4
+    append = B * Hkv * D * 2 * 2 * (1 + eb / 2) + (B * Hkv * 2 * 4 if cfg.kv_dtype == "int8" else 0)
+    return {"kv": kv * L, "q_out": q_out * L, "table": table * L, "append": int(append) * L,
+            "split_kernel_per_launch": kv + B * Hq * D * 2 + table}
+
+
+# ---- device setup ------------------------------------------------------------------
+class Layer:
+    __slots__ = ("k", "v", "km", "vm", "q", "nk", "nv", "out")
+
+
+def setup_device(kvp, cfg, case, dev):
+    import torch
+    from workloads import history_rows_device
+
+    desc = kvp.make_desc(case.num_pages, cfg.page_size, cfg.num_kv_heads, cfg.head_dim,
+                         cfg.kv_dtype)
+    pool = kvp.kvp_pool_create(desc)
+    kv_bytes, meta_bytes = kvp.kvp_pool_bytes(desc)
+    int8 = cfg.kv_dtype == "int8"
+    bt = torch.from_numpy(case.block_tables).to(dev)
+    ctx = torch.from_numpy(case.ctx).to(dev)
+    seq_idx = torch.arange(case.B, dtype=torch.int32, device=dev)
+    new_pos = torch.from_numpy((case.ctx - 1).astype(np.int32)).to(dev)
+    layers = []
+    t0 = time.perf_counter()
+    for l in range(cfg.layers):
+        L = Layer()
+        if int8:
+            L.k = torch.empty(kv_bytes, dtype=torch.int8, device=dev)
+            L.v = torch.empty(kv_bytes, dtype=torch.int8, device=dev)
+            L.km = torch.empty(meta_bytes // 2, dtype=torch.int16, device=dev)
+            L.vm = torch.empty(meta_bytes // 2, dtype=torch.int16, device=dev)
+        else:
+            L.k = torch.empty(kv_bytes // 2, dtype=torch.int16, device=dev)
+            L.v = torch.empty(kv_bytes // 2, dtype=torch.int16, device=dev)
+            L.km = L.vm = None
+        if cfg.device_data:
+            q, hk, hv, hs, hp, nk, nv, _ = history_rows_device(cfg, case, l, dev)
+            q, hk, hv = q.view(torch.int16), hk.view(torch.int16), hv.view(torch.int16)
+            nk, nv = nk.view(torch.int16), nv.view(torch.int16)
+        else:
+            def up(a):
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+            q, hk, hv, nk, nv = up(case.q), up(case.hist_k), up(case.hist_v), up(case.new_k), \
+                up(case.new_v)
+            hs = torch.from_numpy(case.hist_seq).to(dev)
+            hp = torch.from_numpy(case.hist_pos).to(dev)
+        kvp.kvp_kv_append(pool, L.k, L.v, L.km, L.vm, hk, hv, hs, hp, bt)
+        del hk, hv, hs, hp
+        L.q, L.nk, L.nv = q, nk, nv
+        L.out = torch.empty_like(q)
+        layers.append(L)
+        if l % 10 == 9 or l == cfg.layers - 1:
+            torch.cuda.synchronize()
+            log(f"[setup] layer {l + 1}/{cfg.layers} filled ({time.perf_counter() - t0:.1f} s)")
+    torch.cuda.synchronize()
+    return pool, layers, bt, ctx, seq_idx, new_pos
+
+
+def run_gpu(args, kvp, cfg, case):
+    import torch
+    dev = torch.device("cuda:0")
+    pool, layers, bt, ctx, seq_idx, new_pos = setup_device(kvp, cfg, case, dev)
+    B, Hq, D = case.B, cfg.num_q_heads, cfg.head_dim
+    max_ctx = int(case.ctx.max())
+    S, pbytes = kvp.kvp_decode_partials_bytes(pool, B, Hq, max_ctx, args.splits)
+    plan = kvp.kvp_decode_plan(pool.desc, B, Hq, max_ctx, args.splits,
+                               torch.cuda.get_device_properties(0).multi_processor_count)
+    partials = torch.empty(max(pbytes, 4) // 4, dtype=torch.float32, device=dev) if S > 1 else None
+    scale = float(case.scale)
+    log(f"[plan] {plan}")
+
+    def one_step(probe=None):
+        """All layers once.  probe = (layer, start event, end event): that
+        layer's split kernel is bracketed by the two events."""
+        for i, L in enumerate(layers):
+            kvp.kvp_kv_append(pool, L.k, L.v, L.km, L.vm, L.nk, L.nv, seq_idx, new_pos, bt)
+            timed = probe is not None and probe[0] == i
+            if timed:
+                probe[1].record()
+            if S > 1:
+                kvp.kvp_paged_attention_decode_partials(pool, L.q, L.k, L.v, L.km, L.vm, bt, ctx,
+                                                        max_ctx, scale, partials, args.splits)
+                if timed:
+                    probe[2].record()
+                kvp.kvp_lse_merge(partials, B * Hq, S, D, L.out)
+            else:
+                kvp.kvp_paged_attention_decode(pool, L.q, L.k, L.v, L.km, L.vm, bt, ctx, max_ctx,
+                                               scale, L.out, args.splits)
+                if timed:
+                    probe[2].record()
+
+    flush = None
+    if cfg.layers == 1:
+        flush = torch.empty(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    # one layer per step (rotating) has its split kernel bracketed by events:
+    # an event pair costs a few microseconds of queue time, so bracketing
+    # every layer would inflate the step it is meant to measure
+    probes = [((k * 37) % len(layers), ev(), ev()) for k in range(args.steps)]
+    step_evs = [(ev(), ev()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = 0.0
+    if flush is None:
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            step_evs[k][0].record()
+            one_step(probes[k])
+            step_evs[k][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        # caches smaller than the Infinity Cache: evict it between steps, outside
+        # the event pair that times each step
+        for k in range(args.steps):
+            flush.fill_(float(k))
+            step_evs[k][0].record()
+            one_step(probes[k])
+            step_evs[k][1].record()
+        torch.cuda.synchronize()
+    step_ms = np.array([a.elapsed_time(b) for a, b in step_evs])
+    kern_ms = np.array([a.elapsed_time(b) for _, a, b in probes])
+    ms_per_step = wall * 1e3 / args.steps if flush is None else float(step_ms.mean())
+    log(f"[bench] ms/step wall={wall * 1e3 / max(args.steps, 1):.3f} events "
+        f"mean={step_ms.mean():.3f} min={step_ms.min():.3f}; split kernel mean "
+        f"{kern_ms.mean() * 1e3:.1f} us min {kern_ms.min() * 1e3:.1f} us")
+    res = {"ms_per_step": ms_per_step, "step_ms_events": step_ms, "kernel_ms": kern_ms,
+           "plan": plan, "num_splits": S}
+    return res, (pool, layers, bt, ctx)
+
+
+def copy_probe(dev, nbytes=1 << 32, reps=5):
+    """A plain device copy of known size: its rate, and the kernel whose
+    hardware counters scale FETCH_SIZE/WRITE_SIZE readings."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "us": ms * 1e3,
+            "GBps_read_plus_write": 2 * nbytes / (ms * 1e-3) / 1e9}
+
+
+# ---- CPU oracle leg ------------------------------------------------------------------
+def host_layer0(cfg, case, dev):
+    """Layer 0's inputs on the host, drawn exactly as the device setup draws them."""
+    if not cfg.device_data:
+        return case
+    import copy
+    from workloads import history_rows_device
+    q, hk, hv, hs, hp, nk, nv, npos = history_rows_device(cfg, case, 0, dev)
+    c = copy.copy(case)
+    h = lambda t: t.view(__import__("torch").int16).cpu().numpy().view(np.uint16)  # noqa: E731
+    c.q, c.hist_k, c.hist_v, c.new_k, c.new_v = h(q), h(hk), h(hv), h(nk), h(nv)
+    c.hist_seq, c.hist_pos = hs.cpu().numpy(), hp.cpu().numpy()
+    c.new_pos = npos.cpu().numpy()
+    return c
+
+
+def oracle_layer(cfg, hc, seqs):
+    """Oracle pools holding the rows of ``seqs`` (bfloat16 or INT8 per the config)."""
+    import oracle
+    from workloads import POISON_BF16, POISON_F16, POISON_I8
+    lay = oracle.PoolLayout(hc.num_pages, cfg.page_size, cfg.num_kv_heads, cfg.head_dim,
+                            cfg.kv_dtype)
+    k, v, km, vm = lay.empty_pools(POISON_BF16 if cfg.kv_dtype == "bf16" else POISON_I8,
+                                   POISON_F16)
+    need = set(int(s) for s in seqs) | ({0} if cfg.shared_prefix else set())
+    sel = np.isin(hc.hist_seq, list(need))
+    oracle.append(lay, k, v, km, vm, hc.hist_k[sel], hc.hist_v[sel], hc.hist_seq[sel],
+                  hc.hist_pos[sel], hc.block_tables)
+    idx = np.array(sorted(need), dtype=np.int32)
+    oracle.append(lay, k, v, km, vm, hc.new_k[idx], hc.new_v[idx], idx, hc.new_pos[idx],
+                  hc.block_tables)
+    return lay, (k, v, km, vm)
+
+
+def cpu_baseline(cfg, hc, target_s: float):
+    import oracle
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    order = list(range(hc.B))
+    # one sequence first to size the sample, then enough for ~target_s of work
+    lay, pools = oracle_layer(cfg, hc, order[:1])
+    t0 = time.perf_counter()
+    oracle.paged_decode(lay, hc.q, *pools, hc.block_tables, hc.ctx, hc.scale, seqs=order[:1])
+    t1 = time.perf_counter() - t0
+    n = int(min(hc.B, max(1, round(target_s / max(t1, 1e-6)))))
+    seqs = order[:n]
+    lay, pools = oracle_layer(cfg, hc, seqs)
+    # whole passes over the sample until about target_s of CPU time is spent
+    passes, dt = 0, 0.0
+    while passes == 0 or dt < target_s:
+        t0 = time.perf_counter()
+        oracle.paged_decode(lay, hc.q, *pools, hc.block_tables, hc.ctx, hc.scale, seqs=seqs)
+        dt += time.perf_counter() - t0
+        passes += 1
+    # bytes of the sample: one layer of the sampled sequences (same terms as the GPU)
+    sb = step_bytes(dataclasses.replace(cfg, layers=1, batch=n), hc.ctx[seqs])
+    sample_bytes = (sb["kv"] + sb["q_out"] + sb["table"]) * passes
+    gbps = sample_bytes / dt / 1e9
+    return {"value": gbps, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"layer 0, sequences 0..{n - 1} of {hc.B}, {passes} passes (float64 numpy "
+                      f"gather + attention, {dt:.1f} s); GB/s of the same algorithmic bytes",
+            "seconds": dt, "tokens_per_s_equiv": n * passes / dt / cfg.layers,
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
+              "has no multi-GPU mode in this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        r = copy_probe(dev, nbytes=1 << 30, reps=3)
+        print(json.dumps({"copy_calibration": r}))
+        return
+    import paged_kv_cache_465_amd as kvp
+    from workloads import CONFIGS, make_case
+    cfg = CONFIGS[args.config]
+    case = make_case(cfg, with_data=not cfg.device_data)
+    log(f"[config] {cfg.name}: layers={cfg.layers} B={case.B} Hq={cfg.num_q_heads} "
+        f"Hkv={cfg.num_kv_heads} D={cfg.head_dim} P={cfg.page_size} {cfg.kv_dtype} "
+        f"ctx[min,max]=[{int(case.ctx.min())},{int(case.ctx.max())}] pages={case.num_pages}")
+    sb = step_bytes(cfg, case.ctx)
+    total = sb["kv"] + sb["q_out"] + sb["table"] + sb["append"]
+    res, state = run_gpu(args, kvp, cfg, case)
+    ms = res["ms_per_step"]
+    kern_us = float(res["kernel_ms"].mean() * 1e3)
+    achieved = sb["split_kernel_per_launch"] / (kern_us * 1e-6) / 1e9
+    out = {
+        "metric": "paged decode attn: KV-read GB/s (% of HBM peak) + decode tokens/s, 1xMI355X",
+        "value": round(total / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.kv_dtype + " KV, f32 accumulate",
+        "data": "synthetic (seeded N(0,1), bf16-rounded; pages shuffled)",
+        "config": {"workload": cfg.name, "layers": cfg.layers, "batch": case.B,
+                   "context": int(case.ctx.max()) if cfg.ctx_fixed else
+                   [int(case.ctx.min()), int(case.ctx.max())],
+                   "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads,
+                   "head_dim": cfg.head_dim, "page_size": cfg.page_size,
+                   "kv_dtype": cfg.kv_dtype, "num_splits": res["num_splits"],
+                   "waves_per_group": res["plan"]["waves_per_group"]},
+        "tokens_per_s": round(case.B / (ms * 1e-3), 1),
+        "hbm_frac": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "bytes_per_step": {k: int(v) for k, v in sb.items()},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "kernel": "decode_mfma_kernel" if res["plan"]["use_mfma"]
+                     else "decode_valu_kernel",
+                     "kernel_us_mean": round(kern_us, 2),
+                     "bytes_per_launch": int(sb["split_kernel_per_launch"])},
+    }
+    # pages' own figures for this workload are analytic only: context, not a target
+    out["copy_probe"] = copy_probe(dev)
+    hc = None
+    if not (args.no_parity and args.no_cpu_baseline):
+        hc = host_layer0(cfg, case, dev)
+    if not args.no_parity:
+        out["parity"] = parity_sample(cfg, hc, state)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, hc, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def parity_sample(cfg, hc, state, seqs=(0, 13, 31)):
+    """Layer 0 output rows of the timed run for a few sequences against the oracle."""
+    import oracle
+    pool, layers, bt, ctx = state
+    seqs = [s for s in seqs if s < hc.B]
+    lay, pools = oracle_layer(cfg, hc, seqs)
+    ref = oracle.paged_decode(lay, hc.q, *pools, hc.block_tables, hc.ctx, hc.scale, seqs=seqs)
+    got_bits = layers[0].out.cpu().numpy().view(np.uint16)
+    got = (got_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    d = np.abs(got[seqs] - ref[seqs])
+    rel = float(np.linalg.norm(got[seqs] - ref[seqs]) / np.linalg.norm(ref[seqs]))
+    r = {"layer": 0, "seqs": seqs, "max_abs": float(d.max()), "rel_l2": rel,
+         "ok": bool(d.max() <= 1e-2 and rel <= 5e-3)}
+    log(f"[parity] {r}")
+    return r
+
+
+if __name__ == "__main__":
+    main()

@@ -216,6 +216,41 @@ kvp_status kvp_paged_attention_decode(const kvp_pool* pool, const void* q,
                                       void* workspace, size_t workspace_bytes,
                                       kvp_stream_t stream);
 
+/* ---- Decode in two phases (device) -----------------------------------------
+ * The same attention as kvp_paged_attention_decode, with its two kernels
+ * exposed separately: the split kernel writes one normalized partial per
+ * (sequence, query head, split) and kvp_lse_merge combines them.  A caller
+ * that spreads one sequence's pages over several devices gathers the partial
+ * buffers and merges them the same way ("KV Cache Optimization" glossary:
+ * splitting the cache across GPUs and gathering for attention).
+ *
+ * Partials buffer layout, for rows = num_seqs * H_q and S splits (row index
+ * b*H_q + j, split s):
+ *   o[row][s][D]  float32 at byte 0: sum_t p_t v_t / sum_t p_t over the split;
+ *   ml[row][s][2] float32 at byte offset align256(rows*S*D*4):
+ *       ml[..][0] = m, the largest score of the split in base-2 units
+ *                   (score * scale * log2 e); -inf when the split is empty;
+ *       ml[..][1] = l = sum_t 2^(score_t*log2e - m); 0 when the split is empty.
+ * kvp_decode_partials_bytes gives the byte size and the split count S the
+ * planner picks for these arguments (num_splits_req <= 0: automatic). */
+kvp_status kvp_decode_partials_bytes(const kvp_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t max_context_len, int32_t num_splits_req,
+                                     int32_t* num_splits, size_t* bytes);
+/* Split kernel only; every partial of the layout above is written (empty
+ * splits too).  *num_splits (may be NULL) receives S.  partials is a device
+ * buffer of at least kvp_decode_partials_bytes bytes; KVP_E_INVAL otherwise. */
+kvp_status kvp_paged_attention_decode_partials(
+    const kvp_pool* pool, const void* q, const void* k_pool, const void* v_pool,
+    const void* k_meta, const void* v_meta, const int32_t* block_tables, int32_t max_blocks,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    float scale, int32_t num_splits_req, void* partials, size_t partials_bytes,
+    int32_t* num_splits, kvp_stream_t stream);
+/* Log-sum-exp merge: out[row][:] = sum_s w_s o_s / sum_s w_s with
+ * w_s = l_s 2^(m_s - max_s m_s), rounded to bfloat16; rows whose splits are
+ * all empty give 0.  head_dim is 64 or 128; out is [rows][D] bfloat16. */
+kvp_status kvp_lse_merge(const void* partials, int32_t rows, int32_t num_splits, int32_t head_dim,
+                         void* out, kvp_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -225,6 +225,47 @@ def kvp_paged_attention_decode(pool: Pool, q, k_pool, v_pool, k_meta, v_meta, bl
         _dev(workspace, "workspace"), ws_bytes, _stream(stream)), "kvp_paged_attention_decode")
 
 
+def kvp_decode_partials_bytes(pool: Pool, num_seqs: int, num_q_heads: int,
+                              max_context_len: int, num_splits_req: int = 0):
+    """(num_splits, bytes) of the partials buffer the split kernel writes."""
+    b = ctypes.c_size_t()
+    s = ctypes.c_int32()
+    _check(_L.kvp_decode_partials_bytes(pool.handle, int(num_seqs), int(num_q_heads),
+                                        int(max_context_len), int(num_splits_req),
+                                        ctypes.byref(s), ctypes.byref(b)),
+           "kvp_decode_partials_bytes")
+    return int(s.value), int(b.value)
+
+
+def kvp_paged_attention_decode_partials(pool: Pool, q, k_pool, v_pool, k_meta, v_meta,
+                                        block_tables, context_lens, max_context_len: int,
+                                        scale: float, partials, num_splits_req: int = 0,
+                                        stream=None) -> int:
+    """Split kernel only: per-split (o, m, l) partials into ``partials``; returns S."""
+    eb = 1 if pool.desc.dtype == KVP_INT8 else 2
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables/context_lens must cover the batch")
+    nbytes = partials.numel() * partials.element_size()
+    s = ctypes.c_int32()
+    _check(_L.kvp_paged_attention_decode_partials(
+        pool.handle, _dev(q, "q", 2), _dev(k_pool, "k_pool", eb), _dev(v_pool, "v_pool", eb),
+        _dev(k_meta, "k_meta", 2), _dev(v_meta, "v_meta", 2), _dev(block_tables, "block_tables", 4),
+        int(block_tables.shape[1]), _dev(context_lens, "context_lens", 4), B, Hq,
+        int(max_context_len), float(scale), int(num_splits_req), _dev(partials, "partials"),
+        nbytes, ctypes.byref(s), _stream(stream)), "kvp_paged_attention_decode_partials")
+    return int(s.value)
+
+
+def kvp_lse_merge(partials, rows: int, num_splits: int, head_dim: int, out, stream=None) -> None:
+    """Merge per-split partials by log-sum-exp into ``out`` ([rows, D] bfloat16 bits)."""
+    if out.numel() != int(rows) * int(head_dim):
+        raise ValueError("out must hold rows * head_dim elements")
+    _check(_L.kvp_lse_merge(_dev(partials, "partials"), int(rows), int(num_splits),
+                            int(head_dim), _dev(out, "out", 2), _stream(stream)),
+           "kvp_lse_merge")
+
+
 __all__ = [
     "KVP_OK", "KVP_E_INVAL", "KVP_E_NOPAGES", "KVP_E_UNSUPPORTED", "KVP_E_HIP", "KVP_BF16",
     "KVP_INT8", "KvpError", "Pool", "PoolDesc", "make_desc", "kvp_status_string",
@@ -232,4 +273,5 @@ __all__ = [
     "kvp_pool_free_count", "kvp_pool_refcount", "kvp_pages_alloc", "kvp_pages_ref",
     "kvp_pages_free", "kvp_seq_grow", "kvp_seq_share", "kvp_seq_release", "kvp_decode_plan",
     "kvp_kv_append", "kvp_decode_workspace_bytes", "kvp_paged_attention_decode",
+    "kvp_decode_partials_bytes", "kvp_paged_attention_decode_partials", "kvp_lse_merge",
 ]

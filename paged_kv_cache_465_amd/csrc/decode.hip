@@ -53,6 +53,7 @@ struct DecodeArgs {
   float* part_ml;
   int32_t max_blocks, num_kv_heads, num_q_heads, group, num_pages, num_splits, pages_per_split;
   int32_t ctx_cap;
+  int32_t write_partials;  // 1: store (o, m, l) per split; 0: store the bf16 output
   float scale_log2;  // scale * log2(e)
 };
 
@@ -107,7 +108,7 @@ __device__ __forceinline__ void combine_and_store(const DecodeArgs& a, const Wor
     }
     const float res = L > 0.0f ? O / L : 0.0f;
     const int64_t row = int64_t(wr.b) * a.num_q_heads + int64_t(wr.h) * g + j;
-    if (a.num_splits == 1) {
+    if (!a.write_partials) {
       a.out[row * D + d] = f32_to_bf16_rne(res);
     } else {
       const int64_t pr = row * a.num_splits + wr.s;
@@ -148,16 +149,11 @@ struct PageRegs {
   int phys;  // page id, -1 when the table entry is out of range
 };
 
-// Largest workgroup each instance is compiled for.  Instances whose live
-// registers exceed what two waves per SIMD allow are built for 256 threads
-// (one wave per SIMD, the full register file); kvp_decode_plan applies the
-// same rule when it picks waves_per_group.
-constexpr int mfma_max_threads(int P, int D, int NT) {
-  return (NT == 4 || (NT == 2 && P == 32 && D == 128)) ? 256 : 512;
-}
-constexpr int valu_max_threads(int P, int D, int G) {
-  return (G == 3 && P == 32 && D == 128) ? 256 : 512;
-}
+// Largest workgroup each instance is compiled for: four wavefronts, one per
+// SIMD, which is what kvp_decode_plan asks for (fewer when the LDS merge
+// buffer of a large group would not fit).
+constexpr int mfma_max_threads(int, int, int) { return 256; }
+constexpr int valu_max_threads(int, int, int) { return 256; }
 
 template <bool INT8, int P, int D, int NT, int DEPTH>
 __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel(DecodeArgs a) {
@@ -237,17 +233,16 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
     for (int st = 0; st < T; ++st)
 #pragma unroll
       for (int i = 0; i < KL; ++i)
-        R.k[st][i] = *reinterpret_cast<const uint4*>(kp + koff[st] + i * (INT8 ? 16 : 64));
+        R.k[st][i] = load_stream<uint4>(kp + koff[st] + i * (INT8 ? 16 : 64));
 #pragma unroll
-    for (int nc = 0; nc < NC; ++nc)
-      R.v[nc] = *reinterpret_cast<const VLoad*>(vp + voff + nc * 16 * P * EB);
+    for (int nc = 0; nc < NC; ++nc) R.v[nc] = load_stream<VLoad>(vp + voff + nc * 16 * P * EB);
     if constexpr (INT8) {
       const char* km = reinterpret_cast<const char*>(a.k_meta) + tile * (P * 4);
       const char* vm = reinterpret_cast<const char*>(a.v_meta) + tile * (P * 4);
 #pragma unroll
       for (int st = 0; st < T; ++st) {
-        R.km[st] = *reinterpret_cast<const uint4*>(km + moff + st * 16);
-        R.vm[st] = *reinterpret_cast<const uint4*>(vm + moff + st * 16);
+        R.km[st] = load_stream<uint4>(km + moff + st * 16);
+        R.vm[st] = load_stream<uint4>(vm + moff + st * 16);
       }
     }
   };
@@ -514,17 +509,16 @@ __global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(
     for (int u = 0; u < TPL; ++u)
 #pragma unroll
       for (int i = 0; i < KL; ++i)
-        R.k[u][i] = *reinterpret_cast<const uint4*>(kp + ((tr + 16 * u) * D + c * DQ) * EB + 16 * i);
+        R.k[u][i] = load_stream<uint4>(kp + ((tr + 16 * u) * D + c * DQ) * EB + 16 * i);
 #pragma unroll
-    for (int i = 0; i < VL; ++i)
-      R.v[i] = *reinterpret_cast<const uint4*>(vp + (lane * DV * P) * EB + 16 * i);
+    for (int i = 0; i < VL; ++i) R.v[i] = load_stream<uint4>(vp + (lane * DV * P) * EB + 16 * i);
     if constexpr (INT8) {
       const uint32_t* km = reinterpret_cast<const uint32_t*>(a.k_meta) + tile * P;
       const uint32_t* vm = reinterpret_cast<const uint32_t*>(a.v_meta) + tile * P;
 #pragma unroll
       for (int u = 0; u < TPL; ++u) {
-        R.km[u] = km[tr + 16 * u];
-        R.vm[u] = vm[tr + 16 * u];
+        R.km[u] = load_stream<uint32_t>(km + tr + 16 * u);
+        R.vm[u] = load_stream<uint32_t>(vm + tr + 16 * u);
       }
     }
   };
@@ -750,6 +744,114 @@ hipError_t launch_decode_pd(const DecodeArgs& a, bool mfma, int g, dim3 grid, di
 
 }  // namespace kvp
 
+namespace {
+
+size_t partials_o_bytes(size_t parts, int D) {
+  return (parts * size_t(D) * sizeof(float) + 255) & ~size_t(255);
+}
+
+size_t partials_bytes(size_t parts, int D) {
+  return partials_o_bytes(parts, D) + parts * 2 * sizeof(float);
+}
+
+hipError_t launch_merge(const float* part_o, const float* part_ml, uint16_t* out, int rows, int S,
+                        int D, hipStream_t s) {
+  const dim3 mg(static_cast<unsigned>((rows + 3) / 4));
+  if (D == 128)
+    hipLaunchKernelGGL((kvp::merge_kernel<128>), mg, dim3(256), 0, s, part_o, part_ml, out, rows, S);
+  else
+    hipLaunchKernelGGL((kvp::merge_kernel<64>), mg, dim3(256), 0, s, part_o, part_ml, out, rows, S);
+  return hipGetLastError();
+}
+
+// Validate the decode arguments and fill the plan.  partials_only forces the
+// split kernel to write (o, m, l) partials even for one split.
+kvp_status prepare_decode(const kvp_pool* pool, const void* q, const void* k_pool,
+                          const void* v_pool, const void* k_meta, const void* v_meta,
+                          const int32_t* block_tables, int32_t max_blocks,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t max_context_len, float scale, int32_t num_splits_req,
+                          kvp_pool_desc* d, kvp_decode_plan_t* plan, bool* empty) {
+  *empty = false;
+  if (kvp_pool_get_desc(pool, d) != KVP_OK) return KVP_E_INVAL;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks <= 0) return KVP_E_INVAL;
+  if (num_q_heads % d->num_kv_heads) return KVP_E_INVAL;
+  if (int64_t(max_blocks) * d->page_size > 0x7fffffff) return KVP_E_INVAL;
+  if (max_context_len < 0 || int64_t(max_context_len) > int64_t(max_blocks) * d->page_size)
+    return KVP_E_INVAL;
+  if (!std::isfinite(scale)) return KVP_E_INVAL;
+  if (num_seqs == 0) {
+    *empty = true;
+    return KVP_OK;
+  }
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens) return KVP_E_INVAL;
+  const bool int8 = d->dtype == KVP_INT8;
+  if (int8 != (k_meta != nullptr) || int8 != (v_meta != nullptr)) return KVP_E_INVAL;
+  const int cus = kvp::cu_count_current_device();
+  if (cus <= 0) return KVP_E_HIP;
+  const kvp_status st =
+      kvp_decode_plan(d, num_seqs, num_q_heads, max_context_len, num_splits_req, cus, plan);
+  if (st != KVP_OK) return st;
+  if (int64_t(num_seqs) * d->num_kv_heads * plan->num_splits > 0x7fffffff)
+    return KVP_E_UNSUPPORTED;
+  return KVP_OK;
+}
+
+kvp_status launch_split_kernel(const kvp_pool_desc& d, const kvp_decode_plan_t& plan,
+                               const void* q, const void* k_pool, const void* v_pool,
+                               const void* k_meta, const void* v_meta,
+                               const int32_t* block_tables, int32_t max_blocks,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t max_context_len, float scale,
+                               void* out, float* part_o, float* part_ml, hipStream_t s) {
+  using namespace kvp;
+  const int g = num_q_heads / d.num_kv_heads;
+  DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_meta = static_cast<const uint16_t*>(k_meta);
+  a.v_meta = static_cast<const uint16_t*>(v_meta);
+  a.bt = block_tables;
+  a.ctx_lens = context_lens;
+  a.out = static_cast<uint16_t*>(out);
+  a.part_o = part_o;
+  a.part_ml = part_ml;
+  a.max_blocks = max_blocks;
+  a.num_kv_heads = d.num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.group = g;
+  a.num_pages = d.num_pages;
+  a.num_splits = plan.num_splits;
+  a.pages_per_split = plan.pages_per_split;
+  a.ctx_cap = max_context_len;
+  a.write_partials = part_o != nullptr;
+  a.scale_log2 = scale * kLog2e;
+
+  const int W = plan.waves_per_group;
+  const int HP = plan.use_mfma ? ((g + 15) / 16) * 16 : g;
+  size_t lds = size_t(W) * (size_t(g) * d.head_dim + 2 * HP) * sizeof(float);
+  if (!plan.use_mfma) lds += size_t(W) * g * d.page_size * sizeof(float);
+  const int64_t wgs = int64_t(num_seqs) * d.num_kv_heads * plan.num_splits;
+  const dim3 grid(static_cast<unsigned>(wgs)), block(static_cast<unsigned>(W * 64));
+  const bool int8 = d.dtype == KVP_INT8;
+  hipError_t e;
+  const int key = (d.page_size == 32) * 4 + (d.head_dim == 128) * 2 + int8;
+  switch (key) {
+    case 0: e = launch_decode_pd<false, 16, 64>(a, plan.use_mfma, g, grid, block, lds, s); break;
+    case 1: e = launch_decode_pd<true, 16, 64>(a, plan.use_mfma, g, grid, block, lds, s); break;
+    case 2: e = launch_decode_pd<false, 16, 128>(a, plan.use_mfma, g, grid, block, lds, s); break;
+    case 3: e = launch_decode_pd<true, 16, 128>(a, plan.use_mfma, g, grid, block, lds, s); break;
+    case 4: e = launch_decode_pd<false, 32, 64>(a, plan.use_mfma, g, grid, block, lds, s); break;
+    case 5: e = launch_decode_pd<true, 32, 64>(a, plan.use_mfma, g, grid, block, lds, s); break;
+    case 6: e = launch_decode_pd<false, 32, 128>(a, plan.use_mfma, g, grid, block, lds, s); break;
+    default: e = launch_decode_pd<true, 32, 128>(a, plan.use_mfma, g, grid, block, lds, s); break;
+  }
+  return e == hipSuccess ? KVP_OK : KVP_E_HIP;
+}
+
+}  // namespace
+
 extern "C" kvp_status kvp_decode_workspace_bytes(const kvp_pool* pool, int32_t num_seqs,
                                                  int32_t num_q_heads, int32_t max_context_len,
                                                  int32_t num_splits_req, size_t* bytes) {
@@ -771,85 +873,93 @@ extern "C" kvp_status kvp_paged_attention_decode(
     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
     float scale, void* out, int32_t num_splits_req, void* workspace, size_t workspace_bytes,
     kvp_stream_t stream) {
-  using namespace kvp;
   kvp_pool_desc d;
-  if (kvp_pool_get_desc(pool, &d) != KVP_OK) return KVP_E_INVAL;
-  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks <= 0) return KVP_E_INVAL;
-  if (num_q_heads % d.num_kv_heads) return KVP_E_INVAL;
-  if (int64_t(max_blocks) * d.page_size > 0x7fffffff) return KVP_E_INVAL;
-  if (max_context_len < 0 || int64_t(max_context_len) > int64_t(max_blocks) * d.page_size)
-    return KVP_E_INVAL;
-  if (!std::isfinite(scale)) return KVP_E_INVAL;
-  if (num_seqs == 0) return KVP_OK;
-  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return KVP_E_INVAL;
-  const bool int8 = d.dtype == KVP_INT8;
-  if (int8 != (k_meta != nullptr) || int8 != (v_meta != nullptr)) return KVP_E_INVAL;
-  const int g = num_q_heads / d.num_kv_heads;
-  const int cus = cu_count_current_device();
-  if (cus <= 0) return KVP_E_HIP;
   kvp_decode_plan_t plan;
-  kvp_status st =
-      kvp_decode_plan(&d, num_seqs, num_q_heads, max_context_len, num_splits_req, cus, &plan);
-  if (st != KVP_OK) return st;
+  bool empty;
+  kvp_status st = prepare_decode(pool, q, k_pool, v_pool, k_meta, v_meta, block_tables,
+                                 max_blocks, context_lens, num_seqs, num_q_heads,
+                                 max_context_len, scale, num_splits_req, &d, &plan, &empty);
+  if (st != KVP_OK || empty) return st;
+  if (!out) return KVP_E_INVAL;
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return KVP_E_INVAL;
-  const int64_t wgs = int64_t(num_seqs) * d.num_kv_heads * plan.num_splits;
-  if (wgs > 0x7fffffff) return KVP_E_UNSUPPORTED;
-
-  DecodeArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k_pool = k_pool;
-  a.v_pool = v_pool;
-  a.k_meta = static_cast<const uint16_t*>(k_meta);
-  a.v_meta = static_cast<const uint16_t*>(v_meta);
-  a.bt = block_tables;
-  a.ctx_lens = context_lens;
-  a.out = static_cast<uint16_t*>(out);
   const size_t parts = size_t(num_seqs) * num_q_heads * plan.num_splits;
-  const size_t o_bytes = (parts * d.head_dim * sizeof(float) + 255) & ~size_t(255);
-  a.part_o = plan.num_splits > 1 ? static_cast<float*>(workspace) : nullptr;
-  a.part_ml = plan.num_splits > 1
-                  ? reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes)
-                  : nullptr;
-  a.max_blocks = max_blocks;
-  a.num_kv_heads = d.num_kv_heads;
-  a.num_q_heads = num_q_heads;
-  a.group = g;
-  a.num_pages = d.num_pages;
-  a.num_splits = plan.num_splits;
-  a.pages_per_split = plan.pages_per_split;
-  a.ctx_cap = max_context_len;
-  a.scale_log2 = scale * kLog2e;
-
-  const int W = plan.waves_per_group;
-  const int HP = plan.use_mfma ? ((g + 15) / 16) * 16 : g;
-  size_t lds = size_t(W) * (size_t(g) * d.head_dim + 2 * HP) * sizeof(float);
-  if (!plan.use_mfma) lds += size_t(W) * g * d.page_size * sizeof(float);
-  const dim3 grid(static_cast<unsigned>(wgs)), block(static_cast<unsigned>(W * 64));
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e;
-  const int key = (d.page_size == 32) * 4 + (d.head_dim == 128) * 2 + int8;
-  switch (key) {
-    case 0: e = launch_decode_pd<false, 16, 64>(a, plan.use_mfma, g, grid, block, lds, s); break;
-    case 1: e = launch_decode_pd<true, 16, 64>(a, plan.use_mfma, g, grid, block, lds, s); break;
-    case 2: e = launch_decode_pd<false, 16, 128>(a, plan.use_mfma, g, grid, block, lds, s); break;
-    case 3: e = launch_decode_pd<true, 16, 128>(a, plan.use_mfma, g, grid, block, lds, s); break;
-    case 4: e = launch_decode_pd<false, 32, 64>(a, plan.use_mfma, g, grid, block, lds, s); break;
-    case 5: e = launch_decode_pd<true, 32, 64>(a, plan.use_mfma, g, grid, block, lds, s); break;
-    case 6: e = launch_decode_pd<false, 32, 128>(a, plan.use_mfma, g, grid, block, lds, s); break;
-    default: e = launch_decode_pd<true, 32, 128>(a, plan.use_mfma, g, grid, block, lds, s); break;
-  }
-  if (e != hipSuccess) return KVP_E_HIP;
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
   if (plan.num_splits > 1) {
-    const int rows = num_seqs * num_q_heads;
-    const dim3 mg(static_cast<unsigned>((rows + 3) / 4));
-    if (d.head_dim == 128)
-      hipLaunchKernelGGL((merge_kernel<128>), mg, dim3(256), 0, s, a.part_o, a.part_ml, a.out,
-                         rows, plan.num_splits);
-    else
-      hipLaunchKernelGGL((merge_kernel<64>), mg, dim3(256), 0, s, a.part_o, a.part_ml, a.out,
-                         rows, plan.num_splits);
-    if (hipGetLastError() != hipSuccess) return KVP_E_HIP;
+    part_o = static_cast<float*>(workspace);
+    part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       partials_o_bytes(parts, d.head_dim));
   }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = launch_split_kernel(d, plan, q, k_pool, v_pool, k_meta, v_meta, block_tables, max_blocks,
+                           context_lens, num_seqs, num_q_heads, max_context_len, scale, out,
+                           part_o, part_ml, s);
+  if (st != KVP_OK) return st;
+  if (plan.num_splits > 1 &&
+      launch_merge(part_o, part_ml, static_cast<uint16_t*>(out), num_seqs * num_q_heads,
+                   plan.num_splits, d.head_dim, s) != hipSuccess)
+    return KVP_E_HIP;
   return KVP_OK;
+}
+
+extern "C" kvp_status kvp_decode_partials_bytes(const kvp_pool* pool, int32_t num_seqs,
+                                                int32_t num_q_heads, int32_t max_context_len,
+                                                int32_t num_splits_req, int32_t* num_splits,
+                                                size_t* bytes) {
+  kvp_pool_desc d;
+  if (!bytes || kvp_pool_get_desc(pool, &d) != KVP_OK) return KVP_E_INVAL;
+  const int cus = kvp::cu_count_current_device();
+  if (cus <= 0) return KVP_E_HIP;
+  kvp_decode_plan_t plan;
+  const kvp_status st =
+      kvp_decode_plan(&d, num_seqs, num_q_heads, max_context_len, num_splits_req, cus, &plan);
+  if (st != KVP_OK) return st;
+  if (num_splits) *num_splits = plan.num_splits;
+  *bytes = partials_bytes(size_t(num_seqs) * num_q_heads * plan.num_splits, d.head_dim);
+  return KVP_OK;
+}
+
+extern "C" kvp_status kvp_paged_attention_decode_partials(
+    const kvp_pool* pool, const void* q, const void* k_pool, const void* v_pool,
+    const void* k_meta, const void* v_meta, const int32_t* block_tables, int32_t max_blocks,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    float scale, int32_t num_splits_req, void* partials, size_t partials_bytes_avail,
+    int32_t* num_splits, kvp_stream_t stream) {
+  kvp_pool_desc d;
+  kvp_decode_plan_t plan;
+  bool empty;
+  kvp_status st = prepare_decode(pool, q, k_pool, v_pool, k_meta, v_meta, block_tables,
+                                 max_blocks, context_lens, num_seqs, num_q_heads,
+                                 max_context_len, scale, num_splits_req, &d, &plan, &empty);
+  if (st != KVP_OK) return st;
+  if (empty) {
+    if (num_splits) *num_splits = 0;
+    return KVP_OK;
+  }
+  const size_t parts = size_t(num_seqs) * num_q_heads * plan.num_splits;
+  if (!partials || partials_bytes_avail < partials_bytes(parts, d.head_dim)) return KVP_E_INVAL;
+  float* part_o = static_cast<float*>(partials);
+  float* part_ml = reinterpret_cast<float*>(static_cast<char*>(partials) +
+                                            partials_o_bytes(parts, d.head_dim));
+  st = launch_split_kernel(d, plan, q, k_pool, v_pool, k_meta, v_meta, block_tables, max_blocks,
+                           context_lens, num_seqs, num_q_heads, max_context_len, scale, nullptr,
+                           part_o, part_ml, reinterpret_cast<hipStream_t>(stream));
+  if (st == KVP_OK && num_splits) *num_splits = plan.num_splits;
+  return st;
+}
+
+extern "C" kvp_status kvp_lse_merge(const void* partials, int32_t rows, int32_t num_splits,
+                                    int32_t head_dim, void* out, kvp_stream_t stream) {
+  if (rows < 0 || num_splits <= 0 || (head_dim != 64 && head_dim != 128)) return KVP_E_INVAL;
+  if (rows == 0) return KVP_OK;
+  if (!partials || !out) return KVP_E_INVAL;
+  const size_t parts = size_t(rows) * num_splits;
+  const float* part_o = static_cast<const float*>(partials);
+  const float* part_ml = reinterpret_cast<const float*>(static_cast<const char*>(partials) +
+                                                        partials_o_bytes(parts, head_dim));
+  return launch_merge(part_o, part_ml, static_cast<uint16_t*>(out), rows, num_splits, head_dim,
+                      reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? KVP_OK
+             : KVP_E_HIP;
 }

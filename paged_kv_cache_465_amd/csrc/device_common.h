@@ -13,7 +13,26 @@ typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Streaming loads of K/V page data: every byte is read once per decode step,
+// so the loads carry the non-temporal hint and do not displace reusable lines
+// (q, block tables) in L2 and the Infinity Cache.
+template <typename T> __device__ __forceinline__ T load_stream(const void* p);
+template <> __device__ __forceinline__ uint4 load_stream<uint4>(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <> __device__ __forceinline__ uint2 load_stream<uint2>(const void* p) {
+  const u32x2_t v = __builtin_nontemporal_load(static_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+template <> __device__ __forceinline__ uint32_t load_stream<uint32_t>(const void* p) {
+  return __builtin_nontemporal_load(static_cast<const uint32_t*>(p));
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);

@@ -167,9 +167,12 @@ kvp_status kvp_seq_release(kvp_pool* pool, int32_t* row, int32_t n_blocks) {
 }
 
 // Split planner.  A workgroup covers one (sequence, KV head) pair and one range
-// of logical blocks; its wavefronts share the range page by page.  The split
-// count is raised until there are about two workgroups per compute unit (so
-// the chip fills and the last wave of work is short), but never so far that a
+// of logical blocks; its wavefronts share the range page by page.  Measured on
+// MI355X, page streaming peaks with about one wavefront per SIMD (four per
+// compute unit) and loses bandwidth with every extra split (more partial
+// traffic, a merge, shorter streams), so workgroups have four wavefronts and
+// the split count is the smallest that gives the chip that many wavefronts:
+// S = round(4 * CUs / (pairs * waves)), at least 1, never so large that a
 // wavefront streams fewer than four pages.  Splits are single-GPU analogues of
 // spreading one sequence's cache over several devices and gathering partial
 // results ("KV Cache Optimization" glossary, multi-GPU KV splitting).
@@ -187,11 +190,7 @@ kvp_status kvp_decode_plan(const kvp_pool_desc* desc, int32_t num_seqs, int32_t 
   // per padded head, plus the vector path's probability broadcast; <= 64 KiB.
   const int32_t heads_pad = use_mfma ? ((g + 15) / 16) * 16 : g;
   const int64_t lds_per_wave = (int64_t(g) * D + 2 * heads_pad + (use_mfma ? 0 : g * P)) * 4;
-  // Instances with the most live registers are built for 4 waves (the kernel
-  // file's mfma_max_threads / valu_max_threads); the rest for 8.
-  const bool big = use_mfma ? (g > 32 || (g > 16 && P == 32 && D == 128))
-                            : (g == 3 && P == 32 && D == 128);
-  int32_t waves = big ? 4 : 8;
+  int32_t waves = 4;
   while (waves > 1 && waves * lds_per_wave > 65536) waves /= 2;
   const int32_t nblk = ceil_div(std::max(max_context_len, 1), P);
   const int64_t items = int64_t(num_seqs) * desc->num_kv_heads;
@@ -199,8 +198,9 @@ kvp_status kvp_decode_plan(const kvp_pool_desc* desc, int32_t num_seqs, int32_t 
   if (num_splits_req > 0) {
     S = num_splits_req;
   } else {
-    const int64_t target = 2 * int64_t(std::max(num_cus, 1));
-    S = items > 0 ? int32_t(std::min<int64_t>((target + items - 1) / items, 1 << 20)) : 1;
+    const int64_t target_waves = 4 * int64_t(std::max(num_cus, 1));
+    const int64_t per_split = std::max<int64_t>(items * waves, 1);
+    S = int32_t(std::min<int64_t>((target_waves + per_split / 2) / per_split, 1 << 20));
     const int32_t max_by_work = std::max(1, nblk / (waves * 4));
     S = std::max(1, std::min(S, max_by_work));
   }
