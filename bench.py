@@ -36,6 +36,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD's published figure
+PROFILES = os.path.join(ROOT, "profiles")
+# sources that decide the split kernel's code and launch shape
+KERNEL_SOURCES = ("paged_kv_cache_465_amd/csrc/decode.hip",
+                  "paged_kv_cache_465_amd/csrc/device_common.h",
+                  "paged_kv_cache_465_amd/csrc/pool.cpp")
 MALL_FLUSH_BYTES = 1 << 30      # > 256 MB Infinity Cache
 
 
@@ -214,6 +219,31 @@ def run_gpu(args, kvp, cfg, case):
     return res, (pool, layers, bt, ctx)
 
 
+def kernel_source_digest() -> str:
+    """sha256 over the split kernel's sources (counter readings are tied to it)."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch of the split kernel from the committed counter
+    readings (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads
+    for a plain copy of known size), or None when there are none for this
+    workload or the kernel's sources changed after they were taken."""
+    path = os.path.join(PROFILES, f"decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return rec
+
+
 def copy_probe(dev, nbytes=1 << 32, reps=5):
     """A plain device copy of known size: its rate, and the kernel whose
     hardware counters scale FETCH_SIZE/WRITE_SIZE readings."""
@@ -366,7 +396,11 @@ def main(argv=None):
                      "kernel_us_mean": round(kern_us, 2),
                      "bytes_per_launch": int(sb["split_kernel_per_launch"])},
     }
-    # pages' own figures for this workload are analytic only: context, not a target
+    rec = recorded_traffic(cfg.name)
+    if rec is not None:
+        out["roofline"]["traffic"] = rec["traffic_bytes_per_launch"]
+        out["roofline"]["traffic_over_algorithmic"] = round(
+            rec["traffic_bytes_per_launch"] / sb["split_kernel_per_launch"], 4)
     out["copy_probe"] = copy_probe(dev)
     hc = None
     if not (args.no_parity and args.no_cpu_baseline):
