@@ -354,3 +354,68 @@ def test_append_special_rows_int8(kvp):
     _pools_equal((kp.cpu().numpy(), vp.cpu().numpy(), kmt.cpu().numpy().view(np.uint16),
                   vmt.cpu().numpy().view(np.uint16)), (k, v, km, vm))
     pool.close()
+
+
+# ---- two-phase decode: split kernel + log-sum-exp merge --------------------------
+@pytest.mark.parametrize("cfg", [c for c in SMALL if c.name in
+                                 ("tiny", "tiny_g2", "l8b_small", "int8_small", "prefix_small",
+                                  "l8b_small_g24")], ids=lambda c: c.name)
+@pytest.mark.parametrize("splits", [1, 3])
+def test_partials_layout_and_merge(kvp, cfg, splits):
+    """The partials buffer holds, per (row, split), the split's normalized
+    output and (m, l) in base-2 units as documented; merging it gives the full
+    decode's output (bit for bit when the full decode splits too)."""
+    case = _case(cfg)
+    k, v, km, vm, ref = _oracle(case)
+    log(f"[partials] {cfg.name} S={splits}")
+    gc = GpuCase(kvp, case)
+    gc.upload(k, v, km, vm)
+    c = case.cfg
+    B, Hq, D, P = case.B, c.num_q_heads, c.head_dim, c.page_size
+    mx = int(case.ctx.max())
+    S, nbytes = kvp.kvp_decode_partials_bytes(gc.pool, B, Hq, mx, splits)
+    plan = kvp.kvp_decode_plan(gc.desc, B, Hq, mx, splits)
+    assert S == plan["num_splits"] and S <= splits
+    part = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    got_S = kvp.kvp_paged_attention_decode_partials(gc.pool, gc.q, gc.k_pool, gc.v_pool,
+                                                    gc.k_meta, gc.v_meta, gc.bt, gc.ctx, mx,
+                                                    float(case.scale), part, splits)
+    assert got_S == S
+    out = torch.empty_like(gc.q)
+    kvp.kvp_lse_merge(part, B * Hq, S, D, out)
+    torch.cuda.synchronize()
+    merged = out.cpu().numpy().view(np.uint16)
+    full = gc.decode(num_splits=splits)
+    if S > 1:
+        assert np.array_equal(merged, full)
+    assert_close(merged, ref, f"{cfg.name} merged S={S}")
+
+    # the documented layout, checked against the oracle split by split
+    rows = B * Hq
+    o_bytes = (rows * S * D * 4 + 255) // 256 * 256
+    p = part.cpu().numpy()
+    po = p[: rows * S * D].reshape(B, Hq, S, D)
+    pml = p[o_bytes // 4: o_bytes // 4 + rows * S * 2].reshape(B, Hq, S, 2)
+    lay = layout_of(case)
+    qf = (case.q.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    sc = float(np.float32(case.scale))
+    pps = plan["pages_per_split"]
+    g = Hq // c.num_kv_heads
+    for b in range(B):
+        n = int(case.ctx[b])
+        Kf, Vf = oracle.gather_sequence(lay, k, v, km, vm, case.block_tables[b], n)
+        for s in range(S):
+            lo, hi = s * pps * P, min((s + 1) * pps * P, n)
+            for j in range(Hq):
+                if hi <= lo:
+                    assert pml[b, j, s, 0] == -np.inf and pml[b, j, s, 1] == 0.0
+                    continue
+                sco = (Kf[j // g, lo:hi] @ qf[b, j]) * sc * np.log2(np.e)
+                m = sco.max()
+                l = np.exp2(sco - m).sum()
+                o = oracle.attend(qf[b, j][None], Kf[j // g, lo:hi][None], Vf[j // g, lo:hi][None],
+                                  sc)[0]
+                assert abs(pml[b, j, s, 0] - m) <= 1e-4 * max(1.0, abs(m)), (b, j, s)
+                assert abs(pml[b, j, s, 1] - l) <= 1e-4 * l, (b, j, s)
+                assert np.abs(po[b, j, s] - o).max() <= 2e-3 * max(1.0, np.abs(o).max()), (b, j, s)
+    gc.close()
