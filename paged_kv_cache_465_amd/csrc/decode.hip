@@ -51,7 +51,8 @@ struct DecodeArgs {
   uint16_t* out;
   float* part_o;
   float* part_ml;
-  int32_t max_blocks, num_kv_heads, num_q_heads, group, num_pages, num_splits, pages_per_split;
+  int32_t num_seqs, max_blocks, num_kv_heads, num_q_heads, group, num_pages, num_splits,
+      pages_per_split;
   int32_t ctx_cap;
   int32_t write_partials;  // 1: store (o, m, l) per split; 0: store the bf16 output
   float scale_log2;  // scale * log2(e)
@@ -63,14 +64,23 @@ struct WorkRange {
 
 // Which (sequence, KV head, split) this workgroup owns and which contiguous
 // run of logical blocks [kb0, kb0 + cnt) wave `wave` streams.
+//
+// Workgroups are handed to the eight XCDs round robin (workgroup i to XCD
+// i mod 8), so the index order decides each XCD's share of the work.  The KV
+// head varies fastest (the heads of one sequence carry equal work), then the
+// sequence, and the split slowest: every XCD gets the same mix of long and
+// short sequences and of first and last splits, and the always-full first
+// splits are dispatched first.  (With the split fastest and eight KV heads,
+// an even split count gave each XCD a single split index: half the XCDs
+// streamed every sequence's first pages while the other half idled.)
 template <int P>
 __device__ __forceinline__ WorkRange work_range(const DecodeArgs& a, int wave, int W) {
   WorkRange w;
   int item = blockIdx.x;
-  w.s = item % a.num_splits;
-  item /= a.num_splits;
   w.h = item % a.num_kv_heads;
-  w.b = item / a.num_kv_heads;
+  item /= a.num_kv_heads;
+  w.b = item % a.num_seqs;
+  w.s = item / a.num_seqs;
   int ctx = a.ctx_lens[w.b];
   ctx = min(max(ctx, 0), a.ctx_cap);
   w.ctx = ctx;
@@ -817,6 +827,7 @@ kvp_status launch_split_kernel(const kvp_pool_desc& d, const kvp_decode_plan_t& 
   a.out = static_cast<uint16_t*>(out);
   a.part_o = part_o;
   a.part_ml = part_ml;
+  a.num_seqs = num_seqs;
   a.max_blocks = max_blocks;
   a.num_kv_heads = d.num_kv_heads;
   a.num_q_heads = num_q_heads;
