@@ -75,6 +75,9 @@ def step_bytes(cfg, ctx: np.ndarray) -> dict:
     """
     eb = 1 if cfg.kv_dtype == "int8" else 2
     n = ctx.astype(np.int64)
+    if cfg.window_tokens > 0:
+        # tokens attended with sinks + a recent window
+        n = np.minimum(n, cfg.sink_tokens + cfg.window_tokens)
     Hkv, Hq, D, P, L = cfg.num_kv_heads, cfg.num_q_heads, cfg.head_dim, cfg.page_size, cfg.layers
     kv = int((n * Hkv * 2 * D * eb).sum())
     if cfg.kv_dtype == "int8":
@@ -147,22 +150,39 @@ def run_gpu(args, kvp, cfg, case):
     pool, layers, bt, ctx, seq_idx, new_pos = setup_device(kvp, cfg, case, dev)
     B, Hq, D = case.B, cfg.num_q_heads, cfg.head_dim
     max_ctx = int(case.ctx.max())
-    S, pbytes = kvp.kvp_decode_partials_bytes(pool, B, Hq, max_ctx, args.splits)
-    plan = kvp.kvp_decode_plan(pool.desc, B, Hq, max_ctx, args.splits,
+    plan_ctx = max_ctx
+    if cfg.window_tokens > 0:
+        P = cfg.page_size
+        plan_ctx = min(max_ctx, (-(-cfg.sink_tokens // P) + -(-cfg.window_tokens // P) + 1) * P)
+    S, pbytes = kvp.kvp_decode_partials_bytes(pool, B, Hq, plan_ctx, args.splits)
+    plan = kvp.kvp_decode_plan(pool.desc, B, Hq, plan_ctx, args.splits,
                                torch.cuda.get_device_properties(0).multi_processor_count)
     partials = torch.empty(max(pbytes, 4) // 4, dtype=torch.float32, device=dev) if S > 1 else None
     scale = float(case.scale)
     log(f"[plan] {plan}")
 
+    windowed = cfg.window_tokens > 0
+    if windowed:
+        wsb = kvp.kvp_decode_window_workspace_bytes(pool, B, Hq, max_ctx, cfg.sink_tokens,
+                                                    cfg.window_tokens, args.splits)
+        wspace = torch.empty(max(wsb, 4) // 4, dtype=torch.float32, device=dev) if wsb else None
+
     def one_step(probe=None):
         """All layers once.  probe = (layer, start event, end event): that
-        layer's split kernel is bracketed by the two events."""
+        layer's split kernel (with a window: the whole decode call) is
+        bracketed by the two events."""
         for i, L in enumerate(layers):
             kvp.kvp_kv_append(pool, L.k, L.v, L.km, L.vm, L.nk, L.nv, seq_idx, new_pos, bt)
             timed = probe is not None and probe[0] == i
             if timed:
                 probe[1].record()
-            if S > 1:
+            if windowed:
+                kvp.kvp_paged_attention_decode_window(
+                    pool, L.q, L.k, L.v, L.km, L.vm, bt, ctx, max_ctx, scale, cfg.sink_tokens,
+                    cfg.window_tokens, L.out, args.splits, wspace)
+                if timed:
+                    probe[2].record()
+            elif S > 1:
                 kvp.kvp_paged_attention_decode_partials(pool, L.q, L.k, L.v, L.km, L.vm, bt, ctx,
                                                         max_ctx, scale, partials, args.splits)
                 if timed:
@@ -298,6 +318,15 @@ def oracle_layer(cfg, hc, seqs):
     return lay, (k, v, km, vm)
 
 
+def oracle_decode(cfg, lay, hc, pools, seqs):
+    """The oracle's output for ``seqs`` (sinks + window when the config has one)."""
+    import oracle
+    if cfg.window_tokens > 0:
+        return oracle.paged_decode_window(lay, hc.q, *pools, hc.block_tables, hc.ctx, hc.scale,
+                                          cfg.sink_tokens, cfg.window_tokens, seqs=seqs)
+    return oracle.paged_decode(lay, hc.q, *pools, hc.block_tables, hc.ctx, hc.scale, seqs=seqs)
+
+
 def cpu_baseline(cfg, hc, target_s: float):
     import oracle
     try:
@@ -309,7 +338,7 @@ def cpu_baseline(cfg, hc, target_s: float):
     # one sequence first to size the sample, then enough for ~target_s of work
     lay, pools = oracle_layer(cfg, hc, order[:1])
     t0 = time.perf_counter()
-    oracle.paged_decode(lay, hc.q, *pools, hc.block_tables, hc.ctx, hc.scale, seqs=order[:1])
+    oracle_decode(cfg, lay, hc, pools, order[:1])
     t1 = time.perf_counter() - t0
     n = int(min(hc.B, max(1, round(target_s / max(t1, 1e-6)))))
     seqs = order[:n]
@@ -318,7 +347,7 @@ def cpu_baseline(cfg, hc, target_s: float):
     passes, dt = 0, 0.0
     while passes == 0 or dt < target_s:
         t0 = time.perf_counter()
-        oracle.paged_decode(lay, hc.q, *pools, hc.block_tables, hc.ctx, hc.scale, seqs=seqs)
+        oracle_decode(cfg, lay, hc, pools, seqs)
         dt += time.perf_counter() - t0
         passes += 1
     # bytes of the sample: one layer of the sampled sequences (same terms as the GPU)
@@ -358,8 +387,8 @@ def main(argv=None):
         print(json.dumps({"copy_calibration": r}))
         return
     import paged_kv_cache_465_amd as kvp
-    from workloads import CONFIGS, make_case
-    cfg = CONFIGS[args.config]
+    from workloads import CONFIGS, EXTRA_CONFIGS, make_case
+    cfg = {**CONFIGS, **EXTRA_CONFIGS}[args.config]
     case = make_case(cfg, with_data=not cfg.device_data)
     log(f"[config] {cfg.name}: layers={cfg.layers} B={case.B} Hq={cfg.num_q_heads} "
         f"Hkv={cfg.num_kv_heads} D={cfg.head_dim} P={cfg.page_size} {cfg.kv_dtype} "
@@ -385,6 +414,8 @@ def main(argv=None):
                    "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads,
                    "head_dim": cfg.head_dim, "page_size": cfg.page_size,
                    "kv_dtype": cfg.kv_dtype, "num_splits": res["num_splits"],
+                   **({"sink_tokens": cfg.sink_tokens, "window_tokens": cfg.window_tokens}
+                      if cfg.window_tokens > 0 else {}),
                    "waves_per_group": res["plan"]["waves_per_group"]},
         "tokens_per_s": round(case.B / (ms * 1e-3), 1),
         "hbm_frac": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -394,6 +425,8 @@ def main(argv=None):
                      "traffic": None, "kernel": "decode_mfma_kernel" if res["plan"]["use_mfma"]
                      else "decode_valu_kernel",
                      "kernel_us_mean": round(kern_us, 2),
+                     "timed": "decode call (split + merge kernels)" if cfg.window_tokens > 0
+                     else "split kernel",
                      "bytes_per_launch": int(sb["split_kernel_per_launch"])},
     }
     rec = recorded_traffic(cfg.name)
@@ -418,7 +451,7 @@ def parity_sample(cfg, hc, state, seqs=(0, 13, 31)):
     pool, layers, bt, ctx = state
     seqs = [s for s in seqs if s < hc.B]
     lay, pools = oracle_layer(cfg, hc, seqs)
-    ref = oracle.paged_decode(lay, hc.q, *pools, hc.block_tables, hc.ctx, hc.scale, seqs=seqs)
+    ref = oracle_decode(cfg, lay, hc, pools, seqs)
     got_bits = layers[0].out.cpu().numpy().view(np.uint16)
     got = (got_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     d = np.abs(got[seqs] - ref[seqs])

@@ -153,6 +153,15 @@ kvp_status kvp_seq_share(kvp_pool* pool, const int32_t* src_row, int32_t* dst_ro
  * (the request completed). */
 kvp_status kvp_seq_release(kvp_pool* pool, int32_t* row, int32_t n_blocks);
 
+/* Drop the pages of a sequence of ctx_len tokens that hold only tokens a
+ * sink + window decode (kvp_paged_attention_decode_window) never reads:
+ * blocks ceil(sink_tokens/P) .. floor((ctx_len - window_tokens)/P) - 1.  Their
+ * references are released and their entries set to -1; entries that are
+ * already -1 are skipped.  Nothing happens when sink_tokens + window_tokens >=
+ * ctx_len.  window_tokens must be > 0.  All or nothing. */
+kvp_status kvp_seq_evict_window(kvp_pool* pool, int32_t* row, int32_t max_blocks, int32_t ctx_len,
+                                int32_t sink_tokens, int32_t window_tokens);
+
 /* ---- Append (device) ------------------------------------------------------
  * For each of n_tokens new tokens i: sequence seq_idx[i], position pos[i];
  * write k_new[i][h][:] and v_new[i][h][:] (bfloat16 [n_tokens][H_kv][D]) into
@@ -215,6 +224,28 @@ kvp_status kvp_paged_attention_decode(const kvp_pool* pool, const void* q,
                                       float scale, void* out, int32_t num_splits_req,
                                       void* workspace, size_t workspace_bytes,
                                       kvp_stream_t stream);
+
+/* ---- Decode over attention sinks and a recent window (device) --------------
+ * "KV-Cache Optimization Techniques", section "Token Eviction Strategies",
+ * eq. 5 (StreamingLLM): keep the first s tokens ("attention sinks") and the
+ * last w tokens; section "Sliding Window Cache", eq. 6: the window alone
+ * (s = 0).  For a sequence of n = context_lens[b] tokens with
+ * sink_tokens + window_tokens < n, the query attends only to tokens t < s and
+ * t >= n - w; otherwise to all n tokens.  window_tokens == 0 means no window
+ * (the same result as kvp_paged_attention_decode).  Pages that hold only
+ * dropped tokens are never read, so their table entries may be -1 (see
+ * kvp_seq_evict_window).  Everything else is as kvp_paged_attention_decode;
+ * the workspace is sized by kvp_decode_window_workspace_bytes. */
+kvp_status kvp_decode_window_workspace_bytes(const kvp_pool* pool, int32_t num_seqs,
+                                             int32_t num_q_heads, int32_t max_context_len,
+                                             int32_t sink_tokens, int32_t window_tokens,
+                                             int32_t num_splits_req, size_t* bytes);
+kvp_status kvp_paged_attention_decode_window(
+    const kvp_pool* pool, const void* q, const void* k_pool, const void* v_pool,
+    const void* k_meta, const void* v_meta, const int32_t* block_tables, int32_t max_blocks,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    float scale, int32_t sink_tokens, int32_t window_tokens, void* out, int32_t num_splits_req,
+    void* workspace, size_t workspace_bytes, kvp_stream_t stream);
 
 /* ---- Decode in two phases (device) -----------------------------------------
  * The same attention as kvp_paged_attention_decode, with its two kernels

@@ -11,6 +11,8 @@
   ceil(n / P) pages, so at most P - 1 slots of its last page are unused.
 * ``gqa_ratio``: section "Multi-Query and Grouped-Query Caching", eq. 7, the
   GQA/MHA cache-size ratio G / H with G the number of KV heads.
+* ``window_cache_elems``: section "Sliding Window Cache", eq. 6: a window of
+  w tokens holds w * 2 * L * d_k values per KV head, whatever the context.
 """
 from __future__ import annotations
 
@@ -48,3 +50,8 @@ def int8_row_ratio(head_dim: int) -> float:
     """Bytes of an INT8 row (D codes + float16 scale + float16 zero) over its
     bfloat16 size: the "2x" of section "KV-Cache Quantization" less metadata."""
     return (head_dim + 4) / (2 * head_dim)
+
+
+def window_cache_elems(window: int, layers: int, head_dim: int) -> int:
+    """Eq. 6: K and V values a w-token window keeps per KV head."""
+    return window * 2 * layers * head_dim

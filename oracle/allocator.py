@@ -66,3 +66,14 @@ class PoolModel:
             self.ref[p] -= c
             if self.ref[p] == 0:
                 del self.ref[p]
+
+
+def window_evicted_blocks(n: int, page_size: int, sink: int, window: int):
+    """Logical blocks of a sequence of n tokens that hold no position a sink +
+    window decode attends to ("KV-Cache Optimization Techniques", section
+    "Token Eviction Strategies", eq. 5): every block of the sequence minus the
+    blocks of the kept positions."""
+    from .paged_attention import kept_positions
+    nblk = -(-n // page_size)
+    kept = set((kept_positions(n, sink, window) // page_size).tolist())
+    return sorted(set(range(nblk)) - kept)

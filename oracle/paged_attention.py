@@ -9,6 +9,12 @@ result ("Understanding KV-Cache Optimization in Modern LLM Serving", section
 physical blocks without changing model output), so this is the definition of
 attention applied to the gathered rows.
 
+Sinks and a recent window ("KV-Cache Optimization Techniques", section "Token
+Eviction Strategies", eq. 5, StreamingLLM: the cache keeps tokens 1..s and
+t-w+1..t; section "Sliding Window Cache", eq. 6, the window alone): the query
+of a sequence of n tokens attends to positions 0..s-1 and n-w..n-1 (0-based),
+or to all n when s + w >= n.
+
 Readings taken where the pages leave a step open:
 * the scale is an explicit float32 argument (1/sqrt(D) in every workload);
 * query head j uses KV head j // g with g = H_q / H_kv ("Multi-Query and
@@ -120,6 +126,60 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndar
         s = (K[h] @ q[j]) * scale
         p = np.exp(s - s.max())
         out[j] = (p @ V[h]) / p.sum()
+    return out
+
+
+def kept_positions(n: int, sink: int, window: int) -> np.ndarray:
+    """Positions a sequence of n tokens attends to with s sink tokens and a
+    recent window of w tokens (eq. 5; eq. 6 when s = 0).  w = 0: no window."""
+    if window <= 0 or sink + window >= n:
+        return np.arange(n)
+    return np.concatenate([np.arange(sink), np.arange(n - window, n)])
+
+
+def gather_positions(layout: PoolLayout, k_pool, v_pool, k_meta, v_meta,
+                     block_table_row: np.ndarray, positions: np.ndarray):
+    """K and V rows of the listed token positions, in that order: float64
+    [H_kv, len, D] each.  Only the pages holding those positions are read."""
+    P, H, D = layout.page_size, layout.num_kv_heads, layout.head_dim
+    positions = np.asarray(positions, dtype=np.int64)
+    if positions.size == 0:
+        z = np.zeros((H, 0, D))
+        return z, z.copy()
+    pages = np.asarray(block_table_row, dtype=np.int64)[positions // P]
+    rows = positions % P
+    if (pages < 0).any() or (pages >= layout.num_pages).any():
+        raise ValueError("a kept position lies in a page outside the pool")
+    kp = np.asarray(k_pool).reshape(layout.num_pages, H, P, D)
+    vp = np.asarray(v_pool).reshape(layout.num_pages, H, D, P)
+    hh = np.arange(H)[None, :]
+    kr = kp[pages[:, None], hh, rows[:, None], :]    # [len, H, D]
+    vr = vp[pages[:, None], hh, :, rows[:, None]]    # [len, H, D] (V tile is [D][P])
+    if layout.dtype == "bf16":
+        K, V = _to_f64(kr), _to_f64(vr)
+    else:
+        km = np.asarray(k_meta).reshape(layout.num_pages, H, P, 2)[pages[:, None], hh,
+                                                                   rows[:, None]]  # [len, H, 2]
+        vm = np.asarray(v_meta).reshape(layout.num_pages, H, P, 2)[pages[:, None], hh,
+                                                                   rows[:, None]]
+        K = dequantize(kr, km[..., 0], km[..., 1])
+        V = dequantize(vr, vm[..., 0], vm[..., 1])
+    return K.transpose(1, 0, 2), V.transpose(1, 0, 2)
+
+
+def paged_decode_window(layout: PoolLayout, q_bits: np.ndarray, k_pool, v_pool, k_meta, v_meta,
+                        block_tables: np.ndarray, context_lens: np.ndarray, scale, sink: int,
+                        window: int, seqs=None) -> np.ndarray:
+    """Eq. 1 over the kept positions of eq. 5 / eq. 6: float64 [B, H_q, D]."""
+    q = _to_f64(q_bits)
+    B = q.shape[0]
+    sel = range(B) if seqs is None else seqs
+    out = np.zeros(q.shape)
+    sc = float(np.float32(scale))
+    for b in sel:
+        pos = kept_positions(int(context_lens[b]), sink, window)
+        K, V = gather_positions(layout, k_pool, v_pool, k_meta, v_meta, block_tables[b], pos)
+        out[b] = attend(q[b], K, V, sc)
     return out
 
 

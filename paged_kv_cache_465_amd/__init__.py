@@ -148,6 +148,14 @@ def kvp_seq_release(pool: Pool, row: np.ndarray, n_blocks: int) -> None:
     _check(_L.kvp_seq_release(pool.handle, _ptr(row), int(n_blocks)), "kvp_seq_release")
 
 
+def kvp_seq_evict_window(pool: Pool, row: np.ndarray, ctx_len: int, sink_tokens: int,
+                         window_tokens: int) -> None:
+    """Release the pages of ``row`` that hold only tokens outside sinks + window."""
+    row = _i32(row)
+    _check(_L.kvp_seq_evict_window(pool.handle, _ptr(row), row.size, int(ctx_len),
+                                   int(sink_tokens), int(window_tokens)), "kvp_seq_evict_window")
+
+
 def kvp_decode_plan(desc: PoolDesc, num_seqs: int, num_q_heads: int, max_context_len: int,
                     num_splits_req: int = 0, num_cus: int = 256) -> dict:
     p = DecodePlan()
@@ -225,6 +233,40 @@ def kvp_paged_attention_decode(pool: Pool, q, k_pool, v_pool, k_meta, v_meta, bl
         _dev(workspace, "workspace"), ws_bytes, _stream(stream)), "kvp_paged_attention_decode")
 
 
+def kvp_decode_window_workspace_bytes(pool: Pool, num_seqs: int, num_q_heads: int,
+                                      max_context_len: int, sink_tokens: int, window_tokens: int,
+                                      num_splits_req: int = 0) -> int:
+    b = ctypes.c_size_t()
+    _check(_L.kvp_decode_window_workspace_bytes(pool.handle, int(num_seqs), int(num_q_heads),
+                                                int(max_context_len), int(sink_tokens),
+                                                int(window_tokens), int(num_splits_req),
+                                                ctypes.byref(b)),
+           "kvp_decode_window_workspace_bytes")
+    return int(b.value)
+
+
+def kvp_paged_attention_decode_window(pool: Pool, q, k_pool, v_pool, k_meta, v_meta,
+                                      block_tables, context_lens, max_context_len: int,
+                                      scale: float, sink_tokens: int, window_tokens: int, out,
+                                      num_splits_req: int = 0, workspace=None,
+                                      stream=None) -> None:
+    """Decode attending only to the first sink_tokens and the last window_tokens tokens."""
+    eb = 1 if pool.desc.dtype == KVP_INT8 else 2
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables/context_lens must cover the batch")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_L.kvp_paged_attention_decode_window(
+        pool.handle, _dev(q, "q", 2), _dev(k_pool, "k_pool", eb), _dev(v_pool, "v_pool", eb),
+        _dev(k_meta, "k_meta", 2), _dev(v_meta, "v_meta", 2), _dev(block_tables, "block_tables", 4),
+        int(block_tables.shape[1]), _dev(context_lens, "context_lens", 4), B, Hq,
+        int(max_context_len), float(scale), int(sink_tokens), int(window_tokens),
+        _dev(out, "out", 2), int(num_splits_req), _dev(workspace, "workspace"), ws_bytes,
+        _stream(stream)), "kvp_paged_attention_decode_window")
+
+
 def kvp_decode_partials_bytes(pool: Pool, num_seqs: int, num_q_heads: int,
                               max_context_len: int, num_splits_req: int = 0):
     """(num_splits, bytes) of the partials buffer the split kernel writes."""
@@ -274,4 +316,6 @@ __all__ = [
     "kvp_pages_free", "kvp_seq_grow", "kvp_seq_share", "kvp_seq_release", "kvp_decode_plan",
     "kvp_kv_append", "kvp_decode_workspace_bytes", "kvp_paged_attention_decode",
     "kvp_decode_partials_bytes", "kvp_paged_attention_decode_partials", "kvp_lse_merge",
+    "kvp_seq_evict_window", "kvp_decode_window_workspace_bytes",
+    "kvp_paged_attention_decode_window",
 ]

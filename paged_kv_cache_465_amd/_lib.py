@@ -60,6 +60,15 @@ PROTOTYPES = {
                                                       c_float, c_int32, c_void_p, c_size_t,
                                                       P_int32, c_void_p]),
     "kvp_lse_merge": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
+    "kvp_seq_evict_window": (c_int32, [c_void_p, P_int32, c_int32, c_int32, c_int32, c_int32]),
+    "kvp_decode_window_workspace_bytes": (c_int32, [c_void_p, c_int32, c_int32, c_int32,
+                                                    c_int32, c_int32, c_int32,
+                                                    ctypes.POINTER(c_size_t)]),
+    "kvp_paged_attention_decode_window": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p,
+                                                    c_void_p, c_void_p, c_void_p, c_int32,
+                                                    c_void_p, c_int32, c_int32, c_int32, c_float,
+                                                    c_int32, c_int32, c_void_p, c_int32,
+                                                    c_void_p, c_size_t, c_void_p]),
 }
 
 _lib = None

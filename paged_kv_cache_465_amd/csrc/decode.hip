@@ -54,16 +54,51 @@ struct DecodeArgs {
   int32_t num_seqs, max_blocks, num_kv_heads, num_q_heads, group, num_pages, num_splits,
       pages_per_split;
   int32_t ctx_cap;
+  int32_t sink_tokens, window_tokens;  // window_tokens > 0: attend only to the kept set
   int32_t write_partials;  // 1: store (o, m, l) per split; 0: store the bf16 output
   float scale_log2;  // scale * log2(e)
 };
 
+// The tokens a sequence of n attends to.  Without a window, 0..n-1.  With a
+// window ("KV-Cache Optimization Techniques", section "Token Eviction
+// Strategies", eq. 5, attention sinks plus a recent window; section "Sliding
+// Window Cache", eq. 6, when there are no sinks) and sink + window < n, only
+// t < sink or t >= n - window.  The pages streamed are the virtual block list
+// "sink blocks, then window blocks": virtual block v is logical block v below
+// sink_blk and win_first + (v - sink_blk) from there on; blocks in between hold
+// only dropped tokens and are never read (their table entries may be -1).
 struct WorkRange {
-  int b, h, s, ctx, kb0, cnt;
+  int b, h, s, ctx;
+  int kb0, cnt;            // this wave's virtual blocks [kb0, kb0 + cnt)
+  int sink_blk, win_first;
+  int sink_end, win_start;  // kept: t < ctx and (t < sink_end or t >= win_start)
+  __device__ __forceinline__ int logical(int v) const {
+    return v < sink_blk ? v : win_first + (v - sink_blk);
+  }
 };
 
+// Rows of one page that take part (relative token bounds of the kept set).
+struct PageMask {
+  int end, sink_end, win_start;
+  bool partial;  // some row of the page is not kept
+  __device__ __forceinline__ bool valid(int r) const {
+    return r < end && (r < sink_end || r >= win_start);
+  }
+};
+
+template <int P>
+__device__ __forceinline__ PageMask page_mask(const WorkRange& w, int lblk) {
+  const int base = lblk * P;
+  PageMask m;
+  m.end = w.ctx - base;
+  m.sink_end = w.sink_end - base;
+  m.win_start = w.win_start - base;
+  m.partial = !(m.end >= P && (m.sink_end >= P || m.win_start <= 0));
+  return m;
+}
+
 // Which (sequence, KV head, split) this workgroup owns and which contiguous
-// run of logical blocks [kb0, kb0 + cnt) wave `wave` streams.
+// run of virtual blocks [kb0, kb0 + cnt) wave `wave` streams.
 //
 // Workgroups are handed to the eight XCDs round robin (workgroup i to XCD
 // i mod 8), so the index order decides each XCD's share of the work.  The KV
@@ -85,8 +120,20 @@ __device__ __forceinline__ WorkRange work_range(const DecodeArgs& a, int wave, i
   ctx = min(max(ctx, 0), a.ctx_cap);
   w.ctx = ctx;
   const int nblk = (ctx + P - 1) / P;
+  int nvirt = nblk;
+  w.sink_blk = nblk;
+  w.win_first = nblk;
+  w.sink_end = ctx;
+  w.win_start = ctx;
+  if (a.window_tokens > 0 && int64_t(a.sink_tokens) + a.window_tokens < int64_t(ctx)) {
+    w.sink_end = a.sink_tokens;
+    w.win_start = ctx - a.window_tokens;
+    w.sink_blk = (a.sink_tokens + P - 1) / P;
+    w.win_first = max(w.win_start / P, w.sink_blk);
+    nvirt = w.sink_blk + (nblk - w.win_first);
+  }
   const int blk0 = w.s * a.pages_per_split;
-  const int blk1 = min(blk0 + a.pages_per_split, nblk);
+  const int blk1 = min(blk0 + a.pages_per_split, nvirt);
   const int n = max(blk1 - blk0, 0);
   const int cw = (n + W - 1) / W;
   w.kb0 = blk0 + wave * cw;
@@ -233,7 +280,7 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
   const int32_t* btrow = a.bt + int64_t(wr.b) * a.max_blocks;
 
   auto issue = [&](PageRegs<INT8, P, D>& R, int k) {
-    int phys = btrow[wr.kb0 + k];
+    int phys = btrow[wr.logical(wr.kb0 + k)];
     const bool ok = unsigned(phys) < unsigned(a.num_pages);
     R.phys = ok ? phys : -1;
     const int64_t tile = int64_t(ok ? phys : 0) * H + wr.h;
@@ -270,8 +317,8 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
 
   auto compute = [&](const PageRegs<INT8, P, D>& R, int k) {
     if (R.phys < 0) return;  // absent page: its tokens do not take part
-    const int rem = wr.ctx - (wr.kb0 + k) * P;  // valid rows in this page (>= 1)
-    const bool tail = rem < P;
+    const PageMask pm = page_mask<P>(wr, wr.logical(wr.kb0 + k));
+    const bool tail = pm.partial;
 
     // K operands for all sub-tiles (shared by every head tile).
     OpA kop[T][KK];
@@ -306,7 +353,7 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
           __builtin_memcpy(wv, &raw, sizeof(raw));
 #pragma unroll
           for (int e = 0; e < EV; ++e) {
-            if (EV * gq + e >= rem) wv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            if (!pm.valid(EV * gq + e)) wv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
           }
           __builtin_memcpy(&raw, wv, sizeof(raw));
         }
@@ -363,7 +410,7 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
         for (int st = 0; st < T; ++st)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (EV * gq + 4 * st + i >= rem) x[st][i] = -INFINITY;
+            if (!pm.valid(EV * gq + 4 * st + i)) x[st][i] = -INFINITY;
       }
       float mloc = x[0][0];
 #pragma unroll
@@ -393,7 +440,7 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
         for (int st = 0; st < T; ++st)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const bool valid = !tail || (EV * gq + 4 * st + i < rem);
+            const bool valid = !tail || pm.valid(EV * gq + 4 * st + i);
             const float pv = valid ? p[st][i] * vs[st][i] : 0.0f;
             zs += valid ? p[st][i] * vz[st][i] : 0.0f;
             pop[4 * st + i] = (_Float16)pv;
@@ -509,7 +556,7 @@ __global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(
   const int32_t* btrow = a.bt + int64_t(wr.b) * a.max_blocks;
 
   auto issue = [&](Regs& R, int k) {
-    int phys = btrow[wr.kb0 + k];
+    int phys = btrow[wr.logical(wr.kb0 + k)];
     const bool ok = unsigned(phys) < unsigned(a.num_pages);
     R.phys = ok ? phys : -1;
     const int64_t tile = int64_t(ok ? phys : 0) * H + wr.h;
@@ -545,8 +592,8 @@ __global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(
 
   auto compute = [&](const Regs& R, int k) {
     if (R.phys < 0) return;
-    const int rem = wr.ctx - (wr.kb0 + k) * P;
-    const bool tail = rem < P;
+    const PageMask pm = page_mask<P>(wr, wr.logical(wr.kb0 + k));
+    const bool tail = pm.partial;
     float x[TPL][G];
 #pragma unroll
     for (int u = 0; u < TPL; ++u) {
@@ -577,7 +624,7 @@ __global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(
           sc = s * dsum + z * qsum[j];
         }
         x[u][j] = sc * a.scale_log2;
-        if (tail && tr + 16 * u >= rem) x[u][j] = -INFINITY;
+        if (tail && !pm.valid(tr + 16 * u)) x[u][j] = -INFINITY;
       }
     }
 #pragma unroll
@@ -593,7 +640,7 @@ __global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(
 #pragma unroll
       for (int u = 0; u < TPL; ++u) {
         const float p = fast_exp2(x[u][j] - mnew);
-        const bool valid = !tail || tr + 16 * u < rem;
+        const bool valid = !tail || pm.valid(tr + 16 * u);
         float pv = p;
         if constexpr (INT8) {
           const float vs = (float)__builtin_bit_cast(_Float16, uint16_t(R.vm[u] & 0xffffu));
@@ -627,7 +674,7 @@ __global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(
             f = bf16_to_f32((wv[idx >> 1] >> (16 * (idx & 1))) & 0xffffu);
           else
             f = float(int8_t((wv[idx >> 2] >> (8 * (idx & 3))) & 0xffu));
-          if (!INT8 && tail && t >= rem) f = 0.0f;
+          if (!INT8 && tail && !pm.valid(t)) f = 0.0f;
           vv[e][t] = f;
         }
     }
@@ -776,11 +823,22 @@ hipError_t launch_merge(const float* part_o, const float* part_ml, uint16_t* out
 
 // Validate the decode arguments and fill the plan.  partials_only forces the
 // split kernel to write (o, m, l) partials even for one split.
+// Tokens the planner sizes splits for: with a window, a sequence streams at
+// most ceil(sink/P) + ceil(window/P) + 1 pages.
+int32_t planned_context(int32_t max_context_len, int32_t page_size, int32_t sink_tokens,
+                        int32_t window_tokens) {
+  if (window_tokens <= 0) return max_context_len;
+  const int64_t blocks = (int64_t(sink_tokens) + page_size - 1) / page_size +
+                         (int64_t(window_tokens) + page_size - 1) / page_size + 1;
+  return int32_t(std::min<int64_t>(max_context_len, blocks * page_size));
+}
+
 kvp_status prepare_decode(const kvp_pool* pool, const void* q, const void* k_pool,
                           const void* v_pool, const void* k_meta, const void* v_meta,
                           const int32_t* block_tables, int32_t max_blocks,
                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                           int32_t max_context_len, float scale, int32_t num_splits_req,
+                          int32_t sink_tokens, int32_t window_tokens,
                           kvp_pool_desc* d, kvp_decode_plan_t* plan, bool* empty) {
   *empty = false;
   if (kvp_pool_get_desc(pool, d) != KVP_OK) return KVP_E_INVAL;
@@ -790,6 +848,7 @@ kvp_status prepare_decode(const kvp_pool* pool, const void* q, const void* k_poo
   if (max_context_len < 0 || int64_t(max_context_len) > int64_t(max_blocks) * d->page_size)
     return KVP_E_INVAL;
   if (!std::isfinite(scale)) return KVP_E_INVAL;
+  if (sink_tokens < 0 || window_tokens < 0) return KVP_E_INVAL;
   if (num_seqs == 0) {
     *empty = true;
     return KVP_OK;
@@ -799,8 +858,10 @@ kvp_status prepare_decode(const kvp_pool* pool, const void* q, const void* k_poo
   if (int8 != (k_meta != nullptr) || int8 != (v_meta != nullptr)) return KVP_E_INVAL;
   const int cus = kvp::cu_count_current_device();
   if (cus <= 0) return KVP_E_HIP;
-  const kvp_status st =
-      kvp_decode_plan(d, num_seqs, num_q_heads, max_context_len, num_splits_req, cus, plan);
+  const kvp_status st = kvp_decode_plan(
+      d, num_seqs, num_q_heads,
+      planned_context(max_context_len, d->page_size, sink_tokens, window_tokens),
+      num_splits_req, cus, plan);
   if (st != KVP_OK) return st;
   if (int64_t(num_seqs) * d->num_kv_heads * plan->num_splits > 0x7fffffff)
     return KVP_E_UNSUPPORTED;
@@ -813,6 +874,7 @@ kvp_status launch_split_kernel(const kvp_pool_desc& d, const kvp_decode_plan_t& 
                                const int32_t* block_tables, int32_t max_blocks,
                                const int32_t* context_lens, int32_t num_seqs,
                                int32_t num_q_heads, int32_t max_context_len, float scale,
+                               int32_t sink_tokens, int32_t window_tokens,
                                void* out, float* part_o, float* part_ml, hipStream_t s) {
   using namespace kvp;
   const int g = num_q_heads / d.num_kv_heads;
@@ -836,6 +898,8 @@ kvp_status launch_split_kernel(const kvp_pool_desc& d, const kvp_decode_plan_t& 
   a.num_splits = plan.num_splits;
   a.pages_per_split = plan.pages_per_split;
   a.ctx_cap = max_context_len;
+  a.sink_tokens = sink_tokens;
+  a.window_tokens = window_tokens;
   a.write_partials = part_o != nullptr;
   a.scale_log2 = scale * kLog2e;
 
@@ -878,18 +942,22 @@ extern "C" kvp_status kvp_decode_workspace_bytes(const kvp_pool* pool, int32_t n
   return KVP_OK;
 }
 
-extern "C" kvp_status kvp_paged_attention_decode(
-    const kvp_pool* pool, const void* q, const void* k_pool, const void* v_pool,
-    const void* k_meta, const void* v_meta, const int32_t* block_tables, int32_t max_blocks,
-    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
-    float scale, void* out, int32_t num_splits_req, void* workspace, size_t workspace_bytes,
-    kvp_stream_t stream) {
+namespace {
+
+kvp_status decode_full(const kvp_pool* pool, const void* q, const void* k_pool, const void* v_pool,
+                       const void* k_meta, const void* v_meta, const int32_t* block_tables,
+                       int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs,
+                       int32_t num_q_heads, int32_t max_context_len, float scale,
+                       int32_t sink_tokens, int32_t window_tokens, void* out,
+                       int32_t num_splits_req, void* workspace, size_t workspace_bytes,
+                       kvp_stream_t stream) {
   kvp_pool_desc d;
   kvp_decode_plan_t plan;
   bool empty;
   kvp_status st = prepare_decode(pool, q, k_pool, v_pool, k_meta, v_meta, block_tables,
                                  max_blocks, context_lens, num_seqs, num_q_heads,
-                                 max_context_len, scale, num_splits_req, &d, &plan, &empty);
+                                 max_context_len, scale, num_splits_req, sink_tokens,
+                                 window_tokens, &d, &plan, &empty);
   if (st != KVP_OK || empty) return st;
   if (!out) return KVP_E_INVAL;
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
@@ -904,14 +972,53 @@ extern "C" kvp_status kvp_paged_attention_decode(
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   st = launch_split_kernel(d, plan, q, k_pool, v_pool, k_meta, v_meta, block_tables, max_blocks,
-                           context_lens, num_seqs, num_q_heads, max_context_len, scale, out,
-                           part_o, part_ml, s);
+                           context_lens, num_seqs, num_q_heads, max_context_len, scale,
+                           sink_tokens, window_tokens, out, part_o, part_ml, s);
   if (st != KVP_OK) return st;
   if (plan.num_splits > 1 &&
       launch_merge(part_o, part_ml, static_cast<uint16_t*>(out), num_seqs * num_q_heads,
                    plan.num_splits, d.head_dim, s) != hipSuccess)
     return KVP_E_HIP;
   return KVP_OK;
+}
+
+}  // namespace
+
+extern "C" kvp_status kvp_paged_attention_decode(
+    const kvp_pool* pool, const void* q, const void* k_pool, const void* v_pool,
+    const void* k_meta, const void* v_meta, const int32_t* block_tables, int32_t max_blocks,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    float scale, void* out, int32_t num_splits_req, void* workspace, size_t workspace_bytes,
+    kvp_stream_t stream) {
+  return decode_full(pool, q, k_pool, v_pool, k_meta, v_meta, block_tables, max_blocks,
+                     context_lens, num_seqs, num_q_heads, max_context_len, scale, 0, 0, out,
+                     num_splits_req, workspace, workspace_bytes, stream);
+}
+
+extern "C" kvp_status kvp_decode_window_workspace_bytes(const kvp_pool* pool, int32_t num_seqs,
+                                                        int32_t num_q_heads,
+                                                        int32_t max_context_len,
+                                                        int32_t sink_tokens,
+                                                        int32_t window_tokens,
+                                                        int32_t num_splits_req, size_t* bytes) {
+  kvp_pool_desc d;
+  if (!bytes || kvp_pool_get_desc(pool, &d) != KVP_OK) return KVP_E_INVAL;
+  if (sink_tokens < 0 || window_tokens < 0 || max_context_len < 0) return KVP_E_INVAL;
+  return kvp_decode_workspace_bytes(
+      pool, num_seqs, num_q_heads,
+      planned_context(max_context_len, d.page_size, sink_tokens, window_tokens), num_splits_req,
+      bytes);
+}
+
+extern "C" kvp_status kvp_paged_attention_decode_window(
+    const kvp_pool* pool, const void* q, const void* k_pool, const void* v_pool,
+    const void* k_meta, const void* v_meta, const int32_t* block_tables, int32_t max_blocks,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    float scale, int32_t sink_tokens, int32_t window_tokens, void* out, int32_t num_splits_req,
+    void* workspace, size_t workspace_bytes, kvp_stream_t stream) {
+  return decode_full(pool, q, k_pool, v_pool, k_meta, v_meta, block_tables, max_blocks,
+                     context_lens, num_seqs, num_q_heads, max_context_len, scale, sink_tokens,
+                     window_tokens, out, num_splits_req, workspace, workspace_bytes, stream);
 }
 
 extern "C" kvp_status kvp_decode_partials_bytes(const kvp_pool* pool, int32_t num_seqs,
@@ -942,7 +1049,7 @@ extern "C" kvp_status kvp_paged_attention_decode_partials(
   bool empty;
   kvp_status st = prepare_decode(pool, q, k_pool, v_pool, k_meta, v_meta, block_tables,
                                  max_blocks, context_lens, num_seqs, num_q_heads,
-                                 max_context_len, scale, num_splits_req, &d, &plan, &empty);
+                                 max_context_len, scale, num_splits_req, 0, 0, &d, &plan, &empty);
   if (st != KVP_OK) return st;
   if (empty) {
     if (num_splits) *num_splits = 0;
@@ -954,8 +1061,8 @@ extern "C" kvp_status kvp_paged_attention_decode_partials(
   float* part_ml = reinterpret_cast<float*>(static_cast<char*>(partials) +
                                             partials_o_bytes(parts, d.head_dim));
   st = launch_split_kernel(d, plan, q, k_pool, v_pool, k_meta, v_meta, block_tables, max_blocks,
-                           context_lens, num_seqs, num_q_heads, max_context_len, scale, nullptr,
-                           part_o, part_ml, reinterpret_cast<hipStream_t>(stream));
+                           context_lens, num_seqs, num_q_heads, max_context_len, scale, 0, 0,
+                           nullptr, part_o, part_ml, reinterpret_cast<hipStream_t>(stream));
   if (st == KVP_OK && num_splits) *num_splits = plan.num_splits;
   return st;
 }

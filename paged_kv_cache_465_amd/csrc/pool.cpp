@@ -166,6 +166,29 @@ kvp_status kvp_seq_release(kvp_pool* pool, int32_t* row, int32_t n_blocks) {
   return KVP_OK;
 }
 
+// Pages of a sequence that hold only tokens a sink + window decode drops:
+// blocks ceil(sink/P) .. floor((n - window)/P) - 1 ("KV-Cache Optimization
+// Techniques", section "Token Eviction Strategies", eq. 5; section "Sliding
+// Window Cache", eq. 6: memory stays bounded by the window).  Their references
+// are dropped and the entries set to -1; entries already -1 are skipped.
+kvp_status kvp_seq_evict_window(kvp_pool* pool, int32_t* row, int32_t max_blocks, int32_t ctx_len,
+                                int32_t sink_tokens, int32_t window_tokens) {
+  if (!pool || !row || max_blocks <= 0 || ctx_len < 0 || sink_tokens < 0 || window_tokens <= 0)
+    return KVP_E_INVAL;
+  const int32_t P = pool->desc.page_size;
+  if (ceil_div(ctx_len, P) > max_blocks) return KVP_E_INVAL;
+  if (int64_t(sink_tokens) + window_tokens >= ctx_len) return KVP_OK;
+  const int32_t first = ceil_div(sink_tokens, P);
+  const int32_t last = (ctx_len - window_tokens) / P;  // exclusive
+  std::vector<int32_t> ids;
+  for (int32_t i = first; i < last; ++i)
+    if (row[i] >= 0) ids.push_back(row[i]);
+  const kvp_status s = kvp_pages_free(pool, int32_t(ids.size()), ids.data());
+  if (s != KVP_OK) return s;
+  for (int32_t i = first; i < last; ++i) row[i] = -1;
+  return KVP_OK;
+}
+
 // Split planner.  A workgroup covers one (sequence, KV head) pair and one range
 // of logical blocks; its wavefronts share the range page by page.  Measured on
 // MI355X, page streaming peaks with about one wavefront per SIMD (four per

@@ -294,3 +294,75 @@ def pin_shared_prefix_memory():
     assert slots - unique_tokens == 1200
     # only each sequence's own last page has empty slots
     assert sum(oracle.waste(int(n), cfg.page_size) for n in case.ctx) == 1200
+
+
+# ---------------------------------------------------------------- sinks + window
+def pin_window_vs_sdpa(case, sink, window, tol=1e-12):
+    """Eq. 5: with s sinks and a w-token window the output is attention over
+    the rows t < s and t >= n - w of the contiguous sequence, computed by the
+    library routine on rows chosen by a boolean mask over 0..n-1."""
+    k, v, km, vm = oracle_pools(case)
+    lay = layout_of(case)
+    out = oracle.paged_decode_window(lay, case.q, k, v, km, vm, case.block_tables, case.ctx,
+                                     case.scale, sink, window)
+    for b in range(case.B):
+        K, V = logical_rows(case, b)
+        n = K.shape[0]
+        t = np.arange(n)
+        keep = (t < sink) | (t >= n - window) if sink + window < n else np.ones(n, bool)
+        if case.cfg.kv_dtype == "int8":
+            Kf = np.stack([_dequant_exact(K[i]) for i in np.nonzero(keep)[0]])
+            Vf = np.stack([_dequant_exact(V[i]) for i in np.nonzero(keep)[0]])
+        else:
+            Kf, Vf = _bf16_f64(K[keep]), _bf16_f64(V[keep])
+        ref = _sdpa(_bf16_f64(case.q[b]), Kf, Vf, float(np.float32(case.scale)))
+        err = np.abs(out[b] - ref).max()
+        assert err <= tol, f"seq {b} (s={sink}, w={window}): oracle vs sdpa {err:.3e}"
+
+
+def pin_window_degenerate(case):
+    """No window (w = 0) or s + w >= n: exactly the full decode.  s = 0: exactly
+    attention over the last w rows (eq. 6, K_{t-w+1:t})."""
+    k, v, km, vm = oracle_pools(case)
+    lay = layout_of(case)
+    full = oracle.paged_decode(lay, case.q, k, v, km, vm, case.block_tables, case.ctx, case.scale)
+    n_max = int(case.ctx.max())
+    for s, w in ((0, 0), (5, 0), (0, n_max), (3, n_max - 3), (n_max, 1)):
+        got = oracle.paged_decode_window(lay, case.q, k, v, km, vm, case.block_tables, case.ctx,
+                                         case.scale, s, w)
+        assert np.array_equal(got, full), (s, w)
+    w = 7
+    got = oracle.paged_decode_window(lay, case.q, k, v, km, vm, case.block_tables, case.ctx,
+                                     case.scale, 0, w)
+    qf = _bf16_f64(case.q)
+    sc = float(np.float32(case.scale))
+    for b in range(case.B):
+        n = int(case.ctx[b])
+        K, V = oracle.gather_sequence(lay, k, v, km, vm, case.block_tables[b], n)
+        ref = oracle.attend(qf[b], K[:, max(n - w, 0):], V[:, max(n - w, 0):], sc)
+        assert np.array_equal(got[b], ref), b
+
+
+def pin_window_memory_bound(page_size=16, sink=4, window=40, steps=400):
+    """Eq. 6: memory is bounded whatever the context.  A sequence grown one
+    token at a time, evicting after each step, never holds more than
+    ceil(s/P) + ceil(w/P) + 1 pages, and always holds every page a kept
+    position lies in (so at least the w * 2 * L * d_k values of eq. 6)."""
+    model = oracle.PoolModel(10_000)
+    held = {}
+    bound = -(-sink // page_size) + -(-window // page_size) + 1
+    next_id = 0
+    for n in range(1, steps + 1):
+        blk = (n - 1) // page_size
+        if blk not in held:
+            model.check_alloc(1, [next_id])
+            held[blk] = next_id
+            next_id += 1
+        drop = [b for b in oracle.window_evicted_blocks(n, page_size, sink, window) if b in held]
+        model.free([held.pop(b) for b in drop])
+        assert len(held) <= bound, (n, len(held), bound)
+        kept_blocks = set((oracle.kept_positions(n, sink, window) // page_size).tolist())
+        assert kept_blocks <= set(held), n
+        # the pages held carry at least eq. 6's |cache| (one layer, d_k = 128)
+        assert len(held) * page_size * 2 * 128 >= oracle.window_cache_elems(min(n, window), 1, 128)
+    assert model.free_count == 10_000 - len(held)

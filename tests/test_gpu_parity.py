@@ -263,7 +263,19 @@ def _sampled_check(kvp, cfg, seqs, splits=0):
     gc = GpuCase(kvp, case)
     gc.append_history()
     gc.append_new()
-    out = gc.decode(num_splits=splits)
+    if cfg.window_tokens > 0:
+        mx = int(case.ctx.max())
+        wsb = kvp.kvp_decode_window_workspace_bytes(gc.pool, case.B, cfg.num_q_heads, mx,
+                                                    cfg.sink_tokens, cfg.window_tokens, splits)
+        ws = torch.full((max(wsb, 4) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        o = torch.empty_like(gc.q)
+        kvp.kvp_paged_attention_decode_window(gc.pool, gc.q, gc.k_pool, gc.v_pool, gc.k_meta,
+                                              gc.v_meta, gc.bt, gc.ctx, mx, float(case.scale),
+                                              cfg.sink_tokens, cfg.window_tokens, o, splits, ws)
+        torch.cuda.synchronize()
+        out = o.cpu().numpy().view(np.uint16)
+    else:
+        out = gc.decode(num_splits=splits)
     # oracle: only the sampled sequences' rows (prefix rows of sequence 0 too)
     lay = layout_of(case)
     from workloads import POISON_BF16, POISON_F16, POISON_I8
@@ -279,6 +291,7 @@ def _sampled_check(kvp, cfg, seqs, splits=0):
     per_page = cfg.num_kv_heads * cfg.page_size * cfg.head_dim
     for b in seqs:
         pages = case.block_tables[b][: -(-int(case.ctx[b]) // cfg.page_size)]
+        pages = pages[pages >= 0]
         for name, g, r, n in (("K", gk, k, per_page), ("V", gv, v, per_page),
                               ("Km", gkm, km, per_page // cfg.head_dim * 2),
                               ("Vm", gvm, vm, per_page // cfg.head_dim * 2)):
@@ -287,8 +300,13 @@ def _sampled_check(kvp, cfg, seqs, splits=0):
             gp = g.reshape(case.num_pages, n)[pages]
             rp = r.reshape(case.num_pages, n)[pages]
             assert np.array_equal(gp.view(np.uint8), rp.view(np.uint8)), f"{name} pages of seq {b}"
-    ref = oracle.paged_decode(lay, case.q, k, v, km, vm, case.block_tables, case.ctx, case.scale,
-                              seqs=seqs)
+    if cfg.window_tokens > 0:
+        ref = oracle.paged_decode_window(lay, case.q, k, v, km, vm, case.block_tables, case.ctx,
+                                         case.scale, cfg.sink_tokens, cfg.window_tokens,
+                                         seqs=seqs)
+    else:
+        ref = oracle.paged_decode(lay, case.q, k, v, km, vm, case.block_tables, case.ctx,
+                                  case.scale, seqs=seqs)
     seqs = list(seqs)
     m, r = assert_close(out[seqs], ref[seqs], cfg.name)
     log(f"  max_abs={m:.2e} rel_l2={r:.2e}")
@@ -305,6 +323,13 @@ def test_full_int8_long(kvp):
 
 def test_full_shared_prefix(kvp):
     _sampled_check(kvp, SHARED_PREFIX_MQA, seqs=range(0, 100, 9))
+
+
+def test_full_streaming_window(kvp):
+    """64 sequences at 32,768 tokens whose caches hold 4 sink tokens and the
+    last 4,096 (dropped pages were never allocated: table entries -1)."""
+    from workloads import STREAMING_WINDOW
+    _sampled_check(kvp, STREAMING_WINDOW, seqs=(0, 21, 63))
 
 
 def test_append_special_rows_int8(kvp):
@@ -418,4 +443,94 @@ def test_partials_layout_and_merge(kvp, cfg, splits):
                 assert abs(pml[b, j, s, 0] - m) <= 1e-4 * max(1.0, abs(m)), (b, j, s)
                 assert abs(pml[b, j, s, 1] - l) <= 1e-4 * l, (b, j, s)
                 assert np.abs(po[b, j, s] - o).max() <= 2e-3 * max(1.0, np.abs(o).max()), (b, j, s)
+    gc.close()
+
+
+# ---- sinks + recent window ("Token Eviction Strategies", eq. 5; eq. 6 with s = 0) --------
+def _evicted_case(case, sink, window):
+    """Oracle pools with every page that only holds dropped tokens poisoned and
+    its table entries set to -1 (pages a kept block still names stay)."""
+    from workloads import POISON_BF16, POISON_F16, POISON_I8
+    c = case.cfg
+    P = c.page_size
+    k, v, km, vm = (None if a is None else a.copy() for a in _oracle(case)[:4])
+    bt = case.block_tables.copy()
+    kept_pages, dropped_pages = set(), set()
+    for b in range(case.B):
+        n = int(case.ctx[b])
+        drop = oracle.window_evicted_blocks(n, P, sink, window)
+        for i in range(-(-n // P)):
+            (dropped_pages if i in drop else kept_pages).add(int(bt[b, i]))
+        bt[b, drop] = -1
+    per_page = c.num_kv_heads * P * c.head_dim
+    int8 = c.kv_dtype == "int8"
+    for p in dropped_pages - kept_pages:
+        if int8:
+            k.view(np.uint8).reshape(case.num_pages, per_page)[p] = POISON_I8
+            v.view(np.uint8).reshape(case.num_pages, per_page)[p] = POISON_I8
+            km.reshape(case.num_pages, -1)[p] = POISON_F16
+            vm.reshape(case.num_pages, -1)[p] = POISON_F16
+        else:
+            k.reshape(case.num_pages, per_page)[p] = POISON_BF16
+            v.reshape(case.num_pages, per_page)[p] = POISON_BF16
+    return k, v, km, vm, bt, len(dropped_pages - kept_pages)
+
+
+WINDOW_CFGS = [c for c in SMALL if c.name in ("tiny", "tiny_g1", "tiny_g2", "tiny_p32_d64",
+                                               "l8b_small", "l8b_small_g16", "int8_small",
+                                               "int8_small_g2", "int8_small_p16_d64",
+                                               "prefix_small")]
+
+
+@pytest.mark.parametrize("cfg", WINDOW_CFGS, ids=lambda c: c.name)
+@pytest.mark.parametrize("sink,window", [(4, 64), (0, 17), (16, 33), (1, 1), (3, 200)])
+def test_window_decode_matches_oracle(kvp, cfg, sink, window):
+    """Sinks + window decode against the oracle, with the dropped pages freed
+    (table entries -1) and their bytes NaN-poisoned: nothing dropped is read."""
+    case = _case(cfg)
+    k, v, km, vm, bt, n_poisoned = _evicted_case(case, sink, window)
+    lay = layout_of(case)
+    ref = oracle.paged_decode_window(lay, case.q, k, v, km, vm, bt, case.ctx, case.scale, sink,
+                                     window)
+    log(f"[window] {cfg.name} s={sink} w={window} poisoned_pages={n_poisoned}")
+    gc = GpuCase(kvp, case, block_tables=bt)
+    gc.upload(k, v, km, vm)
+    c = case.cfg
+    mx = int(case.ctx.max())
+    for splits in (0, 1, 3):
+        wsb = kvp.kvp_decode_window_workspace_bytes(gc.pool, case.B, c.num_q_heads, mx, sink,
+                                                    window, splits)
+        ws = (torch.full((max(wsb, 4) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+              if wsb else None)
+        out = torch.full_like(gc.q, int(np.uint16(0x7FC0).view(np.int16)))
+        kvp.kvp_paged_attention_decode_window(gc.pool, gc.q, gc.k_pool, gc.v_pool, gc.k_meta,
+                                              gc.v_meta, gc.bt, gc.ctx, mx, float(case.scale),
+                                              sink, window, out, splits, ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint16)
+        m, r = assert_close(got, ref, f"{cfg.name} s={sink} w={window} S={splits}")
+    gc.close()
+
+
+@pytest.mark.parametrize("cfg", [SMALL[0], SMALL[6], SMALL[11]], ids=lambda c: c.name)
+def test_window_covering_everything_is_the_full_decode(kvp, cfg):
+    """window_tokens = 0, or sink + window >= every length: bit-identical to
+    kvp_paged_attention_decode (same kernel path, nothing dropped)."""
+    case = _case(cfg)
+    log(f"[window=all] {cfg.name}")
+    gc = GpuCase(kvp, case)
+    gc.upload(*_oracle(case)[:4])
+    full = gc.decode(num_splits=2)
+    c = case.cfg
+    mx = int(case.ctx.max())
+    for sink, window in ((0, 0), (0, mx), (mx, 1), (7, mx - 7)):
+        wsb = kvp.kvp_decode_window_workspace_bytes(gc.pool, case.B, c.num_q_heads, mx, sink,
+                                                    window, 2)
+        ws = torch.empty((max(wsb, 4) // 4,), dtype=torch.float32, device="cuda")
+        out = torch.empty_like(gc.q)
+        kvp.kvp_paged_attention_decode_window(gc.pool, gc.q, gc.k_pool, gc.v_pool, gc.k_meta,
+                                              gc.v_meta, gc.bt, gc.ctx, mx, float(case.scale),
+                                              sink, window, out, 2, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint16), full), (sink, window)
     gc.close()

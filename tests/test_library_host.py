@@ -233,3 +233,36 @@ def test_merge_and_partials_argument_checks(kvp):
         pool.handle, dummy, dummy, dummy, dummy, dummy, dummy, 4, dummy, 2, 64, 64, 0.1, 0, dummy,
         1 << 20, ctypes.byref(ns), None) == kvp.KVP_E_INVAL
     pool.close()
+
+
+@pytest.mark.parametrize("P,n,sink,window", [(16, 300, 4, 64), (16, 300, 0, 17), (32, 1000, 40, 100),
+                                             (16, 100, 90, 20), (16, 33, 0, 1), (32, 65, 31, 2)])
+def test_evict_window_frees_the_oracle_blocks(kvp, P, n, sink, window):
+    """kvp_seq_evict_window releases exactly the blocks that hold no kept
+    position (derived by the oracle from the kept set), leaves the others,
+    and is idempotent; a shared page only loses one reference."""
+    d = kvp.make_desc(64, P, 1, 64, "bf16")
+    pool = kvp.kvp_pool_create(d)
+    mb = -(-n // P)
+    row = np.full(mb, -1, dtype=np.int32)
+    kvp.kvp_seq_grow(pool, row, 0, n)
+    other = np.full(mb, -1, dtype=np.int32)
+    kvp.kvp_seq_share(pool, row, other, 1)              # block 0 shared by a second sequence
+    before = row.copy()
+    free0 = kvp.kvp_pool_free_count(pool)
+    kvp.kvp_seq_evict_window(pool, row, n, sink, window)
+    dropped = oracle.window_evicted_blocks(n, P, sink, window)
+    for i in range(mb):
+        if i in dropped:
+            assert row[i] == -1
+        else:
+            assert row[i] == before[i]
+    freed_pages = [before[i] for i in dropped if not (i == 0)]
+    assert kvp.kvp_pool_free_count(pool) == free0 + len(freed_pages)
+    if 0 in dropped:
+        assert kvp.kvp_pool_refcount(pool, int(before[0])) == 1   # still held by `other`
+    kvp.kvp_seq_evict_window(pool, row, n, sink, window)          # idempotent
+    assert kvp.kvp_pool_free_count(pool) == free0 + len(freed_pages)
+    with pytest.raises(kvp.KvpError):
+        kvp.kvp_seq_evict_window(pool, row, n, sink, 0)
+    pool.close()

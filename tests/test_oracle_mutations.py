@@ -42,6 +42,11 @@ def _all_pins():
             checks.append((f"layout_{c.name}",
                            lambda c=c: pins.pin_append_and_gather_layout(_case(c))))
         checks.append((f"sdpa_{c.name}", lambda c=c: pins.pin_attention_vs_sdpa(_case(c))))
+    for sink, window in ((4, 16), (0, 7)):
+        checks.append((f"window_{sink}_{window}",
+                       lambda s=sink, w=window: pins.pin_window_vs_sdpa(_case(TINY), s, w)))
+    checks.append(("window_degenerate", lambda: pins.pin_window_degenerate(_case(TINY))))
+    checks.append(("window_memory", pins.pin_window_memory_bound))
     return checks
 
 
@@ -167,7 +172,31 @@ _ORIG_GATHER = opa.gather_sequence
 _ORIG_DEQUANT = oq.dequantize
 _ORIG_APPEND = opa.append
 
+def _kept_off_by_one(n, sink, window):
+    if window <= 0 or sink + window >= n:
+        return np.arange(n)
+    return np.concatenate([np.arange(sink), np.arange(n - window + 1, n)])
+
+
+def _kept_no_sinks(n, sink, window):
+    if window <= 0 or sink + window >= n:
+        return np.arange(n)
+    return np.arange(n - window, n)
+
+
+def _kept_overlap_twice(n, sink, window):
+    if window <= 0:
+        return np.arange(n)
+    return np.concatenate([np.arange(min(sink, n)), np.arange(max(n - window, 0), n)])
+
+
 MUTANTS = {
+    "window_off_by_one": [(opa, "kept_positions", _kept_off_by_one),
+                          (oracle, "kept_positions", _kept_off_by_one)],
+    "window_sinks_dropped": [(opa, "kept_positions", _kept_no_sinks),
+                             (oracle, "kept_positions", _kept_no_sinks)],
+    "window_overlap_counted_twice": [(opa, "kept_positions", _kept_overlap_twice),
+                                     (oracle, "kept_positions", _kept_overlap_twice)],
     "gqa_interleaved_groups": [(opa, "attend", _attend_wrong_group),
                                (oracle, "attend", _attend_wrong_group)],
     "scale_dropped": [(opa, "attend", _attend_no_scale), (oracle, "attend", _attend_no_scale)],

@@ -84,3 +84,17 @@ def test_pool_model_semantics():
     assert m.refcount(0) == 1 and m.refcount(2) == 0 and m.free_count == 2
     with pytest.raises(oracle.AllocError):
         m.share([2])
+
+
+@pytest.mark.parametrize("sink,window", [(0, 7), (4, 16), (1, 1), (16, 33), (3, 50)])
+def test_window_vs_library_sdpa(small_case, sink, window):
+    pins.pin_window_vs_sdpa(small_case, sink, window)
+
+
+def test_window_degenerate_cases(small_case):
+    pins.pin_window_degenerate(small_case)
+
+
+def test_window_memory_bound():
+    pins.pin_window_memory_bound()
+    pins.pin_window_memory_bound(page_size=32, sink=0, window=100, steps=700)

@@ -40,6 +40,8 @@ class DecodeConfig:
     outlier_channels: int = 0       # channels (of H_kv*D) scaled by outlier_gain, K and V drawn separately
     outlier_gain: float = 1.0
     q_gain: float = 1.0
+    sink_tokens: int = 0            # with window_tokens > 0: the cache holds only positions
+    window_tokens: int = 0          #   < sink_tokens and the last window_tokens positions
     device_data: bool = False       # draw K/V/q on the GPU with torch's generator (too big for host)
     seed: int = BASE_SEED
 
@@ -81,6 +83,17 @@ SHARED_PREFIX_MQA = DecodeConfig(
 
 CONFIGS = {c.name: c for c in (TINY, LLAMA3_8B_LAYER, LLAMA3_70B_FULL, INT8_LONG,
                                SHARED_PREFIX_MQA)}
+
+# Streaming decode with attention sinks and a recent window ("KV-Cache
+# Optimization Techniques", section "Token Eviction Strategies", eq. 5): a
+# Llama-3-8B-shaped layer, 64 sequences that have reached 32,768 tokens, of
+# which the cache still holds the first 4 and the last 4,096.
+STREAMING_WINDOW = DecodeConfig(
+    name="streaming_window", layers=1, batch=64, num_q_heads=32, num_kv_heads=8,
+    head_dim=128, page_size=16, ctx_fixed=(32768,) * 64, sink_tokens=4, window_tokens=4096,
+    seed=465006)
+
+EXTRA_CONFIGS = {c.name: c for c in (STREAMING_WINDOW,)}
 
 
 def variant(cfg: DecodeConfig, **kw) -> DecodeConfig:

@@ -97,22 +97,34 @@ def _history_ranges(cfg: DecodeConfig, ctx: np.ndarray):
     return starts
 
 
+def held_positions(cfg: DecodeConfig, n: int) -> np.ndarray:
+    """Positions the workload's cache holds for a sequence of n tokens: all of
+    them, or (window configs) those below sink_tokens and the last
+    window_tokens."""
+    if cfg.window_tokens <= 0 or cfg.sink_tokens + cfg.window_tokens >= n:
+        return np.arange(n)
+    return np.concatenate([np.arange(cfg.sink_tokens), np.arange(n - cfg.window_tokens, n)])
+
+
 def _tables(cfg: DecodeConfig, ctx: np.ndarray, rng: np.random.Generator):
     P = cfg.page_size
     n_prefix = cfg.shared_prefix // P
-    own = [_ceil_div(int(n), P) - n_prefix for n in ctx]
-    used = n_prefix + sum(own)
+    # blocks each sequence holds pages for (beyond the shared prefix)
+    own_blocks = [np.unique(held_positions(cfg, int(n)) // P) for n in ctx]
+    own_blocks = [blk[blk >= n_prefix] for blk in own_blocks]
+    used = n_prefix + sum(len(o) for o in own_blocks)
     num_pages = cfg.pool_pages if cfg.pool_pages is not None else \
         int(np.ceil((1.0 + cfg.pool_slack) * used))
     assert num_pages >= used
     perm = rng.permutation(num_pages).astype(np.int32)
-    max_blocks = max(n_prefix + o for o in own)
+    max_blocks = max(_ceil_div(int(n), P) for n in ctx)
     bt = np.full((cfg.batch, max_blocks), -1, dtype=np.int32)
     cursor = n_prefix
     for b in range(cfg.batch):
         bt[b, :n_prefix] = perm[:n_prefix]
-        bt[b, n_prefix:n_prefix + own[b]] = perm[cursor:cursor + own[b]]
-        cursor += own[b]
+        k = len(own_blocks[b])
+        bt[b, own_blocks[b]] = perm[cursor:cursor + k]
+        cursor += k
     return num_pages, max_blocks, bt
 
 
@@ -153,7 +165,8 @@ def make_case(cfg: DecodeConfig, with_data: bool = True) -> DecodeCase:
     starts = _history_ranges(cfg, ctx)
     seqs, poss = [], []
     for b in range(B):
-        p = np.arange(starts[b], ctx[b] - 1, dtype=np.int32)
+        p = held_positions(cfg, int(ctx[b])).astype(np.int32)
+        p = p[(p >= starts[b]) & (p < ctx[b] - 1)]
         poss.append(p)
         seqs.append(np.full(p.shape, b, dtype=np.int32))
     case.hist_seq = np.concatenate(seqs) if seqs else np.zeros(0, np.int32)
