@@ -36,6 +36,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD's published figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix-core peak
 PROFILES = os.path.join(ROOT, "profiles")
 # sources that decide the split kernel's code and launch shape
 KERNEL_SOURCES = ("paged_kv_cache_465_amd/csrc/decode.hip",
@@ -65,7 +66,26 @@ def parse_args(argv=None):
 
 
 # ---- algorithmic bytes -----------------------------------------------------------
-def step_bytes(cfg, ctx: np.ndarray) -> dict:
+def is_chunked(cfg) -> bool:
+    return cfg.q_len > 1 or cfg.q_len_hi > 1
+
+
+def step_flops(cfg, ctx: np.ndarray, q_start: np.ndarray) -> int:
+    """Multiply-adds x 2 of q.K^T and P.V over every (query row, position it
+    attends to), all layers: 4 * D * H_q per (row, position)."""
+    total = 0
+    for b in range(len(ctx)):
+        n, L = int(ctx[b]), int(q_start[b + 1] - q_start[b])
+        if cfg.window_tokens > 0:
+            n_att = min(n, cfg.sink_tokens + cfg.window_tokens)
+            total += L * n_att
+        else:
+            pos = n - L + np.arange(L)
+            total += int(np.maximum(pos + 1, 0).sum())
+    return 4 * cfg.head_dim * cfg.num_q_heads * total * cfg.layers
+
+
+def step_bytes(cfg, ctx: np.ndarray, n_rows: int = None) -> dict:
     """Bytes a step must move at minimum, per term, summed over sequences and layers.
 
     Per sequence of n tokens and per layer: K and V rows n*H_kv*D elements each
@@ -83,11 +103,12 @@ def step_bytes(cfg, ctx: np.ndarray) -> dict:
     if cfg.kv_dtype == "int8":
         kv += int((n * Hkv * 2 * 4).sum())
     B = int(n.shape[0])
-    q_out = B * Hq * D * 2 * 2
+    N = B if n_rows is None else int(n_rows)     # query rows (new tokens) in a step
+    q_out = N * Hq * D * 2 * 2
     table = int((-(-n // P) * 4).sum()) + B * 4
-    append = B * Hkv * D * 2 * 2 * (1 + eb / 2) + (B * Hkv * 2 * 4 if cfg.kv_dtype == "int8" else 0)
+    append = N * Hkv * D * 2 * 2 * (1 + eb / 2) + (N * Hkv * 2 * 4 if cfg.kv_dtype == "int8" else 0)
     return {"kv": kv * L, "q_out": q_out * L, "table": table * L, "append": int(append) * L,
-            "split_kernel_per_launch": kv + B * Hq * D * 2 + table}
+            "split_kernel_per_launch": kv + N * Hq * D * 2 + table}
 
 
 # ---- device setup ------------------------------------------------------------------
@@ -106,8 +127,8 @@ def setup_device(kvp, cfg, case, dev):
     int8 = cfg.kv_dtype == "int8"
     bt = torch.from_numpy(case.block_tables).to(dev)
     ctx = torch.from_numpy(case.ctx).to(dev)
-    seq_idx = torch.arange(case.B, dtype=torch.int32, device=dev)
-    new_pos = torch.from_numpy((case.ctx - 1).astype(np.int32)).to(dev)
+    seq_idx = torch.from_numpy(case.new_seq.astype(np.int32)).to(dev)
+    new_pos = torch.from_numpy(case.new_pos.astype(np.int32)).to(dev)
     layers = []
     t0 = time.perf_counter()
     for l in range(cfg.layers):
@@ -162,6 +183,9 @@ def run_gpu(args, kvp, cfg, case):
     log(f"[plan] {plan}")
 
     windowed = cfg.window_tokens > 0
+    chunked = is_chunked(cfg)
+    q_start = torch.from_numpy(case.q_start.astype(np.int32)).to(dev)
+    max_q_len = int(np.diff(case.q_start).max())
     if windowed:
         wsb = kvp.kvp_decode_window_workspace_bytes(pool, B, Hq, max_ctx, cfg.sink_tokens,
                                                     cfg.window_tokens, args.splits)
@@ -176,7 +200,12 @@ def run_gpu(args, kvp, cfg, case):
             timed = probe is not None and probe[0] == i
             if timed:
                 probe[1].record()
-            if windowed:
+            if chunked:
+                kvp.kvp_paged_attention_prefill(pool, L.q, q_start, L.k, L.v, L.km, L.vm, bt, ctx,
+                                                max_q_len, max_ctx, scale, L.out)
+                if timed:
+                    probe[2].record()
+            elif windowed:
                 kvp.kvp_paged_attention_decode_window(
                     pool, L.q, L.k, L.v, L.km, L.vm, bt, ctx, max_ctx, scale, cfg.sink_tokens,
                     cfg.window_tokens, L.out, args.splits, wspace)
@@ -297,6 +326,7 @@ def host_layer0(cfg, case, dev):
     c.q, c.hist_k, c.hist_v, c.new_k, c.new_v = h(q), h(hk), h(hv), h(nk), h(nv)
     c.hist_seq, c.hist_pos = hs.cpu().numpy(), hp.cpu().numpy()
     c.new_pos = npos.cpu().numpy()
+    c.new_seq = np.arange(c.B, dtype=np.int32)
     return c
 
 
@@ -312,15 +342,18 @@ def oracle_layer(cfg, hc, seqs):
     sel = np.isin(hc.hist_seq, list(need))
     oracle.append(lay, k, v, km, vm, hc.hist_k[sel], hc.hist_v[sel], hc.hist_seq[sel],
                   hc.hist_pos[sel], hc.block_tables)
-    idx = np.array(sorted(need), dtype=np.int32)
-    oracle.append(lay, k, v, km, vm, hc.new_k[idx], hc.new_v[idx], idx, hc.new_pos[idx],
-                  hc.block_tables)
+    nsel = np.isin(hc.new_seq, list(need))
+    oracle.append(lay, k, v, km, vm, hc.new_k[nsel], hc.new_v[nsel], hc.new_seq[nsel],
+                  hc.new_pos[nsel], hc.block_tables)
     return lay, (k, v, km, vm)
 
 
 def oracle_decode(cfg, lay, hc, pools, seqs):
     """The oracle's output for ``seqs`` (sinks + window when the config has one)."""
     import oracle
+    if is_chunked(cfg):
+        return oracle.paged_prefill(lay, hc.q, hc.q_start, *pools, hc.block_tables, hc.ctx,
+                                    hc.scale, seqs=seqs)
     if cfg.window_tokens > 0:
         return oracle.paged_decode_window(lay, hc.q, *pools, hc.block_tables, hc.ctx, hc.scale,
                                           cfg.sink_tokens, cfg.window_tokens, seqs=seqs)
@@ -351,7 +384,8 @@ def cpu_baseline(cfg, hc, target_s: float):
         dt += time.perf_counter() - t0
         passes += 1
     # bytes of the sample: one layer of the sampled sequences (same terms as the GPU)
-    sb = step_bytes(dataclasses.replace(cfg, layers=1, batch=n), hc.ctx[seqs])
+    n_rows = int(sum(hc.q_start[b + 1] - hc.q_start[b] for b in seqs))
+    sb = step_bytes(dataclasses.replace(cfg, layers=1, batch=n), hc.ctx[seqs], n_rows)
     sample_bytes = (sb["kv"] + sb["q_out"] + sb["table"]) * passes
     gbps = sample_bytes / dt / 1e9
     return {"value": gbps, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
@@ -393,12 +427,32 @@ def main(argv=None):
     log(f"[config] {cfg.name}: layers={cfg.layers} B={case.B} Hq={cfg.num_q_heads} "
         f"Hkv={cfg.num_kv_heads} D={cfg.head_dim} P={cfg.page_size} {cfg.kv_dtype} "
         f"ctx[min,max]=[{int(case.ctx.min())},{int(case.ctx.max())}] pages={case.num_pages}")
-    sb = step_bytes(cfg, case.ctx)
+    n_rows = int(case.q_start[-1])
+    sb = step_bytes(cfg, case.ctx, n_rows)
     total = sb["kv"] + sb["q_out"] + sb["table"] + sb["append"]
+    flops = step_flops(cfg, case.ctx, case.q_start)
     res, state = run_gpu(args, kvp, cfg, case)
     ms = res["ms_per_step"]
     kern_us = float(res["kernel_ms"].mean() * 1e3)
     achieved = sb["split_kernel_per_launch"] / (kern_us * 1e-6) / 1e9
+    # the bound: arithmetic intensity of a launch against the bf16 matrix-core
+    # ridge (2.5 PFLOP/s dense / 8 TB/s)
+    flops_launch = flops / cfg.layers
+    intensity = flops_launch / sb["split_kernel_per_launch"]
+    mfma_bound = intensity > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if is_chunked(cfg):
+        kernel_name = "prefill_mfma_kernel"
+    elif res["plan"]["use_mfma"]:
+        kernel_name = "decode_mfma_kernel"
+    else:
+        kernel_name = "decode_valu_kernel"
+    if mfma_bound:
+        tflops = flops_launch / (kern_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4)}
     out = {
         "metric": "paged decode attn: KV-read GB/s (% of HBM peak) + decode tokens/s, 1xMI355X",
         "value": round(total / (ms * 1e-3) / 1e9, 2),
@@ -417,17 +471,19 @@ def main(argv=None):
                    **({"sink_tokens": cfg.sink_tokens, "window_tokens": cfg.window_tokens}
                       if cfg.window_tokens > 0 else {}),
                    "waves_per_group": res["plan"]["waves_per_group"]},
-        "tokens_per_s": round(case.B / (ms * 1e-3), 1),
+        "tokens_per_s": round(n_rows / (ms * 1e-3), 1),
+        "flops_per_step": int(flops),
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
         "hbm_frac": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "bytes_per_step": {k: int(v) for k, v in sb.items()},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "kernel": "decode_mfma_kernel" if res["plan"]["use_mfma"]
-                     else "decode_valu_kernel",
+        "roofline": {**roof, "traffic": None, "kernel": kernel_name,
                      "kernel_us_mean": round(kern_us, 2),
                      "timed": "decode call (split + merge kernels)" if cfg.window_tokens > 0
                      else "split kernel",
-                     "bytes_per_launch": int(sb["split_kernel_per_launch"])},
+                     "bytes_per_launch": int(sb["split_kernel_per_launch"]),
+                     "flops_per_launch": int(flops_launch),
+                     "intensity_flop_per_byte": round(intensity, 2),
+                     "hbm_GBps": round(achieved, 1)},
     }
     rec = recorded_traffic(cfg.name)
     if rec is not None:
@@ -454,8 +510,9 @@ def parity_sample(cfg, hc, state, seqs=(0, 13, 31)):
     ref = oracle_decode(cfg, lay, hc, pools, seqs)
     got_bits = layers[0].out.cpu().numpy().view(np.uint16)
     got = (got_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    d = np.abs(got[seqs] - ref[seqs])
-    rel = float(np.linalg.norm(got[seqs] - ref[seqs]) / np.linalg.norm(ref[seqs]))
+    rows = np.concatenate([np.arange(hc.q_start[b], hc.q_start[b + 1]) for b in seqs])
+    d = np.abs(got[rows] - ref[rows])
+    rel = float(np.linalg.norm(got[rows] - ref[rows]) / np.linalg.norm(ref[rows]))
     r = {"layer": 0, "seqs": seqs, "max_abs": float(d.max()), "rel_l2": rel,
          "ok": bool(d.max() <= 1e-2 and rel <= 5e-3)}
     log(f"[parity] {r}")

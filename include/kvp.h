@@ -247,6 +247,26 @@ kvp_status kvp_paged_attention_decode_window(
     float scale, int32_t sink_tokens, int32_t window_tokens, void* out, int32_t num_splits_req,
     void* workspace, size_t workspace_bytes, kvp_stream_t stream);
 
+/* ---- Several new tokens per sequence: chunked prefill, verification (device)
+ * "KV-Cache Optimization Techniques", section "Cache-Aware Scheduling": long
+ * prompts are processed in chunks against the cache.  Sequence b holds
+ * n_b = context_lens[b] tokens, the last q_len_b = q_start[b+1] - q_start[b]
+ * of which are its chunk, already written to its pages (kvp_kv_append).
+ * Query row q_start[b] + i (0 <= i < q_len_b) sits at position
+ * n_b - q_len_b + i and attends to positions 0 .. n_b - q_len_b + i (causal),
+ * eq. 1 over those positions, query head j through KV head j / g:
+ *   q, out        [N][H_q][D] bfloat16, N = q_start[B]; rows in position order;
+ *   q_start       [B + 1] int32 device array, q_start[0] = 0, nondecreasing;
+ *   max_q_len     host bound on every q_len_b (rows beyond it are not computed);
+ *   max_context_len  host bound on context_lens, as for decode.
+ * A row whose position would be negative (q_len_b > n_b) gives 0.  Scores,
+ * softmax and sums are float32; out is rounded to bfloat16.  No workspace. */
+kvp_status kvp_paged_attention_prefill(
+    const kvp_pool* pool, const void* q, const int32_t* q_start, const void* k_pool,
+    const void* v_pool, const void* k_meta, const void* v_meta, const int32_t* block_tables,
+    int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+    int32_t max_q_len, int32_t max_context_len, float scale, void* out, kvp_stream_t stream);
+
 /* ---- Decode in two phases (device) -----------------------------------------
  * The same attention as kvp_paged_attention_decode, with its two kernels
  * exposed separately: the split kernel writes one normalized partial per

@@ -9,6 +9,13 @@ result ("Understanding KV-Cache Optimization in Modern LLM Serving", section
 physical blocks without changing model output), so this is the definition of
 attention applied to the gathered rows.
 
+Several new tokens per sequence ("KV-Cache Optimization Techniques", section
+"Cache-Aware Scheduling": chunked prefill processes a prompt in chunks against
+the cache): a sequence holding n tokens whose last q_len are the chunk's own
+(already written to its pages) has query row i at position n - q_len + i, and
+that row attends to positions 0 .. n - q_len + i (causal; eq. 1 over those
+rows).
+
 Sinks and a recent window ("KV-Cache Optimization Techniques", section "Token
 Eviction Strategies", eq. 5, StreamingLLM: the cache keeps tokens 1..s and
 t-w+1..t; section "Sliding Window Cache", eq. 6, the window alone): the query
@@ -180,6 +187,31 @@ def paged_decode_window(layout: PoolLayout, q_bits: np.ndarray, k_pool, v_pool, 
         pos = kept_positions(int(context_lens[b]), sink, window)
         K, V = gather_positions(layout, k_pool, v_pool, k_meta, v_meta, block_tables[b], pos)
         out[b] = attend(q[b], K, V, sc)
+    return out
+
+
+def paged_prefill(layout: PoolLayout, q_bits: np.ndarray, q_start: np.ndarray, k_pool, v_pool,
+                  k_meta, v_meta, block_tables: np.ndarray, context_lens: np.ndarray, scale,
+                  seqs=None) -> np.ndarray:
+    """Causal multi-query attention over pages: float64 [N, H_q, D].
+
+    q_bits: bfloat16 bits [N, H_q, D]; rows q_start[b] .. q_start[b+1]-1 are
+    sequence b's chunk, in position order.  A row whose position would be
+    negative (chunk longer than the sequence) attends to nothing and gives 0."""
+    q = _to_f64(q_bits)
+    out = np.zeros(q.shape)
+    B = len(q_start) - 1
+    sc = float(np.float32(scale))
+    sel = range(B) if seqs is None else seqs
+    for b in sel:
+        r0, r1 = int(q_start[b]), int(q_start[b + 1])
+        n = int(context_lens[b])
+        K, V = gather_sequence(layout, k_pool, v_pool, k_meta, v_meta, block_tables[b], n)
+        for i in range(r1 - r0):
+            pos = n - (r1 - r0) + i
+            if pos < 0:
+                continue
+            out[r0 + i] = attend(q[r0 + i], K[:, :pos + 1], V[:, :pos + 1], sc)
     return out
 
 

@@ -267,6 +267,26 @@ def kvp_paged_attention_decode_window(pool: Pool, q, k_pool, v_pool, k_meta, v_m
         _stream(stream)), "kvp_paged_attention_decode_window")
 
 
+def kvp_paged_attention_prefill(pool: Pool, q, q_start, k_pool, v_pool, k_meta, v_meta,
+                                block_tables, context_lens, max_q_len: int,
+                                max_context_len: int, scale: float, out, stream=None) -> None:
+    """Causal multi-query attention: q/out [N, H_q, D], rows q_start[b]..q_start[b+1]-1
+    are sequence b's chunk (its last positions)."""
+    eb = 1 if pool.desc.dtype == KVP_INT8 else 2
+    B = int(context_lens.numel())
+    if q_start.numel() != B + 1 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("q_start must have B+1 entries and block_tables B rows")
+    if out.shape != q.shape or q.dim() != 3:
+        raise ValueError("q and out must be [N, H_q, D]")
+    _check(_L.kvp_paged_attention_prefill(
+        pool.handle, _dev(q, "q", 2), _dev(q_start, "q_start", 4), _dev(k_pool, "k_pool", eb),
+        _dev(v_pool, "v_pool", eb), _dev(k_meta, "k_meta", 2), _dev(v_meta, "v_meta", 2),
+        _dev(block_tables, "block_tables", 4), int(block_tables.shape[1]),
+        _dev(context_lens, "context_lens", 4), B, int(q.shape[1]), int(max_q_len),
+        int(max_context_len), float(scale), _dev(out, "out", 2), _stream(stream)),
+        "kvp_paged_attention_prefill")
+
+
 def kvp_decode_partials_bytes(pool: Pool, num_seqs: int, num_q_heads: int,
                               max_context_len: int, num_splits_req: int = 0):
     """(num_splits, bytes) of the partials buffer the split kernel writes."""
@@ -317,5 +337,5 @@ __all__ = [
     "kvp_kv_append", "kvp_decode_workspace_bytes", "kvp_paged_attention_decode",
     "kvp_decode_partials_bytes", "kvp_paged_attention_decode_partials", "kvp_lse_merge",
     "kvp_seq_evict_window", "kvp_decode_window_workspace_bytes",
-    "kvp_paged_attention_decode_window",
+    "kvp_paged_attention_decode_window", "kvp_paged_attention_prefill",
 ]

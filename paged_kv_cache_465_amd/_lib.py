@@ -60,6 +60,10 @@ PROTOTYPES = {
                                                       c_float, c_int32, c_void_p, c_size_t,
                                                       P_int32, c_void_p]),
     "kvp_lse_merge": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
+    "kvp_paged_attention_prefill": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                              c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                                              c_int32, c_int32, c_int32, c_int32, c_float,
+                                              c_void_p, c_void_p]),
     "kvp_seq_evict_window": (c_int32, [c_void_p, P_int32, c_int32, c_int32, c_int32, c_int32]),
     "kvp_decode_window_workspace_bytes": (c_int32, [c_void_p, c_int32, c_int32, c_int32,
                                                     c_int32, c_int32, c_int32,

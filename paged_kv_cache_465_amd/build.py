@@ -22,7 +22,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
-DEVICE_SOURCES = ["append.hip", "decode.hip"]
+DEVICE_SOURCES = ["append.hip", "decode.hip", "prefill.hip"]
 HOST_SOURCES = ["pool.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]

@@ -32,9 +32,10 @@ def logical_rows(case: DecodeCase, b: int):
         K[p[keep]] = case.hist_k[sel[keep]]
         V[p[keep]] = case.hist_v[sel[keep]]
         filled[p[keep]] = True
-    K[n - 1] = case.new_k[b]
-    V[n - 1] = case.new_v[b]
-    filled[n - 1] = True
+    mine = np.nonzero(case.new_seq == b)[0]
+    K[case.new_pos[mine]] = case.new_k[mine]
+    V[case.new_pos[mine]] = case.new_v[mine]
+    filled[case.new_pos[mine]] = True
     assert filled.all()
     return K, V
 
@@ -48,7 +49,7 @@ def oracle_pools(case: DecodeCase, with_new: bool = True):
                   case.block_tables)
     if with_new:
         oracle.append(lay, k, v, km, vm, case.new_k, case.new_v,
-                      np.arange(case.B, dtype=np.int32), case.new_pos, case.block_tables)
+                      case.new_seq, case.new_pos, case.block_tables)
     return k, v, km, vm
 
 

@@ -66,7 +66,7 @@ class GpuCase:
         c = self.case
         self.kvp.kvp_kv_append(self.pool, self.k_pool, self.v_pool, self.k_meta, self.v_meta,
                                dev16(c.new_k, self.device), dev16(c.new_v, self.device),
-                               dev32(np.arange(c.B), self.device), dev32(c.new_pos, self.device),
+                               dev32(c.new_seq, self.device), dev32(c.new_pos, self.device),
                                self.bt)
 
     def upload(self, k, v, km, vm):

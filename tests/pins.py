@@ -36,6 +36,19 @@ def _bf16_f64(bits):
         .astype(np.float64)
 
 
+def prefill_cases():
+    """Small chunked cases: fixed and ragged chunk lengths, g = 1, 2, 4, 8, INT8."""
+    return [
+        variant(TINY, name="tiny_chunk5", q_len=5),
+        variant(TINY, name="tiny_chunk_ragged", q_len=1, q_len_hi=9, batch=3, ctx_fixed=(37, 100, 8),
+                pool_pages=24),
+        variant(TINY, name="tiny_chunk_g1", q_len=4, num_q_heads=2, num_kv_heads=2, pool_pages=32),
+        variant(TINY, name="tiny_chunk_g8_p32_int8", q_len=6, page_size=32, kv_dtype="int8",
+                num_q_heads=16, num_kv_heads=2, head_dim=128, pool_pages=16, outlier_channels=3,
+                outlier_gain=8.0),
+    ]
+
+
 # Small cases: the tiny workload and its MHA (g=1), g=2, H_kv=2 and peaky variants.
 def small_cases():
     return [
@@ -366,3 +379,48 @@ def pin_window_memory_bound(page_size=16, sink=4, window=40, steps=400):
         # the pages held carry at least eq. 6's |cache| (one layer, d_k = 128)
         assert len(held) * page_size * 2 * 128 >= oracle.window_cache_elems(min(n, window), 1, 128)
     assert model.free_count == 10_000 - len(held)
+
+
+# ---------------------------------------------------------------- multi-query chunks
+def pin_prefill_vs_sdpa(case, tol=1e-12):
+    """Chunk rows of a sequence of n tokens: torch's SDPA in float64 over the
+    contiguous rows with an explicit boolean mask (row i may see column t iff
+    t <= n - q_len + i), per query head."""
+    k, v, km, vm = oracle_pools(case)
+    lay = layout_of(case)
+    out = oracle.paged_prefill(lay, case.q, case.q_start, k, v, km, vm, case.block_tables,
+                               case.ctx, case.scale)
+    g = case.cfg.num_q_heads // case.cfg.num_kv_heads
+    for b in range(case.B):
+        K, V = logical_rows(case, b)
+        n = K.shape[0]
+        r0, r1 = int(case.q_start[b]), int(case.q_start[b + 1])
+        L = r1 - r0
+        if case.cfg.kv_dtype == "int8":
+            Kf = np.stack([_dequant_exact(K[t]) for t in range(n)])
+            Vf = np.stack([_dequant_exact(V[t]) for t in range(n)])
+        else:
+            Kf, Vf = _bf16_f64(K), _bf16_f64(V)
+        qf = _bf16_f64(case.q[r0:r1])                       # [L, H_q, D]
+        mask = np.arange(n)[None, :] <= (n - L + np.arange(L))[:, None]   # [L, n]
+        qt = torch.from_numpy(np.ascontiguousarray(qf.transpose(1, 0, 2)))[None]  # [1,Hq,L,D]
+        kt = torch.from_numpy(np.ascontiguousarray(Kf.transpose(1, 0, 2)))[None]  # [1,Hkv,n,D]
+        vt = torch.from_numpy(np.ascontiguousarray(Vf.transpose(1, 0, 2)))[None]
+        kt = kt.repeat_interleave(g, dim=1)
+        vt = vt.repeat_interleave(g, dim=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt, vt, attn_mask=torch.from_numpy(mask), scale=float(np.float32(case.scale)))
+        ref = ref[0].numpy().transpose(1, 0, 2)              # [L, Hq, D]
+        err = np.abs(out[r0:r1] - ref).max() if L else 0.0
+        assert err <= tol, f"seq {b}: oracle prefill vs sdpa {err:.3e}"
+
+
+def pin_prefill_single_row_is_decode(case):
+    """A chunk of one token is the decode step, bit for bit."""
+    assert (np.diff(case.q_start) == 1).all()
+    k, v, km, vm = oracle_pools(case)
+    lay = layout_of(case)
+    a = oracle.paged_prefill(lay, case.q, case.q_start, k, v, km, vm, case.block_tables,
+                             case.ctx, case.scale)
+    d = oracle.paged_decode(lay, case.q, k, v, km, vm, case.block_tables, case.ctx, case.scale)
+    assert np.array_equal(a, d)

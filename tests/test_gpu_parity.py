@@ -263,7 +263,9 @@ def _sampled_check(kvp, cfg, seqs, splits=0):
     gc = GpuCase(kvp, case)
     gc.append_history()
     gc.append_new()
-    if cfg.window_tokens > 0:
+    if cfg.q_len > 1 or cfg.q_len_hi > 1:
+        out = _run_prefill(kvp, gc, case)
+    elif cfg.window_tokens > 0:
         mx = int(case.ctx.max())
         wsb = kvp.kvp_decode_window_workspace_bytes(gc.pool, case.B, cfg.num_q_heads, mx,
                                                     cfg.sink_tokens, cfg.window_tokens, splits)
@@ -284,9 +286,9 @@ def _sampled_check(kvp, cfg, seqs, splits=0):
     sel = np.isin(case.hist_seq, list(need))
     oracle.append(lay, k, v, km, vm, case.hist_k[sel], case.hist_v[sel], case.hist_seq[sel],
                   case.hist_pos[sel], case.block_tables)
-    idx = np.array(sorted(need), dtype=np.int32)
-    oracle.append(lay, k, v, km, vm, case.new_k[idx], case.new_v[idx], idx, case.new_pos[idx],
-                  case.block_tables)
+    nsel = np.isin(case.new_seq, list(need))
+    oracle.append(lay, k, v, km, vm, case.new_k[nsel], case.new_v[nsel], case.new_seq[nsel],
+                  case.new_pos[nsel], case.block_tables)
     gk, gv, gkm, gvm = gc.pools_host()
     per_page = cfg.num_kv_heads * cfg.page_size * cfg.head_dim
     for b in seqs:
@@ -300,6 +302,14 @@ def _sampled_check(kvp, cfg, seqs, splits=0):
             gp = g.reshape(case.num_pages, n)[pages]
             rp = r.reshape(case.num_pages, n)[pages]
             assert np.array_equal(gp.view(np.uint8), rp.view(np.uint8)), f"{name} pages of seq {b}"
+    if cfg.q_len > 1 or cfg.q_len_hi > 1:
+        ref = oracle.paged_prefill(lay, case.q, case.q_start, k, v, km, vm, case.block_tables,
+                                   case.ctx, case.scale, seqs=seqs)
+        rows = np.concatenate([np.arange(case.q_start[b], case.q_start[b + 1]) for b in seqs])
+        m, r = assert_close(out[rows], ref[rows], cfg.name)
+        log(f"  max_abs={m:.2e} rel_l2={r:.2e}")
+        gc.close()
+        return
     if cfg.window_tokens > 0:
         ref = oracle.paged_decode_window(lay, case.q, k, v, km, vm, case.block_tables, case.ctx,
                                          case.scale, cfg.sink_tokens, cfg.window_tokens,
@@ -534,3 +544,95 @@ def test_window_covering_everything_is_the_full_decode(kvp, cfg):
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy().view(np.uint16), full), (sink, window)
     gc.close()
+
+
+# ---- several new tokens per sequence (chunked prefill, verification) ---------------------
+from .pins import prefill_cases  # noqa: E402
+
+PREFILL = prefill_cases() + [
+    variant(LLAMA3_8B_LAYER, name="l8b_chunk150", batch=3, ctx_lo=200, ctx_hi=700, q_len=150),
+    variant(LLAMA3_8B_LAYER, name="l8b_chunk_g16", batch=3, num_q_heads=128, ctx_lo=30,
+            ctx_hi=500, q_len=20),
+    variant(INT8_LONG, name="int8_chunk64", batch=2, ctx_lo=300, ctx_hi=900, q_len=64),
+    variant(INT8_LONG, name="int8_chunk_p16_d64", batch=3, page_size=16, head_dim=64, ctx_lo=1,
+            ctx_hi=400, q_len=3, q_len_hi=40),
+    variant(SHARED_PREFIX_MQA, name="prefix_chunk7", batch=4, shared_prefix=64,
+            ctx_fixed=(101, 80, 97, 129), q_len=7),
+]
+
+
+def _prefill_oracle(case):
+    key = ("prefill", case.cfg.name)
+    if key not in _CACHE:
+        k, v, km, vm = oracle_pools(case)
+        out = oracle.paged_prefill(layout_of(case), case.q, case.q_start, k, v, km, vm,
+                                   case.block_tables, case.ctx, case.scale)
+        _CACHE[key] = (k, v, km, vm, out)
+    return _CACHE[key]
+
+
+def _run_prefill(kvp, gc, case, max_q_len=None):
+    c = case.cfg
+    qs = dev32(case.q_start)
+    out = torch.full_like(gc.q, int(np.uint16(0x7FC0).view(np.int16)))
+    mq = int(np.diff(case.q_start).max()) if max_q_len is None else max_q_len
+    kvp.kvp_paged_attention_prefill(gc.pool, gc.q, qs, gc.k_pool, gc.v_pool, gc.k_meta, gc.v_meta,
+                                    gc.bt, gc.ctx, mq, int(case.ctx.max()), float(case.scale), out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("cfg", PREFILL, ids=lambda c: c.name)
+def test_prefill_matches_oracle(kvp, cfg):
+    """Chunk rows appended through kv_append (pool bytes bit-exact), then the
+    causal multi-query attention against the oracle; the same call on the
+    oracle's pool bytes gives the same bits."""
+    case = _case(cfg)
+    k, v, km, vm, ref = _prefill_oracle(case)
+    log(f"[prefill] {cfg.name} B={case.B} q_len={np.diff(case.q_start).tolist()[:6]} "
+        f"ctx={case.ctx.tolist()[:6]} Hq={cfg.num_q_heads} Hkv={cfg.num_kv_heads}")
+    gc = GpuCase(kvp, case)
+    gc.append_history()
+    gc.append_new()
+    torch.cuda.synchronize()
+    _pools_equal(gc.pools_host(), (k, v, km, vm))
+    out = _run_prefill(kvp, gc, case)
+    m, r = assert_close(out, ref, cfg.name)
+    log(f"  max_abs={m:.2e} rel_l2={r:.2e}")
+    gc.upload(k, v, km, vm)
+    assert np.array_equal(out, _run_prefill(kvp, gc, case))
+    # a generous max_q_len adds empty tiles and may pick the 32-row-per-wavefront
+    # instance (another compilation of the same arithmetic): still within tolerance
+    big = _run_prefill(kvp, gc, case, max_q_len=int(np.diff(case.q_start).max()) + 40)
+    assert_close(big, ref, cfg.name + " generous max_q_len")
+    gc.close()
+
+
+@pytest.mark.parametrize("cfg", [SMALL[0], SMALL[6], SMALL[11]], ids=lambda c: c.name)
+def test_prefill_one_token_equals_decode(kvp, cfg):
+    """A chunk of one token per sequence is the decode step (within tolerance;
+    different kernels, the same float32 arithmetic up to summation order)."""
+    case = _case(cfg)
+    log(f"[prefill=decode] {cfg.name}")
+    gc = GpuCase(kvp, case)
+    gc.upload(*_oracle(case)[:4])
+    a = _run_prefill(kvp, gc, case)
+    d = gc.decode(num_splits=1)
+    ma, rel, _, ulps = compare_outputs(a, (d.astype(np.uint32) << 16).view(np.float32)
+                                       .astype(np.float64))
+    assert ma <= 1e-2 and rel <= 5e-3 and ulps <= 1.0
+    assert_close(a, _oracle(case)[4], cfg.name)
+    gc.close()
+
+
+def test_full_spec_verify(kvp):
+    """32 sequences of 4,096 tokens verifying 4 drafted tokens each
+    (Llama-3-70B-shaped layer), sampled rows against the oracle."""
+    from workloads import SPEC_VERIFY
+    _sampled_check(kvp, SPEC_VERIFY, seqs=(0, 17, 31))
+
+
+def test_full_chunked_prefill(kvp):
+    """8 sequences taking a 512-token chunk on a Llama-3-8B-shaped layer."""
+    from workloads import CHUNKED_PREFILL
+    _sampled_check(kvp, CHUNKED_PREFILL, seqs=(0, 5))

@@ -47,6 +47,8 @@ def _all_pins():
                        lambda s=sink, w=window: pins.pin_window_vs_sdpa(_case(TINY), s, w)))
     checks.append(("window_degenerate", lambda: pins.pin_window_degenerate(_case(TINY))))
     checks.append(("window_memory", pins.pin_window_memory_bound))
+    for c in pins.prefill_cases()[:2]:
+        checks.append((f"prefill_{c.name}", lambda c=c: pins.pin_prefill_vs_sdpa(_case(c))))
     return checks
 
 
@@ -190,7 +192,39 @@ def _kept_overlap_twice(n, sink, window):
     return np.concatenate([np.arange(min(sink, n)), np.arange(max(n - window, 0), n)])
 
 
+def _prefill_causal_off_by_one(layout, q_bits, q_start, k_pool, v_pool, k_meta, v_meta,
+                               block_tables, context_lens, scale, seqs=None):
+    q = opa._to_f64(q_bits)
+    out = np.zeros(q.shape)
+    for b in range(len(q_start) - 1):
+        r0, r1 = int(q_start[b]), int(q_start[b + 1])
+        n = int(context_lens[b])
+        K, V = opa.gather_sequence(layout, k_pool, v_pool, k_meta, v_meta, block_tables[b], n)
+        for i in range(r1 - r0):
+            pos = n - (r1 - r0) + i
+            out[r0 + i] = opa.attend(q[r0 + i], K[:, :pos], V[:, :pos], float(np.float32(scale)))
+    return out
+
+
+def _prefill_anchored_at_zero(layout, q_bits, q_start, k_pool, v_pool, k_meta, v_meta,
+                              block_tables, context_lens, scale, seqs=None):
+    q = opa._to_f64(q_bits)
+    out = np.zeros(q.shape)
+    for b in range(len(q_start) - 1):
+        r0, r1 = int(q_start[b]), int(q_start[b + 1])
+        n = int(context_lens[b])
+        K, V = opa.gather_sequence(layout, k_pool, v_pool, k_meta, v_meta, block_tables[b], n)
+        for i in range(r1 - r0):
+            out[r0 + i] = opa.attend(q[r0 + i], K[:, :i + 1], V[:, :i + 1],
+                                     float(np.float32(scale)))
+    return out
+
+
 MUTANTS = {
+    "prefill_causal_off_by_one": [(opa, "paged_prefill", _prefill_causal_off_by_one),
+                                  (oracle, "paged_prefill", _prefill_causal_off_by_one)],
+    "prefill_anchored_at_zero": [(opa, "paged_prefill", _prefill_anchored_at_zero),
+                                 (oracle, "paged_prefill", _prefill_anchored_at_zero)],
     "window_off_by_one": [(opa, "kept_positions", _kept_off_by_one),
                           (oracle, "kept_positions", _kept_off_by_one)],
     "window_sinks_dropped": [(opa, "kept_positions", _kept_no_sinks),

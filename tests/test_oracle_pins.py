@@ -98,3 +98,12 @@ def test_window_degenerate_cases(small_case):
 def test_window_memory_bound():
     pins.pin_window_memory_bound()
     pins.pin_window_memory_bound(page_size=32, sink=0, window=100, steps=700)
+
+
+@pytest.mark.parametrize("cfg", pins.prefill_cases(), ids=lambda c: c.name)
+def test_prefill_vs_library_sdpa(cfg):
+    pins.pin_prefill_vs_sdpa(make_case(cfg))
+
+
+def test_prefill_single_row_is_decode(small_case):
+    pins.pin_prefill_single_row_is_decode(small_case)

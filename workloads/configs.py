@@ -40,6 +40,8 @@ class DecodeConfig:
     outlier_channels: int = 0       # channels (of H_kv*D) scaled by outlier_gain, K and V drawn separately
     outlier_gain: float = 1.0
     q_gain: float = 1.0
+    q_len: int = 1                  # new query tokens per sequence (chunked prefill / verification)
+    q_len_hi: int = 0               # > q_len: per-sequence chunk lengths ~ U{q_len..q_len_hi}
     sink_tokens: int = 0            # with window_tokens > 0: the cache holds only positions
     window_tokens: int = 0          #   < sink_tokens and the last window_tokens positions
     device_data: bool = False       # draw K/V/q on the GPU with torch's generator (too big for host)
@@ -93,7 +95,20 @@ STREAMING_WINDOW = DecodeConfig(
     head_dim=128, page_size=16, ctx_fixed=(32768,) * 64, sink_tokens=4, window_tokens=4096,
     seed=465006)
 
-EXTRA_CONFIGS = {c.name: c for c in (STREAMING_WINDOW,)}
+# Several new tokens per sequence against the paged cache ("KV-Cache
+# Optimization Techniques", section "Cache-Aware Scheduling": chunked prefill).
+# Verification of 4 drafted tokens per sequence on a Llama-3-70B-shaped layer:
+SPEC_VERIFY = DecodeConfig(
+    name="spec_verify", layers=1, batch=32, num_q_heads=64, num_kv_heads=8, head_dim=128,
+    page_size=16, ctx_fixed=(4096,) * 32, q_len=4, seed=465007)
+
+# A 512-token prompt chunk per sequence on a Llama-3-8B-shaped layer, the cache
+# already holding 1.5k-7.5k tokens of each prompt (context incl. the chunk):
+CHUNKED_PREFILL = DecodeConfig(
+    name="chunked_prefill", layers=1, batch=8, num_q_heads=32, num_kv_heads=8, head_dim=128,
+    page_size=16, ctx_lo=2048, ctx_hi=8192, q_len=512, seed=465008)
+
+EXTRA_CONFIGS = {c.name: c for c in (STREAMING_WINDOW, SPEC_VERIFY, CHUNKED_PREFILL)}
 
 
 def variant(cfg: DecodeConfig, **kw) -> DecodeConfig:

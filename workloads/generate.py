@@ -60,14 +60,16 @@ class DecodeCase:
     max_blocks: int
     block_tables: np.ndarray   # int32 [B, max_blocks], -1 where unused
     scale: np.float32
-    q: Optional[np.ndarray] = None        # uint16 [B, H_q, D]
+    q: Optional[np.ndarray] = None        # uint16 [N, H_q, D] (one row per new token)
     hist_k: Optional[np.ndarray] = None   # uint16 [T, H_kv, D]
     hist_v: Optional[np.ndarray] = None
     hist_seq: Optional[np.ndarray] = None  # int32 [T]
     hist_pos: Optional[np.ndarray] = None  # int32 [T]
-    new_k: Optional[np.ndarray] = None    # uint16 [B, H_kv, D]
+    new_k: Optional[np.ndarray] = None    # uint16 [N, H_kv, D] (N = sum of chunk lengths)
     new_v: Optional[np.ndarray] = None
-    new_pos: Optional[np.ndarray] = None  # int32 [B] (= ctx - 1)
+    new_pos: Optional[np.ndarray] = None  # int32 [N]: the chunk's positions (ctx - q_len ..)
+    new_seq: Optional[np.ndarray] = None  # int32 [N]: sequence of each new row
+    q_start: Optional[np.ndarray] = None  # int32 [B+1]: rows q_start[b].. of q / new_* are b's
 
     @property
     def B(self) -> int:
@@ -150,10 +152,19 @@ def make_case(cfg: DecodeConfig, with_data: bool = True) -> DecodeCase:
     """Build one host decode case of ``cfg`` (one layer's worth of K/V)."""
     rng = np.random.Generator(np.random.PCG64(cfg.seed))
     ctx = _context_lengths(cfg, rng)
+    if cfg.q_len_hi > cfg.q_len:
+        qlens = rng.integers(cfg.q_len, cfg.q_len_hi, size=cfg.batch, endpoint=True)
+    else:
+        qlens = np.full(cfg.batch, cfg.q_len)
+    qlens = np.minimum(qlens, np.maximum(ctx, 1)).astype(np.int64)
     num_pages, max_blocks, bt = _tables(cfg, ctx, rng)
     scale = np.float32(1.0 / np.sqrt(np.float64(cfg.head_dim)))
     case = DecodeCase(cfg=cfg, ctx=ctx, num_pages=num_pages, max_blocks=max_blocks,
                       block_tables=bt, scale=scale)
+    case.q_start = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    case.new_seq = np.repeat(np.arange(cfg.batch, dtype=np.int32), qlens)
+    case.new_pos = np.concatenate([np.arange(int(ctx[b]) - int(qlens[b]), int(ctx[b]))
+                                   for b in range(cfg.batch)]).astype(np.int32)
     if not with_data or cfg.device_data:
         return case
     Hkv, D, Hq, B = cfg.num_kv_heads, cfg.head_dim, cfg.num_q_heads, cfg.batch
@@ -161,12 +172,13 @@ def make_case(cfg: DecodeConfig, with_data: bool = True) -> DecodeCase:
     if cfg.outlier_channels:
         out_k = np.sort(rng.choice(Hkv * D, cfg.outlier_channels, replace=False))
         out_v = np.sort(rng.choice(Hkv * D, cfg.outlier_channels, replace=False))
-    case.q = _normal_bf16(rng, (B, Hq, D), gain=cfg.q_gain)
+    N = int(case.q_start[-1])
+    case.q = _normal_bf16(rng, (N, Hq, D), gain=cfg.q_gain)
     starts = _history_ranges(cfg, ctx)
     seqs, poss = [], []
     for b in range(B):
         p = held_positions(cfg, int(ctx[b])).astype(np.int32)
-        p = p[(p >= starts[b]) & (p < ctx[b] - 1)]
+        p = p[(p >= starts[b]) & (p < ctx[b] - qlens[b])]
         poss.append(p)
         seqs.append(np.full(p.shape, b, dtype=np.int32))
     case.hist_seq = np.concatenate(seqs) if seqs else np.zeros(0, np.int32)
@@ -174,9 +186,8 @@ def make_case(cfg: DecodeConfig, with_data: bool = True) -> DecodeCase:
     T = int(case.hist_pos.shape[0])
     case.hist_k = _normal_bf16(rng, (T, Hkv, D), outliers=out_k, gain_out=cfg.outlier_gain)
     case.hist_v = _normal_bf16(rng, (T, Hkv, D), outliers=out_v, gain_out=cfg.outlier_gain)
-    case.new_k = _normal_bf16(rng, (B, Hkv, D), outliers=out_k, gain_out=cfg.outlier_gain)
-    case.new_v = _normal_bf16(rng, (B, Hkv, D), outliers=out_v, gain_out=cfg.outlier_gain)
-    case.new_pos = (ctx - 1).astype(np.int32)
+    case.new_k = _normal_bf16(rng, (N, Hkv, D), outliers=out_k, gain_out=cfg.outlier_gain)
+    case.new_v = _normal_bf16(rng, (N, Hkv, D), outliers=out_v, gain_out=cfg.outlier_gain)
     return case
 
 
@@ -185,6 +196,7 @@ def history_rows_device(cfg: DecodeConfig, case: DecodeCase, layer: int, device)
 
     Returns (q, hist_k, hist_v, hist_seq, hist_pos, new_k, new_v, new_pos)."""
     import torch
+    assert cfg.q_len == 1 and cfg.q_len_hi <= 1, "device draws cover one new token per sequence"
     g = torch.Generator(device=device)
     g.manual_seed(cfg.seed * 100 + layer)
     Hkv, D, Hq, B = cfg.num_kv_heads, cfg.head_dim, cfg.num_q_heads, cfg.batch
