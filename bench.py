@@ -405,6 +405,59 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def prefix_cache_bench(kvp, dev, n_req=100, prefix=2000, suffix=512, P=16, copies=4096):
+    """Host prefix-cache calls for the shared-prefix workload ("Prefix
+    Caching": 100 requests sharing a 2000-token prefix): per request one match,
+    one grow and one insert; then the device page copy (copy-on-write) over
+    ``copies`` pages of a Llama-3-8B-shaped layer (8 KV heads, D = 128)."""
+    import torch
+    rng = np.random.default_rng(465009)
+    desc = kvp.make_desc(16384, P, 8, 128, "bf16")
+    pool = kvp.kvp_pool_create(desc)
+    cache = kvp.kvp_prefix_cache_create(pool)
+    shared = rng.integers(0, 128000, prefix).tolist()
+    reqs = [shared + rng.integers(0, 128000, suffix).tolist() for _ in range(n_req)]
+    rows = []
+    t0 = time.perf_counter()
+    matched = 0
+    for toks in reqs:
+        got = kvp.kvp_prefix_match(cache, toks)
+        row = np.full(-(-len(toks) // P), -1, dtype=np.int32)
+        row[:got.size] = got
+        kvp.kvp_seq_grow(pool, row, got.size * P, len(toks))
+        kvp.kvp_prefix_insert(cache, toks, row)
+        rows.append(row)
+        matched += got.size
+    host_s = time.perf_counter() - t0
+    unique = n_req * (prefix + suffix) // P - matched
+    # device copy-on-write throughput
+    kv_bytes, _ = kvp.kvp_pool_bytes(desc)
+    k = torch.zeros(kv_bytes // 2, dtype=torch.int16, device=dev)
+    v = torch.zeros_like(k)
+    perm = rng.permutation(16384).astype(np.int32)
+    pairs = torch.from_numpy(np.stack([perm[:copies], perm[copies:2 * copies]], 1).copy()).to(dev)
+    kvp.kvp_copy_pages(pool, k, v, None, None, pairs)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(10):
+        kvp.kvp_copy_pages(pool, k, v, None, None, pairs)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / 10
+    page_bytes = 2 * 8 * P * 128 * 2
+    moved = 2 * copies * page_bytes   # read + write, K and V
+    cache.close()
+    pool.close()
+    return {"metric": "prefix cache: host us per request; page copy GB/s", "data": "synthetic",
+            "config": {"workload": "prefix_cache", "requests": n_req, "shared_tokens": prefix,
+                       "own_tokens": suffix, "page_size": P},
+            "host_us_per_request": round(host_s * 1e6 / n_req, 2),
+            "pages_matched": int(matched), "pages_unique": int(unique),
+            "copy_pages": copies, "copy_us": round(us, 2),
+            "copy_GBps_read_plus_write": round(moved / (us * 1e-6) / 1e9, 1)}
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -421,6 +474,9 @@ def main(argv=None):
         print(json.dumps({"copy_calibration": r}))
         return
     import paged_kv_cache_465_amd as kvp
+    if args.config == "prefix_cache":
+        print(json.dumps(prefix_cache_bench(kvp, dev)), flush=True)
+        return
     from workloads import CONFIGS, EXTRA_CONFIGS, make_case
     cfg = {**CONFIGS, **EXTRA_CONFIGS}[args.config]
     case = make_case(cfg, with_data=not cfg.device_data)

@@ -162,6 +162,55 @@ kvp_status kvp_seq_release(kvp_pool* pool, int32_t* row, int32_t n_blocks);
 kvp_status kvp_seq_evict_window(kvp_pool* pool, int32_t* row, int32_t max_blocks, int32_t ctx_len,
                                 int32_t sink_tokens, int32_t window_tokens);
 
+/* ---- Prefix cache (host) ------------------------------------------------------
+ * "KV-Cache Optimization Techniques", section "Prefix Caching": requests that
+ * share a prefix reuse its KV-cache; the token sequence is hashed, cached
+ * prefixes form a radix tree for longest-prefix matching, and shared pages
+ * are copied on write.  The cache is a radix tree over whole pages: one node
+ * per block of P token ids, keyed by a 64-bit hash chained over the whole
+ * prefix, holding the page with that block's K/V and one reference to it.
+ * Token ids of every matched block are compared, so a hash collision can
+ * only shorten a match.  The pool must outlive the cache; the cache is not
+ * thread safe (serialize with the pool). */
+typedef struct kvp_prefix_cache kvp_prefix_cache;  /* opaque, host memory */
+
+kvp_status kvp_prefix_cache_create(kvp_pool* pool, kvp_prefix_cache** out);
+/* Drops the cache's reference on every cached page (pages no sequence holds
+ * return to the free list).  NULL is a no-op. */
+void kvp_prefix_cache_destroy(kvp_prefix_cache* cache);
+/* Pages the cache holds a reference to, or -1 for NULL. */
+int32_t kvp_prefix_cache_pages(const kvp_prefix_cache* cache);
+/* Longest cached prefix of tokens[0..n_tokens) in whole blocks, at most
+ * max_pages blocks: *n_blocks_out = k and pages_out[0..k) are its pages in
+ * block order, each with one reference added for the caller (the pages go
+ * into the new sequence's block table; release them with kvp_pages_free or
+ * kvp_seq_release).  Matched nodes become most recently used. */
+kvp_status kvp_prefix_match(kvp_prefix_cache* cache, const int32_t* tokens, int32_t n_tokens,
+                            int32_t* pages_out, int32_t max_pages, int32_t* n_blocks_out);
+/* Cache the full blocks of a sequence whose K/V are in pages[0..n_tokens/P):
+ * blocks already cached keep their page; each newly cached block's page
+ * (which must be in use) gets one reference held by the cache.  All or
+ * nothing; a hash collision with different tokens stops caching there. */
+kvp_status kvp_prefix_insert(kvp_prefix_cache* cache, const int32_t* tokens, int32_t n_tokens,
+                             const int32_t* pages);
+/* Evict least-recently-used leaf blocks whose page only the cache holds,
+ * until n_pages pages went back to the free list or none is left; parents
+ * left without children become candidates in turn.  *n_freed (may be NULL)
+ * receives the count. */
+kvp_status kvp_prefix_evict(kvp_prefix_cache* cache, int32_t n_pages, int32_t* n_freed);
+
+/* Make the blocks a sequence will write to private before appending tokens
+ * cur_len .. new_len-1: missing blocks get fresh pages; if the partly filled
+ * last block (the one holding position cur_len) is also held elsewhere
+ * (reference count > 1), the row gets a fresh page for it, one reference to
+ * the shared page is dropped, and the pair (old page, new page) is written to
+ * copy_src[0], copy_dst[0] with *n_copies = 1 (0 otherwise): copy it on the
+ * device with kvp_copy_pages before appending.  All or nothing
+ * (KVP_E_NOPAGES if the free list is short). */
+kvp_status kvp_seq_prepare_append(kvp_pool* pool, int32_t* row, int32_t max_blocks,
+                                  int32_t cur_len, int32_t new_len, int32_t* copy_src,
+                                  int32_t* copy_dst, int32_t* n_copies);
+
 /* ---- Append (device) ------------------------------------------------------
  * For each of n_tokens new tokens i: sequence seq_idx[i], position pos[i];
  * write k_new[i][h][:] and v_new[i][h][:] (bfloat16 [n_tokens][H_kv][D]) into
@@ -178,6 +227,14 @@ kvp_status kvp_kv_append(const kvp_pool* pool, void* k_pool, void* v_pool,
                          const int32_t* seq_idx, const int32_t* pos, int32_t n_tokens,
                          const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks,
                          kvp_stream_t stream);
+
+/* Copy whole pages of one layer's pools (K, V and, for INT8, both metadata
+ * arrays; every KV head): for i < n, page src_dst[2i] to page src_dst[2i+1].
+ * src_dst is a device array of n int32 pairs; a pair naming a page outside
+ * the pool, or the same page twice, is skipped.  Pairs must not overlap (no
+ * page both written and read by the call). */
+kvp_status kvp_copy_pages(const kvp_pool* pool, void* k_pool, void* v_pool, void* k_meta,
+                          void* v_meta, const int32_t* src_dst, int32_t n, kvp_stream_t stream);
 
 /* ---- Decode plan (host, pure) -----------------------------------------------
  * Work is split into B * H_kv * num_splits workgroups: each covers one

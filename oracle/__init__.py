@@ -12,6 +12,7 @@ Modules:
   quantize         eq. 3 per-token INT8 rows
   accounting       memory closed forms (memory formula, eq. 2, eq. 7, waste)
   allocator        page allocator semantics (parity unpinned for id order)
+  prefix           prefix caching: longest cached whole-block prefix (eq. 2)
 """
 from .accounting import (alloc_tokens, bytes_per_token, gqa_ratio, int8_row_ratio, kv_bytes,
                          paged_bytes, prefix_cached_bytes, waste, window_cache_elems)
@@ -19,6 +20,7 @@ from .allocator import AllocError, NoPages, PoolModel, window_evicted_blocks
 from .paged_attention import (PoolLayout, append, attend, gather_positions, gather_sequence,
                               kept_positions, paged_decode, paged_decode_window, paged_prefill,
                               slot)
+from .prefix import PrefixModel
 from .quantize import dequantize, quantize_rows
 
 __all__ = [
@@ -27,5 +29,5 @@ __all__ = [
     "window_evicted_blocks", "PoolLayout", "append", "attend", "gather_positions",
     "gather_sequence", "kept_positions", "paged_decode", "paged_decode_window", "paged_prefill",
     "slot",
-    "dequantize", "quantize_rows",
+    "dequantize", "quantize_rows", "PrefixModel",
 ]

@@ -156,6 +156,86 @@ def kvp_seq_evict_window(pool: Pool, row: np.ndarray, ctx_len: int, sink_tokens:
                                    int(sink_tokens), int(window_tokens)), "kvp_seq_evict_window")
 
 
+class PrefixCache:
+    """Owner of one host prefix cache (kvp_prefix_cache_create / _destroy)."""
+
+    def __init__(self, pool: Pool):
+        h = ctypes.c_void_p()
+        _check(_L.kvp_prefix_cache_create(pool.handle, ctypes.byref(h)), "kvp_prefix_cache_create")
+        self.handle = h
+        self.pool = pool   # the pool must outlive the cache
+
+    def close(self) -> None:
+        if self.handle:
+            _L.kvp_prefix_cache_destroy(self.handle)
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def kvp_prefix_cache_create(pool: Pool) -> PrefixCache:
+    return PrefixCache(pool)
+
+
+def kvp_prefix_cache_pages(cache: PrefixCache) -> int:
+    return int(_L.kvp_prefix_cache_pages(cache.handle))
+
+
+def kvp_prefix_match(cache: PrefixCache, tokens, max_pages: int = None) -> np.ndarray:
+    """Pages of the longest cached whole-block prefix of ``tokens`` (each with a
+    reference added for the caller)."""
+    tokens = _i32(np.ascontiguousarray(tokens, dtype=np.int32))
+    P = cache.pool.desc.page_size
+    cap = tokens.size // P if max_pages is None else int(max_pages)
+    out = np.empty(max(cap, 1), dtype=np.int32)
+    n = ctypes.c_int32()
+    _check(_L.kvp_prefix_match(cache.handle, _ptr(tokens), tokens.size, _ptr(out), cap,
+                               ctypes.byref(n)), "kvp_prefix_match")
+    return out[:n.value].copy()
+
+
+def kvp_prefix_insert(cache: PrefixCache, tokens, pages) -> None:
+    tokens = _i32(np.ascontiguousarray(tokens, dtype=np.int32))
+    pages = _i32(np.ascontiguousarray(pages, dtype=np.int32))
+    if pages.size < tokens.size // cache.pool.desc.page_size:
+        raise ValueError("one page per full block of tokens is needed")
+    _check(_L.kvp_prefix_insert(cache.handle, _ptr(tokens), tokens.size, _ptr(pages)),
+           "kvp_prefix_insert")
+
+
+def kvp_prefix_evict(cache: PrefixCache, n_pages: int) -> int:
+    n = ctypes.c_int32()
+    _check(_L.kvp_prefix_evict(cache.handle, int(n_pages), ctypes.byref(n)), "kvp_prefix_evict")
+    return int(n.value)
+
+
+def kvp_seq_prepare_append(pool: Pool, row: np.ndarray, cur_len: int, new_len: int):
+    """Private pages for appending cur_len..new_len-1; returns [(src, dst)] copies to run."""
+    row = _i32(row)
+    src = np.full(1, -1, dtype=np.int32)
+    dst = np.full(1, -1, dtype=np.int32)
+    n = ctypes.c_int32()
+    _check(_L.kvp_seq_prepare_append(pool.handle, _ptr(row), row.size, int(cur_len),
+                                     int(new_len), _ptr(src), _ptr(dst), ctypes.byref(n)),
+           "kvp_seq_prepare_append")
+    return [(int(src[0]), int(dst[0]))] if n.value else []
+
+
+def kvp_copy_pages(pool: Pool, k_pool, v_pool, k_meta, v_meta, src_dst, stream=None) -> None:
+    """Copy pages on the device; src_dst is an int32 device tensor [n, 2]."""
+    eb = 1 if pool.desc.dtype == KVP_INT8 else 2
+    n = int(src_dst.shape[0]) if src_dst.dim() == 2 else 0
+    if src_dst.dim() != 2 or src_dst.shape[1] != 2:
+        raise ValueError("src_dst must be [n, 2]")
+    _check(_L.kvp_copy_pages(pool.handle, _dev(k_pool, "k_pool", eb), _dev(v_pool, "v_pool", eb),
+                             _dev(k_meta, "k_meta", 2), _dev(v_meta, "v_meta", 2),
+                             _dev(src_dst, "src_dst", 4), n, _stream(stream)), "kvp_copy_pages")
+
+
 def kvp_decode_plan(desc: PoolDesc, num_seqs: int, num_q_heads: int, max_context_len: int,
                     num_splits_req: int = 0, num_cus: int = 256) -> dict:
     p = DecodePlan()
@@ -337,5 +417,7 @@ __all__ = [
     "kvp_kv_append", "kvp_decode_workspace_bytes", "kvp_paged_attention_decode",
     "kvp_decode_partials_bytes", "kvp_paged_attention_decode_partials", "kvp_lse_merge",
     "kvp_seq_evict_window", "kvp_decode_window_workspace_bytes",
-    "kvp_paged_attention_decode_window", "kvp_paged_attention_prefill",
+    "kvp_paged_attention_decode_window", "kvp_paged_attention_prefill", "PrefixCache",
+    "kvp_prefix_cache_create", "kvp_prefix_cache_pages", "kvp_prefix_match",
+    "kvp_prefix_insert", "kvp_prefix_evict", "kvp_seq_prepare_append", "kvp_copy_pages",
 ]

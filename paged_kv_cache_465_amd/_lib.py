@@ -64,6 +64,16 @@ PROTOTYPES = {
                                               c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                               c_int32, c_int32, c_int32, c_int32, c_float,
                                               c_void_p, c_void_p]),
+    "kvp_prefix_cache_create": (c_int32, [c_void_p, ctypes.POINTER(c_void_p)]),
+    "kvp_prefix_cache_destroy": (None, [c_void_p]),
+    "kvp_prefix_cache_pages": (c_int32, [c_void_p]),
+    "kvp_prefix_match": (c_int32, [c_void_p, P_int32, c_int32, P_int32, c_int32, P_int32]),
+    "kvp_prefix_insert": (c_int32, [c_void_p, P_int32, c_int32, P_int32]),
+    "kvp_prefix_evict": (c_int32, [c_void_p, c_int32, P_int32]),
+    "kvp_seq_prepare_append": (c_int32, [c_void_p, P_int32, c_int32, c_int32, c_int32, P_int32,
+                                         P_int32, P_int32]),
+    "kvp_copy_pages": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_int32, c_void_p]),
     "kvp_seq_evict_window": (c_int32, [c_void_p, P_int32, c_int32, c_int32, c_int32, c_int32]),
     "kvp_decode_window_workspace_bytes": (c_int32, [c_void_p, c_int32, c_int32, c_int32,
                                                     c_int32, c_int32, c_int32,

@@ -23,7 +23,7 @@ HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
 DEVICE_SOURCES = ["append.hip", "decode.hip", "prefill.hip"]
-HOST_SOURCES = ["pool.cpp"]
+HOST_SOURCES = ["pool.cpp", "prefix_cache.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
 # Device code: gfx950 only; packed-fp32 instructions off; IEEE-rounded fp32

@@ -173,3 +173,59 @@ extern "C" kvp_status kvp_kv_append(const kvp_pool* pool, void* k_pool, void* v_
   }
   return e == hipSuccess ? KVP_OK : KVP_E_HIP;
 }
+
+// Copy whole pages (every KV head) of one layer's pools: the device half of
+// copy-on-write for pages several sequences share ("KV-Cache Optimization
+// Techniques", section "Prefix Caching": an existing prefix is reused via
+// copy-on-write).  A page occupies page_bytes contiguous bytes of the K pool,
+// the same of the V pool, and meta_bytes of each metadata array.  Workgroup
+// (pair, part) copies one quarter-page strip of K, V and metadata with 16-byte
+// accesses; pairs naming a page outside the pool are skipped.
+namespace kvp {
+
+__global__ __launch_bounds__(256) void copy_pages_kernel(char* k, char* v, char* km, char* vm,
+                                                         const int32_t* pairs, int32_t n,
+                                                         int32_t num_pages, int64_t page_bytes,
+                                                         int64_t meta_bytes) {
+  const int pair = blockIdx.x >> 2, part = blockIdx.x & 3;
+  if (pair >= n) return;
+  const int src = pairs[2 * pair], dst = pairs[2 * pair + 1];
+  if (unsigned(src) >= unsigned(num_pages) || unsigned(dst) >= unsigned(num_pages) || src == dst)
+    return;
+  const int64_t strip = page_bytes / 4;  // page bytes are a multiple of 64
+  const int64_t s0 = int64_t(src) * page_bytes + part * strip;
+  const int64_t d0 = int64_t(dst) * page_bytes + part * strip;
+  for (int64_t o = int64_t(threadIdx.x) * 16; o < strip; o += 256 * 16) {
+    *reinterpret_cast<uint4*>(k + d0 + o) = *reinterpret_cast<const uint4*>(k + s0 + o);
+    *reinterpret_cast<uint4*>(v + d0 + o) = *reinterpret_cast<const uint4*>(v + s0 + o);
+  }
+  if (km && part == 0) {
+    const int64_t ms = int64_t(src) * meta_bytes, md = int64_t(dst) * meta_bytes;
+    for (int64_t o = int64_t(threadIdx.x) * 16; o < meta_bytes; o += 256 * 16) {
+      *reinterpret_cast<uint4*>(km + md + o) = *reinterpret_cast<const uint4*>(km + ms + o);
+      *reinterpret_cast<uint4*>(vm + md + o) = *reinterpret_cast<const uint4*>(vm + ms + o);
+    }
+  }
+}
+
+}  // namespace kvp
+
+extern "C" kvp_status kvp_copy_pages(const kvp_pool* pool, void* k_pool, void* v_pool,
+                                     void* k_meta, void* v_meta, const int32_t* src_dst,
+                                     int32_t n, kvp_stream_t stream) {
+  kvp_pool_desc d;
+  if (kvp_pool_get_desc(pool, &d) != KVP_OK || n < 0) return KVP_E_INVAL;
+  if (n == 0) return KVP_OK;
+  if (!k_pool || !v_pool || !src_dst) return KVP_E_INVAL;
+  const bool int8 = d.dtype == KVP_INT8;
+  if (int8 != (k_meta != nullptr) || int8 != (v_meta != nullptr)) return KVP_E_INVAL;
+  const int64_t elem = int8 ? 1 : 2;
+  const int64_t page_bytes = int64_t(d.num_kv_heads) * d.page_size * d.head_dim * elem;
+  const int64_t meta_bytes = int8 ? int64_t(d.num_kv_heads) * d.page_size * 4 : 0;
+  if (int64_t(n) * 4 > 0x7fffffff) return KVP_E_UNSUPPORTED;
+  hipLaunchKernelGGL(kvp::copy_pages_kernel, dim3(unsigned(n) * 4), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<char*>(k_pool),
+                     static_cast<char*>(v_pool), static_cast<char*>(k_meta),
+                     static_cast<char*>(v_meta), src_dst, n, d.num_pages, page_bytes, meta_bytes);
+  return hipGetLastError() == hipSuccess ? KVP_OK : KVP_E_HIP;
+}

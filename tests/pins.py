@@ -424,3 +424,47 @@ def pin_prefill_single_row_is_decode(case):
                              case.ctx, case.scale)
     d = oracle.paged_decode(lay, case.q, k, v, km, vm, case.block_tables, case.ctx, case.scale)
     assert np.array_equal(a, d)
+
+
+# ---------------------------------------------------------------- prefix caching
+def pin_prefix_eq2(N=100, T=2512, shared=2000, P=16):
+    """Eq. 2 with the worked numbers of "Prefix Caching" (N = 100 requests,
+    P_shared = 2000 tokens; T = 2512, a whole number of pages):
+    caching every request's full blocks leaves P_shared/P + N*(T-P_shared)/P
+    distinct pages, i.e. the prefix-cached memory of eq. 2 divided by the
+    bytes of one page, and each later request matches exactly the prefix."""
+    rng = np.random.default_rng(3)
+    prefix = rng.integers(0, 50_000, shared).tolist()
+    model = oracle.PrefixModel(P)
+    next_page = 0
+    for r in range(N):
+        toks = prefix + rng.integers(0, 50_000, T - shared).tolist()
+        got = model.match(toks)
+        assert len(got) == (shared // P if r > 0 else 0), (r, len(got))
+        pages = got + list(range(next_page, next_page + T // P - len(got)))
+        next_page += T // P - len(got)
+        model.insert(toks, pages)
+    c = 1.0  # bytes per token: any unit
+    expect = oracle.prefix_cached_bytes(N, T, shared, c) / (c * P)
+    assert model.unique_pages() == expect == shared // P + N * (T - shared) // P
+
+
+def pin_prefix_longest_match(trials=300, P=4):
+    """The model's match is the longest common whole-block prefix with any
+    inserted sequence, found by brute force over the inserted token lists."""
+    rng = np.random.default_rng(5)
+    model = oracle.PrefixModel(P)
+    seqs = []
+    base = rng.integers(0, 3, 64).tolist()        # small alphabet: many shared prefixes
+    for t in range(trials):
+        cut = int(rng.integers(0, 64))
+        toks = base[:cut] + rng.integers(0, 3, int(rng.integers(0, 40))).tolist()
+        best = 0
+        for s in seqs:
+            k = 0
+            while (k + 1) * P <= min(len(s), len(toks)) and s[:(k + 1) * P] == toks[:(k + 1) * P]:
+                k += 1
+            best = max(best, k)
+        assert len(model.match(toks)) == best, t
+        model.insert(toks, list(range(1000 * t, 1000 * t + len(toks) // P)))
+        seqs.append(toks)

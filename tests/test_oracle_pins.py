@@ -107,3 +107,11 @@ def test_prefill_vs_library_sdpa(cfg):
 
 def test_prefill_single_row_is_decode(small_case):
     pins.pin_prefill_single_row_is_decode(small_case)
+
+
+def test_prefix_cache_model_eq2():
+    pins.pin_prefix_eq2()
+
+
+def test_prefix_cache_model_longest_match():
+    pins.pin_prefix_longest_match()
