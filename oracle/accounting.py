@@ -46,6 +46,11 @@ def gqa_ratio(kv_heads: int, q_heads: int) -> float:
     return kv_heads / q_heads
 
 
+def int4_row_ratio(head_dim: int) -> float:
+    """Bytes of an INT4 row (D/2 code bytes + float16 scale + zero) over bfloat16."""
+    return (head_dim / 2 + 4) / (2 * head_dim)
+
+
 def int8_row_ratio(head_dim: int) -> float:
     """Bytes of an INT8 row (D codes + float16 scale + float16 zero) over its
     bfloat16 size: the "2x" of section "KV-Cache Quantization" less metadata."""

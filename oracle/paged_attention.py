@@ -31,7 +31,10 @@ Readings taken where the pages leave a step open:
 
 The pool layout is the library header's contract, written out here from its
 text: K[page][h][t][d], V stored transposed per (page, head) as [d][t],
-float16 (scale, zero) pairs per token per head for INT8 pools.
+float16 (scale, zero) pairs per token per head for INT8 pools.  INT4 pools
+hold two channels per byte (even channel in the low nibble, code + 8):
+K bytes [page][h][t][d/2], V bytes [page][h][d/2][t].  FP8 pools hold one
+e4m3 code per byte in the INT8 layout, with (scale, 0) metadata.
 """
 from __future__ import annotations
 
@@ -39,7 +42,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .quantize import bf16_bits_to_f32, dequantize, quantize_rows
+from .quantize import (bf16_bits_to_f32, dequantize, dequantize_fp8, quantize_rows,
+                       quantize_rows_fp8, quantize_rows_int4)
 
 
 @dataclass(frozen=True)
@@ -48,12 +52,16 @@ class PoolLayout:
     page_size: int      # P
     num_kv_heads: int   # H_kv
     head_dim: int       # D
-    dtype: str = "bf16"  # "bf16" | "int8"
+    dtype: str = "bf16"  # "bf16" | "int8" | "int4" | "fp8"
 
     @property
     def elems(self) -> int:
         """Elements of one K (or V) array."""
         return self.num_pages * self.num_kv_heads * self.page_size * self.head_dim
+
+    @property
+    def quantized(self) -> bool:
+        return self.dtype != "bf16"
 
     @property
     def meta_elems(self) -> int:
@@ -66,6 +74,13 @@ class PoolLayout:
             k = np.full(self.elems, k_fill, dtype=np.uint16)
             v = np.full(self.elems, k_fill, dtype=np.uint16)
             return k, v, None, None
+        if self.dtype in ("int4", "fp8"):
+            nbytes = self.elems // 2 if self.dtype == "int4" else self.elems
+            k = np.full(nbytes, k_fill, dtype=np.uint8)
+            v = np.full(nbytes, k_fill, dtype=np.uint8)
+            km = np.full(self.meta_elems, meta_fill, dtype=np.uint16)
+            vm = np.full(self.meta_elems, meta_fill, dtype=np.uint16)
+            return k, v, km, vm
         k = np.full(self.elems, k_fill, dtype=np.uint8).view(np.int8)
         v = np.full(self.elems, k_fill, dtype=np.uint8).view(np.int8)
         km = np.full(self.meta_elems, meta_fill, dtype=np.uint16)
@@ -95,6 +110,9 @@ def gather_sequence(layout: PoolLayout, k_pool, v_pool, k_meta, v_meta,
     pages = np.asarray(block_table_row[:nb], dtype=np.int64)
     if (pages < 0).any() or (pages >= layout.num_pages).any():
         raise ValueError("block table names a page outside the pool")
+    if layout.dtype in ("int4", "fp8"):
+        return gather_positions(layout, k_pool, v_pool, k_meta, v_meta, block_table_row,
+                                np.arange(ctx))
     kp = np.asarray(k_pool).reshape(layout.num_pages, H, P, D)[pages]      # [nb,H,P,D]
     vp = np.asarray(v_pool).reshape(layout.num_pages, H, D, P)[pages]      # [nb,H,D,P]
     if layout.dtype == "bf16":
@@ -136,6 +154,21 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndar
     return out
 
 
+def _unpack_nibbles(b: np.ndarray) -> np.ndarray:
+    """Bytes holding channel pairs (even channel low, code + 8) -> codes [..., 2n]."""
+    b = np.asarray(b, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.int64)
+    out[..., 0::2] = (b & 0xF).astype(np.int64) - 8
+    out[..., 1::2] = (b >> 4).astype(np.int64) - 8
+    return out
+
+
+def _pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """Codes in -8..7 [..., 2n] -> bytes [..., n] (even channel in the low nibble)."""
+    c = (np.asarray(codes, dtype=np.int64) + 8).astype(np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
 def kept_positions(n: int, sink: int, window: int) -> np.ndarray:
     """Positions a sequence of n tokens attends to with s sink tokens and a
     recent window of w tokens (eq. 5; eq. 6 when s = 0).  w = 0: no window."""
@@ -157,9 +190,29 @@ def gather_positions(layout: PoolLayout, k_pool, v_pool, k_meta, v_meta,
     rows = positions % P
     if (pages < 0).any() or (pages >= layout.num_pages).any():
         raise ValueError("a kept position lies in a page outside the pool")
+    hh = np.arange(H)[None, :]
+    if layout.dtype in ("int4", "fp8"):
+        km = np.asarray(k_meta).reshape(layout.num_pages, H, P, 2)[pages[:, None], hh,
+                                                                   rows[:, None]]  # [len, H, 2]
+        vm = np.asarray(v_meta).reshape(layout.num_pages, H, P, 2)[pages[:, None], hh,
+                                                                   rows[:, None]]
+        if layout.dtype == "fp8":
+            kb = np.asarray(k_pool).reshape(layout.num_pages, H, P, D)[pages[:, None], hh,
+                                                                       rows[:, None], :]
+            vb = np.asarray(v_pool).reshape(layout.num_pages, H, D, P)[pages[:, None], hh, :,
+                                                                       rows[:, None]]
+            K = dequantize_fp8(kb, km[..., 0])
+            V = dequantize_fp8(vb, vm[..., 0])
+        else:
+            kb = np.asarray(k_pool).reshape(layout.num_pages, H, P, D // 2)[pages[:, None], hh,
+                                                                            rows[:, None], :]
+            vb = np.asarray(v_pool).reshape(layout.num_pages, H, D // 2, P)[pages[:, None], hh,
+                                                                            :, rows[:, None]]
+            K = dequantize(_unpack_nibbles(kb), km[..., 0], km[..., 1])
+            V = dequantize(_unpack_nibbles(vb), vm[..., 0], vm[..., 1])
+        return K.transpose(1, 0, 2), V.transpose(1, 0, 2)
     kp = np.asarray(k_pool).reshape(layout.num_pages, H, P, D)
     vp = np.asarray(v_pool).reshape(layout.num_pages, H, D, P)
-    hh = np.arange(H)[None, :]
     kr = kp[pages[:, None], hh, rows[:, None], :]    # [len, H, D]
     vr = vp[pages[:, None], hh, :, rows[:, None]]    # [len, H, D] (V tile is [D][P])
     if layout.dtype == "bf16":
@@ -237,7 +290,8 @@ def append(layout: PoolLayout, k_pool, v_pool, k_meta, v_meta, k_rows, v_rows,
     hold the sequence's rows at the positions the page table gives).
 
     k_rows, v_rows: bfloat16 bits [N, H_kv, D]; seq_idx, pos: [N].
-    INT8 pools store each (token, head) row quantized (``quantize_rows``).
+    INT8 pools store each (token, head) row quantized (``quantize_rows``);
+    INT4 and FP8 pools with ``quantize_rows_int4`` / ``quantize_rows_fp8``.
     Rows are written in order, so a later row wins a shared slot.
     """
     P, H, D = layout.page_size, layout.num_kv_heads, layout.head_dim
@@ -247,15 +301,30 @@ def append(layout: PoolLayout, k_pool, v_pool, k_meta, v_meta, k_rows, v_rows,
     if (pages < 0).any() or (pages >= layout.num_pages).any():
         raise ValueError("append names a page outside the pool")
     t = pos % P
-    kp = np.asarray(k_pool).reshape(layout.num_pages, H, P, D)
-    vp = np.asarray(v_pool).reshape(layout.num_pages, H, D, P)
     hh = np.arange(H)
+    if layout.dtype in ("bf16", "int8"):
+        kp = np.asarray(k_pool).reshape(layout.num_pages, H, P, D)
+        vp = np.asarray(v_pool).reshape(layout.num_pages, H, D, P)
     if layout.dtype == "bf16":
         kp[pages[:, None], hh[None, :], t[:, None], :] = k_rows
         vp[pages[:, None], hh[None, :], :, t[:, None]] = v_rows
         return
     km = np.asarray(k_meta).reshape(layout.num_pages, H, P, 2)
     vm = np.asarray(v_meta).reshape(layout.num_pages, H, P, 2)
+    if layout.dtype in ("int4", "fp8"):
+        kb = np.asarray(k_pool).reshape(layout.num_pages, H, P, -1)          # [.., t, bytes]
+        vb = np.asarray(v_pool).reshape(layout.num_pages, H, -1, P)          # [.., bytes, t]
+        quant = quantize_rows_int4 if layout.dtype == "int4" else quantize_rows_fp8
+        for rows, pool, meta, transposed in ((k_rows, kb, km, False), (v_rows, vb, vm, True)):
+            codes, s16, z16 = quant(rows)
+            stored = _pack_nibbles(codes) if layout.dtype == "int4" else codes
+            if transposed:
+                pool[pages[:, None], hh[None, :], :, t[:, None]] = stored
+            else:
+                pool[pages[:, None], hh[None, :], t[:, None], :] = stored
+            meta[pages[:, None], hh[None, :], t[:, None], 0] = s16
+            meta[pages[:, None], hh[None, :], t[:, None], 1] = z16
+        return
     for rows, pool, meta, transposed in ((k_rows, kp, km, False), (v_rows, vp, vm, True)):
         codes, s16, z16 = quantize_rows(rows)
         if transposed:

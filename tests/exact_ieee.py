@@ -55,19 +55,27 @@ def f16(x) -> Fraction:
     return round_fmt(Fraction(x), F16)
 
 
-def quantize_row_exact(xs):
-    """The INT8 row contract, one IEEE operation at a time, in exact rationals.
+def quantize_row_exact(xs, steps=254, lo=-128, hi=127):
+    """The INT8 row contract (or, with steps=14, lo=-8, hi=7, the INT4 one),
+    one IEEE operation at a time, in exact rationals.
 
     xs: iterable of exact values (bfloat16 values are exact float32 values).
     Returns (codes list[int], scale Fraction, zero Fraction)."""
     xs = [Fraction(x) for x in xs]
     mn, mx = min(xs), max(xs)
     z = f16(f32(f32(mx + mn) * Fraction(1, 2)))
-    s = f16(f32(f32(mx - mn) / 254))
+    s = f16(f32(f32(mx - mn) / steps))
     if s == 0:
         s = Fraction(1)
     codes = []
     for x in xs:
         q = f32(f32(x - z) / s)
-        codes.append(max(-128, min(127, round_half_even_int(q))))
+        codes.append(max(lo, min(hi, round_half_even_int(q))))
     return codes, s, z
+
+
+def fp8_scale_exact(xs):
+    """f16(f32(max|x| / 448)), 1 if that rounds to 0 (the FP8 row scale)."""
+    amax = max(abs(Fraction(x)) for x in xs)
+    s = f16(f32(amax / 448))
+    return Fraction(1) if s == 0 else s

@@ -21,7 +21,7 @@ from oracle import quantize as oq
 from workloads import TINY, f32_to_bf16_bits, make_case, variant
 
 from .casetools import layout_of, logical_rows, oracle_pools
-from .exact_ieee import quantize_row_exact
+from .exact_ieee import fp8_scale_exact, quantize_row_exact
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -126,10 +126,11 @@ def pin_attention_vs_sdpa(case, tol=1e-12):
                               case.scale)
     for b in range(case.B):
         K, V = logical_rows(case, b)
-        if case.cfg.kv_dtype == "int8":
+        dt = case.cfg.kv_dtype
+        if dt != "bf16":
             # the library routine sees the dequantized rows of the row contract
-            Kf = np.stack([_dequant_exact(K[t]) for t in range(K.shape[0])])
-            Vf = np.stack([_dequant_exact(V[t]) for t in range(V.shape[0])])
+            Kf = np.stack([_dequant_exact(K[t], dt) for t in range(K.shape[0])])
+            Vf = np.stack([_dequant_exact(V[t], dt) for t in range(V.shape[0])])
         else:
             Kf, Vf = _bf16_f64(K), _bf16_f64(V)
         ref = _sdpa(_bf16_f64(case.q[b]), Kf, Vf, float(np.float32(case.scale)))
@@ -137,12 +138,23 @@ def pin_attention_vs_sdpa(case, tol=1e-12):
         assert err <= tol, f"seq {b}: oracle vs sdpa {err:.3e}"
 
 
-def _dequant_exact(rows_bits):
-    """[H, D] bfloat16 rows -> float64 values after the exact-rational row contract."""
+def _dequant_exact(rows_bits, dtype="int8"):
+    """[H, D] bfloat16 rows -> float64 values after the exact row contract of
+    ``dtype`` (exact-rational IEEE steps for INT8/INT4; for FP8 the
+    exact-rational scale and torch's float8_e4m3fn conversion of x / s)."""
     xs = _bf16_f64(rows_bits)
     res = np.zeros_like(xs)
     for h in range(xs.shape[0]):
-        codes, s, z = quantize_row_exact(xs[h].tolist())
+        if dtype == "fp8":
+            s = fp8_scale_exact(xs[h].tolist())
+            q = (xs[h].astype(np.float32) / np.float32(float(s))).astype(np.float32)
+            e4 = torch.from_numpy(np.clip(q, -448, 448)).to(torch.float8_e4m3fn)
+            res[h] = float(s) * e4.to(torch.float64).numpy()
+            continue
+        if dtype == "int4":
+            codes, s, z = quantize_row_exact(xs[h].tolist(), steps=14, lo=-8, hi=7)
+        else:
+            codes, s, z = quantize_row_exact(xs[h].tolist())
         res[h] = [float(s * c + z) for c in codes]
     return res
 
@@ -323,9 +335,10 @@ def pin_window_vs_sdpa(case, sink, window, tol=1e-12):
         n = K.shape[0]
         t = np.arange(n)
         keep = (t < sink) | (t >= n - window) if sink + window < n else np.ones(n, bool)
-        if case.cfg.kv_dtype == "int8":
-            Kf = np.stack([_dequant_exact(K[i]) for i in np.nonzero(keep)[0]])
-            Vf = np.stack([_dequant_exact(V[i]) for i in np.nonzero(keep)[0]])
+        dt = case.cfg.kv_dtype
+        if dt != "bf16":
+            Kf = np.stack([_dequant_exact(K[i], dt) for i in np.nonzero(keep)[0]])
+            Vf = np.stack([_dequant_exact(V[i], dt) for i in np.nonzero(keep)[0]])
         else:
             Kf, Vf = _bf16_f64(K[keep]), _bf16_f64(V[keep])
         ref = _sdpa(_bf16_f64(case.q[b]), Kf, Vf, float(np.float32(case.scale)))
@@ -396,9 +409,10 @@ def pin_prefill_vs_sdpa(case, tol=1e-12):
         n = K.shape[0]
         r0, r1 = int(case.q_start[b]), int(case.q_start[b + 1])
         L = r1 - r0
-        if case.cfg.kv_dtype == "int8":
-            Kf = np.stack([_dequant_exact(K[t]) for t in range(n)])
-            Vf = np.stack([_dequant_exact(V[t]) for t in range(n)])
+        dt = case.cfg.kv_dtype
+        if dt != "bf16":
+            Kf = np.stack([_dequant_exact(K[t], dt) for t in range(n)])
+            Vf = np.stack([_dequant_exact(V[t], dt) for t in range(n)])
         else:
             Kf, Vf = _bf16_f64(K), _bf16_f64(V)
         qf = _bf16_f64(case.q[r0:r1])                       # [L, H_q, D]
@@ -468,3 +482,147 @@ def pin_prefix_longest_match(trials=300, P=4):
         assert len(model.match(toks)) == best, t
         model.insert(toks, list(range(1000 * t, 1000 * t + len(toks) // P)))
         seqs.append(toks)
+
+
+# ---------------------------------------------------------------- INT4 and FP8 rows
+def pin_int4_exact_rational(rows_bits):
+    """quantize_rows_int4 equals the exact-rational IEEE model of its contract."""
+    from oracle import quantize as oq
+    codes, s16, z16 = oq.quantize_rows_int4(rows_bits)
+    x = _bf16_f64(rows_bits)
+    for i in range(x.shape[0]):
+        c, s, z = quantize_row_exact(x[i].tolist(), steps=14, lo=-8, hi=7)
+        assert codes[i].tolist() == c, i
+        assert float(np.uint16(s16[i]).view(np.float16)) == float(s)
+        assert float(np.uint16(z16[i]).view(np.float16)) == float(z)
+
+
+def pin_int4_round_trip_and_ties():
+    """Round trip within s*(1/2 + 2^-15) when nothing clamps; tie rows round
+    half to even; a row already on the grid reconstructs exactly."""
+    from oracle import quantize as oq
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((200, 128)).astype(np.float32)
+    bits = f32_to_bf16_bits(x)
+    codes, s16, z16 = oq.quantize_rows_int4(bits)
+    s = s16.view(np.float16).astype(np.float64)[:, None]
+    z = z16.view(np.float16).astype(np.float64)[:, None]
+    err = np.abs(_bf16_f64(bits) - (s * codes + z))
+    unclamped = (codes > -8) & (codes < 7)
+    assert (err[unclamped] <= (s * (0.5 + 2.0 ** -15) * np.ones_like(err))[unclamped]).all()
+    # range -7..7 with s = 1, z = 0: ties 2.5 -> 2, 3.5 -> 4, -0.5 -> -0
+    tie = np.zeros(128, np.float32)
+    tie[:6] = [-7, 7, 2.5, 3.5, -0.5, 1.5]
+    c, s1, z1 = oq.quantize_rows_int4(f32_to_bf16_bits(tie)[None])
+    assert c[0, :6].tolist() == [-7, 7, 2, 4, 0, 2]
+    grid = (np.arange(128) % 15 - 7).astype(np.float32) * 0.25
+    c, s1, z1 = oq.quantize_rows_int4(f32_to_bf16_bits(grid)[None])
+    back = s1.view(np.float16).astype(np.float64) * c[0] + z1.view(np.float16).astype(np.float64)
+    assert np.array_equal(back, grid.astype(np.float64))
+
+
+def pin_fp8_encode_vs_torch():
+    """e4m3 codes: torch's float8_e4m3fn conversion (a library routine) gives
+    the same code for every |value| <= 448; larger magnitudes saturate to
+    +-448; the code table decodes as torch decodes."""
+    from oracle import quantize as oq
+    rng = np.random.default_rng(13)
+    x = np.concatenate([rng.standard_normal(100_000).astype(np.float32) * np.float32(40),
+                        rng.standard_normal(20_000).astype(np.float32) * np.float32(0.01),
+                        np.float32([0.0, -0.0, 448, -448, 2.0 ** -9, 2.0 ** -10, 1.5 * 2 ** -9,
+                                    2.0 ** -6, 240.0, 232.0, 248.0])])
+    enc = oq.e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(enc, ref)
+    big = np.float32([449.0, 464.0, 479.0, 1e6, -512.0])
+    assert oq.e4m3_encode(big).tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE]
+    dec = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    dec = dec.to(torch.float64).numpy()
+    t = oq.e4m3_table()
+    assert np.array_equal(np.isnan(t), np.isnan(dec)) and np.array_equal(t[~np.isnan(t)],
+                                                                         dec[~np.isnan(dec)])
+
+
+def pin_fp8_rows():
+    """FP8 rows: the scale is the exact-rational f16(f32(amax/448)); every code
+    is the e4m3 rounding of the float32 quotient x / s; |x| / s <= 448 up to
+    the scale's own rounding, so only the extreme element can saturate."""
+    from oracle import quantize as oq
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((64, 128)).astype(np.float32)
+    x[:, 5] *= 8
+    bits = f32_to_bf16_bits(x)
+    codes, s16, z16 = oq.quantize_rows_fp8(bits)
+    assert (z16 == 0).all()
+    xf = _bf16_f64(bits)
+    for i in range(64):
+        s = fp8_scale_exact(xf[i].tolist())
+        assert float(np.uint16(s16[i]).view(np.float16)) == float(s)
+        q = (bf16_bits_to_f32_np(bits[i]) / np.float32(float(s))).astype(np.float32)
+        ref = torch.from_numpy(np.clip(q, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8)
+        assert np.array_equal(codes[i], ref.numpy()), i
+    # relative error of the nearest e4m3 value is at most 2^-4 in the normal range
+    back = oq.dequantize_fp8(codes, s16)
+    s = s16.view(np.float16).astype(np.float64)[:, None]
+    normal = np.abs(xf) >= s * 2.0 ** -6
+    assert (np.abs(back - xf)[normal] <= 2.0 ** -4 * np.abs(xf)[normal] + 1e-300).all()
+
+
+def bf16_bits_to_f32_np(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def pin_int4_memory_ratios():
+    """"KV-Cache Quantization": FP16 -> INT4 is 4x; "Multi-Query and Grouped-Query
+    Caching": GQA with the LLaMA-2 70B numbers (H = 64, G = 8) times INT4 is the
+    printed 32x.  With float16 scale and zero per row the INT4 row is (D/2+4)/(2D)
+    of bfloat16 (0.266 at D = 128)."""
+    g = _golden("memory_closed_forms.json")["gqa_llama2_70b"]
+    int4_over_fp16 = 0.5 / 2
+    total = oracle.gqa_ratio(g["kv_groups"], g["q_heads"]) * int4_over_fp16
+    assert 1 / total == g["int4_times_gqa_printed"]
+    assert 1 / int4_over_fp16 == g["int4_reduction_printed"]
+    from oracle.accounting import int4_row_ratio
+    assert int4_row_ratio(128) == 68 / 256
+
+
+def pin_quantized_layout():
+    """INT4 and FP8 pool bytes sit where the header's index formulas put them:
+    INT4 K byte ((page*H + h)*P + t)*(D/2) + d/2 and V byte
+    ((page*H + h)*(D/2) + d/2)*P + t, channel d in the low nibble when d is
+    even, holding code + 8; FP8 codes in the INT8 layout."""
+    from oracle import quantize as oq
+    P, H, D, NP = 16, 2, 64, 3
+    x = np.zeros((1, H, D), np.float32)
+    x[0, 0, :15] = np.arange(-7, 8)          # row range -7..7: s = 1, z = 0, codes = x
+    x[0, 0, 15:] = 0
+    x[0, 1, :] = np.linspace(-3, 3, D)
+    bits = f32_to_bf16_bits(x)
+    bt = np.array([[2, 0]], np.int32)
+    for dt in ("int4", "fp8"):
+        lay = oracle.PoolLayout(NP, P, H, D, dt)
+        k, v, km, vm = lay.empty_pools(0x7F, 0)
+        oracle.append(lay, k, v, km, vm, bits, bits, np.array([0]), np.array([5]), bt)
+        page, t = 2, 5
+        quant = oq.quantize_rows_int4 if dt == "int4" else oq.quantize_rows_fp8
+        codes, s16, z16 = quant(bits[0])
+        for h in range(H):
+            for d in range(D):
+                if dt == "int4":
+                    kb = k[((page * H + h) * P + t) * (D // 2) + d // 2]
+                    vb = v[((page * H + h) * (D // 2) + d // 2) * P + t]
+                    nib = lambda b: (int(b) >> (4 * (d % 2))) & 0xF  # noqa: E731
+                    assert nib(kb) == codes[h, d] + 8 and nib(vb) == codes[h, d] + 8, (h, d)
+                else:
+                    assert k[((page * H + h) * P + t) * D + d] == codes[h, d]
+                    assert v[((page * H + h) * D + d) * P + t] == codes[h, d]
+            assert km[((page * H + h) * P + t) * 2] == s16[h]
+            assert vm[((page * H + h) * P + t) * 2 + 1] == z16[h]
+        if dt == "int4":
+            assert codes[0, :15].tolist() == list(range(-7, 8))
+        # every byte outside the written row keeps its fill
+        touched = np.zeros(k.size, bool)
+        for h in range(H):
+            per = D // 2 if dt == "int4" else D
+            touched[((page * H + h) * P + t) * per:((page * H + h) * P + t + 1) * per] = True
+        assert (k[~touched] == 0x7F).all()

@@ -47,6 +47,10 @@ def _all_pins():
                        lambda s=sink, w=window: pins.pin_window_vs_sdpa(_case(TINY), s, w)))
     checks.append(("window_degenerate", lambda: pins.pin_window_degenerate(_case(TINY))))
     checks.append(("window_memory", pins.pin_window_memory_bound))
+    checks.append(("int4_layout", pins.pin_quantized_layout))
+    checks.append(("int4_round_trip", pins.pin_int4_round_trip_and_ties))
+    checks.append(("fp8_vs_torch", pins.pin_fp8_encode_vs_torch))
+    checks.append(("fp8_rows", pins.pin_fp8_rows))
     for c in pins.prefill_cases()[:2]:
         checks.append((f"prefill_{c.name}", lambda c=c: pins.pin_prefill_vs_sdpa(_case(c))))
     return checks
@@ -220,7 +224,42 @@ def _prefill_anchored_at_zero(layout, q_bits, q_start, k_pool, v_pool, k_meta, v
     return out
 
 
+def _int4_fifteen_steps(x_bits):
+    x = oq.bf16_bits_to_f32(x_bits)
+    mn, mx = x.min(axis=-1), x.max(axis=-1)
+    z16 = ((mx + mn) * np.float32(0.5)).astype(np.float16)
+    s16 = ((mx - mn) / np.float32(15.0)).astype(np.float16)
+    s16 = np.where(s16 == np.float16(0.0), np.float16(1.0), s16)
+    q = np.rint((x - z16.astype(np.float32)[..., None]) / s16.astype(np.float32)[..., None])
+    return np.clip(q, -8, 7).astype(np.int8), s16.view(np.uint16), z16.view(np.uint16)
+
+
+def _e4m3_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    lo = np.clip(np.searchsorted(oq._E4M3_POS, a, side="right") - 1, 0, 0x7E).astype(np.uint8)
+    return np.where(np.signbit(x), lo | np.uint8(0x80), lo).astype(np.uint8)
+
+
+def _pack_swapped(codes):
+    c = (np.asarray(codes, dtype=np.int64) + 8).astype(np.uint8)
+    return (c[..., 1::2] | (c[..., 0::2] << 4)).astype(np.uint8)
+
+
+def _unpack_swapped(b):
+    b = np.asarray(b, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.int64)
+    out[..., 1::2] = (b & 0xF).astype(np.int64) - 8
+    out[..., 0::2] = (b >> 4).astype(np.int64) - 8
+    return out
+
+
 MUTANTS = {
+    "int4_fifteen_steps": [(oq, "quantize_rows_int4", _int4_fifteen_steps),
+                           (opa, "quantize_rows_int4", _int4_fifteen_steps)],
+    "fp8_truncating_round": [(oq, "e4m3_encode", _e4m3_truncate)],
+    "int4_nibbles_swapped": [(opa, "_pack_nibbles", _pack_swapped),
+                             (opa, "_unpack_nibbles", _unpack_swapped)],
     "prefill_causal_off_by_one": [(opa, "paged_prefill", _prefill_causal_off_by_one),
                                   (oracle, "paged_prefill", _prefill_causal_off_by_one)],
     "prefill_anchored_at_zero": [(opa, "paged_prefill", _prefill_anchored_at_zero),

@@ -115,3 +115,41 @@ def test_prefix_cache_model_eq2():
 
 def test_prefix_cache_model_longest_match():
     pins.pin_prefix_longest_match()
+
+
+def test_int4_matches_exact_rational_ieee():
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((48, 128)).astype(np.float32)
+    x[:, [3, 70]] *= 8
+    from workloads import f32_to_bf16_bits
+    pins.pin_int4_exact_rational(f32_to_bf16_bits(x))
+
+
+def test_int4_round_trip_and_ties():
+    pins.pin_int4_round_trip_and_ties()
+
+
+def test_fp8_encode_vs_torch():
+    pins.pin_fp8_encode_vs_torch()
+
+
+def test_fp8_rows():
+    pins.pin_fp8_rows()
+
+
+def test_int4_memory_ratios():
+    pins.pin_int4_memory_ratios()
+
+
+@pytest.mark.parametrize("dtype", ["int4", "fp8"])
+def test_quantized_attention_vs_library_sdpa(dtype):
+    """Attention over INT4 / FP8 pools equals torch SDPA over the rows the
+    row contract reconstructs (exact-rational dequantization for INT4; the
+    e4m3 value table times the scale for FP8)."""
+    cfg = variant(TINY, name="tiny_" + dtype, kv_dtype=dtype, num_q_heads=8, num_kv_heads=2,
+                  head_dim=128, pool_pages=32, outlier_channels=3, outlier_gain=8.0)
+    pins.pin_attention_vs_sdpa(make_case(cfg))
+
+
+def test_quantized_pool_layout():
+    pins.pin_quantized_layout()
