@@ -89,24 +89,26 @@ def step_bytes(cfg, ctx: np.ndarray, n_rows: int = None) -> dict:
     """Bytes a step must move at minimum, per term, summed over sequences and layers.
 
     Per sequence of n tokens and per layer: K and V rows n*H_kv*D elements each
-    (plus one float16 (scale, zero) pair per row for INT8), the query and output
+    (plus one float16 (scale, zero) pair per row for the quantized formats:
+    INT8 and FP8 one byte per element, INT4 half a byte), the query and output
     rows H_q*D bfloat16 each, the used block-table entries and the context
     length (int32), and the appended row (read once, written once, K and V).
     """
-    eb = 1 if cfg.kv_dtype == "int8" else 2
+    eb = {"bf16": 2, "int8": 1, "fp8": 1, "int4": 0.5}[cfg.kv_dtype]
+    quant = cfg.kv_dtype != "bf16"
     n = ctx.astype(np.int64)
     if cfg.window_tokens > 0:
         # tokens attended with sinks + a recent window
         n = np.minimum(n, cfg.sink_tokens + cfg.window_tokens)
     Hkv, Hq, D, P, L = cfg.num_kv_heads, cfg.num_q_heads, cfg.head_dim, cfg.page_size, cfg.layers
     kv = int((n * Hkv * 2 * D * eb).sum())
-    if cfg.kv_dtype == "int8":
+    if quant:
         kv += int((n * Hkv * 2 * 4).sum())
     B = int(n.shape[0])
     N = B if n_rows is None else int(n_rows)     # query rows (new tokens) in a step
     q_out = N * Hq * D * 2 * 2
     table = int((-(-n // P) * 4).sum()) + B * 4
-    append = N * Hkv * D * 2 * 2 * (1 + eb / 2) + (N * Hkv * 2 * 4 if cfg.kv_dtype == "int8" else 0)
+    append = N * Hkv * D * 2 * 2 * (1 + eb / 2) + (N * Hkv * 2 * 4 if quant else 0)
     return {"kv": kv * L, "q_out": q_out * L, "table": table * L, "append": int(append) * L,
             "split_kernel_per_launch": kv + N * Hq * D * 2 + table}
 
@@ -124,7 +126,7 @@ def setup_device(kvp, cfg, case, dev):
                          cfg.kv_dtype)
     pool = kvp.kvp_pool_create(desc)
     kv_bytes, meta_bytes = kvp.kvp_pool_bytes(desc)
-    int8 = cfg.kv_dtype == "int8"
+    quant = cfg.kv_dtype != "bf16"
     bt = torch.from_numpy(case.block_tables).to(dev)
     ctx = torch.from_numpy(case.ctx).to(dev)
     seq_idx = torch.from_numpy(case.new_seq.astype(np.int32)).to(dev)
@@ -133,7 +135,7 @@ def setup_device(kvp, cfg, case, dev):
     t0 = time.perf_counter()
     for l in range(cfg.layers):
         L = Layer()
-        if int8:
+        if quant:
             L.k = torch.empty(kv_bytes, dtype=torch.int8, device=dev)
             L.v = torch.empty(kv_bytes, dtype=torch.int8, device=dev)
             L.km = torch.empty(meta_bytes // 2, dtype=torch.int16, device=dev)

@@ -54,6 +54,22 @@
  * with every float32 operation IEEE round-to-nearest-even.  Inputs need
  * |x| <= 65504 so that z is finite in float16.
  *
+ * INT4 rows (the same section: FP16 -> INT4 is a 4x smaller cache): the
+ * INT8 contract with 14 steps and codes clamped to [-8, 7],
+ *     z = f16((mx + mn) * 0.5f),  s = f16((mx - mn) / 14.0f) (1 if 0),
+ *     code[d] = clamp(rint_even((x[d] - float(z)) / float(s)), -8, 7),
+ * stored two channels per byte as code + 8, channel 2j in the low nibble of
+ * byte j.  K:  byte ((page*H_kv + h)*P + t)*(D/2) + d/2
+ *        V:  byte ((page*H_kv + h)*(D/2) + d/2)*P + t
+ * (every byte belongs to one token, so appends never share a byte).
+ *
+ * FP8 rows: OCP e4m3 ("e4m3fn": 4 exponent bits with bias 7, 3 mantissa
+ * bits, largest finite 448, no infinities) with one float16 scale per row:
+ *     s = f16(max|x| / 448.0f) (1 if 0),  code[d] = e4m3(x[d] / float(s)),
+ * x / s in float32, e4m3() rounding to nearest with ties to the even code and
+ * saturating to +-448; stored value float(s) * e4m3_value(code).  Codes use
+ * the INT8 layout (one byte per element); the metadata pair is (scale, 0).
+ *
  * ---------------------------------------------------------------------------
  * Ownership.  The caller owns every device buffer (pools, metadata, q, out,
  * tables, lengths, workspace) and keeps it alive until the work queued on the
@@ -95,14 +111,14 @@ typedef enum {
   KVP_E_HIP = 4           /* a HIP runtime call failed */
 } kvp_status;
 
-typedef enum { KVP_BF16 = 0, KVP_INT8 = 1 } kvp_kv_dtype;
+typedef enum { KVP_BF16 = 0, KVP_INT8 = 1, KVP_INT4 = 2, KVP_FP8 = 3 } kvp_kv_dtype;
 
 typedef struct {
   int32_t num_pages;     /* pages in the pool, > 0 */
   int32_t page_size;     /* P: 16 or 32 */
   int32_t num_kv_heads;  /* H_kv, > 0 */
   int32_t head_dim;      /* D: 64 or 128 */
-  kvp_kv_dtype dtype;
+  kvp_kv_dtype dtype;     /* KVP_BF16, KVP_INT8, KVP_INT4 or KVP_FP8 */
 } kvp_pool_desc;
 
 typedef struct kvp_pool kvp_pool; /* opaque; host memory owned by the library */
@@ -115,8 +131,9 @@ const char* kvp_status_string(kvp_status s);
  * when the request completes; section "Prefix Caching": pages shared by
  * requests with a common prefix). -------------------------------------- */
 
-/* Bytes of one layer's K (or V) array, and of its INT8 metadata array (0 for
- * bfloat16).  Either output pointer may be NULL. */
+/* Bytes of one layer's K (or V) array, and of its metadata array (0 for
+ * bfloat16; INT8, INT4 and FP8 pools have one).  Either output pointer may be
+ * NULL. */
 kvp_status kvp_pool_bytes(const kvp_pool_desc* desc, size_t* kv_bytes, size_t* meta_bytes);
 
 /* Create a pool object: every page free, reference count 0.  *out receives a
@@ -215,8 +232,9 @@ kvp_status kvp_seq_prepare_append(kvp_pool* pool, int32_t* row, int32_t max_bloc
  * For each of n_tokens new tokens i: sequence seq_idx[i], position pos[i];
  * write k_new[i][h][:] and v_new[i][h][:] (bfloat16 [n_tokens][H_kv][D]) into
  * row pos[i] % P of page block_tables[seq_idx[i]][pos[i] / P], for every KV
- * head h; INT8 pools quantize each row as described above and write its code
- * row and (scale, zero).  k_meta/v_meta must be NULL for bfloat16 pools.
+ * head h; INT8, INT4 and FP8 pools quantize each row as described above and
+ * write its codes and (scale, zero).  k_meta/v_meta must be NULL for bfloat16
+ * pools and non-NULL otherwise.
  * All pointers are device pointers.  Rows whose seq_idx is outside
  * [0, num_seqs), whose pos is outside [0, max_blocks*P) or whose page id is
  * outside [0, num_pages) are not written.  Two tokens naming the same row
@@ -317,7 +335,8 @@ kvp_status kvp_paged_attention_decode_window(
  *   max_q_len     host bound on every q_len_b (rows beyond it are not computed);
  *   max_context_len  host bound on context_lens, as for decode.
  * A row whose position would be negative (q_len_b > n_b) gives 0.  Scores,
- * softmax and sums are float32; out is rounded to bfloat16.  No workspace. */
+ * softmax and sums are float32; out is rounded to bfloat16.  No workspace.
+ * Reads KVP_BF16 and KVP_INT8 pools; KVP_E_UNSUPPORTED for INT4 and FP8. */
 kvp_status kvp_paged_attention_prefill(
     const kvp_pool* pool, const void* q, const int32_t* q_start, const void* k_pool,
     const void* v_pool, const void* k_meta, const void* v_meta, const int32_t* block_tables,

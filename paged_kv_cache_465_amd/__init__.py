@@ -19,8 +19,9 @@ from ._lib import DecodePlan, PoolDesc
 _L = _lib.load()
 
 KVP_OK, KVP_E_INVAL, KVP_E_NOPAGES, KVP_E_UNSUPPORTED, KVP_E_HIP = range(5)
-KVP_BF16, KVP_INT8 = 0, 1
-_DTYPES = {"bf16": KVP_BF16, "int8": KVP_INT8}
+KVP_BF16, KVP_INT8, KVP_INT4, KVP_FP8 = 0, 1, 2, 3
+_DTYPES = {"bf16": KVP_BF16, "int8": KVP_INT8, "int4": KVP_INT4, "fp8": KVP_FP8}
+_DTYPE_NAMES = {v: k for k, v in _DTYPES.items()}
 
 
 class KvpError(RuntimeError):
@@ -53,7 +54,13 @@ class Pool:
 
     @property
     def dtype(self) -> str:
-        return "int8" if self.desc.dtype == KVP_INT8 else "bf16"
+        return _DTYPE_NAMES[self.desc.dtype]
+
+    @property
+    def elem_bytes(self) -> int:
+        """Element size of the device tensors that hold the K/V pools: bfloat16
+        pools are 2-byte words, code pools are bytes."""
+        return 2 if self.desc.dtype == KVP_BF16 else 1
 
     def close(self) -> None:
         if self.handle:
@@ -227,7 +234,7 @@ def kvp_seq_prepare_append(pool: Pool, row: np.ndarray, cur_len: int, new_len: i
 
 def kvp_copy_pages(pool: Pool, k_pool, v_pool, k_meta, v_meta, src_dst, stream=None) -> None:
     """Copy pages on the device; src_dst is an int32 device tensor [n, 2]."""
-    eb = 1 if pool.desc.dtype == KVP_INT8 else 2
+    eb = pool.elem_bytes
     n = int(src_dst.shape[0]) if src_dst.dim() == 2 else 0
     if src_dst.dim() != 2 or src_dst.shape[1] != 2:
         raise ValueError("src_dst must be [n, 2]")
@@ -270,7 +277,7 @@ def _stream(stream):
 def kvp_kv_append(pool: Pool, k_pool, v_pool, k_meta, v_meta, k_new, v_new, seq_idx, pos,
                   block_tables, stream=None) -> None:
     """Write k_new/v_new [N, H_kv, D] (bf16) into the slots the tables name."""
-    eb = 1 if pool.desc.dtype == KVP_INT8 else 2
+    eb = pool.elem_bytes
     n = int(seq_idx.numel())
     if pos.numel() != n or k_new.shape[0] != n or v_new.shape[0] != n:
         raise ValueError("seq_idx, pos, k_new and v_new must agree in length")
@@ -298,7 +305,7 @@ def kvp_paged_attention_decode(pool: Pool, q, k_pool, v_pool, k_meta, v_meta, bl
                                num_splits_req: int = 0, workspace=None,
                                stream=None) -> None:
     """out[b, j] = softmax(scale * q[b, j] K_b^T) V_b over the sequence's pages."""
-    eb = 1 if pool.desc.dtype == KVP_INT8 else 2
+    eb = pool.elem_bytes
     B, Hq = int(q.shape[0]), int(q.shape[1])
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
         raise ValueError("block_tables/context_lens must cover the batch")
@@ -331,7 +338,7 @@ def kvp_paged_attention_decode_window(pool: Pool, q, k_pool, v_pool, k_meta, v_m
                                       num_splits_req: int = 0, workspace=None,
                                       stream=None) -> None:
     """Decode attending only to the first sink_tokens and the last window_tokens tokens."""
-    eb = 1 if pool.desc.dtype == KVP_INT8 else 2
+    eb = pool.elem_bytes
     B, Hq = int(q.shape[0]), int(q.shape[1])
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
         raise ValueError("block_tables/context_lens must cover the batch")
@@ -352,7 +359,7 @@ def kvp_paged_attention_prefill(pool: Pool, q, q_start, k_pool, v_pool, k_meta, 
                                 max_context_len: int, scale: float, out, stream=None) -> None:
     """Causal multi-query attention: q/out [N, H_q, D], rows q_start[b]..q_start[b+1]-1
     are sequence b's chunk (its last positions)."""
-    eb = 1 if pool.desc.dtype == KVP_INT8 else 2
+    eb = pool.elem_bytes
     B = int(context_lens.numel())
     if q_start.numel() != B + 1 or block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("q_start must have B+1 entries and block_tables B rows")
@@ -384,7 +391,7 @@ def kvp_paged_attention_decode_partials(pool: Pool, q, k_pool, v_pool, k_meta, v
                                         scale: float, partials, num_splits_req: int = 0,
                                         stream=None) -> int:
     """Split kernel only: per-split (o, m, l) partials into ``partials``; returns S."""
-    eb = 1 if pool.desc.dtype == KVP_INT8 else 2
+    eb = pool.elem_bytes
     B, Hq = int(q.shape[0]), int(q.shape[1])
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
         raise ValueError("block_tables/context_lens must cover the batch")
@@ -410,7 +417,7 @@ def kvp_lse_merge(partials, rows: int, num_splits: int, head_dim: int, out, stre
 
 __all__ = [
     "KVP_OK", "KVP_E_INVAL", "KVP_E_NOPAGES", "KVP_E_UNSUPPORTED", "KVP_E_HIP", "KVP_BF16",
-    "KVP_INT8", "KvpError", "Pool", "PoolDesc", "make_desc", "kvp_status_string",
+    "KVP_INT8", "KVP_INT4", "KVP_FP8", "KvpError", "Pool", "PoolDesc", "make_desc", "kvp_status_string",
     "kvp_pool_bytes", "kvp_pool_create", "kvp_pool_destroy", "kvp_pool_get_desc",
     "kvp_pool_free_count", "kvp_pool_refcount", "kvp_pages_alloc", "kvp_pages_ref",
     "kvp_pages_free", "kvp_seq_grow", "kvp_seq_share", "kvp_seq_release", "kvp_decode_plan",

@@ -4,7 +4,9 @@
 // maps a token's logical position to a physical page; position pos sits in
 // page block_table[pos / P] at row pos % P.  INT8 pools store each (token, KV
 // head) row quantized per token (section "KV-Cache Quantization", eq. 3) with
-// a float16 scale and zero point, following the row contract in kvp.h.
+// a float16 scale and zero point, following the row contract in kvp.h; INT4
+// pools the same contract with 4-bit codes, FP8 pools e4m3 codes with a
+// per-token scale.
 //
 // One wavefront per (token, KV head) row: each lane holds D/64 channels; the
 // row's min and max come from a wavefront reduction.
@@ -29,10 +31,11 @@ struct AppendArgs {
   int32_t n_tokens, num_seqs, max_blocks, num_pages, num_kv_heads;
 };
 
-// The row contract, one IEEE float32 operation at a time (no contraction):
-// z = f16((mx+mn)*0.5), s = f16((mx-mn)/254) (1 if 0),
-// code = clamp(rint_even((x - z)/s), -128, 127).
-template <int E>
+// The row contracts, one IEEE float32 operation at a time (no contraction).
+// Integer codes (INT8: STEPS = 254, codes -128..127; INT4: STEPS = 14, codes
+// -8..7): z = f16((mx+mn)*0.5), s = f16((mx-mn)/STEPS) (1 if 0),
+// code = clamp(rint_even((x - z)/s), LO, HI).
+template <int E, int STEPS, int LO, int HI>
 __device__ __forceinline__ void quantize_row(const float (&x)[E], int32_t (&code)[E],
                                              uint32_t& scale_zero) {
 #pragma clang fp contract(off)
@@ -49,21 +52,38 @@ __device__ __forceinline__ void quantize_row(const float (&x)[E], int32_t (&code
   // all -0 row would round to +0 instead of -0
   asm volatile("" : "+v"(zf));
   const _Float16 z16 = (_Float16)zf;
-  const float sf = (mx - mn) / 254.0f;
+  const float sf = (mx - mn) / float(STEPS);
   _Float16 s16 = (_Float16)sf;
   if (s16 == (_Float16)0.0f) s16 = (_Float16)1.0f;
   const float z = (float)z16, s = (float)s16;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     float q = __builtin_rintf((x[e] - z) / s);
-    q = fminf(fmaxf(q, -128.0f), 127.0f);
+    q = fminf(fmaxf(q, float(LO)), float(HI));
     code[e] = (int32_t)q;
   }
   scale_zero = uint32_t(__builtin_bit_cast(uint16_t, s16)) |
                (uint32_t(__builtin_bit_cast(uint16_t, z16)) << 16);
 }
 
-template <int P, int D, bool INT8>
+// FP8 (e4m3) rows: s = f16(max|x| / 448) (1 if 0), code = e4m3(x / s), zero 0.
+template <int E>
+__device__ __forceinline__ void quantize_row_fp8(const float (&x)[E], int32_t (&code)[E],
+                                                 uint32_t& scale_zero) {
+#pragma clang fp contract(off)
+  float amax = fabsf(x[0]);
+#pragma unroll
+  for (int e = 1; e < E; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  amax = wave_max(amax);
+  _Float16 s16 = (_Float16)(amax / 448.0f);
+  if (s16 == (_Float16)0.0f) s16 = (_Float16)1.0f;
+  const float s = (float)s16;
+#pragma unroll
+  for (int e = 0; e < E; ++e) code[e] = int32_t(f32_to_e4m3(x[e] / s));
+  scale_zero = uint32_t(__builtin_bit_cast(uint16_t, s16));
+}
+
+template <int P, int D, int F>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   constexpr int E = D / 64;  // channels per lane
   const int lane = threadIdx.x & 63;
@@ -86,7 +106,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     kb[e] = a.k_new[src + e];
     vb[e] = a.v_new[src + e];
   }
-  if (!INT8) {
+  if constexpr (F == kBF16) {
     uint16_t* K = static_cast<uint16_t*>(a.k_pool);
     uint16_t* V = static_cast<uint16_t*>(a.v_pool);
     const int64_t krow = (tile * P + t) * D + d0;
@@ -96,45 +116,83 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       V[(tile * D + d0 + e) * P + t] = uint16_t(vb[e]);
     }
     return;
-  }
-  int8_t* K = static_cast<int8_t*>(a.k_pool);
-  int8_t* V = static_cast<int8_t*>(a.v_pool);
-  float xk[E], xv[E];
+  } else {
+    float xk[E], xv[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    xk[e] = bf16_to_f32(kb[e]);
-    xv[e] = bf16_to_f32(vb[e]);
-  }
-  int32_t ck[E], cv[E];
-  uint32_t mk, mv;
-  quantize_row<E>(xk, ck, mk);
-  quantize_row<E>(xv, cv, mv);
-  const int64_t krow = (tile * P + t) * D + d0;
+    for (int e = 0; e < E; ++e) {
+      xk[e] = bf16_to_f32(kb[e]);
+      xv[e] = bf16_to_f32(vb[e]);
+    }
+    int32_t ck[E], cv[E];
+    uint32_t mk, mv;
+    if constexpr (F == kI8) {
+      quantize_row<E, 254, -128, 127>(xk, ck, mk);
+      quantize_row<E, 254, -128, 127>(xv, cv, mv);
+    } else if constexpr (F == kI4) {
+      quantize_row<E, 14, -8, 7>(xk, ck, mk);
+      quantize_row<E, 14, -8, 7>(xv, cv, mv);
+    } else {
+      quantize_row_fp8<E>(xk, ck, mk);
+      quantize_row_fp8<E>(xv, cv, mv);
+    }
+    uint8_t* K = static_cast<uint8_t*>(a.k_pool);
+    uint8_t* V = static_cast<uint8_t*>(a.v_pool);
+    if constexpr (F == kI4) {
+      // channel pairs share a byte (even channel in the low nibble, code + 8);
+      // K row bytes [t][D/2], V bytes [D/2][t] per (page, head) tile
+      constexpr int RB = D / 2;
+      if constexpr (E == 2) {
+        const uint8_t bk = uint8_t((ck[0] + 8) | ((ck[1] + 8) << 4));
+        const uint8_t bv = uint8_t((cv[0] + 8) | ((cv[1] + 8) << 4));
+        K[(tile * P + t) * RB + lane] = bk;
+        V[(tile * RB + lane) * P + t] = bv;
+      } else {
+        // one channel per lane: the even lane of each pair writes both nibbles
+        const int ok = __shfl_xor(ck[0], 1), ov = __shfl_xor(cv[0], 1);
+        if ((lane & 1) == 0) {
+          K[(tile * P + t) * RB + (lane >> 1)] = uint8_t((ck[0] + 8) | ((ok + 8) << 4));
+          V[(tile * RB + (lane >> 1)) * P + t] = uint8_t((cv[0] + 8) | ((ov + 8) << 4));
+        }
+      }
+    } else {
+      const int64_t krow = (tile * P + t) * D + d0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    K[krow + e] = int8_t(ck[e]);
-    V[(tile * D + d0 + e) * P + t] = int8_t(cv[e]);
-  }
-  if (lane == 0) {
-    const int64_t m = (tile * P + t) * 2;
-    *reinterpret_cast<uint32_t*>(a.k_meta + m) = mk;
-    *reinterpret_cast<uint32_t*>(a.v_meta + m) = mv;
+      for (int e = 0; e < E; ++e) {
+        K[krow + e] = uint8_t(ck[e]);
+        V[(tile * D + d0 + e) * P + t] = uint8_t(cv[e]);
+      }
+    }
+    if (lane == 0) {
+      const int64_t m = (tile * P + t) * 2;
+      *reinterpret_cast<uint32_t*>(a.k_meta + m) = mk;
+      *reinterpret_cast<uint32_t*>(a.v_meta + m) = mv;
+    }
   }
 }
 
-template <int P, int D, bool INT8>
+template <int P, int D, int F>
 hipError_t launch_append(AppendArgs a, hipStream_t stream) {
   const int64_t rows = int64_t(a.n_tokens) * a.num_kv_heads;
   const int64_t chunk = int64_t(1) << 24;  // rows per launch, far below grid limits
   for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
     a.row0 = r0;
     const int64_t blocks = (std::min(chunk, rows - r0) + 3) / 4;
-    hipLaunchKernelGGL((append_kernel<P, D, INT8>), dim3(unsigned(blocks)), dim3(256), 0,
-                       stream, a);
+    hipLaunchKernelGGL((append_kernel<P, D, F>), dim3(unsigned(blocks)), dim3(256), 0, stream,
+                       a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+template <int P, int D>
+hipError_t launch_append_fmt(AppendArgs a, int fmt, hipStream_t s) {
+  switch (fmt) {
+    case kBF16: return launch_append<P, D, kBF16>(a, s);
+    case kI8: return launch_append<P, D, kI8>(a, s);
+    case kI4: return launch_append<P, D, kI4>(a, s);
+    default: return launch_append<P, D, kFP8>(a, s);
+  }
 }
 
 }  // namespace kvp
@@ -151,8 +209,8 @@ extern "C" kvp_status kvp_kv_append(const kvp_pool* pool, void* k_pool, void* v_
   if (n_tokens == 0) return KVP_OK;
   if (!k_pool || !v_pool || !k_new || !v_new || !seq_idx || !pos || !block_tables)
     return KVP_E_INVAL;
-  const bool int8 = d.dtype == KVP_INT8;
-  if (int8 != (k_meta != nullptr) || int8 != (v_meta != nullptr)) return KVP_E_INVAL;
+  const bool quant = d.dtype != KVP_BF16;
+  if (quant != (k_meta != nullptr) || quant != (v_meta != nullptr)) return KVP_E_INVAL;
   if (int64_t(max_blocks) * d.page_size > 0x7fffffff) return KVP_E_INVAL;
   AppendArgs a{k_pool, v_pool, static_cast<uint16_t*>(k_meta), static_cast<uint16_t*>(v_meta),
                static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
@@ -160,17 +218,13 @@ extern "C" kvp_status kvp_kv_append(const kvp_pool* pool, void* k_pool, void* v_
                d.num_kv_heads};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
-  const int key = (d.page_size == 32) * 4 + (d.head_dim == 128) * 2 + int8;
-  switch (key) {
-    case 0: e = launch_append<16, 64, false>(a, s); break;
-    case 1: e = launch_append<16, 64, true>(a, s); break;
-    case 2: e = launch_append<16, 128, false>(a, s); break;
-    case 3: e = launch_append<16, 128, true>(a, s); break;
-    case 4: e = launch_append<32, 64, false>(a, s); break;
-    case 5: e = launch_append<32, 64, true>(a, s); break;
-    case 6: e = launch_append<32, 128, false>(a, s); break;
-    default: e = launch_append<32, 128, true>(a, s); break;
-  }
+  const int fmt = int(d.dtype);
+  if (d.page_size == 16)
+    e = d.head_dim == 128 ? launch_append_fmt<16, 128>(a, fmt, s)
+                          : launch_append_fmt<16, 64>(a, fmt, s);
+  else
+    e = d.head_dim == 128 ? launch_append_fmt<32, 128>(a, fmt, s)
+                          : launch_append_fmt<32, 64>(a, fmt, s);
   return e == hipSuccess ? KVP_OK : KVP_E_HIP;
 }
 
@@ -217,11 +271,11 @@ extern "C" kvp_status kvp_copy_pages(const kvp_pool* pool, void* k_pool, void* v
   if (kvp_pool_get_desc(pool, &d) != KVP_OK || n < 0) return KVP_E_INVAL;
   if (n == 0) return KVP_OK;
   if (!k_pool || !v_pool || !src_dst) return KVP_E_INVAL;
-  const bool int8 = d.dtype == KVP_INT8;
-  if (int8 != (k_meta != nullptr) || int8 != (v_meta != nullptr)) return KVP_E_INVAL;
-  const int64_t elem = int8 ? 1 : 2;
-  const int64_t page_bytes = int64_t(d.num_kv_heads) * d.page_size * d.head_dim * elem;
-  const int64_t meta_bytes = int8 ? int64_t(d.num_kv_heads) * d.page_size * 4 : 0;
+  const bool quant = d.dtype != KVP_BF16;
+  if (quant != (k_meta != nullptr) || quant != (v_meta != nullptr)) return KVP_E_INVAL;
+  const int64_t bits = d.dtype == KVP_BF16 ? 16 : (d.dtype == KVP_INT4 ? 4 : 8);
+  const int64_t page_bytes = int64_t(d.num_kv_heads) * d.page_size * d.head_dim * bits / 8;
+  const int64_t meta_bytes = quant ? int64_t(d.num_kv_heads) * d.page_size * 4 : 0;
   if (int64_t(n) * 4 > 0x7fffffff) return KVP_E_UNSUPPORTED;
   hipLaunchKernelGGL(kvp::copy_pages_kernel, dim3(unsigned(n) * 4), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), static_cast<char*>(k_pool),

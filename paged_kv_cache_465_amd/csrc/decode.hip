@@ -4,9 +4,10 @@
 // query token of a sequence attends over the K/V rows of its pages, gathered
 // in logical order through the sequence's page table:
 //   out_j = softmax(scale * q_j K^T) V,  query head j reading KV head j / g
-// (section "Multi-Query and Grouped-Query Caching", eq. 7).  INT8 pools hold
-// codes with a per-token scale and zero point (section "KV-Cache
-// Quantization", eq. 3), dequantized here: q.k = s*(q.c) + z*sum(q) and
+// (section "Multi-Query and Grouped-Query Caching", eq. 7).  Quantized pools
+// hold codes with a per-token scale and zero point (section "KV-Cache
+// Quantization", eq. 3; INT8 and INT4 codes, or FP8 e4m3 values with zero
+// point 0), dequantized here: q.k = s*(q.c) + z*sum(q) and
 // sum_t p_t v_t = sum_t (p_t s_t) c_t + sum_t p_t z_t.
 //
 // Work decomposition.  A workgroup owns one (sequence, KV head) pair and one
@@ -180,15 +181,22 @@ __device__ __forceinline__ void combine_and_store(const DecodeArgs& a, const Wor
 
 // ---------------------------------------------------------------------------
 // Matrix-core kernel.
-template <bool INT8, int P, int D>
+template <int F, int P, int D>
 struct MfmaShape {
+  using FI = FmtInfo<F>;
   static constexpr int T = P / 16;          // 16-token sub-tiles per page
   static constexpr int KK = D / 32;         // 16x16x32 steps over the head dim
   static constexpr int NC = D / 16;         // 16-channel output chunks
   static constexpr int EV = 4 * T;          // tokens per lane in P.V
-  static constexpr int EB = INT8 ? 1 : 2;   // bytes per stored element
-  static constexpr int KL = INT8 ? D / 64 : KK;  // 16-byte K loads per lane per sub-tile
-  static constexpr int VB = EV * EB;        // bytes per lane per V^T chunk
+  static constexpr int RB = D * FI::bits / 8;  // bytes of one stored token row
+  // K bytes a lane holds per 16-token sub-tile: bfloat16, KK pieces of 8
+  // channels 32 apart; codes, D/4 contiguous channels
+  static constexpr int KB = FI::quant ? (D / 4) * FI::bits / 8 : 16 * KK;
+  static constexpr int KLB = KB >= 16 ? 16 : KB;  // bytes per K load
+  static constexpr int KN = KB / KLB;             // K loads per sub-tile
+  // V^T bytes a lane holds per 16-channel chunk: EV tokens of one channel (for
+  // INT4 the byte of the channel pair holding it)
+  static constexpr int VB = F == kBF16 ? EV * 2 : EV;
 };
 
 template <int BYTES> struct LoadT;
@@ -196,13 +204,13 @@ template <> struct LoadT<4> { using type = uint32_t; };
 template <> struct LoadT<8> { using type = uint2; };
 template <> struct LoadT<16> { using type = uint4; };
 
-template <bool INT8, int P, int D>
+template <int F, int P, int D>
 struct PageRegs {
-  using S = MfmaShape<INT8, P, D>;
-  uint4 k[S::T][S::KL];
+  using S = MfmaShape<F, P, D>;
+  typename LoadT<S::KLB>::type k[S::T][S::KN];
   typename LoadT<S::VB>::type v[S::NC];
-  uint4 km[INT8 ? S::T : 1];
-  uint4 vm[INT8 ? S::T : 1];
+  uint4 km[FmtInfo<F>::quant ? S::T : 1];
+  uint4 vm[FmtInfo<F>::quant ? S::T : 1];
   int phys;  // page id, -1 when the table entry is out of range
 };
 
@@ -212,14 +220,36 @@ struct PageRegs {
 constexpr int mfma_max_threads(int, int, int) { return 256; }
 constexpr int valu_max_threads(int, int, int) { return 256; }
 
-template <bool INT8, int P, int D, int NT, int DEPTH>
+// Eight consecutive code channels of a lane (starting at dword w[0]) as the
+// float16 matrix-core operand: INT8 and FP8 take two dwords, INT4 one.
+template <int F>
+__device__ __forceinline__ f16x8_t codes8_to_f16x8(const uint32_t* w) {
+  if constexpr (F == kI4) {
+    return i4x8_to_f16x8(w[0]);
+  } else {
+    f16x2_t a0, a1, b0, b1;
+    if constexpr (F == kI8) {
+      i8x4_to_f16x4(w[0], a0, a1);
+      i8x4_to_f16x4(w[1], b0, b1);
+    } else {
+      fp8x4_to_f16x4(w[0], a0, a1);
+      fp8x4_to_f16x4(w[1], b0, b1);
+    }
+    return f16x8_t{a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
+  }
+}
+
+template <int F, int P, int D, int NT, int DEPTH>
 __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel(DecodeArgs a) {
-  using S = MfmaShape<INT8, P, D>;
-  constexpr int T = S::T, KK = S::KK, NC = S::NC, EV = S::EV, EB = S::EB, KL = S::KL;
+  using S = MfmaShape<F, P, D>;
+  using FI = FmtInfo<F>;
+  constexpr bool Q = FI::quant, ZP = FI::zero;
+  constexpr int T = S::T, KK = S::KK, NC = S::NC, EV = S::EV, RB = S::RB, KB = S::KB;
   constexpr int HP = NT * 16;
-  using OpA = typename std::conditional<INT8, f16x8_t, bf16x8_t>::type;
+  using OpA = typename std::conditional<Q, f16x8_t, bf16x8_t>::type;
   using OpPV = typename std::conditional<
-      T == 1, typename std::conditional<INT8, f16x4_t, bf16x4_t>::type, OpA>::type;
+      T == 1, typename std::conditional<Q, f16x4_t, bf16x4_t>::type, OpA>::type;
+  using KLoad = typename LoadT<S::KLB>::type;
   using VLoad = typename LoadT<S::VB>::type;
   extern __shared__ float smem[];
 
@@ -243,9 +273,9 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
     float qs = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const int d0 = INT8 ? (D / 4) * gq + 8 * kk : 32 * kk + 8 * gq;
+      const int d0 = Q ? (D / 4) * gq + 8 * kk : 32 * kk + 8 * gq;
       uint4 raw = live ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
-      if constexpr (!INT8) {
+      if constexpr (!Q) {
         qop[nt][kk] = __builtin_bit_cast(bf16x8_t, raw);
       } else {
         const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -259,7 +289,7 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
         qop[nt][kk] = v;
       }
     }
-    qsum[nt] = INT8 ? group4_sum(qs) : 0.0f;
+    qsum[nt] = ZP ? group4_sum(qs) : 0.0f;
   }
 
   // Per-lane byte offsets inside a (page, head) tile.
@@ -269,17 +299,20 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
     // sub-tile st, MFMA row r -> token; with two sub-tiles the rows are
     // interleaved so a lane's eight P.V tokens are contiguous.
     const int tok = (T == 1) ? r : 8 * (r >> 2) + 4 * st + (r & 3);
-    koff[st] = (tok * D + (INT8 ? (D / 4) * gq : 8 * gq)) * EB;
+    koff[st] = tok * RB + (Q ? gq * KB : 16 * gq);
   }
-  const int voff = (r * P + EV * gq) * EB;
+  // V^T tile: [D][P] elements, or [D/2][P] bytes for INT4 (channel pairs)
+  const int voff = F == kBF16 ? (r * P + EV * gq) * 2
+                              : (F == kI4 ? (r >> 1) * P : r * P) + EV * gq;
+  constexpr int vstride = F == kBF16 ? 16 * P * 2 : (F == kI4 ? 8 * P : 16 * P);
   const int moff = EV * gq * 4;
 
-  const size_t tile_bytes = size_t(P) * D * EB;
+  const size_t tile_bytes = size_t(P) * RB;
   const char* kbase = static_cast<const char*>(a.k_pool);
   const char* vbase = static_cast<const char*>(a.v_pool);
   const int32_t* btrow = a.bt + int64_t(wr.b) * a.max_blocks;
 
-  auto issue = [&](PageRegs<INT8, P, D>& R, int k) {
+  auto issue = [&](PageRegs<F, P, D>& R, int k) {
     int phys = btrow[wr.logical(wr.kb0 + k)];
     const bool ok = unsigned(phys) < unsigned(a.num_pages);
     R.phys = ok ? phys : -1;
@@ -289,11 +322,11 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
 #pragma unroll
     for (int st = 0; st < T; ++st)
 #pragma unroll
-      for (int i = 0; i < KL; ++i)
-        R.k[st][i] = load_stream<uint4>(kp + koff[st] + i * (INT8 ? 16 : 64));
+      for (int i = 0; i < S::KN; ++i)
+        R.k[st][i] = load_stream<KLoad>(kp + koff[st] + i * (Q ? 16 : 64));
 #pragma unroll
-    for (int nc = 0; nc < NC; ++nc) R.v[nc] = load_stream<VLoad>(vp + voff + nc * 16 * P * EB);
-    if constexpr (INT8) {
+    for (int nc = 0; nc < NC; ++nc) R.v[nc] = load_stream<VLoad>(vp + voff + nc * vstride);
+    if constexpr (Q) {
       const char* km = reinterpret_cast<const char*>(a.k_meta) + tile * (P * 4);
       const char* vm = reinterpret_cast<const char*>(a.v_meta) + tile * (P * 4);
 #pragma unroll
@@ -315,7 +348,7 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
     for (int nc = 0; nc < NC; ++nc) acc[nt][nc] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  auto compute = [&](const PageRegs<INT8, P, D>& R, int k) {
+  auto compute = [&](const PageRegs<F, P, D>& R, int k) {
     if (R.phys < 0) return;  // absent page: its tokens do not take part
     const PageMask pm = page_mask<P>(wr, wr.logical(wr.kb0 + k));
     const bool tail = pm.partial;
@@ -324,28 +357,22 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
     OpA kop[T][KK];
 #pragma unroll
     for (int st = 0; st < T; ++st) {
-      if constexpr (!INT8) {
+      if constexpr (!Q) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) kop[st][kk] = __builtin_bit_cast(bf16x8_t, R.k[st][kk]);
       } else {
+        uint32_t w[KB / 4];
+        __builtin_memcpy(w, R.k[st], KB);
+        constexpr int DW = F == kI4 ? 1 : 2;  // dwords per 8 channels
 #pragma unroll
-        for (int i = 0; i < KL; ++i) {
-          const uint32_t w4[4] = {R.k[st][i].x, R.k[st][i].y, R.k[st][i].z, R.k[st][i].w};
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            f16x2_t a0, a1, b0, b1;
-            i8x4_to_f16x4(w4[2 * half], a0, a1);
-            i8x4_to_f16x4(w4[2 * half + 1], b0, b1);
-            kop[st][2 * i + half] = f16x8_t{a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
-          }
-        }
+        for (int kk = 0; kk < KK; ++kk) kop[st][kk] = codes8_to_f16x8<F>(w + DW * kk);
       }
     }
     // V^T operands.
     OpPV vop[NC];
 #pragma unroll
     for (int nc = 0; nc < NC; ++nc) {
-      if constexpr (!INT8) {
+      if constexpr (!Q) {
         VLoad raw = R.v[nc];
         if (tail) {
           // rows past the sequence may hold anything (NaN): zero them so 0*x stays 0
@@ -365,7 +392,12 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
 #pragma unroll
         for (int i = 0; i < EV / 4; ++i) {
           f16x2_t lo, hi;
-          i8x4_to_f16x4(wv[i], lo, hi);
+          if constexpr (F == kI8)
+            i8x4_to_f16x4(wv[i], lo, hi);
+          else if constexpr (F == kFP8)
+            fp8x4_to_f16x4(wv[i], lo, hi);
+          else
+            i4sel4_to_f16x4(wv[i], (r & 1) != 0, lo, hi);
           v[4 * i + 0] = lo[0];
           v[4 * i + 1] = lo[1];
           v[4 * i + 2] = hi[0];
@@ -374,18 +406,18 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
         vop[nc] = v;
       }
     }
-    // Per-token scale/zero of this lane's rows (INT8).
+    // Per-token scale (and zero point) of this lane's rows.
     float ks[T][4], kz[T][4], vs[T][4], vz[T][4];
-    if constexpr (INT8) {
+    if constexpr (Q) {
 #pragma unroll
       for (int st = 0; st < T; ++st) {
         const uint32_t kw[4] = {R.km[st].x, R.km[st].y, R.km[st].z, R.km[st].w};
         const uint32_t vw[4] = {R.vm[st].x, R.vm[st].y, R.vm[st].z, R.vm[st].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          ks[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] & 0xffffu));
+          ks[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] & 0xffffu)) * FI::scale_mul;
           kz[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] >> 16));
-          vs[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(vw[i] & 0xffffu));
+          vs[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(vw[i] & 0xffffu)) * FI::scale_mul;
           vz[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(vw[i] >> 16));
         }
       }
@@ -401,8 +433,12 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
         for (int kk = 0; kk < KK; ++kk) sc = mfma_16x16x32(kop[st][kk], qop[nt][kk], sc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          x[st][i] = INT8 ? (ks[st][i] * sc[i] + kz[st][i] * qsum[nt]) * a.scale_log2
-                          : sc[i] * a.scale_log2;
+          if constexpr (ZP)
+            x[st][i] = (ks[st][i] * sc[i] + kz[st][i] * qsum[nt]) * a.scale_log2;
+          else if constexpr (Q)
+            x[st][i] = ks[st][i] * sc[i] * a.scale_log2;
+          else
+            x[st][i] = sc[i] * a.scale_log2;
         }
       }
       if (tail) {
@@ -434,7 +470,7 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
 #pragma unroll
       for (int nc = 0; nc < NC; ++nc) acc[nt][nc] *= al;
       OpPV pop;
-      if constexpr (INT8) {
+      if constexpr (Q) {
         float zs = 0.0f;
 #pragma unroll
         for (int st = 0; st < T; ++st)
@@ -442,7 +478,7 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
           for (int i = 0; i < 4; ++i) {
             const bool valid = !tail || pm.valid(EV * gq + 4 * st + i);
             const float pv = valid ? p[st][i] * vs[st][i] : 0.0f;
-            zs += valid ? p[st][i] * vz[st][i] : 0.0f;
+            if constexpr (ZP) zs += valid ? p[st][i] * vz[st][i] : 0.0f;
             pop[4 * st + i] = (_Float16)pv;
           }
         zacc[nt] = zacc[nt] * al + zs;
@@ -463,7 +499,7 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
   };
 
   if (wr.cnt > 0) {
-    PageRegs<INT8, P, D> ring[DEPTH];
+    PageRegs<F, P, D> ring[DEPTH];
 #pragma unroll
     for (int s = 0; s < DEPTH; ++s) issue(ring[s], min(s, wr.cnt - 1));
     for (int k0 = 0; k0 < wr.cnt; k0 += DEPTH) {
@@ -485,13 +521,13 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const float lt = group4_sum(lsum[nt]);
-    const float zt = INT8 ? group4_sum(zacc[nt]) : 0.0f;
+    const float zt = ZP ? group4_sum(zacc[nt]) : 0.0f;
     const int jj = nt * 16 + r;
     if (jj < g) {
 #pragma unroll
       for (int nc = 0; nc < NC; ++nc) {
         f32x4_t v = acc[nt][nc];
-        if constexpr (INT8) v += zt;
+        if constexpr (ZP) v += zt;
         *reinterpret_cast<f32x4_t*>(sm_o + (wave * g + jj) * D + 16 * nc + 4 * gq) = v;
       }
       if (gq == 0) {
@@ -507,14 +543,34 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
 // ---------------------------------------------------------------------------
 // Vector-ALU kernel for g < 4.  Lane l: token row tr = l/4 (+16 per extra
 // sub-tile), channel quarter c = l%4 for q.k; output channels l*D/64.. for P.V.
-template <bool INT8, int P, int D, int G, int DEPTH>
+template <int F>
+__device__ __forceinline__ float code_to_f32(uint32_t byte_or_nibble) {
+  if constexpr (F == kI8) {
+    return float(int8_t(byte_or_nibble & 0xffu));
+  } else if constexpr (F == kI4) {
+    return float(int(byte_or_nibble & 0xfu) - 8);
+  } else {  // e4m3 value times 2^-8 (the scale carries 2^8)
+    const uint32_t b = byte_or_nibble & 0xffu;
+    return (float)__builtin_bit_cast(_Float16, uint16_t(((b & 0x80u) << 8) | ((b & 0x7fu) << 7)));
+  }
+}
+
+template <int F, int P, int D, int G, int DEPTH>
 __global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(DecodeArgs a) {
+  using FI = FmtInfo<F>;
+  constexpr bool Q = FI::quant, ZP = FI::zero;
   constexpr int TPL = P / 16;             // token rows per lane
   constexpr int DQ = D / 4;               // channels per lane for q.k
   constexpr int DV = D / 64;              // output channels per lane
-  constexpr int EB = INT8 ? 1 : 2;
-  constexpr int KL = DQ * EB / 16;        // 16-byte K loads per token row
-  constexpr int VL = DV * P * EB / 16;    // 16-byte V^T loads per lane
+  constexpr int RB = D * FI::bits / 8;    // bytes of a stored token row
+  constexpr int KB = DQ * FI::bits / 8;   // K bytes per lane per token row
+  constexpr int KLB = KB >= 16 ? 16 : KB;
+  constexpr int KN = KB / KLB;
+  // V^T bytes per lane: its DV channels over P tokens ([D][P] elements; for
+  // INT4 the P bytes of the channel pair holding them)
+  constexpr int VBT = F == kI4 ? P : DV * P * FI::bits / 8;
+  constexpr int VL = VBT / 16;
+  using KLoad = typename LoadT<KLB>::type;
   extern __shared__ float smem[];
 
   const int lane = threadIdx.x & 63;
@@ -545,15 +601,16 @@ __global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(
   }
 
   struct Regs {
-    uint4 k[TPL][KL];
+    KLoad k[TPL][KN];
     uint4 v[VL];
     uint32_t km[TPL], vm[TPL];
     int phys;
   };
-  const size_t tile_bytes = size_t(P) * D * EB;
+  const size_t tile_bytes = size_t(P) * RB;
   const char* kbase = static_cast<const char*>(a.k_pool);
   const char* vbase = static_cast<const char*>(a.v_pool);
   const int32_t* btrow = a.bt + int64_t(wr.b) * a.max_blocks;
+  const int vrow = F == kI4 ? (DV == 2 ? lane : (lane >> 1)) * P : lane * VBT;
 
   auto issue = [&](Regs& R, int k) {
     int phys = btrow[wr.logical(wr.kb0 + k)];
@@ -565,11 +622,11 @@ __global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(
 #pragma unroll
     for (int u = 0; u < TPL; ++u)
 #pragma unroll
-      for (int i = 0; i < KL; ++i)
-        R.k[u][i] = load_stream<uint4>(kp + ((tr + 16 * u) * D + c * DQ) * EB + 16 * i);
+      for (int i = 0; i < KN; ++i)
+        R.k[u][i] = load_stream<KLoad>(kp + (tr + 16 * u) * RB + c * KB + KLB * i);
 #pragma unroll
-    for (int i = 0; i < VL; ++i) R.v[i] = load_stream<uint4>(vp + (lane * DV * P) * EB + 16 * i);
-    if constexpr (INT8) {
+    for (int i = 0; i < VL; ++i) R.v[i] = load_stream<uint4>(vp + vrow + 16 * i);
+    if constexpr (Q) {
       const uint32_t* km = reinterpret_cast<const uint32_t*>(a.k_meta) + tile * P;
       const uint32_t* vm = reinterpret_cast<const uint32_t*>(a.v_meta) + tile * P;
 #pragma unroll
@@ -598,17 +655,16 @@ __global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(
 #pragma unroll
     for (int u = 0; u < TPL; ++u) {
       float kv[DQ];
+      uint32_t w[KB / 4];
+      __builtin_memcpy(w, R.k[u], KB);
 #pragma unroll
-      for (int i = 0; i < KL; ++i) {
-        const uint32_t w4[4] = {R.k[u][i].x, R.k[u][i].y, R.k[u][i].z, R.k[u][i].w};
-        if constexpr (!INT8) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) kv[8 * i + e] = bf16_to_f32((w4[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            kv[16 * i + e] = float(int8_t((w4[e >> 2] >> (8 * (e & 3))) & 0xffu));
-        }
+      for (int e = 0; e < DQ; ++e) {
+        if constexpr (F == kBF16)
+          kv[e] = bf16_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        else if constexpr (F == kI4)
+          kv[e] = code_to_f32<F>(w[e >> 3] >> (4 * (e & 7)));
+        else
+          kv[e] = code_to_f32<F>(w[e >> 2] >> (8 * (e & 3)));
       }
 #pragma unroll
       for (int j = 0; j < G; ++j) {
@@ -618,10 +674,14 @@ __global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(
         dsum += __shfl_xor(dsum, 1);
         dsum += __shfl_xor(dsum, 2);
         float sc = dsum;
-        if constexpr (INT8) {
-          const float s = (float)__builtin_bit_cast(_Float16, uint16_t(R.km[u] & 0xffffu));
-          const float z = (float)__builtin_bit_cast(_Float16, uint16_t(R.km[u] >> 16));
-          sc = s * dsum + z * qsum[j];
+        if constexpr (Q) {
+          const float s =
+              (float)__builtin_bit_cast(_Float16, uint16_t(R.km[u] & 0xffffu)) * FI::scale_mul;
+          sc = s * dsum;
+          if constexpr (ZP) {
+            const float z = (float)__builtin_bit_cast(_Float16, uint16_t(R.km[u] >> 16));
+            sc = s * dsum + z * qsum[j];
+          }
         }
         x[u][j] = sc * a.scale_log2;
         if (tail && !pm.valid(tr + 16 * u)) x[u][j] = -INFINITY;
@@ -642,11 +702,14 @@ __global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(
         const float p = fast_exp2(x[u][j] - mnew);
         const bool valid = !tail || pm.valid(tr + 16 * u);
         float pv = p;
-        if constexpr (INT8) {
-          const float vs = (float)__builtin_bit_cast(_Float16, uint16_t(R.vm[u] & 0xffffu));
-          const float vz = (float)__builtin_bit_cast(_Float16, uint16_t(R.vm[u] >> 16));
+        if constexpr (Q) {
+          const float vs =
+              (float)__builtin_bit_cast(_Float16, uint16_t(R.vm[u] & 0xffffu)) * FI::scale_mul;
           pv = valid ? p * vs : 0.0f;
-          zs += valid ? p * vz : 0.0f;
+          if constexpr (ZP) {
+            const float vz = (float)__builtin_bit_cast(_Float16, uint16_t(R.vm[u] >> 16));
+            zs += valid ? p * vz : 0.0f;
+          }
         }
         ps += p;
         if (c == 0) pbuf[j * P + tr + 16 * u] = pv;
@@ -668,13 +731,19 @@ __global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(
       for (int e = 0; e < DV; ++e)
 #pragma unroll
         for (int t = 0; t < P; ++t) {
-          const int idx = e * P + t;
           float f;
-          if constexpr (!INT8)
+          if constexpr (F == kBF16) {
+            const int idx = e * P + t;
             f = bf16_to_f32((wv[idx >> 1] >> (16 * (idx & 1))) & 0xffffu);
-          else
-            f = float(int8_t((wv[idx >> 2] >> (8 * (idx & 3))) & 0xffu));
-          if (!INT8 && tail && !pm.valid(t)) f = 0.0f;
+            if (tail && !pm.valid(t)) f = 0.0f;
+          } else if constexpr (F == kI4) {
+            // byte t of the pair row; this channel's nibble
+            const int nib = DV == 2 ? e : (lane & 1);
+            f = code_to_f32<F>((wv[t >> 2] >> (8 * (t & 3))) >> (4 * nib));
+          } else {
+            const int idx = e * P + t;
+            f = code_to_f32<F>(wv[idx >> 2] >> (8 * (idx & 3)));
+          }
           vv[e][t] = f;
         }
     }
@@ -711,7 +780,7 @@ __global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     const float lt = wave_sum_f(lsum[j]);
-    const float zt = INT8 ? wave_sum_f(zacc[j]) : 0.0f;
+    const float zt = ZP ? wave_sum_f(zacc[j]) : 0.0f;
 #pragma unroll
     for (int e = 0; e < DV; ++e) sm_o[(wave * G + j) * D + lane * DV + e] = acc[j][e] + zt;
     if (lane == 0) {
@@ -775,7 +844,7 @@ int cu_count_current_device() {
   return n;
 }
 
-template <bool INT8, int P, int D>
+template <int F, int P, int D>
 hipError_t launch_decode_pd(const DecodeArgs& a, bool mfma, int g, dim3 grid, dim3 block,
                             size_t lds, hipStream_t s) {
   const int nt = g <= 16 ? 1 : g <= 32 ? 2 : 4;
@@ -783,20 +852,31 @@ hipError_t launch_decode_pd(const DecodeArgs& a, bool mfma, int g, dim3 grid, di
   if (int(block.x) > max_threads) return hipErrorInvalidConfiguration;
   if (mfma) {
     if (g <= 16)
-      hipLaunchKernelGGL((decode_mfma_kernel<INT8, P, D, 1, kDepth>), grid, block, lds, s, a);
+      hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 1, kDepth>), grid, block, lds, s, a);
     else if (g <= 32)
-      hipLaunchKernelGGL((decode_mfma_kernel<INT8, P, D, 2, kDepth>), grid, block, lds, s, a);
+      hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 2, kDepth>), grid, block, lds, s, a);
     else
-      hipLaunchKernelGGL((decode_mfma_kernel<INT8, P, D, 4, kDepth>), grid, block, lds, s, a);
+      hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 4, kDepth>), grid, block, lds, s, a);
   } else {
     if (g == 1)
-      hipLaunchKernelGGL((decode_valu_kernel<INT8, P, D, 1, kDepth>), grid, block, lds, s, a);
+      hipLaunchKernelGGL((decode_valu_kernel<F, P, D, 1, kDepth>), grid, block, lds, s, a);
     else if (g == 2)
-      hipLaunchKernelGGL((decode_valu_kernel<INT8, P, D, 2, kDepth>), grid, block, lds, s, a);
+      hipLaunchKernelGGL((decode_valu_kernel<F, P, D, 2, kDepth>), grid, block, lds, s, a);
     else
-      hipLaunchKernelGGL((decode_valu_kernel<INT8, P, D, 3, kDepth>), grid, block, lds, s, a);
+      hipLaunchKernelGGL((decode_valu_kernel<F, P, D, 3, kDepth>), grid, block, lds, s, a);
   }
   return hipGetLastError();
+}
+
+// Instance for the pool's (page size, head dim); the descriptor was validated.
+template <int F>
+hipError_t launch_decode_fmt(const DecodeArgs& a, int P, int D, bool mfma, int g, dim3 grid,
+                             dim3 block, size_t lds, hipStream_t s) {
+  if (P == 16)
+    return D == 64 ? launch_decode_pd<F, 16, 64>(a, mfma, g, grid, block, lds, s)
+                   : launch_decode_pd<F, 16, 128>(a, mfma, g, grid, block, lds, s);
+  return D == 64 ? launch_decode_pd<F, 32, 64>(a, mfma, g, grid, block, lds, s)
+                 : launch_decode_pd<F, 32, 128>(a, mfma, g, grid, block, lds, s);
 }
 
 }  // namespace kvp
@@ -854,8 +934,8 @@ kvp_status prepare_decode(const kvp_pool* pool, const void* q, const void* k_poo
     return KVP_OK;
   }
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens) return KVP_E_INVAL;
-  const bool int8 = d->dtype == KVP_INT8;
-  if (int8 != (k_meta != nullptr) || int8 != (v_meta != nullptr)) return KVP_E_INVAL;
+  const bool quant = d->dtype != KVP_BF16;
+  if (quant != (k_meta != nullptr) || quant != (v_meta != nullptr)) return KVP_E_INVAL;
   const int cus = kvp::cu_count_current_device();
   if (cus <= 0) return KVP_E_HIP;
   const kvp_status st = kvp_decode_plan(
@@ -909,18 +989,15 @@ kvp_status launch_split_kernel(const kvp_pool_desc& d, const kvp_decode_plan_t& 
   if (!plan.use_mfma) lds += size_t(W) * g * d.page_size * sizeof(float);
   const int64_t wgs = int64_t(num_seqs) * d.num_kv_heads * plan.num_splits;
   const dim3 grid(static_cast<unsigned>(wgs)), block(static_cast<unsigned>(W * 64));
-  const bool int8 = d.dtype == KVP_INT8;
+  const int P = d.page_size, D = d.head_dim;
+  const bool mf = plan.use_mfma;
   hipError_t e;
-  const int key = (d.page_size == 32) * 4 + (d.head_dim == 128) * 2 + int8;
-  switch (key) {
-    case 0: e = launch_decode_pd<false, 16, 64>(a, plan.use_mfma, g, grid, block, lds, s); break;
-    case 1: e = launch_decode_pd<true, 16, 64>(a, plan.use_mfma, g, grid, block, lds, s); break;
-    case 2: e = launch_decode_pd<false, 16, 128>(a, plan.use_mfma, g, grid, block, lds, s); break;
-    case 3: e = launch_decode_pd<true, 16, 128>(a, plan.use_mfma, g, grid, block, lds, s); break;
-    case 4: e = launch_decode_pd<false, 32, 64>(a, plan.use_mfma, g, grid, block, lds, s); break;
-    case 5: e = launch_decode_pd<true, 32, 64>(a, plan.use_mfma, g, grid, block, lds, s); break;
-    case 6: e = launch_decode_pd<false, 32, 128>(a, plan.use_mfma, g, grid, block, lds, s); break;
-    default: e = launch_decode_pd<true, 32, 128>(a, plan.use_mfma, g, grid, block, lds, s); break;
+  switch (d.dtype) {
+    case KVP_BF16: e = launch_decode_fmt<kBF16>(a, P, D, mf, g, grid, block, lds, s); break;
+    case KVP_INT8: e = launch_decode_fmt<kI8>(a, P, D, mf, g, grid, block, lds, s); break;
+    case KVP_INT4: e = launch_decode_fmt<kI4>(a, P, D, mf, g, grid, block, lds, s); break;
+    case KVP_FP8: e = launch_decode_fmt<kFP8>(a, P, D, mf, g, grid, block, lds, s); break;
+    default: return KVP_E_INVAL;
   }
   return e == hipSuccess ? KVP_OK : KVP_E_HIP;
 }

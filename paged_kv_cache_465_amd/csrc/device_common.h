@@ -18,6 +18,19 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// KV storage formats (kvp_kv_dtype values).
+enum KvFmt : int { kBF16 = 0, kI8 = 1, kI4 = 2, kFP8 = 3 };
+
+template <int F>
+struct FmtInfo {
+  static constexpr bool quant = F != kBF16;             // codes + per-token metadata
+  static constexpr bool zero = F == kI8 || F == kI4;    // metadata carries a zero point
+  static constexpr int bits = F == kBF16 ? 16 : (F == kI4 ? 4 : 8);
+  // codes convert to float16 exactly; FP8 codes come out scaled by 2^-8, which
+  // this factor (folded into the per-token scale) undoes
+  static constexpr float scale_mul = F == kFP8 ? 256.0f : 1.0f;
+};
+
 // Streaming loads of K/V page data: every byte is read once per decode step,
 // so the loads carry the non-temporal hint and do not displace reusable lines
 // (q, block tables) in L2 and the Infinity Cache.
@@ -88,6 +101,60 @@ __device__ __forceinline__ void i8x4_to_f16x4(uint32_t w, f16x2_t& lo, f16x2_t& 
   const f16x2_t off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
   lo = __builtin_bit_cast(f16x2_t, a) + off;
   hi = __builtin_bit_cast(f16x2_t, b) + off;
+}
+
+// Four e4m3 codes (one dword) -> float16 values equal to the e4m3 values times
+// 2^-8, exactly: moving sign, exponent and mantissa into a float16's fields
+// with the exponent bias difference (15 - 7) left out keeps every finite code,
+// subnormals included, exact (only the NaN code has no meaning here).
+__device__ __forceinline__ void fp8x4_to_f16x4(uint32_t w, f16x2_t& lo, f16x2_t& hi) {
+  const uint32_t a = __builtin_amdgcn_perm(0u, w, 0x010c000cu);  // b0 << 8 | b1 << 24
+  const uint32_t b = __builtin_amdgcn_perm(0u, w, 0x030c020cu);  // b2 << 8 | b3 << 24
+  lo = __builtin_bit_cast(f16x2_t, (a & 0x80008000u) | ((a >> 1) & 0x3f803f80u));
+  hi = __builtin_bit_cast(f16x2_t, (b & 0x80008000u) | ((b >> 1) & 0x3f803f80u));
+}
+
+// Eight 4-bit codes (one dword; byte j holds channel 2j in its low nibble and
+// 2j+1 in its high nibble, each as code + 8) -> eight exact float16 codes in
+// channel order: interleave the nibbles into bytes, then 0x6400|u = 1024 + u.
+__device__ __forceinline__ f16x8_t i4x8_to_f16x8(uint32_t w) {
+  const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+  const uint32_t c0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // ch0 ch1 ch2 ch3
+  const uint32_t c1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // ch4 ch5 ch6 ch7
+  const f16x2_t off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const f16x2_t p0 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, c0, 0x04010400u)) + off;
+  const f16x2_t p1 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, c0, 0x04030402u)) + off;
+  const f16x2_t p2 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, c1, 0x04010400u)) + off;
+  const f16x2_t p3 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, c1, 0x04030402u)) + off;
+  return f16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Four bytes, each holding this lane's channel in one nibble (the high one
+// when hi_nibble) -> four exact float16 codes.
+__device__ __forceinline__ void i4sel4_to_f16x4(uint32_t w, bool hi_nibble, f16x2_t& lo,
+                                                f16x2_t& hi) {
+  const uint32_t u = (hi_nibble ? (w >> 4) : w) & 0x0f0f0f0fu;
+  const f16x2_t off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  lo = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) + off;
+  hi = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) + off;
+}
+
+// float32 -> e4m3 code (OCP e4m3fn: bias 7, 3 mantissa bits, largest finite
+// 448, no infinities), round to nearest with ties to the even code,
+// magnitudes at or beyond 448 saturating to 448; the sign bit follows y.
+// Scaling by powers of two is exact, so each rint sees the exact quotient.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (!(a < 448.0f)) return sign | 0x7eu;
+  if (a < 0.015625f) {                             // below 2^-6: steps of 2^-9
+    return sign | uint32_t(__builtin_rintf(a * 512.0f));  // 8 is the smallest normal, code 8
+  }
+  const int e = int((__float_as_uint(a) >> 23) & 0xffu) - 127;  // -6 .. 8
+  const float m = __builtin_rintf(a * __uint_as_float(uint32_t(127 + 3 - e) << 23));  // 8 .. 16
+  uint32_t code = (uint32_t(e + 7) << 3) + (uint32_t(m) - 8u);  // m == 16 carries into e + 1
+  if (code > 0x7eu) code = 0x7eu;
+  return sign | code;
 }
 
 __device__ __forceinline__ f32x4_t mfma_16x16x32(const bf16x8_t& a, const bf16x8_t& b,

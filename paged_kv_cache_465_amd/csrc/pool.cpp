@@ -31,7 +31,9 @@ bool desc_valid(const kvp_pool_desc* d) {
   if (d->num_pages <= 0 || d->num_kv_heads <= 0) return false;
   if (d->page_size != 16 && d->page_size != 32) return false;
   if (d->head_dim != 64 && d->head_dim != 128) return false;
-  if (d->dtype != KVP_BF16 && d->dtype != KVP_INT8) return false;
+  if (d->dtype != KVP_BF16 && d->dtype != KVP_INT8 && d->dtype != KVP_INT4 &&
+      d->dtype != KVP_FP8)
+    return false;
   // element offsets must fit in 64 bits comfortably; page offsets in 63 bits
   const double elems = double(d->num_pages) * d->num_kv_heads * d->page_size * d->head_dim;
   return elems < 9.0e18;
@@ -57,9 +59,9 @@ const char* kvp_status_string(kvp_status s) {
 kvp_status kvp_pool_bytes(const kvp_pool_desc* desc, size_t* kv_bytes, size_t* meta_bytes) {
   if (!desc_valid(desc)) return KVP_E_INVAL;
   const size_t rows = size_t(desc->num_pages) * desc->num_kv_heads * desc->page_size;
-  const size_t elem = desc->dtype == KVP_BF16 ? 2 : 1;
-  if (kv_bytes) *kv_bytes = rows * desc->head_dim * elem;
-  if (meta_bytes) *meta_bytes = desc->dtype == KVP_INT8 ? rows * 2 * sizeof(uint16_t) : 0;
+  const size_t bits = desc->dtype == KVP_BF16 ? 16 : (desc->dtype == KVP_INT4 ? 4 : 8);
+  if (kv_bytes) *kv_bytes = rows * desc->head_dim * bits / 8;
+  if (meta_bytes) *meta_bytes = desc->dtype != KVP_BF16 ? rows * 2 * sizeof(uint16_t) : 0;
   return KVP_OK;
 }
 

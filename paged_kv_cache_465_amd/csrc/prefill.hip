@@ -387,6 +387,8 @@ extern "C" kvp_status kvp_paged_attention_prefill(
   if (num_seqs == 0 || max_q_len == 0) return KVP_OK;
   if (!q || !q_start || !k_pool || !v_pool || !block_tables || !context_lens || !out)
     return KVP_E_INVAL;
+  // the multi-query kernel reads bfloat16 and INT8 pools
+  if (d.dtype != KVP_BF16 && d.dtype != KVP_INT8) return KVP_E_UNSUPPORTED;
   const bool int8 = d.dtype == KVP_INT8;
   if (int8 != (k_meta != nullptr) || int8 != (v_meta != nullptr)) return KVP_E_INVAL;
   // rows per wavefront: 32 when the longest chunk has at least that many rows

@@ -84,3 +84,20 @@ def assert_close(out_bf16_bits, ref_f64, what=""):
     assert max_abs <= MAX_ABS_TOL and rel <= REL_L2_TOL and ulps <= 1.0, \
         f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} worst={worst} big_ulps={ulps:.2f}"
     return max_abs, rel
+
+
+def assert_within_one_rounding(a_bits, b_bits, what=""):
+    """Two bfloat16 results of the same attention computed with different
+    summation orders (split counts, kernels): every element pair differs by at
+    most 1e-2 or by one bfloat16 rounding step at its magnitude, whichever is
+    larger (two float32 values a hair apart can round to neighbouring
+    bfloat16 values, which are 1/64 apart in [2, 4))."""
+    a = (np.asarray(a_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    b = (np.asarray(b_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    a, b = a.astype(np.float64), b.astype(np.float64)
+    assert np.isfinite(a).all() and np.isfinite(b).all(), what
+    mag = np.maximum(np.abs(a), np.abs(b))
+    step = np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 7)
+    bound = np.maximum(MAX_ABS_TOL, step)
+    bad = np.abs(a - b) > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements differ by more than one rounding"

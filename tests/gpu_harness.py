@@ -37,8 +37,11 @@ class GpuCase:
                                   c.kv_dtype)
         self.pool = kvp.kvp_pool_create(self.desc)
         kv_bytes, meta_bytes = kvp.kvp_pool_bytes(self.desc)
-        self.int8 = c.kv_dtype == "int8"
-        if self.int8:
+        self.quant = c.kv_dtype != "bf16"
+        # host dtype of code pools as the oracle holds them (INT8 signed, packed
+        # INT4 nibbles and FP8 bytes unsigned)
+        self.code_np = np.int8 if c.kv_dtype == "int8" else np.uint8
+        if self.quant:
             fill = int(np.uint8(POISON_I8).view(np.int8))
             self.k_pool = torch.full((kv_bytes,), fill, dtype=torch.int8, device=device)
             self.v_pool = torch.full((kv_bytes,), fill, dtype=torch.int8, device=device)
@@ -71,7 +74,7 @@ class GpuCase:
 
     def upload(self, k, v, km, vm):
         """Replace the device pools by host pools (e.g. the oracle's)."""
-        if self.int8:
+        if self.quant:
             self.k_pool.copy_(torch.from_numpy(np.ascontiguousarray(k).view(np.int8)))
             self.v_pool.copy_(torch.from_numpy(np.ascontiguousarray(v).view(np.int8)))
             self.k_meta.copy_(torch.from_numpy(np.ascontiguousarray(km).view(np.int16)))
@@ -81,8 +84,9 @@ class GpuCase:
             self.v_pool.copy_(torch.from_numpy(np.ascontiguousarray(v).view(np.int16)))
 
     def pools_host(self):
-        if self.int8:
-            return (self.k_pool.cpu().numpy(), self.v_pool.cpu().numpy(),
+        if self.quant:
+            return (self.k_pool.cpu().numpy().view(self.code_np),
+                    self.v_pool.cpu().numpy().view(self.code_np),
                     self.k_meta.cpu().numpy().view(np.uint16),
                     self.v_meta.cpu().numpy().view(np.uint16))
         return (self.k_pool.cpu().numpy().view(np.uint16),

@@ -1,0 +1,252 @@
+"""INT4 and FP8 KV pools on the GPU against the oracle, through the C ABI.
+
+"KV-Cache Optimization Techniques", section "KV-Cache Quantization": eq. 3
+with 4-bit codes (two per byte) is the 4x reduction over 16-bit storage, and
+an FP8 cache halves the footprint ("KV Cache Optimization" glossary).
+Bit-exact: every pool byte kv_append writes (packed nibbles, e4m3 codes,
+float16 scales and zero points) and every byte it must leave alone.  Within
+the attention tolerance (max-abs 1e-2, rel-L2 5e-3): decode outputs over every
+kernel family, split counts and sink/window selections.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import (FP8_LONG, INT4_LONG, LLAMA3_8B_LAYER, POISON_F16, POISON_I8, TINY,
+                       f32_to_bf16_bits, make_case, variant)
+
+from .casetools import assert_close, assert_within_one_rounding, layout_of, oracle_pools
+from .gpu_harness import GpuCase, dev16, dev32, log
+from .test_gpu_parity import _evicted_case, _pools_equal, _sampled_check
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kvp():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_465_amd as m
+    return m
+
+
+def _family(f):
+    """Shapes covering each kernel family once per (P, D): the vector-ALU
+    kernel for g = 1, 2, 3 and the matrix-core kernel with 1, 2 and 4 head
+    tiles, page sizes 16 and 32, head dims 64 and 128, ragged tails."""
+    base = INT4_LONG if f == "int4" else FP8_LONG
+    return [
+        variant(TINY, name=f"tiny_{f}", kv_dtype=f),                            # MFMA P16 D64
+        variant(TINY, name=f"tiny_g1_{f}", num_q_heads=2, num_kv_heads=2, pool_pages=32,
+                kv_dtype=f),                                                     # VALU g1 P16 D64
+        variant(TINY, name=f"tiny_g3_d128_{f}", num_q_heads=6, num_kv_heads=2, head_dim=128,
+                pool_pages=32, kv_dtype=f),                                      # VALU g3 P16 D128
+        variant(TINY, name=f"tiny_p32_d64_{f}", page_size=32, pool_pages=16,
+                kv_dtype=f),                                                     # MFMA P32 D64
+        variant(TINY, name=f"tiny_p32_g2_{f}", page_size=32, num_q_heads=2, pool_pages=16,
+                kv_dtype=f),                                                     # VALU g2 P32 D64
+        variant(base, name=f"{f}_small", batch=4, ctx_lo=100, ctx_hi=3000),      # MFMA P32 D128
+        variant(base, name=f"{f}_small_g1", batch=3, num_q_heads=8, ctx_lo=1,
+                ctx_hi=600),                                                     # VALU g1 P32 D128
+        variant(base, name=f"{f}_small_g32", batch=2, num_q_heads=64, num_kv_heads=2,
+                ctx_lo=200, ctx_hi=700),                                         # MFMA 2 tiles
+        variant(base, name=f"{f}_small_p16_d64_g2", batch=3, page_size=16, head_dim=64,
+                num_q_heads=16, ctx_lo=1, ctx_hi=900),                           # VALU g2 P16 D64
+        variant(LLAMA3_8B_LAYER, name=f"l8b_small_{f}", batch=6, ctx_lo=1, ctx_hi=700,
+                kv_dtype=f),                                                     # MFMA P16 D128
+        variant(LLAMA3_8B_LAYER, name=f"l8b_small_g64_{f}", batch=2, num_q_heads=64,
+                num_kv_heads=1, ctx_lo=200, ctx_hi=500, kv_dtype=f),             # MFMA 4 tiles
+    ]
+
+
+LOWBIT = _family("int4") + _family("fp8")
+
+_CACHE = {}
+
+
+def _case(cfg):
+    if cfg.name not in _CACHE:
+        _CACHE[cfg.name] = make_case(cfg)
+    return _CACHE[cfg.name]
+
+
+def _oracle(case):
+    key = ("oracle", case.cfg.name)
+    if key not in _CACHE:
+        k, v, km, vm = oracle_pools(case)
+        out = oracle.paged_decode(layout_of(case), case.q, k, v, km, vm, case.block_tables,
+                                  case.ctx, case.scale)
+        _CACHE[key] = (k, v, km, vm, out)
+    return _CACHE[key]
+
+
+@pytest.mark.parametrize("cfg", LOWBIT, ids=lambda c: c.name)
+def test_append_bit_exact_lowbit(kvp, cfg):
+    case = _case(cfg)
+    log(f"[append] {cfg.name} seed={cfg.seed} B={case.B} pages={case.num_pages} "
+        f"P={cfg.page_size} D={cfg.head_dim} dtype={cfg.kv_dtype}")
+    gc = GpuCase(kvp, case)
+    gc.append_history()
+    gc.append_new()
+    torch.cuda.synchronize()
+    _pools_equal(gc.pools_host(), _oracle(case)[:4])
+    gc.close()
+
+
+@pytest.mark.parametrize("cfg", LOWBIT, ids=lambda c: c.name)
+def test_decode_matches_oracle_lowbit(kvp, cfg):
+    case = _case(cfg)
+    k, v, km, vm, ref = _oracle(case)
+    log(f"[decode] {cfg.name} seed={cfg.seed} B={case.B} Hq={cfg.num_q_heads} "
+        f"Hkv={cfg.num_kv_heads} ctx={case.ctx.tolist()[:8]}")
+    gc = GpuCase(kvp, case)
+    gc.append_history()
+    gc.append_new()
+    out = gc.decode()
+    m, r = assert_close(out, ref, f"{cfg.name} auto split")
+    log(f"  auto: max_abs={m:.2e} rel_l2={r:.2e}")
+    gc.upload(k, v, km, vm)
+    assert np.array_equal(out, gc.decode())
+    gc.close()
+
+
+@pytest.mark.parametrize("name", ["int4_small", "fp8_small", "tiny_p32_g2_int4",
+                                  "l8b_small_g64_fp8"])
+@pytest.mark.parametrize("splits", [1, 3, 1000])
+def test_split_counts_lowbit(kvp, name, splits):
+    cfg = next(c for c in LOWBIT if c.name == name)
+    case = _case(cfg)
+    ref = _oracle(case)[4]
+    log(f"[splits] {cfg.name} S={splits}")
+    gc = GpuCase(kvp, case)
+    gc.upload(*_oracle(case)[:4])
+    out = gc.decode(num_splits=splits)
+    assert_close(out, ref, f"{cfg.name} S={splits}")
+    one = gc.decode(num_splits=1)
+    assert_within_one_rounding(out, one, f"{cfg.name} S={splits} vs S=1")
+    gc.close()
+
+
+@pytest.mark.parametrize("name", ["tiny_int4", "tiny_g1_fp8", "int4_small", "fp8_small_g1",
+                                  "int4_small_p16_d64_g2"])
+@pytest.mark.parametrize("sink,window", [(4, 64), (0, 17), (3, 200)])
+def test_window_decode_lowbit(kvp, name, sink, window):
+    """Sinks + window over INT4/FP8 pools, dropped pages freed (-1) and poisoned."""
+    cfg = next(c for c in LOWBIT if c.name == name)
+    case = _case(cfg)
+    k, v, km, vm, bt, n_poisoned = _evicted_case(case, sink, window, pools=_oracle(case)[:4])
+    lay = layout_of(case)
+    ref = oracle.paged_decode_window(lay, case.q, k, v, km, vm, bt, case.ctx, case.scale, sink,
+                                     window)
+    log(f"[window] {cfg.name} s={sink} w={window} poisoned_pages={n_poisoned}")
+    gc = GpuCase(kvp, case, block_tables=bt)
+    gc.upload(k, v, km, vm)
+    c = case.cfg
+    mx = int(case.ctx.max())
+    for splits in (0, 1, 3):
+        wsb = kvp.kvp_decode_window_workspace_bytes(gc.pool, case.B, c.num_q_heads, mx, sink,
+                                                    window, splits)
+        ws = (torch.full((max(wsb, 4) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+              if wsb else None)
+        out = torch.full_like(gc.q, int(np.uint16(0x7FC0).view(np.int16)))
+        kvp.kvp_paged_attention_decode_window(gc.pool, gc.q, gc.k_pool, gc.v_pool, gc.k_meta,
+                                              gc.v_meta, gc.bt, gc.ctx, mx, float(case.scale),
+                                              sink, window, out, splits, ws)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy().view(np.uint16), ref,
+                     f"{cfg.name} s={sink} w={window} S={splits}")
+    gc.close()
+
+
+def _special_rows(kind):
+    """bfloat16 rows that stress a row contract: signed zeros, constant rows,
+    ties at half steps, tiny and wide ranges, outliers, random rows."""
+    D = 128
+    rng = np.random.default_rng(10 if kind == "int4" else 11)
+    rows = [np.full(D, -0.0, np.float32), np.zeros(D, np.float32), np.full(D, 3.25, np.float32),
+            np.full(D, -1e-30, np.float32)]
+    tie = np.zeros(D, np.float32)
+    if kind == "int4":
+        # range [-7, 7]: z = 0, s = 1, so halves are exact ties
+        tie[:10] = [-7, 7, 2.5, 3.5, -2.5, -0.5, 0.5, 1.5, 6.5, -6.5]
+    else:
+        # amax 448: s = 1, so x itself is encoded; ties between neighbouring
+        # e4m3 values (subnormal, normal, at the top of the range) and a
+        # subnormal that rounds up into the first normal binade
+        tie[:16] = [448, -448, 440, 432, 424, 3 * 2.0**-10, 5 * 2.0**-10, 2.0**-10,
+                    15 * 2.0**-10, 2.0**-6, 1.0625, 1.1875, -3.75, -1.0625, 2.0**-9, 300]
+    rows.append(tie)
+    rows.append(np.linspace(-1e-6, 1e-6, D).astype(np.float32))
+    rows.append((rng.standard_normal(D) * 3000).astype(np.float32))
+    rows.append((rng.standard_normal(D) + 50).astype(np.float32))
+    x = rng.standard_normal(D).astype(np.float32)
+    x[[1, 77]] *= 8
+    rows.append(x)
+    if kind == "fp8":
+        rows.append(np.linspace(-3e38, 3e38, D).astype(np.float32))  # scale overflows to inf
+    rows += [rng.standard_normal(D).astype(np.float32) for _ in range(33 - len(rows))]
+    bits = np.stack([f32_to_bf16_bits(r) for r in rows])
+    bits[0] = 0x8000                                     # exact -0 row
+    return bits
+
+
+@pytest.mark.parametrize("kind", ["int4", "fp8"])
+def test_append_special_rows_lowbit(kvp, kind):
+    """Codes (nibble order, e4m3 rounding and saturation, sign of zero), scales
+    and zero points match the oracle bit for bit on hand-picked rows."""
+    D, P = 128, 32
+    bits = _special_rows(kind)
+    n = bits.shape[0]
+    k_new = bits.reshape(n, 1, D)
+    v_new = bits[::-1].copy().reshape(n, 1, D)
+    bt = np.array([[3, 0]], dtype=np.int32)               # positions 0..31 -> page 3, 32.. -> 0
+    lay = oracle.PoolLayout(4, P, 1, D, kind)
+    k, v, km, vm = lay.empty_pools(POISON_I8, POISON_F16)
+    pos = np.arange(n, dtype=np.int32)
+    seq = np.zeros(n, dtype=np.int32)
+    oracle.append(lay, k, v, km, vm, k_new, v_new, seq, pos, bt)
+    log(f"[append special rows] {kind} n={n}")
+    desc = kvp.make_desc(4, P, 1, D, kind)
+    pool = kvp.kvp_pool_create(desc)
+    kv_bytes, meta_bytes = kvp.kvp_pool_bytes(desc)
+    assert kv_bytes == k.size and meta_bytes == km.size * 2
+    fill = int(np.uint8(POISON_I8).view(np.int8))
+    mfill = int(np.uint16(POISON_F16).view(np.int16))
+    kp = torch.full((kv_bytes,), fill, dtype=torch.int8, device="cuda")
+    vp = kp.clone()
+    kmt = torch.full((meta_bytes // 2,), mfill, dtype=torch.int16, device="cuda")
+    vmt = kmt.clone()
+    kvp.kvp_kv_append(pool, kp, vp, kmt, vmt, dev16(k_new), dev16(v_new), dev32(seq), dev32(pos),
+                      dev32(bt))
+    torch.cuda.synchronize()
+    _pools_equal((kp.cpu().numpy().view(np.uint8), vp.cpu().numpy().view(np.uint8),
+                  kmt.cpu().numpy().view(np.uint16), vmt.cpu().numpy().view(np.uint16)),
+                 (k, v, km, vm))
+    pool.close()
+
+
+@pytest.mark.parametrize("kind", ["int4", "fp8"])
+def test_prefill_rejects_lowbit_pools(kvp, kind):
+    """The multi-query kernel reads bfloat16 and INT8 pools only: an INT4 or
+    FP8 pool is refused before any launch."""
+    cfg = variant(TINY, name=f"tiny_chunk_{kind}", kv_dtype=kind, q_len=3)
+    case = make_case(cfg)
+    gc = GpuCase(kvp, case)
+    out = torch.empty_like(gc.q)
+    with pytest.raises(kvp.KvpError) as e:
+        kvp.kvp_paged_attention_prefill(gc.pool, gc.q, dev32(case.q_start), gc.k_pool, gc.v_pool,
+                                        gc.k_meta, gc.v_meta, gc.bt, gc.ctx, 3,
+                                        int(case.ctx.max()), float(case.scale), out)
+    assert e.value.status == kvp.KVP_E_UNSUPPORTED
+    gc.close()
+
+
+def test_full_int4_long(kvp):
+    """16 sequences of 16k-32k tokens, INT4 pool with outlier channels."""
+    _sampled_check(kvp, INT4_LONG, seqs=(0, 7, 15))
+
+
+def test_full_fp8_long(kvp):
+    """16 sequences of 16k-32k tokens, FP8 pool with outlier channels."""
+    _sampled_check(kvp, FP8_LONG, seqs=(0, 7, 15))

@@ -13,7 +13,7 @@ import oracle
 from workloads import (INT8_LONG, LLAMA3_70B_FULL, LLAMA3_8B_LAYER, SHARED_PREFIX_MQA, TINY,
                        make_case, variant)
 
-from .casetools import assert_close, compare_outputs, layout_of, oracle_pools
+from .casetools import assert_close, assert_within_one_rounding, layout_of, oracle_pools
 from .gpu_harness import GpuCase, dev32, log
 
 pytestmark = pytest.mark.gpu
@@ -131,9 +131,7 @@ def test_split_counts(kvp, cfg, splits):
     out = gc.decode(num_splits=splits)
     assert_close(out, ref, f"{cfg.name} S={splits}")
     one = gc.decode(num_splits=1)
-    ma, rel, _, ulps = compare_outputs(out, (one.astype(np.uint32) << 16).view(np.float32)
-                                       .astype(np.float64))
-    assert ma <= 1e-2 and rel <= 5e-3 and ulps <= 1.0
+    assert_within_one_rounding(out, one, f"{cfg.name} S={splits} vs S=1")
     gc.close()
 
 
@@ -290,17 +288,14 @@ def _sampled_check(kvp, cfg, seqs, splits=0):
     oracle.append(lay, k, v, km, vm, case.new_k[nsel], case.new_v[nsel], case.new_seq[nsel],
                   case.new_pos[nsel], case.block_tables)
     gk, gv, gkm, gvm = gc.pools_host()
-    per_page = cfg.num_kv_heads * cfg.page_size * cfg.head_dim
     for b in seqs:
         pages = case.block_tables[b][: -(-int(case.ctx[b]) // cfg.page_size)]
         pages = pages[pages >= 0]
-        for name, g, r, n in (("K", gk, k, per_page), ("V", gv, v, per_page),
-                              ("Km", gkm, km, per_page // cfg.head_dim * 2),
-                              ("Vm", gvm, vm, per_page // cfg.head_dim * 2)):
+        for name, g, r in (("K", gk, k), ("V", gv, v), ("Km", gkm, km), ("Vm", gvm, vm)):
             if r is None:
                 continue
-            gp = g.reshape(case.num_pages, n)[pages]
-            rp = r.reshape(case.num_pages, n)[pages]
+            gp = g.reshape(case.num_pages, -1)[pages]
+            rp = r.reshape(case.num_pages, -1)[pages]
             assert np.array_equal(gp.view(np.uint8), rp.view(np.uint8)), f"{name} pages of seq {b}"
     if cfg.q_len > 1 or cfg.q_len_hi > 1:
         ref = oracle.paged_prefill(lay, case.q, case.q_start, k, v, km, vm, case.block_tables,
@@ -457,13 +452,15 @@ def test_partials_layout_and_merge(kvp, cfg, splits):
 
 
 # ---- sinks + recent window ("Token Eviction Strategies", eq. 5; eq. 6 with s = 0) --------
-def _evicted_case(case, sink, window):
-    """Oracle pools with every page that only holds dropped tokens poisoned and
-    its table entries set to -1 (pages a kept block still names stay)."""
+def _evicted_case(case, sink, window, pools=None):
+    """Oracle pools (``pools``, else the case's cached ones) with every page
+    that only holds dropped tokens poisoned and its table entries set to -1
+    (pages a kept block still names stay)."""
     from workloads import POISON_BF16, POISON_F16, POISON_I8
     c = case.cfg
     P = c.page_size
-    k, v, km, vm = (None if a is None else a.copy() for a in _oracle(case)[:4])
+    src = _oracle(case)[:4] if pools is None else pools
+    k, v, km, vm = (None if a is None else a.copy() for a in src)
     bt = case.block_tables.copy()
     kept_pages, dropped_pages = set(), set()
     for b in range(case.B):
@@ -472,17 +469,16 @@ def _evicted_case(case, sink, window):
         for i in range(-(-n // P)):
             (dropped_pages if i in drop else kept_pages).add(int(bt[b, i]))
         bt[b, drop] = -1
-    per_page = c.num_kv_heads * P * c.head_dim
-    int8 = c.kv_dtype == "int8"
+    quant = c.kv_dtype != "bf16"
     for p in dropped_pages - kept_pages:
-        if int8:
-            k.view(np.uint8).reshape(case.num_pages, per_page)[p] = POISON_I8
-            v.view(np.uint8).reshape(case.num_pages, per_page)[p] = POISON_I8
+        if quant:
+            k.view(np.uint8).reshape(case.num_pages, -1)[p] = POISON_I8
+            v.view(np.uint8).reshape(case.num_pages, -1)[p] = POISON_I8
             km.reshape(case.num_pages, -1)[p] = POISON_F16
             vm.reshape(case.num_pages, -1)[p] = POISON_F16
         else:
-            k.reshape(case.num_pages, per_page)[p] = POISON_BF16
-            v.reshape(case.num_pages, per_page)[p] = POISON_BF16
+            k.reshape(case.num_pages, -1)[p] = POISON_BF16
+            v.reshape(case.num_pages, -1)[p] = POISON_BF16
     return k, v, km, vm, bt, len(dropped_pages - kept_pages)
 
 
@@ -618,9 +614,7 @@ def test_prefill_one_token_equals_decode(kvp, cfg):
     gc.upload(*_oracle(case)[:4])
     a = _run_prefill(kvp, gc, case)
     d = gc.decode(num_splits=1)
-    ma, rel, _, ulps = compare_outputs(a, (d.astype(np.uint32) << 16).view(np.float32)
-                                       .astype(np.float64))
-    assert ma <= 1e-2 and rel <= 5e-3 and ulps <= 1.0
+    assert_within_one_rounding(a, d, f"{cfg.name} prefill vs decode")
     assert_close(a, _oracle(case)[4], cfg.name)
     gc.close()
 

@@ -30,7 +30,7 @@ def kvp():
 
 def _pools(kvp, desc, lay):
     kv_bytes, meta_bytes = kvp.kvp_pool_bytes(desc)
-    if lay.dtype == "int8":
+    if lay.dtype != "bf16":
         fill = int(np.uint8(POISON_I8).view(np.int8))
         k = torch.full((kv_bytes,), fill, dtype=torch.int8, device="cuda")
         mfill = int(np.uint16(POISON_F16).view(np.int16))
@@ -45,10 +45,11 @@ def _host(t):
     if t is None:
         return None
     a = t.cpu().numpy()
-    return a if a.dtype == np.int8 else a.view(np.uint16)
+    return a.view(np.uint8) if a.dtype == np.int8 else a.view(np.uint16)
 
 
-@pytest.mark.parametrize("dtype,P,D", [("bf16", 16, 128), ("int8", 32, 128), ("bf16", 32, 64)])
+@pytest.mark.parametrize("dtype,P,D", [("bf16", 16, 128), ("int8", 32, 128), ("bf16", 32, 64),
+                                       ("int4", 16, 128), ("fp8", 32, 64)])
 def test_copy_pages_bit_exact(kvp, dtype, P, D):
     """Copied pages equal their sources byte for byte (K, V, metadata); every
     other byte keeps its value; pairs naming pages outside the pool are skipped."""
@@ -60,7 +61,7 @@ def test_copy_pages_bit_exact(kvp, dtype, P, D):
     k = torch.from_numpy(rng.integers(-128, 128, kv_bytes, dtype=np.int8)).cuda()
     v = torch.from_numpy(rng.integers(-128, 128, kv_bytes, dtype=np.int8)).cuda()
     km = vm = None
-    if dtype == "int8":
+    if dtype != "bf16":
         km = torch.from_numpy(rng.integers(-2**15, 2**15, meta_bytes // 2, dtype=np.int16)).cuda()
         vm = torch.from_numpy(rng.integers(-2**15, 2**15, meta_bytes // 2, dtype=np.int16)).cuda()
     else:
@@ -85,7 +86,7 @@ def _bf16_rows(rng, n, H, D):
     return f32_to_bf16_bits(rng.standard_normal((n, H, D)).astype(np.float32))
 
 
-@pytest.mark.parametrize("dtype,P", [("bf16", 16), ("int8", 32)])
+@pytest.mark.parametrize("dtype,P", [("bf16", 16), ("int8", 32), ("int4", 16), ("fp8", 32)])
 def test_prefix_reuse_and_copy_on_write(kvp, dtype, P):
     """A: prompt of 5 pages + 9 tokens, appended and cached.  B: A's first 3
     pages' tokens plus its own suffix: matches A's 3 pages and appends only its

@@ -30,7 +30,7 @@ class DecodeConfig:
     num_kv_heads: int
     head_dim: int
     page_size: int
-    kv_dtype: str = "bf16"          # "bf16" or "int8"
+    kv_dtype: str = "bf16"          # "bf16", "int8", "int4" or "fp8"
     ctx_fixed: Optional[Tuple[int, ...]] = None   # explicit per-sequence ctx
     ctx_lo: int = 0                 # else ctx ~ U{ctx_lo..ctx_hi} (inclusive)
     ctx_hi: int = 0
@@ -108,7 +108,14 @@ CHUNKED_PREFILL = DecodeConfig(
     name="chunked_prefill", layers=1, batch=8, num_q_heads=32, num_kv_heads=8, head_dim=128,
     page_size=16, ctx_lo=2048, ctx_hi=8192, q_len=512, seed=465008)
 
-EXTRA_CONFIGS = {c.name: c for c in (STREAMING_WINDOW, SPEC_VERIFY, CHUNKED_PREFILL)}
+# The long-context quantized cache with 4-bit codes (two per byte, same row
+# contract with 16 levels) and with FP8 e4m3 values under a per-token scale
+# ("KV-Cache Optimization Techniques", section "KV-Cache Quantization").
+INT4_LONG = replace(INT8_LONG, name="int4_long", kv_dtype="int4", seed=465009)
+FP8_LONG = replace(INT8_LONG, name="fp8_long", kv_dtype="fp8", seed=465010)
+
+EXTRA_CONFIGS = {c.name: c for c in (STREAMING_WINDOW, SPEC_VERIFY, CHUNKED_PREFILL, INT4_LONG,
+                                     FP8_LONG)}
 
 
 def variant(cfg: DecodeConfig, **kw) -> DecodeConfig:
