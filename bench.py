@@ -56,6 +56,11 @@ def parse_args(argv=None):
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="llama3_70b_full_cache")
     p.add_argument("--splits", type=int, default=0, help="forced split count (0 = planner)")
+    p.add_argument("--plan", choices=("auto", "uniform", "balanced"), default="auto",
+                   help="decode work plan: the uniform split plan, a balanced schedule built "
+                        "from the host lengths, or auto (balanced when the lengths differ)")
+    p.add_argument("--bins", type=int, default=0,
+                   help="most bins of the balanced schedule (0 = four per compute unit)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle sample")
@@ -186,6 +191,29 @@ def run_gpu(args, kvp, cfg, case):
 
     windowed = cfg.window_tokens > 0
     chunked = is_chunked(cfg)
+    balanced = not chunked and args.splits == 0 and (
+        args.plan == "balanced" or (args.plan == "auto" and int(np.ptp(case.ctx)) > 0))
+    sched = sched_dev = sched_ws = None
+    if balanced:
+        # one schedule serves every layer (they share lengths and tables); the
+        # bench's lengths are the same every step, so it is built once here
+        cus = args.bins or 4 * torch.cuda.get_device_properties(0).multi_processor_count
+        t0 = time.perf_counter()
+        reps = 20
+        for _ in range(reps):
+            sched = kvp.kvp_decode_schedule(pool, case.ctx, Hq, int(case.block_tables.shape[1]),
+                                            cus, cfg.sink_tokens, cfg.window_tokens)
+        sched_host_us = (time.perf_counter() - t0) / reps * 1e6
+        sched_dev = torch.from_numpy(sched.used.copy()).to(dev)
+        wsb = sched.info.workspace_bytes
+        sched_ws = torch.empty(max(wsb, 4) // 4, dtype=torch.float32, device=dev) if wsb else None
+        i = sched.info
+        plan = {"balanced": True, "num_bins": i.num_bins, "num_items": i.num_items,
+                "num_merge": i.num_merge, "num_slots": i.num_slots,
+                "waves_per_group": plan["waves_per_group"], "use_mfma": plan["use_mfma"],
+                "workspace_bytes": int(wsb), "schedule_bytes": int(i.sched_words) * 4,
+                "schedule_host_us": round(sched_host_us, 1)}
+        log(f"[plan] balanced schedule {plan}")
     q_start = torch.from_numpy(case.q_start.astype(np.int32)).to(dev)
     max_q_len = int(np.diff(case.q_start).max())
     if windowed:
@@ -205,6 +233,12 @@ def run_gpu(args, kvp, cfg, case):
             if chunked:
                 kvp.kvp_paged_attention_prefill(pool, L.q, q_start, L.k, L.v, L.km, L.vm, bt, ctx,
                                                 max_q_len, max_ctx, scale, L.out)
+                if timed:
+                    probe[2].record()
+            elif balanced:
+                kvp.kvp_paged_attention_decode_scheduled(pool, L.q, L.k, L.v, L.km, L.vm, bt, ctx,
+                                                         max_ctx, scale, sched_dev, sched, L.out,
+                                                         sched_ws)
                 if timed:
                     probe[2].record()
             elif windowed:
@@ -266,7 +300,8 @@ def run_gpu(args, kvp, cfg, case):
         f"mean={step_ms.mean():.3f} min={step_ms.min():.3f}; split kernel mean "
         f"{kern_ms.mean() * 1e3:.1f} us min {kern_ms.min() * 1e3:.1f} us")
     res = {"ms_per_step": ms_per_step, "step_ms_events": step_ms, "kernel_ms": kern_ms,
-           "plan": plan, "num_splits": S}
+           "plan": plan, "num_splits": S, "balanced": balanced,
+           "merge_launched": bool(balanced and sched.info.num_merge > 0)}
     return res, (pool, layers, bt, ctx)
 
 
@@ -525,7 +560,10 @@ def main(argv=None):
                    [int(case.ctx.min()), int(case.ctx.max())],
                    "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads,
                    "head_dim": cfg.head_dim, "page_size": cfg.page_size,
-                   "kv_dtype": cfg.kv_dtype, "num_splits": res["num_splits"],
+                   "kv_dtype": cfg.kv_dtype,
+                   **({"plan": "balanced", "num_bins": res["plan"]["num_bins"],
+                       "num_merge": res["plan"]["num_merge"]} if res["balanced"]
+                      else {"plan": "uniform", "num_splits": res["num_splits"]}),
                    **({"sink_tokens": cfg.sink_tokens, "window_tokens": cfg.window_tokens}
                       if cfg.window_tokens > 0 else {}),
                    "waves_per_group": res["plan"]["waves_per_group"]},
@@ -536,8 +574,10 @@ def main(argv=None):
         "bytes_per_step": {k: int(v) for k, v in sb.items()},
         "roofline": {**roof, "traffic": None, "kernel": kernel_name,
                      "kernel_us_mean": round(kern_us, 2),
-                     "timed": "decode call (split + merge kernels)" if cfg.window_tokens > 0
-                     else "split kernel",
+                     "timed": ("decode call (split kernel + merge kernel)"
+                               if res["merge_launched"] or (cfg.window_tokens > 0 and
+                                                            not res["balanced"])
+                               else "split kernel"),
                      "bytes_per_launch": int(sb["split_kernel_per_launch"]),
                      "flops_per_launch": int(flops_launch),
                      "intensity_flop_per_byte": round(intensity, 2),

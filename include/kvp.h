@@ -322,6 +322,84 @@ kvp_status kvp_paged_attention_decode_window(
     float scale, int32_t sink_tokens, int32_t window_tokens, void* out, int32_t num_splits_req,
     void* workspace, size_t workspace_bytes, kvp_stream_t stream);
 
+/* ---- Balanced decode for ragged batches (host schedule + device) ----------
+ * "KV-Cache Optimization Techniques", section "PagedAttention": the work of
+ * a decode step is the (sequence, KV head, page) triples.  With ragged
+ * lengths, splitting each sequence the same way leaves the compute units
+ * that hold short sequences idle while the long ones finish.  Here the
+ * caller, who knows the lengths on the host, builds a schedule that gives
+ * every bin an equal share of the streamed blocks.  A bin is one wavefront's
+ * stream on the matrix-core path (g >= 4) and one workgroup on the vector
+ * path (g < 4):
+ *   - the (sequence, KV head) pairs are laid end to end, KV head fastest,
+ *     each contributing its streamed blocks (all ceil(n/P), or with sinks and
+ *     a window, eq. 5 of section "Token Eviction Strategies", the sink blocks
+ *     and the window's blocks);
+ *   - bin k of num_bins covers blocks [k*T/num_bins, (k+1)*T/num_bins) of
+ *     that list (T = all blocks); num_bins = min(max_bins, ceil(T/8)), at
+ *     least 1 (4 bins per compute unit keep one wavefront per SIMD busy);
+ *   - the pieces of pairs a bin covers are its items, processed in order; on
+ *     the matrix-core path the items of a wavefront's stream share its
+ *     register ring, so the next item's pages load while the current one
+ *     finishes, and no barrier separates items; a pair inside one bin writes
+ *     its output directly, a pair cut by bin boundaries writes a float32
+ *     partial per piece and is merged by log-sum-exp afterwards (a second
+ *     kernel, launched only if needed).
+ * With equal lengths whose pairs divide evenly into bins, every pair lands in
+ * one bin and no merge runs. */
+typedef struct {
+  int32_t num_bins;       /* workgroups of the split kernel */
+  int32_t num_items;      /* pieces over all bins */
+  int32_t num_merge;      /* pairs cut across bins (merge entries) */
+  int32_t num_slots;      /* partials those pairs write */
+  int32_t items_offset;   /* word offset of the item records in the schedule */
+  int32_t merge_offset;   /* word offset of the merge records */
+  int32_t sink_tokens;    /* the selection the schedule was built for */
+  int32_t window_tokens;
+  int32_t sched_words;    /* int32 words of the schedule that are used */
+  size_t workspace_bytes; /* device workspace the partials need (0: none) */
+} kvp_schedule_info;
+
+/* Upper bounds, for any lengths, of the schedule size (bytes of int32 words)
+ * and of the workspace the scheduled decode needs, for num_seqs sequences,
+ * num_q_heads query heads and at most max_bins bins (> 0). */
+kvp_status kvp_decode_schedule_bounds(const kvp_pool* pool, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t max_bins,
+                                      size_t* sched_bytes, size_t* workspace_bytes);
+
+/* Build the schedule (host).  context_lens: host array of the B lengths the
+ * device array will hold at decode time (0 <= n <= max_blocks*P, else
+ * KVP_E_INVAL); sink_tokens/window_tokens as for the window decode (0, 0 for
+ * the full decode); max_bins > 0; sched: host buffer of sched_bytes >= the
+ * bound above.  Layout (int32 words):
+ *   [0..7]   num_bins, num_items, num_merge, num_slots, items_offset,
+ *            merge_offset, 0, 0;
+ *   [8 .. 8+num_bins]  bin_start: bin k owns items bin_start[k] .. bin_start[k+1]-1;
+ *   items_offset + 8*i: item i = sequence, KV head, first streamed block,
+ *            end block (exclusive, counted in the sequence's streamed list),
+ *            partial slot (-1: write the output), 0, 0, 0;
+ *   merge_offset + 4*e: entry e = sequence, KV head, first slot, slot count.
+ * The caller copies the first info->sched_words words to device memory. */
+kvp_status kvp_decode_schedule(const kvp_pool* pool, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
+                               int32_t sink_tokens, int32_t window_tokens, int32_t max_bins,
+                               int32_t* sched, size_t sched_bytes, kvp_schedule_info* info);
+
+/* The decode (window decode when info->window_tokens > 0) along a schedule:
+ * the same result as kvp_paged_attention_decode(_window) within float32
+ * summation order.  sched: device copy of the schedule built for these
+ * lengths (device context_lens must equal the host lengths it was built
+ * from; blocks beyond a device length are masked, blocks the schedule does
+ * not name are not read).  workspace: device buffer of at least
+ * info->workspace_bytes (may be NULL when that is 0).  Other arguments as
+ * for kvp_paged_attention_decode. */
+kvp_status kvp_paged_attention_decode_scheduled(
+    const kvp_pool* pool, const void* q, const void* k_pool, const void* v_pool,
+    const void* k_meta, const void* v_meta, const int32_t* block_tables, int32_t max_blocks,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    float scale, const int32_t* sched, const kvp_schedule_info* info, void* out,
+    void* workspace, size_t workspace_bytes, kvp_stream_t stream);
+
 /* ---- Several new tokens per sequence: chunked prefill, verification (device)
  * "KV-Cache Optimization Techniques", section "Cache-Aware Scheduling": long
  * prompts are processed in chunks against the cache.  Sequence b holds

@@ -14,7 +14,7 @@ from typing import Optional
 import numpy as np
 
 from . import _lib
-from ._lib import DecodePlan, PoolDesc
+from ._lib import DecodePlan, PoolDesc, ScheduleInfo
 
 _L = _lib.load()
 
@@ -354,6 +354,68 @@ def kvp_paged_attention_decode_window(pool: Pool, q, k_pool, v_pool, k_meta, v_m
         _stream(stream)), "kvp_paged_attention_decode_window")
 
 
+def kvp_decode_schedule_bounds(pool: Pool, num_seqs: int, num_q_heads: int,
+                               max_bins: int) -> tuple:
+    """(schedule bytes, workspace bytes) upper bounds for any lengths."""
+    sb, wb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(_L.kvp_decode_schedule_bounds(pool.handle, int(num_seqs), int(num_q_heads),
+                                         int(max_bins), ctypes.byref(sb), ctypes.byref(wb)),
+           "kvp_decode_schedule_bounds")
+    return int(sb.value), int(wb.value)
+
+
+class Schedule:
+    """A balanced decode schedule built on the host (kvp_decode_schedule):
+    ``words`` is the int32 host array, ``info`` the ScheduleInfo."""
+
+    def __init__(self, words: np.ndarray, info: ScheduleInfo):
+        self.words = words
+        self.info = info
+
+    @property
+    def used(self) -> np.ndarray:
+        return self.words[: self.info.sched_words]
+
+
+def kvp_decode_schedule(pool: Pool, context_lens, num_q_heads: int, max_blocks: int,
+                        max_bins: int, sink_tokens: int = 0, window_tokens: int = 0) -> Schedule:
+    """Balanced schedule for host context lengths (numpy int32 array); at most
+    max_bins bins (four per compute unit keep one wavefront per SIMD busy)."""
+    ctx = _i32(np.ascontiguousarray(context_lens, dtype=np.int32))
+    sb, _ = kvp_decode_schedule_bounds(pool, ctx.size, num_q_heads, max_bins)
+    words = np.zeros(sb // 4, dtype=np.int32)
+    info = ScheduleInfo()
+    _check(_L.kvp_decode_schedule(pool.handle, _ptr(ctx), ctx.size, int(num_q_heads),
+                                  int(max_blocks), int(sink_tokens), int(window_tokens),
+                                  int(max_bins), _ptr(words), words.nbytes, ctypes.byref(info)),
+           "kvp_decode_schedule")
+    return Schedule(words, info)
+
+
+def kvp_paged_attention_decode_scheduled(pool: Pool, q, k_pool, v_pool, k_meta, v_meta,
+                                         block_tables, context_lens, max_context_len: int,
+                                         scale: float, sched_dev, schedule: Schedule, out,
+                                         workspace=None, stream=None) -> None:
+    """Decode along a balanced schedule; sched_dev is the device copy (int32)
+    of schedule.used."""
+    eb = pool.elem_bytes
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables/context_lens must cover the batch")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if sched_dev.numel() < schedule.info.sched_words:
+        raise ValueError("sched_dev must hold the schedule's used words")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_L.kvp_paged_attention_decode_scheduled(
+        pool.handle, _dev(q, "q", 2), _dev(k_pool, "k_pool", eb), _dev(v_pool, "v_pool", eb),
+        _dev(k_meta, "k_meta", 2), _dev(v_meta, "v_meta", 2), _dev(block_tables, "block_tables", 4),
+        int(block_tables.shape[1]), _dev(context_lens, "context_lens", 4), B, Hq,
+        int(max_context_len), float(scale), _dev(sched_dev, "sched", 4),
+        ctypes.byref(schedule.info), _dev(out, "out", 2), _dev(workspace, "workspace"), ws_bytes,
+        _stream(stream)), "kvp_paged_attention_decode_scheduled")
+
+
 def kvp_paged_attention_prefill(pool: Pool, q, q_start, k_pool, v_pool, k_meta, v_meta,
                                 block_tables, context_lens, max_q_len: int,
                                 max_context_len: int, scale: float, out, stream=None) -> None:
@@ -423,6 +485,8 @@ __all__ = [
     "kvp_pages_free", "kvp_seq_grow", "kvp_seq_share", "kvp_seq_release", "kvp_decode_plan",
     "kvp_kv_append", "kvp_decode_workspace_bytes", "kvp_paged_attention_decode",
     "kvp_decode_partials_bytes", "kvp_paged_attention_decode_partials", "kvp_lse_merge",
+    "kvp_decode_schedule_bounds", "kvp_decode_schedule", "kvp_paged_attention_decode_scheduled",
+    "Schedule", "ScheduleInfo",
     "kvp_seq_evict_window", "kvp_decode_window_workspace_bytes",
     "kvp_paged_attention_decode_window", "kvp_paged_attention_prefill", "PrefixCache",
     "kvp_prefix_cache_create", "kvp_prefix_cache_pages", "kvp_prefix_match",

@@ -25,6 +25,13 @@ class DecodePlan(ctypes.Structure):
                 ("workspace_bytes", c_size_t)]
 
 
+class ScheduleInfo(ctypes.Structure):
+    _fields_ = [("num_bins", c_int32), ("num_items", c_int32), ("num_merge", c_int32),
+                ("num_slots", c_int32), ("items_offset", c_int32), ("merge_offset", c_int32),
+                ("sink_tokens", c_int32), ("window_tokens", c_int32), ("sched_words", c_int32),
+                ("workspace_bytes", c_size_t)]
+
+
 # name -> (restype, argtypes); every symbol include/kvp.h declares
 PROTOTYPES = {
     "kvp_status_string": (ctypes.c_char_p, [c_int32]),
@@ -83,6 +90,17 @@ PROTOTYPES = {
                                                     c_void_p, c_int32, c_int32, c_int32, c_float,
                                                     c_int32, c_int32, c_void_p, c_int32,
                                                     c_void_p, c_size_t, c_void_p]),
+    "kvp_decode_schedule_bounds": (c_int32, [c_void_p, c_int32, c_int32, c_int32,
+                                             ctypes.POINTER(c_size_t), ctypes.POINTER(c_size_t)]),
+    "kvp_decode_schedule": (c_int32, [c_void_p, P_int32, c_int32, c_int32, c_int32, c_int32,
+                                      c_int32, c_int32, P_int32, c_size_t,
+                                      ctypes.POINTER(ScheduleInfo)]),
+    "kvp_paged_attention_decode_scheduled": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p,
+                                                       c_void_p, c_void_p, c_void_p, c_int32,
+                                                       c_void_p, c_int32, c_int32, c_int32,
+                                                       c_float, c_void_p,
+                                                       ctypes.POINTER(ScheduleInfo), c_void_p,
+                                                       c_void_p, c_size_t, c_void_p]),
 }
 
 _lib = None
@@ -96,6 +114,11 @@ def load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing; build it with "
                           "`python -m paged_kv_cache_465_amd.build` (hipcc, gfx950)")
+    # Device memory and streams come from torch, so the library must bind to
+    # the HIP runtime torch has loaded: load torch first (loaded the other
+    # way round, the library could bring up a runtime of its own, in which
+    # torch's streams are not valid).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in PROTOTYPES.items():
         fn = getattr(lib, name)

@@ -23,7 +23,7 @@ HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
 DEVICE_SOURCES = ["append.hip", "decode.hip", "prefill.hip"]
-HOST_SOURCES = ["pool.cpp", "prefix_cache.cpp"]
+HOST_SOURCES = ["pool.cpp", "prefix_cache.cpp", "schedule.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
 # Device code: gfx950 only; packed-fp32 instructions off; IEEE-rounded fp32
@@ -49,7 +49,8 @@ def build(verbose: bool = False) -> str:
         jobs.append([HIPCC, *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        jobs.append([HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+        # host-only C++ (no device code): compiled as plain C++
+        jobs.append([HIPCC, *COMMON, "-x", "c++", "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(4, len(jobs))) as ex:
         outs = list(ex.map(_run, jobs))
     if verbose:

@@ -172,6 +172,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 
 template <int P, int D, int F>
 hipError_t launch_append(AppendArgs a, hipStream_t stream) {
+  discard_stale_error();
   const int64_t rows = int64_t(a.n_tokens) * a.num_kv_heads;
   const int64_t chunk = int64_t(1) << 24;  // rows per launch, far below grid limits
   for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
@@ -277,6 +278,7 @@ extern "C" kvp_status kvp_copy_pages(const kvp_pool* pool, void* k_pool, void* v
   const int64_t page_bytes = int64_t(d.num_kv_heads) * d.page_size * d.head_dim * bits / 8;
   const int64_t meta_bytes = quant ? int64_t(d.num_kv_heads) * d.page_size * 4 : 0;
   if (int64_t(n) * 4 > 0x7fffffff) return KVP_E_UNSUPPORTED;
+  kvp::discard_stale_error();
   hipLaunchKernelGGL(kvp::copy_pages_kernel, dim3(unsigned(n) * 4), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), static_cast<char*>(k_pool),
                      static_cast<char*>(v_pool), static_cast<char*>(k_meta),

@@ -58,6 +58,9 @@ struct DecodeArgs {
   int32_t sink_tokens, window_tokens;  // window_tokens > 0: attend only to the kept set
   int32_t write_partials;  // 1: store (o, m, l) per split; 0: store the bf16 output
   float scale_log2;  // scale * log2(e)
+  const int32_t* sched;    // balanced schedule (bin starts at word 8), or null
+  int32_t items_off;       // word offset of its item records
+  int32_t num_items, num_slots, num_bins;
 };
 
 // The tokens a sequence of n attends to.  Without a window, 0..n-1.  With a
@@ -70,6 +73,7 @@ struct DecodeArgs {
 // only dropped tokens and are never read (their table entries may be -1).
 struct WorkRange {
   int b, h, s, ctx;
+  int slot;                // scheduled item: partial slot, -1 for the direct output
   int kb0, cnt;            // this wave's virtual blocks [kb0, kb0 + cnt)
   int sink_blk, win_first;
   int sink_end, win_start;  // kept: t < ctx and (t < sink_end or t >= win_start)
@@ -109,14 +113,9 @@ __device__ __forceinline__ PageMask page_mask(const WorkRange& w, int lblk) {
 // splits are dispatched first.  (With the split fastest and eight KV heads,
 // an even split count gave each XCD a single split index: half the XCDs
 // streamed every sequence's first pages while the other half idled.)
+// Sequence b's streamed block list (see WorkRange) and its length.
 template <int P>
-__device__ __forceinline__ WorkRange work_range(const DecodeArgs& a, int wave, int W) {
-  WorkRange w;
-  int item = blockIdx.x;
-  w.h = item % a.num_kv_heads;
-  item /= a.num_kv_heads;
-  w.b = item % a.num_seqs;
-  w.s = item / a.num_seqs;
+__device__ __forceinline__ int sequence_blocks(const DecodeArgs& a, WorkRange& w) {
   int ctx = a.ctx_lens[w.b];
   ctx = min(max(ctx, 0), a.ctx_cap);
   w.ctx = ctx;
@@ -133,18 +132,69 @@ __device__ __forceinline__ WorkRange work_range(const DecodeArgs& a, int wave, i
     w.win_first = max(w.win_start / P, w.sink_blk);
     nvirt = w.sink_blk + (nblk - w.win_first);
   }
-  const int blk0 = w.s * a.pages_per_split;
-  const int blk1 = min(blk0 + a.pages_per_split, nvirt);
+  return nvirt;
+}
+
+// Wave `wave` of W takes a contiguous share of virtual blocks [blk0, blk1).
+__device__ __forceinline__ void wave_share(WorkRange& w, int blk0, int blk1, int wave, int W) {
   const int n = max(blk1 - blk0, 0);
   const int cw = (n + W - 1) / W;
   w.kb0 = blk0 + wave * cw;
   w.cnt = max(0, min(cw, blk1 - w.kb0));
+}
+
+// Which (sequence, KV head, split) this workgroup owns and which contiguous
+// run of virtual blocks [kb0, kb0 + cnt) wave `wave` streams.
+//
+// Workgroups are handed to the eight XCDs round robin (workgroup i to XCD
+// i mod 8), so the index order decides each XCD's share of the work.  The KV
+// head varies fastest (the heads of one sequence carry equal work), then the
+// sequence, and the split slowest: every XCD gets the same mix of long and
+// short sequences and of first and last splits, and the always-full first
+// splits are dispatched first.  (With the split fastest and eight KV heads,
+// an even split count gave each XCD a single split index: half the XCDs
+// streamed every sequence's first pages while the other half idled.)
+template <int P>
+__device__ __forceinline__ WorkRange work_range(const DecodeArgs& a, int wave, int W) {
+  WorkRange w;
+  int item = blockIdx.x;
+  w.h = item % a.num_kv_heads;
+  item /= a.num_kv_heads;
+  w.b = item % a.num_seqs;
+  w.s = item / a.num_seqs;
+  w.slot = -1;
+  const int nvirt = sequence_blocks<P>(a, w);
+  const int blk0 = w.s * a.pages_per_split;
+  wave_share(w, blk0, min(blk0 + a.pages_per_split, nvirt), wave, W);
+  return w;
+}
+
+// A schedule item names a sequence and KV head of this call and a partial
+// slot within the workspace (or -1); anything else is skipped.
+__device__ __forceinline__ bool item_valid(const DecodeArgs& a, int i) {
+  const int32_t* it = a.sched + a.items_off + int64_t(i) * 8;
+  return unsigned(it[0]) < unsigned(a.num_seqs) && unsigned(it[1]) < unsigned(a.num_kv_heads) &&
+         it[4] >= -1 && it[4] < a.num_slots;
+}
+
+// Item `i` of a balanced schedule: sequence, KV head, streamed blocks
+// [first, end) (clipped to the device length), partial slot.
+template <int P>
+__device__ __forceinline__ WorkRange item_range(const DecodeArgs& a, int i, int wave, int W) {
+  const int32_t* it = a.sched + a.items_off + int64_t(i) * 8;
+  WorkRange w;
+  w.b = it[0];
+  w.h = it[1];
+  w.s = 0;
+  w.slot = it[4];
+  const int nvirt = sequence_blocks<P>(a, w);
+  wave_share(w, max(it[2], 0), min(it[3], nvirt), wave, W);
   return w;
 }
 
 // Merge the W wavefronts' (m, l, o) partials held in LDS and store either the
 // final bfloat16 output (one split) or this split's normalized partial.
-template <int D>
+template <int D, bool SCHED>
 __device__ __forceinline__ void combine_and_store(const DecodeArgs& a, const WorkRange& wr,
                                                   const float* sm_o, const float* sm_m,
                                                   const float* sm_l, int W, int HP) {
@@ -166,10 +216,11 @@ __device__ __forceinline__ void combine_and_store(const DecodeArgs& a, const Wor
     }
     const float res = L > 0.0f ? O / L : 0.0f;
     const int64_t row = int64_t(wr.b) * a.num_q_heads + int64_t(wr.h) * g + j;
-    if (!a.write_partials) {
+    const bool direct = SCHED ? wr.slot < 0 : !a.write_partials;
+    if (direct) {
       a.out[row * D + d] = f32_to_bf16_rne(res);
     } else {
-      const int64_t pr = row * a.num_splits + wr.s;
+      const int64_t pr = SCHED ? int64_t(wr.slot) * g + j : row * a.num_splits + wr.s;
       a.part_o[pr * D + d] = res;
       if (d == 0) {
         a.part_ml[pr * 2] = M;
@@ -239,8 +290,8 @@ __device__ __forceinline__ f16x8_t codes8_to_f16x8(const uint32_t* w) {
   }
 }
 
-template <int F, int P, int D, int NT, int DEPTH>
-__global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel(DecodeArgs a) {
+template <int F, int P, int D, int NT, int DEPTH, bool SCHED>
+__device__ __forceinline__ void mfma_item(const DecodeArgs& a, const WorkRange& wr, float* smem) {
   using S = MfmaShape<F, P, D>;
   using FI = FmtInfo<F>;
   constexpr bool Q = FI::quant, ZP = FI::zero;
@@ -251,13 +302,11 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
       T == 1, typename std::conditional<Q, f16x4_t, bf16x4_t>::type, OpA>::type;
   using KLoad = typename LoadT<S::KLB>::type;
   using VLoad = typename LoadT<S::VB>::type;
-  extern __shared__ float smem[];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
   const int r = lane & 15, gq = lane >> 4;
-  const WorkRange wr = work_range<P>(a, wave, W);
   const int g = a.group;
   const int H = a.num_kv_heads;
 
@@ -537,7 +586,398 @@ __global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel
     }
   }
   __syncthreads();
-  combine_and_store<D>(a, wr, sm_o, sm_m, sm_l, W, HP);
+  combine_and_store<D, SCHED>(a, wr, sm_o, sm_m, sm_l, W, HP);
+}
+
+// One workgroup: a (sequence, KV head, split) of the uniform plan.
+template <int F, int P, int D, int NT, int DEPTH>
+__global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel(DecodeArgs a) {
+  extern __shared__ float smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
+  mfma_item<F, P, D, NT, DEPTH, false>(a, work_range<P>(a, wave, W), smem);
+}
+
+// ---------------------------------------------------------------------------
+// Balanced schedule on the matrix-core path: one wavefront streams one bin.
+// The bin's items (pieces of (sequence, KV head) pairs) pass through the
+// same register ring one after another, so the loads of an item's first
+// pages are in flight while the previous item's last pages are computed, and
+// no workgroup barrier separates items: the wavefront writes each item's
+// result (the output, or a normalized partial for the merge) from its own
+// registers.  Wavefronts of a workgroup are independent.
+
+// Where one side (issue or compute) of a stream stands: item `item` of the
+// schedule (== end once the stream is done), page k of its range.
+struct StreamPos {
+  int item, k;
+  WorkRange wr;
+};
+
+// From p.item on: the first valid item (with nonempty range when
+// need_pages), its range loaded and k = 0.
+template <int P>
+__device__ __forceinline__ void stream_seek(const DecodeArgs& a, StreamPos& p, int end,
+                                            bool need_pages) {
+  for (; p.item < end; ++p.item) {
+    if (!item_valid(a, p.item)) continue;
+    p.wr = item_range<P>(a, p.item, 0, 1);
+    if (!need_pages || p.wr.cnt > 0) break;
+  }
+  p.k = 0;
+}
+
+template <int F, int P, int D, int NT, int DEPTH>
+__global__ __launch_bounds__(256) void decode_mfma_stream_kernel(DecodeArgs a) {
+  using S = MfmaShape<F, P, D>;
+  using FI = FmtInfo<F>;
+  constexpr bool Q = FI::quant, ZP = FI::zero;
+  constexpr int T = S::T, KK = S::KK, NC = S::NC, EV = S::EV, RB = S::RB, KB = S::KB;
+  using OpA = typename std::conditional<Q, f16x8_t, bf16x8_t>::type;
+  using OpPV = typename std::conditional<
+      T == 1, typename std::conditional<Q, f16x4_t, bf16x4_t>::type, OpA>::type;
+  using KLoad = typename LoadT<S::KLB>::type;
+  using VLoad = typename LoadT<S::VB>::type;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int bin = blockIdx.x * (blockDim.x >> 6) + wave;
+  if (bin >= a.num_bins) return;  // the whole wavefront; nothing here waits on the others
+  const int r = lane & 15, gq = lane >> 4;
+  const int g = a.group;
+  const int H = a.num_kv_heads;
+  const int i_begin = max(a.sched[8 + bin], 0);
+  const int end = min(a.sched[9 + bin], a.num_items);
+
+  int koff[T];
+#pragma unroll
+  for (int st = 0; st < T; ++st) {
+    const int tok = (T == 1) ? r : 8 * (r >> 2) + 4 * st + (r & 3);
+    koff[st] = tok * RB + (Q ? gq * KB : 16 * gq);
+  }
+  const int voff = F == kBF16 ? (r * P + EV * gq) * 2
+                              : (F == kI4 ? (r >> 1) * P : r * P) + EV * gq;
+  constexpr int vstride = F == kBF16 ? 16 * P * 2 : (F == kI4 ? 8 * P : 16 * P);
+  const int moff = EV * gq * 4;
+  const size_t tile_bytes = size_t(P) * RB;
+  const char* kbase = static_cast<const char*>(a.k_pool);
+  const char* vbase = static_cast<const char*>(a.v_pool);
+
+  // issue side: loads page ip.k of item ip.item; once the stream's pages are
+  // all issued it repeats the last page (a cache hit) so the ring's load
+  // pattern stays fixed
+  StreamPos ip;
+  ip.item = i_begin;
+  stream_seek<P>(a, ip, end, true);
+  bool issued_all = ip.item >= end;
+  auto issue = [&](PageRegs<F, P, D>& R) __attribute__((always_inline)) {
+    const int32_t* btrow = a.bt + int64_t(ip.wr.b) * a.max_blocks;
+    int phys = btrow[ip.wr.logical(ip.wr.kb0 + ip.k)];
+    const bool ok = unsigned(phys) < unsigned(a.num_pages);
+    R.phys = ok ? phys : -1;
+    const int64_t tile = int64_t(ok ? phys : 0) * H + ip.wr.h;
+    const char* kp = kbase + tile * tile_bytes;
+    const char* vp = vbase + tile * tile_bytes;
+#pragma unroll
+    for (int st = 0; st < T; ++st)
+#pragma unroll
+      for (int i = 0; i < S::KN; ++i)
+        R.k[st][i] = load_stream<KLoad>(kp + koff[st] + i * (Q ? 16 : 64));
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc) R.v[nc] = load_stream<VLoad>(vp + voff + nc * vstride);
+    if constexpr (Q) {
+      const char* km = reinterpret_cast<const char*>(a.k_meta) + tile * (P * 4);
+      const char* vm = reinterpret_cast<const char*>(a.v_meta) + tile * (P * 4);
+#pragma unroll
+      for (int st = 0; st < T; ++st) {
+        R.km[st] = load_stream<uint4>(km + moff + st * 16);
+        R.vm[st] = load_stream<uint4>(vm + moff + st * 16);
+      }
+    }
+    // advance to the next page of the stream (or stay on the last one)
+    if (!issued_all) {
+      if (++ip.k >= ip.wr.cnt) {
+        StreamPos nx = ip;
+        ++nx.item;
+        stream_seek<P>(a, nx, end, true);
+        if (nx.item < end) ip = nx;
+        else { issued_all = true; ip.k = ip.wr.cnt - 1; }
+      }
+    }
+  };
+
+  // per-item state: q operands, online softmax
+  OpA qop[NT][KK];
+  float qsum[NT];
+  float m[NT], lsum[NT], zacc[NT];
+  f32x4_t acc[NT][NC];
+  auto begin_item = [&](const WorkRange& wr) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int jj = nt * 16 + r;
+      const bool live = jj < g;
+      const uint16_t* qrow =
+          a.q + (int64_t(wr.b) * a.num_q_heads + int64_t(wr.h) * g + (live ? jj : 0)) * D;
+      float qs = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int d0 = Q ? (D / 4) * gq + 8 * kk : 32 * kk + 8 * gq;
+        uint4 raw = live ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
+        if constexpr (!Q) {
+          qop[nt][kk] = __builtin_bit_cast(bf16x8_t, raw);
+        } else {
+          const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+          f16x8_t v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float f = bf16_to_f32((w4[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+            v[e] = (_Float16)f;
+            qs += f;
+          }
+          qop[nt][kk] = v;
+        }
+      }
+      qsum[nt] = ZP ? group4_sum(qs) : 0.0f;
+      m[nt] = -INFINITY;
+      lsum[nt] = 0.0f;
+      zacc[nt] = 0.0f;
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc) acc[nt][nc] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  };
+  // the item's result: o / l (and m, l for a partial), straight from registers
+  auto finish_item = [&](const WorkRange& wr) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float lt = group4_sum(lsum[nt]);
+      const float zt = ZP ? group4_sum(zacc[nt]) : 0.0f;
+      const int jj = nt * 16 + r;
+      if (jj < g) {
+        const int64_t row = int64_t(wr.b) * a.num_q_heads + int64_t(wr.h) * g + jj;
+        const int64_t pr = int64_t(wr.slot) * g + jj;
+#pragma unroll
+        for (int nc = 0; nc < NC; ++nc) {
+          f32x4_t v = acc[nt][nc];
+          if constexpr (ZP) v += zt;
+          const int d = 16 * nc + 4 * gq;
+          if (wr.slot < 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              a.out[row * D + d + i] = f32_to_bf16_rne(lt > 0.0f ? v[i] / lt : 0.0f);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a.part_o[pr * D + d + i] = lt > 0.0f ? v[i] / lt : 0.0f;
+          }
+        }
+        if (wr.slot >= 0 && gq == 0) {
+          a.part_ml[pr * 2] = m[nt];
+          a.part_ml[pr * 2 + 1] = lt;
+        }
+      }
+    }
+  };
+
+  auto compute = [&](const PageRegs<F, P, D>& R, const WorkRange& wr,
+                     int k) __attribute__((always_inline)) {
+    if (R.phys < 0) return;  // absent page: its tokens do not take part
+    const PageMask pm = page_mask<P>(wr, wr.logical(wr.kb0 + k));
+    const bool tail = pm.partial;
+
+    // K operands for all sub-tiles (shared by every head tile).
+    OpA kop[T][KK];
+#pragma unroll
+    for (int st = 0; st < T; ++st) {
+      if constexpr (!Q) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kop[st][kk] = __builtin_bit_cast(bf16x8_t, R.k[st][kk]);
+      } else {
+        uint32_t w[KB / 4];
+        __builtin_memcpy(w, R.k[st], KB);
+        constexpr int DW = F == kI4 ? 1 : 2;  // dwords per 8 channels
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kop[st][kk] = codes8_to_f16x8<F>(w + DW * kk);
+      }
+    }
+    // V^T operands.
+    OpPV vop[NC];
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc) {
+      if constexpr (!Q) {
+        VLoad raw = R.v[nc];
+        if (tail) {
+          // rows past the sequence may hold anything (NaN): zero them so 0*x stays 0
+          uint32_t wv[EV / 2];
+          __builtin_memcpy(wv, &raw, sizeof(raw));
+#pragma unroll
+          for (int e = 0; e < EV; ++e) {
+            if (!pm.valid(EV * gq + e)) wv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          }
+          __builtin_memcpy(&raw, wv, sizeof(raw));
+        }
+        vop[nc] = __builtin_bit_cast(OpPV, raw);
+      } else {
+        uint32_t wv[EV / 4];
+        __builtin_memcpy(wv, &R.v[nc], sizeof(R.v[nc]));
+        OpPV v;
+#pragma unroll
+        for (int i = 0; i < EV / 4; ++i) {
+          f16x2_t lo, hi;
+          if constexpr (F == kI8)
+            i8x4_to_f16x4(wv[i], lo, hi);
+          else if constexpr (F == kFP8)
+            fp8x4_to_f16x4(wv[i], lo, hi);
+          else
+            i4sel4_to_f16x4(wv[i], (r & 1) != 0, lo, hi);
+          v[4 * i + 0] = lo[0];
+          v[4 * i + 1] = lo[1];
+          v[4 * i + 2] = hi[0];
+          v[4 * i + 3] = hi[1];
+        }
+        vop[nc] = v;
+      }
+    }
+    // Per-token scale (and zero point) of this lane's rows.
+    float ks[T][4], kz[T][4], vs[T][4], vz[T][4];
+    if constexpr (Q) {
+#pragma unroll
+      for (int st = 0; st < T; ++st) {
+        const uint32_t kw[4] = {R.km[st].x, R.km[st].y, R.km[st].z, R.km[st].w};
+        const uint32_t vw[4] = {R.vm[st].x, R.vm[st].y, R.vm[st].z, R.vm[st].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ks[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] & 0xffffu)) * FI::scale_mul;
+          kz[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] >> 16));
+          vs[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(vw[i] & 0xffffu)) * FI::scale_mul;
+          vz[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(vw[i] >> 16));
+        }
+      }
+    }
+
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float x[T][4];
+#pragma unroll
+      for (int st = 0; st < T; ++st) {
+        f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) sc = mfma_16x16x32(kop[st][kk], qop[nt][kk], sc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (ZP)
+            x[st][i] = (ks[st][i] * sc[i] + kz[st][i] * qsum[nt]) * a.scale_log2;
+          else if constexpr (Q)
+            x[st][i] = ks[st][i] * sc[i] * a.scale_log2;
+          else
+            x[st][i] = sc[i] * a.scale_log2;
+        }
+      }
+      if (tail) {
+#pragma unroll
+        for (int st = 0; st < T; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!pm.valid(EV * gq + 4 * st + i)) x[st][i] = -INFINITY;
+      }
+      float mloc = x[0][0];
+#pragma unroll
+      for (int st = 0; st < T; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, x[st][i]);
+      mloc = group4_max(mloc);
+      const float mnew = fmaxf(m[nt], mloc);
+      const float al = fast_exp2(m[nt] - mnew);
+      m[nt] = mnew;
+      float p[T][4];
+      float ps = 0.0f;
+#pragma unroll
+      for (int st = 0; st < T; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[st][i] = fast_exp2(x[st][i] - mnew);
+          ps += p[st][i];
+        }
+      lsum[nt] = lsum[nt] * al + ps;
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc) acc[nt][nc] *= al;
+      OpPV pop;
+      if constexpr (Q) {
+        float zs = 0.0f;
+#pragma unroll
+        for (int st = 0; st < T; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool valid = !tail || pm.valid(EV * gq + 4 * st + i);
+            const float pv = valid ? p[st][i] * vs[st][i] : 0.0f;
+            if constexpr (ZP) zs += valid ? p[st][i] * vz[st][i] : 0.0f;
+            pop[4 * st + i] = (_Float16)pv;
+          }
+        zacc[nt] = zacc[nt] * al + zs;
+      } else {
+#pragma unroll
+        for (int st = 0; st < T; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pop[4 * st + i] = (__bf16)p[st][i];
+      }
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc) {
+        if constexpr (T == 1)
+          acc[nt][nc] = mfma_16x16x16(vop[nc], pop, acc[nt][nc]);
+        else
+          acc[nt][nc] = mfma_16x16x32(vop[nc], pop, acc[nt][nc]);
+      }
+    }
+  };
+
+
+  // compute side: every valid item in order (empty ones give 0 or an empty
+  // partial right away); pages in the order they were issued.  Each item's
+  // pages run through a loop whose ring slots are compile-time constants
+  // (like the uniform kernel's), so the load counter waits stay those of a
+  // steady stream; the item's start and end (q loads, result stores) sit
+  // outside that loop.
+  static_assert(DEPTH == 1 || DEPTH == 2, "stream ring of one or two pages");
+  StreamPos cp;
+  cp.item = i_begin;
+  stream_seek<P>(a, cp, end, false);
+  if (issued_all) {  // no pages at all: only empty items
+    for (; cp.item < end; ++cp.item, stream_seek<P>(a, cp, end, false)) {
+      begin_item(cp.wr);
+      finish_item(cp.wr);
+    }
+    return;
+  }
+  PageRegs<F, P, D> ring[DEPTH];
+#pragma unroll
+  for (int s = 0; s < DEPTH; ++s) issue(ring[s]);
+  // pages of the current item, its first page in ring slot S0
+  auto item_pages = [&](auto s0_tag) __attribute__((always_inline)) {
+    constexpr int S0 = decltype(s0_tag)::value;
+    const int cnt = cp.wr.cnt;
+    int k = 0;
+    for (; k + DEPTH <= cnt; k += DEPTH) {
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s) {
+        compute(ring[(S0 + s) % DEPTH], cp.wr, k + s);
+        issue(ring[(S0 + s) % DEPTH]);
+      }
+    }
+    if (k < cnt) {  // DEPTH == 2 and an odd count: one page left, in slot S0
+      compute(ring[S0], cp.wr, k);
+      issue(ring[S0]);
+    }
+  };
+  int slot0 = 0;
+  for (; cp.item < end; ++cp.item, stream_seek<P>(a, cp, end, false)) {
+    begin_item(cp.wr);
+    if (cp.wr.cnt > 0) {
+      if (DEPTH == 1 || slot0 == 0)
+        item_pages(std::integral_constant<int, 0>{});
+      else
+        item_pages(std::integral_constant<int, DEPTH - 1>{});
+      slot0 = (slot0 + cp.wr.cnt) % DEPTH;
+    }
+    finish_item(cp.wr);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -555,8 +995,8 @@ __device__ __forceinline__ float code_to_f32(uint32_t byte_or_nibble) {
   }
 }
 
-template <int F, int P, int D, int G, int DEPTH>
-__global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(DecodeArgs a) {
+template <int F, int P, int D, int G, int DEPTH, bool SCHED>
+__device__ __forceinline__ void valu_item(const DecodeArgs& a, const WorkRange& wr, float* smem) {
   using FI = FmtInfo<F>;
   constexpr bool Q = FI::quant, ZP = FI::zero;
   constexpr int TPL = P / 16;             // token rows per lane
@@ -571,13 +1011,11 @@ __global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(
   constexpr int VBT = F == kI4 ? P : DV * P * FI::bits / 8;
   constexpr int VL = VBT / 16;
   using KLoad = typename LoadT<KLB>::type;
-  extern __shared__ float smem[];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
   const int tr = lane >> 2, c = lane & 3;
-  const WorkRange wr = work_range<P>(a, wave, W);
   const int H = a.num_kv_heads;
   float* sm_o = smem;                  // [W][G][D]
   float* sm_m = smem + W * G * D;      // [W][G]
@@ -789,23 +1227,39 @@ __global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(
     }
   }
   __syncthreads();
-  combine_and_store<D>(a, wr, sm_o, sm_m, sm_l, W, G);
+  combine_and_store<D, SCHED>(a, wr, sm_o, sm_m, sm_l, W, G);
+}
+
+template <int F, int P, int D, int G, int DEPTH, bool SCHED>
+__global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(DecodeArgs a) {
+  extern __shared__ float smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
+  if constexpr (!SCHED) {
+    valu_item<F, P, D, G, DEPTH, false>(a, work_range<P>(a, wave, W), smem);
+  } else {
+    const int i0 = max(a.sched[8 + blockIdx.x], 0);
+    const int i1 = min(a.sched[9 + blockIdx.x], a.num_items);
+    for (int i = i0; i < i1; ++i) {
+      if (!item_valid(a, i)) continue;
+      valu_item<F, P, D, G, DEPTH, true>(a, item_range<P>(a, i, wave, W), smem);
+      __syncthreads();  // the next item reuses the LDS merge and probability buffers
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the split partials: one wavefront per (sequence, query
-// head).  M = max_s m_s; w_s = l_s 2^(m_s - M); out = sum_s w_s o_s / sum_s w_s.
+// Log-sum-exp merge of split partials, one wavefront per output row:
+// M = max_s m_s; w_s = l_s 2^(m_s - M); out = sum_s w_s o_s / sum_s w_s.
+// Partial s of the row: o at po + s*so (D floats), (m, l) at pml + s*sml.
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
-                                                    const float* __restrict__ part_ml,
-                                                    uint16_t* __restrict__ out, int rows, int S) {
+__device__ __forceinline__ void lse_merge_row(const float* __restrict__ po, int64_t so,
+                                              const float* __restrict__ pml, int64_t sml, int S,
+                                              uint16_t* __restrict__ out_row) {
   constexpr int E = D / 64;
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const float* ml = part_ml + int64_t(row) * S * 2;
   float M = -INFINITY;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, pml[s * sml]);
   M = wave_max(M);
   float o[E];
 #pragma unroll
@@ -813,19 +1267,52 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   float L = 0.0f;
   if (M != -INFINITY) {
     for (int s = 0; s < S; ++s) {
-      const float ms = ml[2 * s], ls = ml[2 * s + 1];
+      const float ms = pml[s * sml], ls = pml[s * sml + 1];
       if (ls > 0.0f) {
         const float w = ls * fast_exp2(ms - M);
         L += w;
-        const float* po = part_o + (int64_t(row) * S + s) * D + lane * E;
+        const float* p = po + s * so + lane * E;
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] += w * po[e];
+        for (int e = 0; e < E; ++e) o[e] += w * p[e];
       }
     }
   }
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    out[int64_t(row) * D + lane * E + e] = f32_to_bf16_rne(L > 0.0f ? o[e] / L : 0.0f);
+  for (int e = 0; e < E; ++e) out_row[lane * E + e] = f32_to_bf16_rne(L > 0.0f ? o[e] / L : 0.0f);
+}
+
+// Uniform plan: row = b*H_q + j holds its S partials at (row*S + s).
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_ml,
+                                                    uint16_t* __restrict__ out, int rows, int S) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  lse_merge_row<D>(part_o + int64_t(row) * S * D, D, part_ml + int64_t(row) * S * 2, 2, S,
+                   out + int64_t(row) * D);
+}
+
+// Balanced schedule: merge entry e = (sequence, KV head, first slot, count);
+// query head j of its group has partial (slot*g + j) for each of its slots.
+template <int D>
+__global__ __launch_bounds__(256) void merge_sched_kernel(const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_ml,
+                                                          const int32_t* __restrict__ entries,
+                                                          uint16_t* __restrict__ out, int rows,
+                                                          int g, int num_q_heads, int num_seqs,
+                                                          int num_slots) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int e = row / g, j = row - e * g;
+  const int32_t* m = entries + int64_t(e) * 4;
+  const int b = m[0], h = m[1], first = m[2], cnt = m[3];
+  // entries that name rows or slots outside this call are skipped
+  if (unsigned(b) >= unsigned(num_seqs) || unsigned(h) >= unsigned(num_q_heads / g) ||
+      first < 0 || cnt < 1 || int64_t(first) + cnt > num_slots)
+    return;
+  const int64_t p0 = int64_t(first) * g + j;
+  lse_merge_row<D>(part_o + p0 * D, int64_t(g) * D, part_ml + p0 * 2, int64_t(g) * 2, cnt,
+                   out + (int64_t(b) * num_q_heads + int64_t(h) * g + j) * D);
 }
 
 // ---------------------------------------------------------------------------
@@ -844,39 +1331,65 @@ int cu_count_current_device() {
   return n;
 }
 
-template <int F, int P, int D>
+template <int F, int P, int D, bool SCHED>
 hipError_t launch_decode_pd(const DecodeArgs& a, bool mfma, int g, dim3 grid, dim3 block,
                             size_t lds, hipStream_t s) {
+  discard_stale_error();
   const int nt = g <= 16 ? 1 : g <= 32 ? 2 : 4;
   const int max_threads = mfma ? mfma_max_threads(P, D, nt) : valu_max_threads(P, D, g);
   if (int(block.x) > max_threads) return hipErrorInvalidConfiguration;
   if (mfma) {
-    if (g <= 16)
-      hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 1, kDepth>), grid, block, lds, s, a);
-    else if (g <= 32)
-      hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 2, kDepth>), grid, block, lds, s, a);
-    else
-      hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 4, kDepth>), grid, block, lds, s, a);
+    // balanced schedule: one stream per wavefront, no LDS
+    if constexpr (SCHED) {
+      if (g <= 16)
+        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 1, kDepth>), grid, block, 0, s, a);
+      else if (g <= 32)
+        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 2, kDepth>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 4, kDepth>), grid, block, 0, s, a);
+    } else {
+      if (g <= 16)
+        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 1, kDepth>), grid, block, lds, s, a);
+      else if (g <= 32)
+        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 2, kDepth>), grid, block, lds, s, a);
+      else
+        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 4, kDepth>), grid, block, lds, s, a);
+    }
   } else {
     if (g == 1)
-      hipLaunchKernelGGL((decode_valu_kernel<F, P, D, 1, kDepth>), grid, block, lds, s, a);
+      hipLaunchKernelGGL((decode_valu_kernel<F, P, D, 1, kDepth, SCHED>), grid, block, lds, s,
+                         a);
     else if (g == 2)
-      hipLaunchKernelGGL((decode_valu_kernel<F, P, D, 2, kDepth>), grid, block, lds, s, a);
+      hipLaunchKernelGGL((decode_valu_kernel<F, P, D, 2, kDepth, SCHED>), grid, block, lds, s,
+                         a);
     else
-      hipLaunchKernelGGL((decode_valu_kernel<F, P, D, 3, kDepth>), grid, block, lds, s, a);
+      hipLaunchKernelGGL((decode_valu_kernel<F, P, D, 3, kDepth, SCHED>), grid, block, lds, s,
+                         a);
   }
   return hipGetLastError();
 }
 
 // Instance for the pool's (page size, head dim); the descriptor was validated.
-template <int F>
+template <int F, bool SCHED>
 hipError_t launch_decode_fmt(const DecodeArgs& a, int P, int D, bool mfma, int g, dim3 grid,
                              dim3 block, size_t lds, hipStream_t s) {
   if (P == 16)
-    return D == 64 ? launch_decode_pd<F, 16, 64>(a, mfma, g, grid, block, lds, s)
-                   : launch_decode_pd<F, 16, 128>(a, mfma, g, grid, block, lds, s);
-  return D == 64 ? launch_decode_pd<F, 32, 64>(a, mfma, g, grid, block, lds, s)
-                 : launch_decode_pd<F, 32, 128>(a, mfma, g, grid, block, lds, s);
+    return D == 64 ? launch_decode_pd<F, 16, 64, SCHED>(a, mfma, g, grid, block, lds, s)
+                   : launch_decode_pd<F, 16, 128, SCHED>(a, mfma, g, grid, block, lds, s);
+  return D == 64 ? launch_decode_pd<F, 32, 64, SCHED>(a, mfma, g, grid, block, lds, s)
+                 : launch_decode_pd<F, 32, 128, SCHED>(a, mfma, g, grid, block, lds, s);
+}
+
+template <bool SCHED>
+hipError_t launch_decode_dtype(const DecodeArgs& a, int dtype, int P, int D, bool mfma, int g,
+                               dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+  switch (dtype) {
+    case KVP_BF16: return launch_decode_fmt<kBF16, SCHED>(a, P, D, mfma, g, grid, block, lds, s);
+    case KVP_INT8: return launch_decode_fmt<kI8, SCHED>(a, P, D, mfma, g, grid, block, lds, s);
+    case KVP_INT4: return launch_decode_fmt<kI4, SCHED>(a, P, D, mfma, g, grid, block, lds, s);
+    case KVP_FP8: return launch_decode_fmt<kFP8, SCHED>(a, P, D, mfma, g, grid, block, lds, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace kvp
@@ -893,6 +1406,7 @@ size_t partials_bytes(size_t parts, int D) {
 
 hipError_t launch_merge(const float* part_o, const float* part_ml, uint16_t* out, int rows, int S,
                         int D, hipStream_t s) {
+  kvp::discard_stale_error();
   const dim3 mg(static_cast<unsigned>((rows + 3) / 4));
   if (D == 128)
     hipLaunchKernelGGL((kvp::merge_kernel<128>), mg, dim3(256), 0, s, part_o, part_ml, out, rows, S);
@@ -955,7 +1469,9 @@ kvp_status launch_split_kernel(const kvp_pool_desc& d, const kvp_decode_plan_t& 
                                const int32_t* context_lens, int32_t num_seqs,
                                int32_t num_q_heads, int32_t max_context_len, float scale,
                                int32_t sink_tokens, int32_t window_tokens,
-                               void* out, float* part_o, float* part_ml, hipStream_t s) {
+                               void* out, float* part_o, float* part_ml, hipStream_t s,
+                               const kvp_schedule_info* sched_info = nullptr,
+                               const int32_t* sched = nullptr) {
   using namespace kvp;
   const int g = num_q_heads / d.num_kv_heads;
   DecodeArgs a;
@@ -982,23 +1498,28 @@ kvp_status launch_split_kernel(const kvp_pool_desc& d, const kvp_decode_plan_t& 
   a.window_tokens = window_tokens;
   a.write_partials = part_o != nullptr;
   a.scale_log2 = scale * kLog2e;
+  a.sched = sched;
+  a.items_off = sched ? sched_info->items_offset : 0;
+  a.num_items = sched ? sched_info->num_items : 0;
+  a.num_slots = sched ? sched_info->num_slots : 0;
+  a.num_bins = sched ? sched_info->num_bins : 0;
 
   const int W = plan.waves_per_group;
   const int HP = plan.use_mfma ? ((g + 15) / 16) * 16 : g;
   size_t lds = size_t(W) * (size_t(g) * d.head_dim + 2 * HP) * sizeof(float);
   if (!plan.use_mfma) lds += size_t(W) * g * d.page_size * sizeof(float);
-  const int64_t wgs = int64_t(num_seqs) * d.num_kv_heads * plan.num_splits;
+  // balanced schedule: a bin is a wavefront on the matrix-core path, a
+  // workgroup on the vector path
+  const int64_t wgs =
+      !sched ? int64_t(num_seqs) * d.num_kv_heads * plan.num_splits
+             : (plan.use_mfma ? (int64_t(sched_info->num_bins) + W - 1) / W
+                              : int64_t(sched_info->num_bins));
   const dim3 grid(static_cast<unsigned>(wgs)), block(static_cast<unsigned>(W * 64));
   const int P = d.page_size, D = d.head_dim;
   const bool mf = plan.use_mfma;
-  hipError_t e;
-  switch (d.dtype) {
-    case KVP_BF16: e = launch_decode_fmt<kBF16>(a, P, D, mf, g, grid, block, lds, s); break;
-    case KVP_INT8: e = launch_decode_fmt<kI8>(a, P, D, mf, g, grid, block, lds, s); break;
-    case KVP_INT4: e = launch_decode_fmt<kI4>(a, P, D, mf, g, grid, block, lds, s); break;
-    case KVP_FP8: e = launch_decode_fmt<kFP8>(a, P, D, mf, g, grid, block, lds, s); break;
-    default: return KVP_E_INVAL;
-  }
+  const hipError_t e =
+      sched ? launch_decode_dtype<true>(a, d.dtype, P, D, mf, g, grid, block, lds, s)
+            : launch_decode_dtype<false>(a, d.dtype, P, D, mf, g, grid, block, lds, s);
   return e == hipSuccess ? KVP_OK : KVP_E_HIP;
 }
 
@@ -1157,4 +1678,56 @@ extern "C" kvp_status kvp_lse_merge(const void* partials, int32_t rows, int32_t 
                       reinterpret_cast<hipStream_t>(stream)) == hipSuccess
              ? KVP_OK
              : KVP_E_HIP;
+}
+
+extern "C" kvp_status kvp_paged_attention_decode_scheduled(
+    const kvp_pool* pool, const void* q, const void* k_pool, const void* v_pool,
+    const void* k_meta, const void* v_meta, const int32_t* block_tables, int32_t max_blocks,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    float scale, const int32_t* sched, const kvp_schedule_info* info, void* out,
+    void* workspace, size_t workspace_bytes, kvp_stream_t stream) {
+  if (!info) return KVP_E_INVAL;
+  kvp_pool_desc d;
+  kvp_decode_plan_t plan;
+  bool empty;
+  kvp_status st = prepare_decode(pool, q, k_pool, v_pool, k_meta, v_meta, block_tables,
+                                 max_blocks, context_lens, num_seqs, num_q_heads,
+                                 max_context_len, scale, 1, info->sink_tokens,
+                                 info->window_tokens, &d, &plan, &empty);
+  if (st != KVP_OK || empty) return st;
+  if (!out || !sched) return KVP_E_INVAL;
+  const int64_t bins = info->num_bins, items = info->num_items;
+  if (bins < 1 || items < 0 || info->num_merge < 0 || info->num_slots < 0 ||
+      info->items_offset < 8 + bins + 1 ||
+      int64_t(info->merge_offset) != info->items_offset + 8 * items)
+    return KVP_E_INVAL;
+  const int g = num_q_heads / d.num_kv_heads;
+  const size_t slots = size_t(info->num_slots);
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (info->num_merge > 0) {
+    const size_t o_bytes = (slots * g * d.head_dim * sizeof(float) + 255) & ~size_t(255);
+    if (!workspace || workspace_bytes < o_bytes + slots * g * 2 * sizeof(float))
+      return KVP_E_INVAL;
+    part_o = static_cast<float*>(workspace);
+    part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = launch_split_kernel(d, plan, q, k_pool, v_pool, k_meta, v_meta, block_tables, max_blocks,
+                           context_lens, num_seqs, num_q_heads, max_context_len, scale,
+                           info->sink_tokens, info->window_tokens, out, part_o, part_ml, s, info,
+                           sched);
+  if (st != KVP_OK || info->num_merge == 0) return st;
+  const int rows = info->num_merge * g;
+  const dim3 mg(static_cast<unsigned>((rows + 3) / 4));
+  const int32_t* entries = sched + info->merge_offset;
+  kvp::discard_stale_error();
+  uint16_t* o16 = static_cast<uint16_t*>(out);
+  if (d.head_dim == 128)
+    hipLaunchKernelGGL((kvp::merge_sched_kernel<128>), mg, dim3(256), 0, s, part_o, part_ml,
+                       entries, o16, rows, g, num_q_heads, num_seqs, info->num_slots);
+  else
+    hipLaunchKernelGGL((kvp::merge_sched_kernel<64>), mg, dim3(256), 0, s, part_o, part_ml,
+                       entries, o16, rows, g, num_q_heads, num_seqs, info->num_slots);
+  return hipGetLastError() == hipSuccess ? KVP_OK : KVP_E_HIP;
 }

@@ -6,6 +6,12 @@
 
 namespace kvp {
 
+// The runtime keeps the last error of any earlier call on this thread until
+// it is read; errors the caller's own calls left behind are not a launch
+// failure of this library, so they are read (and dropped) before launching.
+inline void discard_stale_error() { (void)hipGetLastError(); }
+
+
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;

@@ -359,6 +359,7 @@ constexpr int kPrefillDepth = 2;
 
 template <bool INT8, int P, int D>
 hipError_t launch_prefill_pd(const PrefillArgs& a, int nt, dim3 grid, hipStream_t s) {
+  discard_stale_error();
   if (nt == 1)
     hipLaunchKernelGGL((prefill_mfma_kernel<INT8, P, D, 1, kPrefillDepth>), grid, dim3(256), 0, s, a);
   else

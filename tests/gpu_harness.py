@@ -111,5 +111,31 @@ class GpuCase:
         torch.cuda.synchronize()
         return out.cpu().numpy().view(np.uint16)
 
+    def decode_scheduled(self, max_bins=None, sink=0, window=0, ctx_host=None, q=None,
+                         max_context_len=None) -> np.ndarray:
+        """The decode (window decode when window > 0) along a balanced
+        schedule built from the host lengths (the case's, or ctx_host); by
+        default four bins per compute unit."""
+        c = self.case
+        q = self.q if q is None else q
+        ctx = c.ctx if ctx_host is None else ctx_host
+        if max_bins is None:
+            max_bins = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+        mx = int(ctx.max()) if max_context_len is None else int(max_context_len)
+        sched = self.kvp.kvp_decode_schedule(self.pool, ctx, c.cfg.num_q_heads,
+                                             int(self.bt_host.shape[1]), max_bins, sink, window)
+        sdev = dev32(sched.used, self.device)
+        ws = None
+        if sched.info.workspace_bytes:
+            ws = torch.full((sched.info.workspace_bytes // 4 + 1,), float("nan"),
+                            dtype=torch.float32, device=self.device)
+        out = _fill16(q.numel(), POISON_BF16, self.device).view(q.shape)
+        self.kvp.kvp_paged_attention_decode_scheduled(
+            self.pool, q, self.k_pool, self.v_pool, self.k_meta, self.v_meta, self.bt,
+            dev32(ctx, self.device), mx, float(c.scale), sdev, sched, out, workspace=ws)
+        torch.cuda.synchronize()
+        self.last_schedule = sched
+        return out.cpu().numpy().view(np.uint16)
+
     def close(self):
         self.pool.close()

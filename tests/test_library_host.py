@@ -414,3 +414,101 @@ def test_host_prefix_cache_under_sanitizers(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip() == "ok"
+
+
+# ---- balanced decode schedule (host) ------------------------------------------------
+def _parse_schedule(words):
+    nb, ni, nm, ns, ioff, moff = (int(x) for x in words[:6])
+    starts = words[8:8 + nb + 1]
+    items = words[ioff:ioff + 8 * ni].reshape(ni, 8)
+    merge = words[moff:moff + 4 * nm].reshape(nm, 4)
+    return nb, ns, starts, items, merge
+
+
+def _streamed_blocks(n, P, sink, window):
+    nblk = -(-n // P)
+    if window <= 0:
+        return nblk
+    return nblk - len(oracle.window_evicted_blocks(n, P, sink, window))
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("sink,window", [(0, 0), (4, 300), (0, 17)])
+def test_decode_schedule_covers_every_block_once(kvp, seed, sink, window):
+    """Every (sequence, KV head) pair's streamed blocks are covered exactly once,
+    in order, by consecutive items; a pair cut across bins has consecutive
+    partial slots and one merge entry naming them; bins differ by at most one
+    block; a pair within one bin writes its output (slot -1)."""
+    rng = np.random.default_rng(100 + seed)
+    P = (16, 32)[seed % 2]
+    H = (1, 2, 8)[seed % 3]
+    B = int(rng.integers(1, 70))
+    kind = seed % 3
+    if kind == 0:
+        ctx = rng.integers(0, 3000, B)
+    elif kind == 1:
+        ctx = np.full(B, int(rng.integers(1, 5000)))
+    else:
+        ctx = np.where(rng.random(B) < 0.3, 0, rng.integers(1, 40000, B))
+    max_blocks = int(-(-max(int(ctx.max()), 1) // P))
+    cus = int(rng.choice([8, 80, 256]))
+    pool = kvp.kvp_pool_create(kvp.make_desc(16, P, H, 128, "bf16"))
+    s = kvp.kvp_decode_schedule(pool, ctx.astype(np.int32), 4 * H, max_blocks, cus, sink, window)
+    nb, ns, starts, items, merge = _parse_schedule(s.words)
+    nv = np.array([_streamed_blocks(int(n), P, sink, window) for n in ctx])
+    T = int(nv.sum()) * H
+    assert nb == max(1, min(cus, -(-T // 8)))
+    assert starts[0] == 0 and starts[-1] == len(items) and (np.diff(starts) >= 0).all()
+    loads = [int((items[starts[k]:starts[k + 1], 3] - items[starts[k]:starts[k + 1], 2]).sum())
+             for k in range(nb)]
+    assert sum(loads) == T
+    assert max(loads) - min(loads) <= 1 if T >= nb else True
+    seen = {}
+    for it in items:
+        seen.setdefault((int(it[0]), int(it[1])), []).append(it)
+    assert set(seen) == {(b, h) for b in range(B) for h in range(H)}
+    merged = {(int(m[0]), int(m[1])): (int(m[2]), int(m[3])) for m in merge}
+    for (b, h), its in seen.items():
+        pos = 0
+        for it in its:
+            assert it[2] == pos and it[3] >= it[2]
+            pos = int(it[3])
+        assert pos == nv[b]
+        if len(its) == 1:
+            assert its[0][4] == -1 and (b, h) not in merged
+        else:
+            slots = [int(it[4]) for it in its]
+            assert slots == list(range(slots[0], slots[0] + len(its)))
+            assert merged[(b, h)] == (slots[0], len(its))
+            assert all(it[3] > it[2] for it in its)
+    assert s.info.num_slots == ns == sum(c for _, c in merged.values())
+    assert ns <= 2 * nb
+    pool.close()
+
+
+def test_decode_schedule_equal_lengths_need_no_merge(kvp):
+    """32 sequences of 8,192 tokens, 8 KV heads, P = 16 on 256 compute units:
+    one pair per bin, no partials, no workspace."""
+    pool = kvp.kvp_pool_create(kvp.make_desc(16, 16, 8, 128, "bf16"))
+    s = kvp.kvp_decode_schedule(pool, np.full(32, 8192, np.int32), 64, 512, 256)
+    assert (s.info.num_bins, s.info.num_items, s.info.num_merge, s.info.workspace_bytes) == \
+        (256, 256, 0, 0)
+    pool.close()
+
+
+def test_decode_schedule_rejects_bad_arguments(kvp):
+    pool = kvp.kvp_pool_create(kvp.make_desc(16, 16, 2, 64, "bf16"))
+    for ctx, mb in (([5, -1], 4), ([5, 65], 4)):
+        with pytest.raises(kvp.KvpError):
+            kvp.kvp_decode_schedule(pool, np.array(ctx, np.int32), 4, mb, 8)
+    from paged_kv_cache_465_amd import _lib
+    L = _lib.load()
+    info = _lib.ScheduleInfo()
+    ctx = np.array([10, 20], np.int32)
+    small = np.zeros(4, np.int32)
+    import ctypes
+    st = L.kvp_decode_schedule(pool.handle, ctx.ctypes.data_as(_lib.P_int32), 2, 4, 4, 0, 0, 8,
+                               small.ctypes.data_as(_lib.P_int32), small.nbytes,
+                               ctypes.byref(info))
+    assert st == kvp.KVP_E_INVAL
+    pool.close()
