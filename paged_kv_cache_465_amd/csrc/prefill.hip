@@ -20,6 +20,11 @@
 // a workgroup read the same pages at the same time, and all tiles of one
 // (sequence, KV head) are placed on the same XCD, so page loads are ordinary
 // (cacheable) loads that the tiles share through that XCD's L2.
+//
+// Short chunks (all rows of an item fit one wavefront, e.g. a few drafted
+// tokens to verify): the four wavefronts each take all rows and a quarter of
+// the pages instead, and wavefront 0 merges the four (m, l, o) partials
+// through LDS, so no wavefront idles while one streams every page.
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
@@ -44,7 +49,7 @@ struct PrefillArgs {
   float scale_log2;
 };
 
-template <bool INT8, int P, int D, int NT, int DEPTH>
+template <bool INT8, int P, int D, int NT, int DEPTH, bool SPLIT>
 __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int T = P / 16, KK = D / 32, NC = D / 16, EV = 4 * T;
   constexpr int EB = INT8 ? 1 : 2;
@@ -76,12 +81,18 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
   const int qlen = a.q_start[b + 1] - q0;
   const int ctx = min(max(a.ctx_lens[b], 0), a.ctx_cap);
   const int rows = qlen * g;
-  const int row0 = tile * 4 * ROWS_WAVE + wave * ROWS_WAVE;
-  if (qlen <= 0 || row0 >= rows) return;  // whole wavefront idle (no workgroup barriers below)
+  const int row0 = SPLIT ? 0 : tile * 4 * ROWS_WAVE + wave * ROWS_WAVE;
+  // whole wavefront (tiled) or workgroup (split: b is the workgroup's) idle;
+  // the only barrier below is the split mode's, reached by all or none
+  if (qlen <= 0 || row0 >= rows) return;
   const int row_last = min(row0 + ROWS_WAVE, rows) - 1;
   const int first_pos = ctx - qlen;       // position of chunk row 0
   const int pos_last = min(first_pos + row_last / g, ctx - 1);
-  const int nblk = pos_last >= 0 ? pos_last / P + 1 : 0;
+  const int nblk_all = pos_last >= 0 ? pos_last / P + 1 : 0;
+  // blocks [kb0, kb0 + nblk) of this wavefront: all, or a quarter (split)
+  const int cw = SPLIT ? (nblk_all + 3) / 4 : nblk_all;
+  const int kb0 = SPLIT ? min(wave * cw, nblk_all) : 0;
+  const int nblk = SPLIT ? max(0, min(cw, nblk_all - kb0)) : nblk_all;
 
   // This lane's row in each tile: its query (B operand of S^T = K q^T) and
   // its causal limit (positions <= lim take part).
@@ -146,14 +157,26 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     const int64_t t = int64_t(ok ? phys : 0) * H + h;
     const char* kp = kbase + t * tile_bytes;
     const char* vp = vbase + t * tile_bytes;
+    // tiled: the workgroup's wavefronts share each page through L2 (ordinary
+    // loads); split: each page is read once (non-temporal loads)
+    if constexpr (!SPLIT) {
 #pragma unroll
-    for (int st = 0; st < T; ++st)
+      for (int st = 0; st < T; ++st)
 #pragma unroll
-      for (int i = 0; i < KL; ++i)
-        R.k[st][i] = *reinterpret_cast<const uint4*>(kp + koff[st] + i * (INT8 ? 16 : 64));
+        for (int i = 0; i < KL; ++i)
+          R.k[st][i] = *reinterpret_cast<const uint4*>(kp + koff[st] + i * (INT8 ? 16 : 64));
 #pragma unroll
-    for (int nc = 0; nc < NC; ++nc)
-      R.v[nc] = *reinterpret_cast<const VLoad*>(vp + voff + nc * 16 * P * EB);
+      for (int nc = 0; nc < NC; ++nc)
+        R.v[nc] = *reinterpret_cast<const VLoad*>(vp + voff + nc * 16 * P * EB);
+    } else {
+#pragma unroll
+      for (int st = 0; st < T; ++st)
+#pragma unroll
+        for (int i = 0; i < KL; ++i)
+          R.k[st][i] = load_stream<uint4>(kp + koff[st] + i * (INT8 ? 16 : 64));
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc) R.v[nc] = load_stream<VLoad>(vp + voff + nc * 16 * P * EB);
+    }
     if constexpr (INT8) {
       const char* km = reinterpret_cast<const char*>(a.k_meta) + t * (P * 4);
       const char* vm = reinterpret_cast<const char*>(a.v_meta) + t * (P * 4);
@@ -319,22 +342,76 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
   if (nblk > 0) {
     Regs ring[DEPTH];
 #pragma unroll
-    for (int s = 0; s < DEPTH; ++s) issue(ring[s], min(s, nblk - 1));
+    for (int s = 0; s < DEPTH; ++s) issue(ring[s], kb0 + min(s, nblk - 1));
     for (int k0 = 0; k0 < nblk; k0 += DEPTH) {
 #pragma unroll
       for (int s = 0; s < DEPTH; ++s) {
         const int k = k0 + s;
-        if (k < nblk) compute(ring[s], k);
-        issue(ring[s], min(k + DEPTH, nblk - 1));
+        if (k < nblk) compute(ring[s], kb0 + k);
+        issue(ring[s], kb0 + min(k + DEPTH, nblk - 1));
       }
     }
   }
 
+  if constexpr (SPLIT) {
+    // waves 1..3 leave (o, m, l) of their pages in LDS, in the matrix-core
+    // register layout; wave 0 merges them into its own and writes the rows
+    __shared__ f32x4_t sm_o[3][NT][NC][64];
+    __shared__ float sm_m[3][NT][64], sm_l[3][NT][64];
+    if (wave > 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float lt = group4_sum(lsum[nt]);
+        const float zt = INT8 ? group4_sum(zacc[nt]) : 0.0f;
+#pragma unroll
+        for (int nc = 0; nc < NC; ++nc) {
+          f32x4_t v = acc[nt][nc];
+          if constexpr (INT8) v += zt;
+          sm_o[wave - 1][nt][nc][lane] = v;
+        }
+        sm_m[wave - 1][nt][lane] = m[nt];
+        sm_l[wave - 1][nt][lane] = lt;
+      }
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float l0 = group4_sum(lsum[nt]);
+      const float z0 = INT8 ? group4_sum(zacc[nt]) : 0.0f;
+      float M = m[nt];
+#pragma unroll
+      for (int w = 0; w < 3; ++w) M = fmaxf(M, sm_m[w][nt][lane]);
+      // weights of the four partials (0 for one that saw no position)
+      float f[4];
+      f[0] = m[nt] == -INFINITY ? 0.0f : fast_exp2(m[nt] - M);
+#pragma unroll
+      for (int w = 0; w < 3; ++w) {
+        const float mw = sm_m[w][nt][lane];
+        f[w + 1] = mw == -INFINITY ? 0.0f : fast_exp2(mw - M);
+      }
+      float L = l0 * f[0];
+#pragma unroll
+      for (int w = 0; w < 3; ++w) L += sm_l[w][nt][lane] * f[w + 1];
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc) {
+        f32x4_t v = acc[nt][nc];
+        if constexpr (INT8) v += z0;
+        v *= f[0];
+#pragma unroll
+        for (int w = 0; w < 3; ++w) v += sm_o[w][nt][nc][lane] * f[w + 1];
+        acc[nt][nc] = v;
+      }
+      lsum[nt] = L;  // merged row sum (already over the four lane groups)
+    }
+  }
+
   // Finalize: each lane's row is its own; out = acc / l (bfloat16, RNE).
+  // (Split mode: acc and lsum already hold the merged sums, zero terms in.)
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const float lt = group4_sum(lsum[nt]);
-    const float zt = INT8 ? group4_sum(zacc[nt]) : 0.0f;
+    const float lt = SPLIT ? lsum[nt] : group4_sum(lsum[nt]);
+    const float zt = (INT8 && !SPLIT) ? group4_sum(zacc[nt]) : 0.0f;
     const int mrow = row0 + nt * 16 + r;
     if (mrow < rows) {
       const int i = mrow / g, j = mrow - (mrow / g) * g;
@@ -358,12 +435,23 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
 constexpr int kPrefillDepth = 2;
 
 template <bool INT8, int P, int D>
-hipError_t launch_prefill_pd(const PrefillArgs& a, int nt, dim3 grid, hipStream_t s) {
+hipError_t launch_prefill_pd(const PrefillArgs& a, int nt, bool split, dim3 grid, hipStream_t s) {
   discard_stale_error();
-  if (nt == 1)
-    hipLaunchKernelGGL((prefill_mfma_kernel<INT8, P, D, 1, kPrefillDepth>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((prefill_mfma_kernel<INT8, P, D, 2, kPrefillDepth>), grid, dim3(256), 0, s, a);
+  if (split) {
+    if (nt == 1)
+      hipLaunchKernelGGL((prefill_mfma_kernel<INT8, P, D, 1, kPrefillDepth, true>), grid,
+                         dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_mfma_kernel<INT8, P, D, 2, kPrefillDepth, true>), grid,
+                         dim3(256), 0, s, a);
+  } else {
+    if (nt == 1)
+      hipLaunchKernelGGL((prefill_mfma_kernel<INT8, P, D, 1, kPrefillDepth, false>), grid,
+                         dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_mfma_kernel<INT8, P, D, 2, kPrefillDepth, false>), grid,
+                         dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -392,10 +480,12 @@ extern "C" kvp_status kvp_paged_attention_prefill(
   if (d.dtype != KVP_BF16 && d.dtype != KVP_INT8) return KVP_E_UNSUPPORTED;
   const bool int8 = d.dtype == KVP_INT8;
   if (int8 != (k_meta != nullptr) || int8 != (v_meta != nullptr)) return KVP_E_INVAL;
-  // rows per wavefront: 32 when the longest chunk has at least that many rows
+  // rows per wavefront: 32 when the longest chunk has at least that many rows;
+  // chunks whose rows fit one wavefront split the pages across the four
   const int64_t max_rows = int64_t(max_q_len) * g;
-  const int nt = max_rows >= 32 * 4 ? 2 : 1;
-  const int64_t rows_wg = 4 * 16 * nt;
+  const bool split = max_rows <= 32;
+  const int nt = split ? (max_rows > 16 ? 2 : 1) : (max_rows >= 32 * 4 ? 2 : 1);
+  const int64_t rows_wg = split ? 16 * nt : 4 * 16 * nt;
   const int64_t tiles = (max_rows + rows_wg - 1) / rows_wg;
   const int64_t items = int64_t(num_seqs) * d.num_kv_heads;
   const int64_t wgs = (items + 7) / 8 * 8 * tiles;
@@ -424,14 +514,14 @@ extern "C" kvp_status kvp_paged_attention_prefill(
   hipError_t e;
   const int key = (d.page_size == 32) * 4 + (d.head_dim == 128) * 2 + int8;
   switch (key) {
-    case 0: e = launch_prefill_pd<false, 16, 64>(a, nt, grid, s); break;
-    case 1: e = launch_prefill_pd<true, 16, 64>(a, nt, grid, s); break;
-    case 2: e = launch_prefill_pd<false, 16, 128>(a, nt, grid, s); break;
-    case 3: e = launch_prefill_pd<true, 16, 128>(a, nt, grid, s); break;
-    case 4: e = launch_prefill_pd<false, 32, 64>(a, nt, grid, s); break;
-    case 5: e = launch_prefill_pd<true, 32, 64>(a, nt, grid, s); break;
-    case 6: e = launch_prefill_pd<false, 32, 128>(a, nt, grid, s); break;
-    default: e = launch_prefill_pd<true, 32, 128>(a, nt, grid, s); break;
+    case 0: e = launch_prefill_pd<false, 16, 64>(a, nt, split, grid, s); break;
+    case 1: e = launch_prefill_pd<true, 16, 64>(a, nt, split, grid, s); break;
+    case 2: e = launch_prefill_pd<false, 16, 128>(a, nt, split, grid, s); break;
+    case 3: e = launch_prefill_pd<true, 16, 128>(a, nt, split, grid, s); break;
+    case 4: e = launch_prefill_pd<false, 32, 64>(a, nt, split, grid, s); break;
+    case 5: e = launch_prefill_pd<true, 32, 64>(a, nt, split, grid, s); break;
+    case 6: e = launch_prefill_pd<false, 32, 128>(a, nt, split, grid, s); break;
+    default: e = launch_prefill_pd<true, 32, 128>(a, nt, split, grid, s); break;
   }
   return e == hipSuccess ? KVP_OK : KVP_E_HIP;
 }

@@ -554,6 +554,11 @@ PREFILL = prefill_cases() + [
             ctx_hi=400, q_len=3, q_len_hi=40),
     variant(SHARED_PREFIX_MQA, name="prefix_chunk7", batch=4, shared_prefix=64,
             ctx_fixed=(101, 80, 97, 129), q_len=7),
+    # chunks whose rows fit one wavefront (<= 32): pages split across the four
+    variant(INT8_LONG, name="int8_verify8", batch=3, ctx_lo=50, ctx_hi=1500, q_len=8),
+    variant(LLAMA3_8B_LAYER, name="l8b_verify_g8", batch=4, num_q_heads=64, ctx_lo=8,
+            ctx_hi=900, q_len=3, q_len_hi=4),
+    variant(LLAMA3_8B_LAYER, name="l8b_verify_g4_long", batch=2, ctx_fixed=(4093, 37), q_len=4),
 ]
 
 
