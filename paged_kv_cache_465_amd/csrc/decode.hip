@@ -516,8 +516,12 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const WorkRange& 
           ps += p[st][i];
         }
       lsum[nt] = lsum[nt] * al + ps;
+      // once the running maximum settles, al is exactly 1 for every head:
+      // skip the (identity) rescale of the accumulators
+      if (wave_any(al != 1.0f)) {
 #pragma unroll
-      for (int nc = 0; nc < NC; ++nc) acc[nt][nc] *= al;
+        for (int nc = 0; nc < NC; ++nc) acc[nt][nc] *= al;
+      }
       OpPV pop;
       if constexpr (Q) {
         float zs = 0.0f;
@@ -897,8 +901,12 @@ __global__ __launch_bounds__(256) void decode_mfma_stream_kernel(DecodeArgs a) {
           ps += p[st][i];
         }
       lsum[nt] = lsum[nt] * al + ps;
+      // once the running maximum settles, al is exactly 1 for every head:
+      // skip the (identity) rescale of the accumulators
+      if (wave_any(al != 1.0f)) {
 #pragma unroll
-      for (int nc = 0; nc < NC; ++nc) acc[nt][nc] *= al;
+        for (int nc = 0; nc < NC; ++nc) acc[nt][nc] *= al;
+      }
       OpPV pop;
       if constexpr (Q) {
         float zs = 0.0f;
@@ -935,7 +943,7 @@ __global__ __launch_bounds__(256) void decode_mfma_stream_kernel(DecodeArgs a) {
   // (like the uniform kernel's), so the load counter waits stay those of a
   // steady stream; the item's start and end (q loads, result stores) sit
   // outside that loop.
-  static_assert(DEPTH == 1 || DEPTH == 2, "stream ring of one or two pages");
+  static_assert(DEPTH >= 1 && DEPTH <= 4, "stream ring of one to four pages");
   StreamPos cp;
   cp.item = i_begin;
   stream_seek<P>(a, cp, end, false);
@@ -961,19 +969,34 @@ __global__ __launch_bounds__(256) void decode_mfma_stream_kernel(DecodeArgs a) {
         issue(ring[(S0 + s) % DEPTH]);
       }
     }
-    if (k < cnt) {  // DEPTH == 2 and an odd count: one page left, in slot S0
-      compute(ring[S0], cp.wr, k);
-      issue(ring[S0]);
+    // fewer than DEPTH pages left, from slot S0 on
+#pragma unroll
+    for (int s = 0; s < DEPTH - 1; ++s) {
+      if (k + s < cnt) {
+        compute(ring[(S0 + s) % DEPTH], cp.wr, k + s);
+        issue(ring[(S0 + s) % DEPTH]);
+      }
+    }
+  };
+  auto pages_from_slot = [&](int s0) __attribute__((always_inline)) {
+    if (s0 == 0) {
+      item_pages(std::integral_constant<int, 0>{});
+    } else if constexpr (DEPTH > 1) {
+      if (s0 == 1) {
+        item_pages(std::integral_constant<int, 1>{});
+      } else if constexpr (DEPTH > 2) {
+        if (s0 == 2)
+          item_pages(std::integral_constant<int, 2>{});
+        else if constexpr (DEPTH > 3)
+          item_pages(std::integral_constant<int, 3>{});
+      }
     }
   };
   int slot0 = 0;
   for (; cp.item < end; ++cp.item, stream_seek<P>(a, cp, end, false)) {
     begin_item(cp.wr);
     if (cp.wr.cnt > 0) {
-      if (DEPTH == 1 || slot0 == 0)
-        item_pages(std::integral_constant<int, 0>{});
-      else
-        item_pages(std::integral_constant<int, DEPTH - 1>{});
+      pages_from_slot(slot0);
       slot0 = (slot0 + cp.wr.cnt) % DEPTH;
     }
     finish_item(cp.wr);
@@ -1318,6 +1341,9 @@ __global__ __launch_bounds__(256) void merge_sched_kernel(const float* __restric
 // ---------------------------------------------------------------------------
 // Host side.
 constexpr int kDepth = 2;
+// Pages a matrix-core wavefront keeps in flight: INT4 pages are half the
+// bytes of INT8 ones, so it keeps twice as many.
+template <int F> constexpr int mfma_depth() { return F == kI4 ? 4 : kDepth; }
 
 int cu_count_current_device() {
   static int cache[64] = {0};
@@ -1342,18 +1368,24 @@ hipError_t launch_decode_pd(const DecodeArgs& a, bool mfma, int g, dim3 grid, di
     // balanced schedule: one stream per wavefront, no LDS
     if constexpr (SCHED) {
       if (g <= 16)
-        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 1, kDepth>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 1, mfma_depth<F>()>), grid, block,
+                           0, s, a);
       else if (g <= 32)
-        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 2, kDepth>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 2, mfma_depth<F>()>), grid, block,
+                           0, s, a);
       else
-        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 4, kDepth>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 4, mfma_depth<F>()>), grid, block,
+                           0, s, a);
     } else {
       if (g <= 16)
-        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 1, kDepth>), grid, block, lds, s, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 1, mfma_depth<F>()>), grid, block, lds,
+                           s, a);
       else if (g <= 32)
-        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 2, kDepth>), grid, block, lds, s, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 2, mfma_depth<F>()>), grid, block, lds,
+                           s, a);
       else
-        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 4, kDepth>), grid, block, lds, s, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 4, mfma_depth<F>()>), grid, block, lds,
+                           s, a);
     }
   } else {
     if (g == 1)

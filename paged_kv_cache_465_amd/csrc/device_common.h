@@ -11,6 +11,13 @@ namespace kvp {
 // failure of this library, so they are read (and dropped) before launching.
 inline void discard_stale_error() { (void)hipGetLastError(); }
 
+// True when the predicate holds in any lane of the wavefront (a wave-uniform
+// branch condition).
+__device__ __forceinline__ bool wave_any(bool pred) {
+  return __builtin_amdgcn_ballot_w64(pred) != 0;
+}
+
+
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;

@@ -308,8 +308,12 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
           ps += p[st][i];
         }
       lsum[nt] = lsum[nt] * al + ps;
+      // once the running maximum settles, al is exactly 1 for every row:
+      // skip the (identity) rescale of the accumulators
+      if (wave_any(al != 1.0f)) {
 #pragma unroll
-      for (int nc = 0; nc < NC; ++nc) acc[nt][nc] *= al;
+        for (int nc = 0; nc < NC; ++nc) acc[nt][nc] *= al;
+      }
       OpPV pop;
       if constexpr (INT8) {
         float zs = 0.0f;
@@ -433,6 +437,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
 }
 
 constexpr int kPrefillDepth = 2;
+// tiled mode ring depth (4 measured no faster: the tiled kernel is bound by
+// instruction issue at one wavefront per SIMD, not by load latency)
+constexpr int kPrefillTiledDepth = 2;
 
 template <bool INT8, int P, int D>
 hipError_t launch_prefill_pd(const PrefillArgs& a, int nt, bool split, dim3 grid, hipStream_t s) {
@@ -446,10 +453,10 @@ hipError_t launch_prefill_pd(const PrefillArgs& a, int nt, bool split, dim3 grid
                          dim3(256), 0, s, a);
   } else {
     if (nt == 1)
-      hipLaunchKernelGGL((prefill_mfma_kernel<INT8, P, D, 1, kPrefillDepth, false>), grid,
+      hipLaunchKernelGGL((prefill_mfma_kernel<INT8, P, D, 1, kPrefillTiledDepth, false>), grid,
                          dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((prefill_mfma_kernel<INT8, P, D, 2, kPrefillDepth, false>), grid,
+      hipLaunchKernelGGL((prefill_mfma_kernel<INT8, P, D, 2, kPrefillTiledDepth, false>), grid,
                          dim3(256), 0, s, a);
   }
   return hipGetLastError();
