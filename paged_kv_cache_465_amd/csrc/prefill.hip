@@ -49,8 +49,16 @@ struct PrefillArgs {
   float scale_log2;
 };
 
+// Tiled mode is bound by instruction issue: two workgroups per CU (two
+// wavefronts per SIMD) hide each other's dependency stalls, 18% faster than
+// one on 512-token chunks.  The register budget that needs (<= 256 per
+// wavefront) holds without spills except for 32-token pages of 128
+// channels, which keep one workgroup per CU.
+constexpr int prefill_tiled_wg_per_cu(int P, int D) { return P == 32 && D == 128 ? 1 : 2; }
+
 template <bool INT8, int P, int D, int NT, int DEPTH, bool SPLIT>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, SPLIT ? 1 : prefill_tiled_wg_per_cu(P, D)) void
+prefill_mfma_kernel(PrefillArgs a) {
   constexpr int T = P / 16, KK = D / 32, NC = D / 16, EV = 4 * T;
   constexpr int EB = INT8 ? 1 : 2;
   constexpr int KL = INT8 ? D / 64 : KK;
