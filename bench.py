@@ -536,7 +536,7 @@ def main(argv=None):
     if is_chunked(cfg):
         kernel_name = "prefill_mfma_kernel"
     elif res["plan"]["use_mfma"]:
-        kernel_name = "decode_mfma_kernel"
+        kernel_name = "decode_mfma_stream_kernel" if res["balanced"] else "decode_mfma_kernel"
     else:
         kernel_name = "decode_valu_kernel"
     if mfma_bound:
@@ -575,8 +575,9 @@ def main(argv=None):
         "roofline": {**roof, "traffic": None, "kernel": kernel_name,
                      "kernel_us_mean": round(kern_us, 2),
                      "timed": ("decode call (split kernel + merge kernel)"
-                               if res["merge_launched"] or (cfg.window_tokens > 0 and
-                                                            not res["balanced"])
+                               if res["merge_launched"] else
+                               "window decode call (split kernel, + merge when split)"
+                               if cfg.window_tokens > 0 and not res["balanced"]
                                else "split kernel"),
                      "bytes_per_launch": int(sb["split_kernel_per_launch"]),
                      "flops_per_launch": int(flops_launch),
