@@ -12,11 +12,12 @@
 // Work decomposition.  For one (sequence, KV head) the rows are the pairs
 // (chunk token i, head j of the group), row m = i * g + j.  A workgroup of
 // four wavefronts owns a tile of 4 * 16 * NT consecutive rows; each wavefront
-// owns 16 * NT of them and streams, with a two-page register ring, every page
-// up to the last position its rows see.  The matrix-core tiles are the decode
-// kernel's: S^T = K q^T on 16x16x32, O^T += V^T P^T on 16x16x16 (P = 16) or
-// 16x16x32 (P = 32); a lane holds one row per tile, so the causal limit is a
-// per-lane bound and the online softmax stays lane-local.  The wavefronts of
+// owns 16 * NT of them and streams, with a register ring, every page up to
+// the last position its rows see, 32 tokens per step (two 16-token pages, or
+// one 32-token page).  The matrix-core tiles are the decode kernel's for
+// 32-token pages: S^T = K q^T and O^T += V^T P^T on 16x16x32; a lane holds
+// one row per tile, so the causal limit is a per-lane bound and the online
+// softmax stays lane-local.  The wavefronts of
 // a workgroup read the same pages at the same time, and all tiles of one
 // (sequence, KV head) are placed on the same XCD, so page loads are ordinary
 // (cacheable) loads that the tiles share through that XCD's L2.
@@ -49,17 +50,30 @@ struct PrefillArgs {
   float scale_log2;
 };
 
-// Tiled mode is bound by instruction issue: two workgroups per CU (two
-// wavefronts per SIMD) hide each other's dependency stalls, 18% faster than
-// one on 512-token chunks.  The register budget that needs (<= 256 per
-// wavefront) holds without spills except for 32-token pages of 128
-// channels, which keep one workgroup per CU.
-constexpr int prefill_tiled_wg_per_cu(int P, int D) { return P == 32 && D == 128 ? 1 : 2; }
+// Tiled mode is bound by instruction issue.  Two workgroups per CU (two
+// wavefronts per SIMD, <= 256 registers each) hide each other's dependency
+// stalls; with a one-step ring (a step is 32 tokens: two 16-token pages) the
+// budget holds without spills.  Measured on 512-token chunks of a
+// Llama-3-8B-shaped layer (16-token pages): one workgroup per CU with
+// 16-token steps 1216 us, two per CU 1005 us, paired steps at one per CU
+// 944 us, paired steps with a one-step ring at two per CU 800 us.  Pages of
+// 32 tokens x 128 channels do not fit two per CU; they keep one workgroup
+// per CU and a two-step ring.
+constexpr bool prefill_big_step(int P, int D) { return P == 32 && D == 128; }
+constexpr int prefill_tiled_wg_per_cu(int P, int D) { return prefill_big_step(P, D) ? 1 : 2; }
+constexpr int prefill_tiled_depth(int P, int D) { return prefill_big_step(P, D) ? 2 : 1; }
 
 template <bool INT8, int P, int D, int NT, int DEPTH, bool SPLIT>
 __global__ __launch_bounds__(256, SPLIT ? 1 : prefill_tiled_wg_per_cu(P, D)) void
 prefill_mfma_kernel(PrefillArgs a) {
-  constexpr int T = P / 16, KK = D / 32, NC = D / 16, EV = 4 * T;
+  // One step of the page loop covers VP tokens: one page, or in tiled mode
+  // with 16-token pages two consecutive pages, so that P.V runs on the
+  // 16x16x32 matrix-core shape (the 16x16x16 one does half the work per
+  // instruction) and the softmax bookkeeping is paid once per 32 tokens.
+  constexpr bool PAIR = P == 16 && !SPLIT;
+  constexpr int VP = PAIR ? 2 * P : P;
+  constexpr int NSUB = VP / P;  // pages per step
+  constexpr int T = VP / 16, KK = D / 32, NC = D / 16, EV = 4 * T;
   constexpr int EB = INT8 ? 1 : 2;
   constexpr int KL = INT8 ? D / 64 : KK;
   constexpr int VB = EV * EB;
@@ -96,7 +110,8 @@ prefill_mfma_kernel(PrefillArgs a) {
   const int row_last = min(row0 + ROWS_WAVE, rows) - 1;
   const int first_pos = ctx - qlen;       // position of chunk row 0
   const int pos_last = min(first_pos + row_last / g, ctx - 1);
-  const int nblk_all = pos_last >= 0 ? pos_last / P + 1 : 0;
+  const int nblk_all = pos_last >= 0 ? pos_last / VP + 1 : 0;    // steps
+  const int npages = pos_last >= 0 ? pos_last / P + 1 : 0;        // pages they cover
   // blocks [kb0, kb0 + nblk) of this wavefront: all, or a quarter (split)
   const int cw = SPLIT ? (nblk_all + 3) / 4 : nblk_all;
   const int kb0 = SPLIT ? min(wave * cw, nblk_all) : 0;
@@ -138,14 +153,20 @@ prefill_mfma_kernel(PrefillArgs a) {
     qsum[nt] = INT8 ? group4_sum(qs) : 0.0f;
   }
 
-  int koff[T];
+  // K rows: step token tok = page (tok / P) of the step, row tok % P.
+  int koff[T], ksub[T];
 #pragma unroll
   for (int st = 0; st < T; ++st) {
     const int tok = (T == 1) ? r : 8 * (r >> 2) + 4 * st + (r & 3);
-    koff[st] = (tok * D + (INT8 ? (D / 4) * gq : 8 * gq)) * EB;
+    koff[st] = ((tok % P) * D + (INT8 ? (D / 4) * gq : 8 * gq)) * EB;
+    ksub[st] = tok / P;
   }
-  const int voff = (r * P + EV * gq) * EB;
-  const int moff = EV * gq * 4;
+  // this lane's P.V (and score) tokens EV*gq .. EV*gq + EV - 1 lie in one
+  // page of the step
+  const int vsub = (EV * gq) / P;
+  const int vcol = (EV * gq) % P;
+  const int voff = (r * P + vcol) * EB;
+  const int moff = vcol * 4;
   const size_t tile_bytes = size_t(P) * D * EB;
   const char* kbase = static_cast<const char*>(a.k_pool);
   const char* vbase = static_cast<const char*>(a.v_pool);
@@ -156,15 +177,25 @@ prefill_mfma_kernel(PrefillArgs a) {
     VLoad v[NC];
     uint4 km[INT8 ? T : 1];
     uint4 vm[INT8 ? T : 1];
-    int phys;
+    int phys[NSUB];  // -1: page absent (outside the pool, or past the rows' range)
   };
   auto issue = [&](Regs& R, int k) {
-    const int phys = btrow[k];
-    const bool ok = unsigned(phys) < unsigned(a.num_pages);
-    R.phys = ok ? phys : -1;
-    const int64_t t = int64_t(ok ? phys : 0) * H + h;
-    const char* kp = kbase + t * tile_bytes;
+    int64_t tt[NSUB];
+#pragma unroll
+    for (int u = 0; u < NSUB; ++u) {
+      const int pg = k * NSUB + u;
+      const int phys = pg < npages ? btrow[pg] : -1;
+      const bool ok = unsigned(phys) < unsigned(a.num_pages);
+      R.phys[u] = ok ? phys : -1;
+      tt[u] = int64_t(ok ? phys : 0) * H + h;
+    }
+    // per lane: the page of the step its K rows / V tokens come from
+    auto tile_of = [&](int sub) { return NSUB == 1 || sub == 0 ? tt[0] : tt[NSUB - 1]; };
+    const int64_t t = tile_of(vsub);
     const char* vp = vbase + t * tile_bytes;
+    const char* kps[T];
+#pragma unroll
+    for (int st = 0; st < T; ++st) kps[st] = kbase + tile_of(ksub[st]) * tile_bytes;
     // tiled: the workgroup's wavefronts share each page through L2 (ordinary
     // loads); split: each page is read once (non-temporal loads)
     if constexpr (!SPLIT) {
@@ -172,7 +203,7 @@ prefill_mfma_kernel(PrefillArgs a) {
       for (int st = 0; st < T; ++st)
 #pragma unroll
         for (int i = 0; i < KL; ++i)
-          R.k[st][i] = *reinterpret_cast<const uint4*>(kp + koff[st] + i * (INT8 ? 16 : 64));
+          R.k[st][i] = *reinterpret_cast<const uint4*>(kps[st] + koff[st] + i * (INT8 ? 16 : 64));
 #pragma unroll
       for (int nc = 0; nc < NC; ++nc)
         R.v[nc] = *reinterpret_cast<const VLoad*>(vp + voff + nc * 16 * P * EB);
@@ -181,7 +212,7 @@ prefill_mfma_kernel(PrefillArgs a) {
       for (int st = 0; st < T; ++st)
 #pragma unroll
         for (int i = 0; i < KL; ++i)
-          R.k[st][i] = load_stream<uint4>(kp + koff[st] + i * (INT8 ? 16 : 64));
+          R.k[st][i] = load_stream<uint4>(kps[st] + koff[st] + i * (INT8 ? 16 : 64));
 #pragma unroll
       for (int nc = 0; nc < NC; ++nc) R.v[nc] = load_stream<VLoad>(vp + voff + nc * 16 * P * EB);
     }
@@ -208,8 +239,14 @@ prefill_mfma_kernel(PrefillArgs a) {
   }
 
   auto compute = [&](const Regs& R, int k) {
-    if (R.phys < 0) return;  // absent page: its tokens do not take part
-    const int base = k * P;
+    // absent pages: their tokens do not take part
+    bool any_page = false;
+#pragma unroll
+    for (int u = 0; u < NSUB; ++u) any_page |= R.phys[u] >= 0;
+    if (!any_page) return;
+    // this lane's tokens' page (a select, not a register-array index)
+    const bool page_ok = (NSUB > 1 && vsub) ? R.phys[NSUB - 1] >= 0 : R.phys[0] >= 0;
+    const int base = k * VP;
     const int rem = ctx - base;  // rows of this page inside the sequence (>= 1)
     OpA kop[T][KK];
 #pragma unroll
@@ -236,13 +273,13 @@ prefill_mfma_kernel(PrefillArgs a) {
     for (int nc = 0; nc < NC; ++nc) {
       if constexpr (!INT8) {
         VLoad raw = R.v[nc];
-        if (rem < P) {
+        if (rem < VP || !page_ok) {
           // rows past the sequence may hold anything (NaN): zero them
           uint32_t wv[EV / 2];
           __builtin_memcpy(wv, &raw, sizeof(raw));
 #pragma unroll
           for (int e = 0; e < EV; ++e)
-            if (EV * gq + e >= rem) wv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            if (EV * gq + e >= rem || !page_ok) wv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
           __builtin_memcpy(&raw, wv, sizeof(raw));
         }
         vop[nc] = __builtin_bit_cast(OpPV, raw);
@@ -291,7 +328,7 @@ prefill_mfma_kernel(PrefillArgs a) {
           const float v = INT8 ? (ks[st][i] * sc[i] + kz[st][i] * qsum[nt]) * a.scale_log2
                                : sc[i] * a.scale_log2;
           // causal: this lane's row sees positions <= lim (and < ctx)
-          x[st][i] = (tok <= lim[nt] && tok < ctx) ? v : -INFINITY;
+          x[st][i] = (tok <= lim[nt] && tok < ctx && page_ok) ? v : -INFINITY;
         }
       }
       float mloc = x[0][0];
@@ -329,7 +366,7 @@ prefill_mfma_kernel(PrefillArgs a) {
         for (int st = 0; st < T; ++st)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const bool valid = EV * gq + 4 * st + i < rem;
+            const bool valid = EV * gq + 4 * st + i < rem && page_ok;
             const float pv = valid ? p[st][i] * vs[st][i] : 0.0f;
             zs += valid ? p[st][i] * vz[st][i] : 0.0f;
             pop[4 * st + i] = (_Float16)pv;
@@ -444,10 +481,7 @@ prefill_mfma_kernel(PrefillArgs a) {
   }
 }
 
-constexpr int kPrefillDepth = 2;
-// tiled mode ring depth (4 measured no faster: the tiled kernel is bound by
-// instruction issue at one wavefront per SIMD, not by load latency)
-constexpr int kPrefillTiledDepth = 2;
+constexpr int kPrefillDepth = 2;  // split mode
 
 template <bool INT8, int P, int D>
 hipError_t launch_prefill_pd(const PrefillArgs& a, int nt, bool split, dim3 grid, hipStream_t s) {
@@ -461,10 +495,10 @@ hipError_t launch_prefill_pd(const PrefillArgs& a, int nt, bool split, dim3 grid
                          dim3(256), 0, s, a);
   } else {
     if (nt == 1)
-      hipLaunchKernelGGL((prefill_mfma_kernel<INT8, P, D, 1, kPrefillTiledDepth, false>), grid,
+      hipLaunchKernelGGL((prefill_mfma_kernel<INT8, P, D, 1, prefill_tiled_depth(P, D), false>), grid,
                          dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((prefill_mfma_kernel<INT8, P, D, 2, kPrefillTiledDepth, false>), grid,
+      hipLaunchKernelGGL((prefill_mfma_kernel<INT8, P, D, 2, prefill_tiled_depth(P, D), false>), grid,
                          dim3(256), 0, s, a);
   }
   return hipGetLastError();
