@@ -70,7 +70,7 @@ prefill_mfma_kernel(PrefillArgs a) {
   // with 16-token pages two consecutive pages, so that P.V runs on the
   // 16x16x32 matrix-core shape (the 16x16x16 one does half the work per
   // instruction) and the softmax bookkeeping is paid once per 32 tokens.
-  constexpr bool PAIR = P == 16 && !SPLIT;
+  constexpr bool PAIR = P == 16 && !SPLIT;  // (split mode: measured no faster paired)
   constexpr int VP = PAIR ? 2 * P : P;
   constexpr int NSUB = VP / P;  // pages per step
   constexpr int T = VP / 16, KK = D / 32, NC = D / 16, EV = 4 * T;
