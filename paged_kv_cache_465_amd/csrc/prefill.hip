@@ -109,6 +109,9 @@ prefill_mfma_kernel(PrefillArgs a) {
   if (qlen <= 0 || row0 >= rows) return;
   const int row_last = min(row0 + ROWS_WAVE, rows) - 1;
   const int first_pos = ctx - qlen;       // position of chunk row 0
+  // every row of this wavefront sees positions <= lim_min: steps ending there
+  // (inside the sequence, all pages present) need no mask
+  const int lim_min = first_pos + row0 / g;
   const int pos_last = min(first_pos + row_last / g, ctx - 1);
   const int nblk_all = pos_last >= 0 ? pos_last / VP + 1 : 0;    // steps
   const int npages = pos_last >= 0 ? pos_last / P + 1 : 0;        // pages they cover
@@ -246,8 +249,14 @@ prefill_mfma_kernel(PrefillArgs a) {
     if (!any_page) return;
     // this lane's tokens' page (a select, not a register-array index)
     const bool page_ok = (NSUB > 1 && vsub) ? R.phys[NSUB - 1] >= 0 : R.phys[0] >= 0;
+    bool all_pages = true;
+#pragma unroll
+    for (int u = 0; u < NSUB; ++u) all_pages &= R.phys[u] >= 0;
     const int base = k * VP;
     const int rem = ctx - base;  // rows of this page inside the sequence (>= 1)
+    // wave-uniform: the whole step lies inside the sequence, below every
+    // row's causal limit, on present pages
+    const bool unmasked = all_pages && rem >= VP && base + VP - 1 <= lim_min;
     OpA kop[T][KK];
 #pragma unroll
     for (int st = 0; st < T; ++st) {
@@ -324,12 +333,20 @@ prefill_mfma_kernel(PrefillArgs a) {
         for (int kk = 0; kk < KK; ++kk) sc = mfma_16x16x32(kop[st][kk], qop[nt][kk], sc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int tok = base + EV * gq + 4 * st + i;
           const float v = INT8 ? (ks[st][i] * sc[i] + kz[st][i] * qsum[nt]) * a.scale_log2
                                : sc[i] * a.scale_log2;
-          // causal: this lane's row sees positions <= lim (and < ctx)
-          x[st][i] = (tok <= lim[nt] && tok < ctx && page_ok) ? v : -INFINITY;
+          x[st][i] = v;
         }
+      }
+      if (!unmasked) {
+#pragma unroll
+        for (int st = 0; st < T; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = base + EV * gq + 4 * st + i;
+            // causal: this lane's row sees positions <= lim (and < ctx)
+            if (!(tok <= lim[nt] && tok < ctx && page_ok)) x[st][i] = -INFINITY;
+          }
       }
       float mloc = x[0][0];
 #pragma unroll
