@@ -240,9 +240,19 @@ struct MfmaShape {
   static constexpr int NC = D / 16;         // 16-channel output chunks
   static constexpr int EV = 4 * T;          // tokens per lane in P.V
   static constexpr int RB = D * FI::bits / 8;  // bytes of one stored token row
-  // K bytes a lane holds per 16-token sub-tile: bfloat16, KK pieces of 8
-  // channels 32 apart; codes, D/4 contiguous channels
+  // K bytes a lane holds per 16-token sub-tile.  The four lane groups (gq)
+  // read interleaved 16-byte pieces, so each load instruction covers whole
+  // 64-byte spans of a token row: bfloat16, KK pieces of 8 channels 32
+  // apart; 8-bit codes, D/64 pieces of 16 channels 64 apart; INT4, D/4
+  // contiguous channels (one piece of D/8 bytes).
   static constexpr int KB = FI::quant ? (D / 4) * FI::bits / 8 : 16 * KK;
+  // q channel of k-step kk in lane group gq, matching the K pieces above
+  __device__ static constexpr int q_channel(int kk, int gq) {
+    return F == kBF16 ? 32 * kk + 8 * gq
+         : F == kI4   ? (D / 4) * gq + 8 * kk
+                      : 64 * (kk >> 1) + 16 * gq + 8 * (kk & 1);
+  }
+  __device__ static constexpr int k_lane_offset(int gq) { return F == kI4 ? gq * KB : 16 * gq; }
   static constexpr int KLB = KB >= 16 ? 16 : KB;  // bytes per K load
   static constexpr int KN = KB / KLB;             // K loads per sub-tile
   // V^T bytes a lane holds per 16-channel chunk: EV tokens of one channel (for
@@ -322,7 +332,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const WorkRange& 
     float qs = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const int d0 = Q ? (D / 4) * gq + 8 * kk : 32 * kk + 8 * gq;
+      const int d0 = S::q_channel(kk, gq);
       uint4 raw = live ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
       if constexpr (!Q) {
         qop[nt][kk] = __builtin_bit_cast(bf16x8_t, raw);
@@ -348,7 +358,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const WorkRange& 
     // sub-tile st, MFMA row r -> token; with two sub-tiles the rows are
     // interleaved so a lane's eight P.V tokens are contiguous.
     const int tok = (T == 1) ? r : 8 * (r >> 2) + 4 * st + (r & 3);
-    koff[st] = tok * RB + (Q ? gq * KB : 16 * gq);
+    koff[st] = tok * RB + S::k_lane_offset(gq);
   }
   // V^T tile: [D][P] elements, or [D/2][P] bytes for INT4 (channel pairs)
   const int voff = F == kBF16 ? (r * P + EV * gq) * 2
@@ -372,7 +382,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const WorkRange& 
     for (int st = 0; st < T; ++st)
 #pragma unroll
       for (int i = 0; i < S::KN; ++i)
-        R.k[st][i] = load_stream<KLoad>(kp + koff[st] + i * (Q ? 16 : 64));
+        R.k[st][i] = load_stream<KLoad>(kp + koff[st] + i * 64);
 #pragma unroll
     for (int nc = 0; nc < NC; ++nc) R.v[nc] = load_stream<VLoad>(vp + voff + nc * vstride);
     if constexpr (Q) {
@@ -657,7 +667,7 @@ __global__ __launch_bounds__(256) void decode_mfma_stream_kernel(DecodeArgs a) {
 #pragma unroll
   for (int st = 0; st < T; ++st) {
     const int tok = (T == 1) ? r : 8 * (r >> 2) + 4 * st + (r & 3);
-    koff[st] = tok * RB + (Q ? gq * KB : 16 * gq);
+    koff[st] = tok * RB + S::k_lane_offset(gq);
   }
   const int voff = F == kBF16 ? (r * P + EV * gq) * 2
                               : (F == kI4 ? (r >> 1) * P : r * P) + EV * gq;
@@ -686,7 +696,7 @@ __global__ __launch_bounds__(256) void decode_mfma_stream_kernel(DecodeArgs a) {
     for (int st = 0; st < T; ++st)
 #pragma unroll
       for (int i = 0; i < S::KN; ++i)
-        R.k[st][i] = load_stream<KLoad>(kp + koff[st] + i * (Q ? 16 : 64));
+        R.k[st][i] = load_stream<KLoad>(kp + koff[st] + i * 64);
 #pragma unroll
     for (int nc = 0; nc < NC; ++nc) R.v[nc] = load_stream<VLoad>(vp + voff + nc * vstride);
     if constexpr (Q) {
@@ -725,7 +735,7 @@ __global__ __launch_bounds__(256) void decode_mfma_stream_kernel(DecodeArgs a) {
       float qs = 0.0f;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const int d0 = Q ? (D / 4) * gq + 8 * kk : 32 * kk + 8 * gq;
+        const int d0 = S::q_channel(kk, gq);
         uint4 raw = live ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
         if constexpr (!Q) {
           qop[nt][kk] = __builtin_bit_cast(bf16x8_t, raw);
