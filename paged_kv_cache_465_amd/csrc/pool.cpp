@@ -213,6 +213,9 @@ kvp_status kvp_decode_plan(const kvp_pool_desc* desc, int32_t num_seqs, int32_t 
   const int use_mfma = g >= 4;
   // LDS per wave for the in-workgroup merge: g*D partial outputs plus (m, l)
   // per padded head, plus the vector path's probability broadcast; <= 64 KiB.
+  // (The part holds 160 KiB per workgroup, but for g = 32 four waves with
+  // fewer splits streamed slower than two waves with more: the 64 KiB cap
+  // keeps the occupancy that measured best.)
   const int32_t heads_pad = use_mfma ? ((g + 15) / 16) * 16 : g;
   const int64_t lds_per_wave = (int64_t(g) * D + 2 * heads_pad + (use_mfma ? 0 : g * P)) * 4;
   int32_t waves = 4;
