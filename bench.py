@@ -40,6 +40,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix-core peak
 PROFILES = os.path.join(ROOT, "profiles")
 # sources that decide the split kernel's code and launch shape
 KERNEL_SOURCES = ("paged_kv_cache_465_amd/csrc/decode.hip",
+                  "paged_kv_cache_465_amd/csrc/decode_kernels.h",
+                  "paged_kv_cache_465_amd/csrc/decode_bf16_split.hip",
                   "paged_kv_cache_465_amd/csrc/device_common.h",
                   "paged_kv_cache_465_amd/csrc/pool.cpp")
 MALL_FLUSH_BYTES = 1 << 30      # > 256 MB Infinity Cache

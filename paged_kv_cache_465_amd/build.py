@@ -22,7 +22,9 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
-DEVICE_SOURCES = ["append.hip", "decode.hip", "prefill.hip"]
+# decode kernels: one translation unit per (KV format, plan), so they compile in parallel
+DEVICE_SOURCES = [f"decode_{fmt}_{plan}.hip" for fmt in ("int4", "bf16", "fp8", "int8")
+                  for plan in ("sched", "split")] + ["prefill.hip", "decode.hip", "append.hip"]
 HOST_SOURCES = ["pool.cpp", "prefix_cache.cpp", "schedule.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
@@ -51,7 +53,7 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD, src + ".o")
         # host-only C++ (no device code): compiled as plain C++
         jobs.append([HIPCC, *COMMON, "-x", "c++", "-c", os.path.join(CSRC, src), "-o", obj])
-    with ThreadPoolExecutor(max_workers=min(4, len(jobs))) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4, len(jobs))) as ex:
         outs = list(ex.map(_run, jobs))
     if verbose:
         for o in outs:

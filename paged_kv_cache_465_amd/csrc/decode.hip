@@ -1,1359 +1,26 @@
-// Paged decode attention for gfx950.
-//
-// "KV-Cache Optimization Techniques", section "PagedAttention", eq. 1: the new
-// query token of a sequence attends over the K/V rows of its pages, gathered
-// in logical order through the sequence's page table:
-//   out_j = softmax(scale * q_j K^T) V,  query head j reading KV head j / g
-// (section "Multi-Query and Grouped-Query Caching", eq. 7).  Quantized pools
-// hold codes with a per-token scale and zero point (section "KV-Cache
-// Quantization", eq. 3; INT8 and INT4 codes, or FP8 e4m3 values with zero
-// point 0), dequantized here: q.k = s*(q.c) + z*sum(q) and
-// sum_t p_t v_t = sum_t (p_t s_t) c_t + sum_t p_t z_t.
-//
-// Work decomposition.  A workgroup owns one (sequence, KV head) pair and one
-// range of logical blocks (a split); its W wavefronts each stream a
-// contiguous share of those pages with a register ring of DEPTH pages in
-// flight, keep an online softmax in float32 (running max m, running sum l,
-// rescaled accumulator), and merge in LDS at the end.  With several splits
-// the merged partials (o, m, l) go to a workspace and merge_kernel combines
-// them by log-sum-exp.  Scores live in log2 units (scale * log2 e folded in)
-// so every exponential is one v_exp_f32.
-//
-// Matrix-core path (g >= 4): per 16-token sub-tile, S^T = K q^T on
-// v_mfma_f32_16x16x32 (K rows are the A operand, loaded straight from HBM
-// with 16-byte loads: each lane holds 8 channels of one token), then
-// O^T += V^T P^T on v_mfma_f32_16x16x16 (P = 16) or 16x16x32 (P = 32).  The
-// S^T accumulator layout (lane: head l%16, tokens 4*(l/16)..+3) is exactly the
-// B-operand layout P^T needs, and the O^T accumulator keeps head l%16 in the
-// same lane, so the whole online softmax is lane-local except the max over
-// tokens (two cross-lane steps).  V is stored transposed per (page, head) so
-// each lane's V^T operand is one contiguous load.  Query heads are padded to
-// 16 per tile; NT tiles cover g up to 16*NT.
-//
-// Vector-ALU path (g < 4): four lanes per token row split the channels for
-// the dot products; probabilities are broadcast through LDS for P.V.
+// Paged decode attention for gfx950: host side of the C ABI (planning,
+// argument checks, launches).  The kernels are in decode_kernels.h; the
+// instances of each (KV format, plan) are compiled in a file of their own,
+// decode_<format>_split.hip and decode_<format>_sched.hip.
 #include <algorithm>
 #include <cmath>
-#include <type_traits>
 
-#include "device_common.h"
-#include "kvp.h"
+#include "decode_kernels.h"
 
 namespace kvp {
 
-struct DecodeArgs {
-  const uint16_t* q;
-  const void* k_pool;
-  const void* v_pool;
-  const uint16_t* k_meta;
-  const uint16_t* v_meta;
-  const int32_t* bt;
-  const int32_t* ctx_lens;
-  uint16_t* out;
-  float* part_o;
-  float* part_ml;
-  int32_t num_seqs, max_blocks, num_kv_heads, num_q_heads, group, num_pages, num_splits,
-      pages_per_split;
-  int32_t ctx_cap;
-  int32_t sink_tokens, window_tokens;  // window_tokens > 0: attend only to the kept set
-  int32_t write_partials;  // 1: store (o, m, l) per split; 0: store the bf16 output
-  float scale_log2;  // scale * log2(e)
-  const int32_t* sched;    // balanced schedule (bin starts at word 8), or null
-  int32_t items_off;       // word offset of its item records
-  int32_t num_items, num_slots, num_bins;
-};
-
-// The tokens a sequence of n attends to.  Without a window, 0..n-1.  With a
-// window ("KV-Cache Optimization Techniques", section "Token Eviction
-// Strategies", eq. 5, attention sinks plus a recent window; section "Sliding
-// Window Cache", eq. 6, when there are no sinks) and sink + window < n, only
-// t < sink or t >= n - window.  The pages streamed are the virtual block list
-// "sink blocks, then window blocks": virtual block v is logical block v below
-// sink_blk and win_first + (v - sink_blk) from there on; blocks in between hold
-// only dropped tokens and are never read (their table entries may be -1).
-struct WorkRange {
-  int b, h, s, ctx;
-  int slot;                // scheduled item: partial slot, -1 for the direct output
-  int kb0, cnt;            // this wave's virtual blocks [kb0, kb0 + cnt)
-  int sink_blk, win_first;
-  int sink_end, win_start;  // kept: t < ctx and (t < sink_end or t >= win_start)
-  __device__ __forceinline__ int logical(int v) const {
-    return v < sink_blk ? v : win_first + (v - sink_blk);
-  }
-};
-
-// Rows of one page that take part (relative token bounds of the kept set).
-struct PageMask {
-  int end, sink_end, win_start;
-  bool partial;  // some row of the page is not kept
-  __device__ __forceinline__ bool valid(int r) const {
-    return r < end && (r < sink_end || r >= win_start);
-  }
-};
-
-template <int P>
-__device__ __forceinline__ PageMask page_mask(const WorkRange& w, int lblk) {
-  const int base = lblk * P;
-  PageMask m;
-  m.end = w.ctx - base;
-  m.sink_end = w.sink_end - base;
-  m.win_start = w.win_start - base;
-  m.partial = !(m.end >= P && (m.sink_end >= P || m.win_start <= 0));
-  return m;
-}
-
-// Which (sequence, KV head, split) this workgroup owns and which contiguous
-// run of virtual blocks [kb0, kb0 + cnt) wave `wave` streams.
-//
-// Workgroups are handed to the eight XCDs round robin (workgroup i to XCD
-// i mod 8), so the index order decides each XCD's share of the work.  The KV
-// head varies fastest (the heads of one sequence carry equal work), then the
-// sequence, and the split slowest: every XCD gets the same mix of long and
-// short sequences and of first and last splits, and the always-full first
-// splits are dispatched first.  (With the split fastest and eight KV heads,
-// an even split count gave each XCD a single split index: half the XCDs
-// streamed every sequence's first pages while the other half idled.)
-// Sequence b's streamed block list (see WorkRange) and its length.
-template <int P>
-__device__ __forceinline__ int sequence_blocks(const DecodeArgs& a, WorkRange& w) {
-  int ctx = a.ctx_lens[w.b];
-  ctx = min(max(ctx, 0), a.ctx_cap);
-  w.ctx = ctx;
-  const int nblk = (ctx + P - 1) / P;
-  int nvirt = nblk;
-  w.sink_blk = nblk;
-  w.win_first = nblk;
-  w.sink_end = ctx;
-  w.win_start = ctx;
-  if (a.window_tokens > 0 && int64_t(a.sink_tokens) + a.window_tokens < int64_t(ctx)) {
-    w.sink_end = a.sink_tokens;
-    w.win_start = ctx - a.window_tokens;
-    w.sink_blk = (a.sink_tokens + P - 1) / P;
-    w.win_first = max(w.win_start / P, w.sink_blk);
-    nvirt = w.sink_blk + (nblk - w.win_first);
-  }
-  return nvirt;
-}
-
-// Wave `wave` of W takes a contiguous share of virtual blocks [blk0, blk1).
-__device__ __forceinline__ void wave_share(WorkRange& w, int blk0, int blk1, int wave, int W) {
-  const int n = max(blk1 - blk0, 0);
-  const int cw = (n + W - 1) / W;
-  w.kb0 = blk0 + wave * cw;
-  w.cnt = max(0, min(cw, blk1 - w.kb0));
-}
-
-// Which (sequence, KV head, split) this workgroup owns and which contiguous
-// run of virtual blocks [kb0, kb0 + cnt) wave `wave` streams.
-//
-// Workgroups are handed to the eight XCDs round robin (workgroup i to XCD
-// i mod 8), so the index order decides each XCD's share of the work.  The KV
-// head varies fastest (the heads of one sequence carry equal work), then the
-// sequence, and the split slowest: every XCD gets the same mix of long and
-// short sequences and of first and last splits, and the always-full first
-// splits are dispatched first.  (With the split fastest and eight KV heads,
-// an even split count gave each XCD a single split index: half the XCDs
-// streamed every sequence's first pages while the other half idled.)
-template <int P>
-__device__ __forceinline__ WorkRange work_range(const DecodeArgs& a, int wave, int W) {
-  WorkRange w;
-  int item = blockIdx.x;
-  w.h = item % a.num_kv_heads;
-  item /= a.num_kv_heads;
-  w.b = item % a.num_seqs;
-  w.s = item / a.num_seqs;
-  w.slot = -1;
-  const int nvirt = sequence_blocks<P>(a, w);
-  const int blk0 = w.s * a.pages_per_split;
-  wave_share(w, blk0, min(blk0 + a.pages_per_split, nvirt), wave, W);
-  return w;
-}
-
-// A schedule item names a sequence and KV head of this call and a partial
-// slot within the workspace (or -1); anything else is skipped.
-__device__ __forceinline__ bool item_valid(const DecodeArgs& a, int i) {
-  const int32_t* it = a.sched + a.items_off + int64_t(i) * 8;
-  return unsigned(it[0]) < unsigned(a.num_seqs) && unsigned(it[1]) < unsigned(a.num_kv_heads) &&
-         it[4] >= -1 && it[4] < a.num_slots;
-}
-
-// Item `i` of a balanced schedule: sequence, KV head, streamed blocks
-// [first, end) (clipped to the device length), partial slot.
-template <int P>
-__device__ __forceinline__ WorkRange item_range(const DecodeArgs& a, int i, int wave, int W) {
-  const int32_t* it = a.sched + a.items_off + int64_t(i) * 8;
-  WorkRange w;
-  w.b = it[0];
-  w.h = it[1];
-  w.s = 0;
-  w.slot = it[4];
-  const int nvirt = sequence_blocks<P>(a, w);
-  wave_share(w, max(it[2], 0), min(it[3], nvirt), wave, W);
-  return w;
-}
-
-// Merge the W wavefronts' (m, l, o) partials held in LDS and store either the
-// final bfloat16 output (one split) or this split's normalized partial.
-template <int D, bool SCHED>
-__device__ __forceinline__ void combine_and_store(const DecodeArgs& a, const WorkRange& wr,
-                                                  const float* sm_o, const float* sm_m,
-                                                  const float* sm_l, int W, int HP) {
-  const int g = a.group;
-  for (int e = threadIdx.x; e < g * D; e += blockDim.x) {
-    const int j = e / D, d = e - j * D;
-    float M = -INFINITY;
-    for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w * HP + j]);
-    float L = 0.0f, O = 0.0f;
-    if (M != -INFINITY) {
-      for (int w = 0; w < W; ++w) {
-        const float mw = sm_m[w * HP + j];
-        if (mw != -INFINITY) {
-          const float f = fast_exp2(mw - M);
-          L += sm_l[w * HP + j] * f;
-          O += sm_o[(w * g + j) * D + d] * f;
-        }
-      }
-    }
-    const float res = L > 0.0f ? O / L : 0.0f;
-    const int64_t row = int64_t(wr.b) * a.num_q_heads + int64_t(wr.h) * g + j;
-    const bool direct = SCHED ? wr.slot < 0 : !a.write_partials;
-    if (direct) {
-      a.out[row * D + d] = f32_to_bf16_rne(res);
-    } else {
-      const int64_t pr = SCHED ? int64_t(wr.slot) * g + j : row * a.num_splits + wr.s;
-      a.part_o[pr * D + d] = res;
-      if (d == 0) {
-        a.part_ml[pr * 2] = M;
-        a.part_ml[pr * 2 + 1] = L;
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Matrix-core kernel.
-template <int F, int P, int D>
-struct MfmaShape {
-  using FI = FmtInfo<F>;
-  static constexpr int T = P / 16;          // 16-token sub-tiles per page
-  static constexpr int KK = D / 32;         // 16x16x32 steps over the head dim
-  static constexpr int NC = D / 16;         // 16-channel output chunks
-  static constexpr int EV = 4 * T;          // tokens per lane in P.V
-  static constexpr int RB = D * FI::bits / 8;  // bytes of one stored token row
-  // K bytes a lane holds per 16-token sub-tile.  The four lane groups (gq)
-  // read interleaved 16-byte pieces, so each load instruction covers whole
-  // 64-byte spans of a token row: bfloat16, KK pieces of 8 channels 32
-  // apart; 8-bit codes, D/64 pieces of 16 channels 64 apart; INT4, D/4
-  // contiguous channels (one piece of D/8 bytes).
-  static constexpr int KB = FI::quant ? (D / 4) * FI::bits / 8 : 16 * KK;
-  // q channel of k-step kk in lane group gq, matching the K pieces above
-  __device__ static constexpr int q_channel(int kk, int gq) {
-    return F == kBF16 ? 32 * kk + 8 * gq
-         : F == kI4   ? (D / 4) * gq + 8 * kk
-                      : 64 * (kk >> 1) + 16 * gq + 8 * (kk & 1);
-  }
-  __device__ static constexpr int k_lane_offset(int gq) { return F == kI4 ? gq * KB : 16 * gq; }
-  static constexpr int KLB = KB >= 16 ? 16 : KB;  // bytes per K load
-  static constexpr int KN = KB / KLB;             // K loads per sub-tile
-  // V^T bytes a lane holds per 16-channel chunk: EV tokens of one channel (for
-  // INT4 the byte of the channel pair holding it)
-  static constexpr int VB = F == kBF16 ? EV * 2 : EV;
-};
-
-template <int BYTES> struct LoadT;
-template <> struct LoadT<4> { using type = uint32_t; };
-template <> struct LoadT<8> { using type = uint2; };
-template <> struct LoadT<16> { using type = uint4; };
-
-template <int F, int P, int D>
-struct PageRegs {
-  using S = MfmaShape<F, P, D>;
-  typename LoadT<S::KLB>::type k[S::T][S::KN];
-  typename LoadT<S::VB>::type v[S::NC];
-  uint4 km[FmtInfo<F>::quant ? S::T : 1];
-  uint4 vm[FmtInfo<F>::quant ? S::T : 1];
-  int phys;  // page id, -1 when the table entry is out of range
-};
-
-// Largest workgroup each instance is compiled for: four wavefronts, one per
-// SIMD, which is what kvp_decode_plan asks for (fewer when the LDS merge
-// buffer of a large group would not fit).
-constexpr int mfma_max_threads(int, int, int) { return 256; }
-constexpr int valu_max_threads(int, int, int) { return 256; }
-
-// Eight consecutive code channels of a lane (starting at dword w[0]) as the
-// float16 matrix-core operand: INT8 and FP8 take two dwords, INT4 one.
-template <int F>
-__device__ __forceinline__ f16x8_t codes8_to_f16x8(const uint32_t* w) {
-  if constexpr (F == kI4) {
-    return i4x8_to_f16x8(w[0]);
-  } else {
-    f16x2_t a0, a1, b0, b1;
-    if constexpr (F == kI8) {
-      i8x4_to_f16x4(w[0], a0, a1);
-      i8x4_to_f16x4(w[1], b0, b1);
-    } else {
-      fp8x4_to_f16x4(w[0], a0, a1);
-      fp8x4_to_f16x4(w[1], b0, b1);
-    }
-    return f16x8_t{a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
-  }
-}
-
-template <int F, int P, int D, int NT, int DEPTH, bool SCHED>
-__device__ __forceinline__ void mfma_item(const DecodeArgs& a, const WorkRange& wr, float* smem) {
-  using S = MfmaShape<F, P, D>;
-  using FI = FmtInfo<F>;
-  constexpr bool Q = FI::quant, ZP = FI::zero;
-  constexpr int T = S::T, KK = S::KK, NC = S::NC, EV = S::EV, RB = S::RB, KB = S::KB;
-  constexpr int HP = NT * 16;
-  using OpA = typename std::conditional<Q, f16x8_t, bf16x8_t>::type;
-  using OpPV = typename std::conditional<
-      T == 1, typename std::conditional<Q, f16x4_t, bf16x4_t>::type, OpA>::type;
-  using KLoad = typename LoadT<S::KLB>::type;
-  using VLoad = typename LoadT<S::VB>::type;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int W = blockDim.x >> 6;
-  const int r = lane & 15, gq = lane >> 4;
-  const int g = a.group;
-  const int H = a.num_kv_heads;
-
-  // q^T as the B operand of S^T = K q^T: lane holds head nt*16 + r, 8 channels.
-  OpA qop[NT][KK];
-  float qsum[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int jj = nt * 16 + r;
-    const bool live = jj < g;
-    const uint16_t* qrow =
-        a.q + (int64_t(wr.b) * a.num_q_heads + int64_t(wr.h) * g + (live ? jj : 0)) * D;
-    float qs = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int d0 = S::q_channel(kk, gq);
-      uint4 raw = live ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
-      if constexpr (!Q) {
-        qop[nt][kk] = __builtin_bit_cast(bf16x8_t, raw);
-      } else {
-        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-        f16x8_t v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float f = bf16_to_f32((w4[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-          v[e] = (_Float16)f;
-          qs += f;
-        }
-        qop[nt][kk] = v;
-      }
-    }
-    qsum[nt] = ZP ? group4_sum(qs) : 0.0f;
-  }
-
-  // Per-lane byte offsets inside a (page, head) tile.
-  int koff[T];
-#pragma unroll
-  for (int st = 0; st < T; ++st) {
-    // sub-tile st, MFMA row r -> token; with two sub-tiles the rows are
-    // interleaved so a lane's eight P.V tokens are contiguous.
-    const int tok = (T == 1) ? r : 8 * (r >> 2) + 4 * st + (r & 3);
-    koff[st] = tok * RB + S::k_lane_offset(gq);
-  }
-  // V^T tile: [D][P] elements, or [D/2][P] bytes for INT4 (channel pairs)
-  const int voff = F == kBF16 ? (r * P + EV * gq) * 2
-                              : (F == kI4 ? (r >> 1) * P : r * P) + EV * gq;
-  constexpr int vstride = F == kBF16 ? 16 * P * 2 : (F == kI4 ? 8 * P : 16 * P);
-  const int moff = EV * gq * 4;
-
-  const size_t tile_bytes = size_t(P) * RB;
-  const char* kbase = static_cast<const char*>(a.k_pool);
-  const char* vbase = static_cast<const char*>(a.v_pool);
-  const int32_t* btrow = a.bt + int64_t(wr.b) * a.max_blocks;
-
-  auto issue = [&](PageRegs<F, P, D>& R, int k) {
-    int phys = btrow[wr.logical(wr.kb0 + k)];
-    const bool ok = unsigned(phys) < unsigned(a.num_pages);
-    R.phys = ok ? phys : -1;
-    const int64_t tile = int64_t(ok ? phys : 0) * H + wr.h;
-    const char* kp = kbase + tile * tile_bytes;
-    const char* vp = vbase + tile * tile_bytes;
-#pragma unroll
-    for (int st = 0; st < T; ++st)
-#pragma unroll
-      for (int i = 0; i < S::KN; ++i)
-        R.k[st][i] = load_stream<KLoad>(kp + koff[st] + i * 64);
-#pragma unroll
-    for (int nc = 0; nc < NC; ++nc) R.v[nc] = load_stream<VLoad>(vp + voff + nc * vstride);
-    if constexpr (Q) {
-      const char* km = reinterpret_cast<const char*>(a.k_meta) + tile * (P * 4);
-      const char* vm = reinterpret_cast<const char*>(a.v_meta) + tile * (P * 4);
-#pragma unroll
-      for (int st = 0; st < T; ++st) {
-        R.km[st] = load_stream<uint4>(km + moff + st * 16);
-        R.vm[st] = load_stream<uint4>(vm + moff + st * 16);
-      }
-    }
-  };
-
-  float m[NT], lsum[NT], zacc[NT];
-  f32x4_t acc[NT][NC];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m[nt] = -INFINITY;
-    lsum[nt] = 0.0f;
-    zacc[nt] = 0.0f;
-#pragma unroll
-    for (int nc = 0; nc < NC; ++nc) acc[nt][nc] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-
-  auto compute = [&](const PageRegs<F, P, D>& R, int k) {
-    if (R.phys < 0) return;  // absent page: its tokens do not take part
-    const PageMask pm = page_mask<P>(wr, wr.logical(wr.kb0 + k));
-    const bool tail = pm.partial;
-
-    // K operands for all sub-tiles (shared by every head tile).
-    OpA kop[T][KK];
-#pragma unroll
-    for (int st = 0; st < T; ++st) {
-      if constexpr (!Q) {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kop[st][kk] = __builtin_bit_cast(bf16x8_t, R.k[st][kk]);
-      } else {
-        uint32_t w[KB / 4];
-        __builtin_memcpy(w, R.k[st], KB);
-        constexpr int DW = F == kI4 ? 1 : 2;  // dwords per 8 channels
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kop[st][kk] = codes8_to_f16x8<F>(w + DW * kk);
-      }
-    }
-    // V^T operands.
-    OpPV vop[NC];
-#pragma unroll
-    for (int nc = 0; nc < NC; ++nc) {
-      if constexpr (!Q) {
-        VLoad raw = R.v[nc];
-        if (tail) {
-          // rows past the sequence may hold anything (NaN): zero them so 0*x stays 0
-          uint32_t wv[EV / 2];
-          __builtin_memcpy(wv, &raw, sizeof(raw));
-#pragma unroll
-          for (int e = 0; e < EV; ++e) {
-            if (!pm.valid(EV * gq + e)) wv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          }
-          __builtin_memcpy(&raw, wv, sizeof(raw));
-        }
-        vop[nc] = __builtin_bit_cast(OpPV, raw);
-      } else {
-        uint32_t wv[EV / 4];
-        __builtin_memcpy(wv, &R.v[nc], sizeof(R.v[nc]));
-        OpPV v;
-#pragma unroll
-        for (int i = 0; i < EV / 4; ++i) {
-          f16x2_t lo, hi;
-          if constexpr (F == kI8)
-            i8x4_to_f16x4(wv[i], lo, hi);
-          else if constexpr (F == kFP8)
-            fp8x4_to_f16x4(wv[i], lo, hi);
-          else
-            i4sel4_to_f16x4(wv[i], (r & 1) != 0, lo, hi);
-          v[4 * i + 0] = lo[0];
-          v[4 * i + 1] = lo[1];
-          v[4 * i + 2] = hi[0];
-          v[4 * i + 3] = hi[1];
-        }
-        vop[nc] = v;
-      }
-    }
-    // Per-token scale (and zero point) of this lane's rows.
-    float ks[T][4], kz[T][4], vs[T][4], vz[T][4];
-    if constexpr (Q) {
-#pragma unroll
-      for (int st = 0; st < T; ++st) {
-        const uint32_t kw[4] = {R.km[st].x, R.km[st].y, R.km[st].z, R.km[st].w};
-        const uint32_t vw[4] = {R.vm[st].x, R.vm[st].y, R.vm[st].z, R.vm[st].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ks[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] & 0xffffu)) * FI::scale_mul;
-          kz[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] >> 16));
-          vs[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(vw[i] & 0xffffu)) * FI::scale_mul;
-          vz[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(vw[i] >> 16));
-        }
-      }
-    }
-
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float x[T][4];
-#pragma unroll
-      for (int st = 0; st < T; ++st) {
-        f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) sc = mfma_16x16x32(kop[st][kk], qop[nt][kk], sc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (ZP)
-            x[st][i] = (ks[st][i] * sc[i] + kz[st][i] * qsum[nt]) * a.scale_log2;
-          else if constexpr (Q)
-            x[st][i] = ks[st][i] * sc[i] * a.scale_log2;
-          else
-            x[st][i] = sc[i] * a.scale_log2;
-        }
-      }
-      if (tail) {
-#pragma unroll
-        for (int st = 0; st < T; ++st)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (!pm.valid(EV * gq + 4 * st + i)) x[st][i] = -INFINITY;
-      }
-      float mloc = x[0][0];
-#pragma unroll
-      for (int st = 0; st < T; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, x[st][i]);
-      mloc = group4_max(mloc);
-      const float mnew = fmaxf(m[nt], mloc);
-      const float al = fast_exp2(m[nt] - mnew);
-      m[nt] = mnew;
-      float p[T][4];
-      float ps = 0.0f;
-#pragma unroll
-      for (int st = 0; st < T; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[st][i] = fast_exp2(x[st][i] - mnew);
-          ps += p[st][i];
-        }
-      lsum[nt] = lsum[nt] * al + ps;
-      // once the running maximum settles, al is exactly 1 for every head:
-      // skip the (identity) rescale of the accumulators
-      if (wave_any(al != 1.0f)) {
-#pragma unroll
-        for (int nc = 0; nc < NC; ++nc) acc[nt][nc] *= al;
-      }
-      OpPV pop;
-      if constexpr (Q) {
-        float zs = 0.0f;
-#pragma unroll
-        for (int st = 0; st < T; ++st)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool valid = !tail || pm.valid(EV * gq + 4 * st + i);
-            const float pv = valid ? p[st][i] * vs[st][i] : 0.0f;
-            if constexpr (ZP) zs += valid ? p[st][i] * vz[st][i] : 0.0f;
-            pop[4 * st + i] = (_Float16)pv;
-          }
-        zacc[nt] = zacc[nt] * al + zs;
-      } else {
-#pragma unroll
-        for (int st = 0; st < T; ++st)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pop[4 * st + i] = (__bf16)p[st][i];
-      }
-#pragma unroll
-      for (int nc = 0; nc < NC; ++nc) {
-        if constexpr (T == 1)
-          acc[nt][nc] = mfma_16x16x16(vop[nc], pop, acc[nt][nc]);
-        else
-          acc[nt][nc] = mfma_16x16x32(vop[nc], pop, acc[nt][nc]);
-      }
-    }
-  };
-
-  if (wr.cnt > 0) {
-    PageRegs<F, P, D> ring[DEPTH];
-#pragma unroll
-    for (int s = 0; s < DEPTH; ++s) issue(ring[s], min(s, wr.cnt - 1));
-    for (int k0 = 0; k0 < wr.cnt; k0 += DEPTH) {
-#pragma unroll
-      for (int s = 0; s < DEPTH; ++s) {
-        const int k = k0 + s;
-        if (k < wr.cnt) compute(ring[s], k);
-        // always refill (clamped to the last page: a cache hit, no HBM traffic)
-        // so the in-order load counter stays a compile-time pattern
-        issue(ring[s], min(k + DEPTH, wr.cnt - 1));
-      }
-    }
-  }
-
-  // Wavefront partials -> LDS.
-  float* sm_o = smem;                 // [W][g][D]
-  float* sm_m = smem + W * g * D;     // [W][HP]
-  float* sm_l = sm_m + W * HP;        // [W][HP]
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const float lt = group4_sum(lsum[nt]);
-    const float zt = ZP ? group4_sum(zacc[nt]) : 0.0f;
-    const int jj = nt * 16 + r;
-    if (jj < g) {
-#pragma unroll
-      for (int nc = 0; nc < NC; ++nc) {
-        f32x4_t v = acc[nt][nc];
-        if constexpr (ZP) v += zt;
-        *reinterpret_cast<f32x4_t*>(sm_o + (wave * g + jj) * D + 16 * nc + 4 * gq) = v;
-      }
-      if (gq == 0) {
-        sm_m[wave * HP + jj] = m[nt];
-        sm_l[wave * HP + jj] = lt;
-      }
-    }
-  }
-  __syncthreads();
-  combine_and_store<D, SCHED>(a, wr, sm_o, sm_m, sm_l, W, HP);
-}
-
-// One workgroup: a (sequence, KV head, split) of the uniform plan.
-template <int F, int P, int D, int NT, int DEPTH>
-__global__ __launch_bounds__(mfma_max_threads(P, D, NT)) void decode_mfma_kernel(DecodeArgs a) {
-  extern __shared__ float smem[];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int W = blockDim.x >> 6;
-  mfma_item<F, P, D, NT, DEPTH, false>(a, work_range<P>(a, wave, W), smem);
-}
-
-// ---------------------------------------------------------------------------
-// Balanced schedule on the matrix-core path: one wavefront streams one bin.
-// The bin's items (pieces of (sequence, KV head) pairs) pass through the
-// same register ring one after another, so the loads of an item's first
-// pages are in flight while the previous item's last pages are computed, and
-// no workgroup barrier separates items: the wavefront writes each item's
-// result (the output, or a normalized partial for the merge) from its own
-// registers.  Wavefronts of a workgroup are independent.
-
-// Where one side (issue or compute) of a stream stands: item `item` of the
-// schedule (== end once the stream is done), page k of its range.
-struct StreamPos {
-  int item, k;
-  WorkRange wr;
-};
-
-// From p.item on: the first valid item (with nonempty range when
-// need_pages), its range loaded and k = 0.
-template <int P>
-__device__ __forceinline__ void stream_seek(const DecodeArgs& a, StreamPos& p, int end,
-                                            bool need_pages) {
-  for (; p.item < end; ++p.item) {
-    if (!item_valid(a, p.item)) continue;
-    p.wr = item_range<P>(a, p.item, 0, 1);
-    if (!need_pages || p.wr.cnt > 0) break;
-  }
-  p.k = 0;
-}
-
-template <int F, int P, int D, int NT, int DEPTH>
-__global__ __launch_bounds__(256) void decode_mfma_stream_kernel(DecodeArgs a) {
-  using S = MfmaShape<F, P, D>;
-  using FI = FmtInfo<F>;
-  constexpr bool Q = FI::quant, ZP = FI::zero;
-  constexpr int T = S::T, KK = S::KK, NC = S::NC, EV = S::EV, RB = S::RB, KB = S::KB;
-  using OpA = typename std::conditional<Q, f16x8_t, bf16x8_t>::type;
-  using OpPV = typename std::conditional<
-      T == 1, typename std::conditional<Q, f16x4_t, bf16x4_t>::type, OpA>::type;
-  using KLoad = typename LoadT<S::KLB>::type;
-  using VLoad = typename LoadT<S::VB>::type;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int bin = blockIdx.x * (blockDim.x >> 6) + wave;
-  if (bin >= a.num_bins) return;  // the whole wavefront; nothing here waits on the others
-  const int r = lane & 15, gq = lane >> 4;
-  const int g = a.group;
-  const int H = a.num_kv_heads;
-  const int i_begin = max(a.sched[8 + bin], 0);
-  const int end = min(a.sched[9 + bin], a.num_items);
-
-  int koff[T];
-#pragma unroll
-  for (int st = 0; st < T; ++st) {
-    const int tok = (T == 1) ? r : 8 * (r >> 2) + 4 * st + (r & 3);
-    koff[st] = tok * RB + S::k_lane_offset(gq);
-  }
-  const int voff = F == kBF16 ? (r * P + EV * gq) * 2
-                              : (F == kI4 ? (r >> 1) * P : r * P) + EV * gq;
-  constexpr int vstride = F == kBF16 ? 16 * P * 2 : (F == kI4 ? 8 * P : 16 * P);
-  const int moff = EV * gq * 4;
-  const size_t tile_bytes = size_t(P) * RB;
-  const char* kbase = static_cast<const char*>(a.k_pool);
-  const char* vbase = static_cast<const char*>(a.v_pool);
-
-  // issue side: loads page ip.k of item ip.item; once the stream's pages are
-  // all issued it repeats the last page (a cache hit) so the ring's load
-  // pattern stays fixed
-  StreamPos ip;
-  ip.item = i_begin;
-  stream_seek<P>(a, ip, end, true);
-  bool issued_all = ip.item >= end;
-  auto issue = [&](PageRegs<F, P, D>& R) __attribute__((always_inline)) {
-    const int32_t* btrow = a.bt + int64_t(ip.wr.b) * a.max_blocks;
-    int phys = btrow[ip.wr.logical(ip.wr.kb0 + ip.k)];
-    const bool ok = unsigned(phys) < unsigned(a.num_pages);
-    R.phys = ok ? phys : -1;
-    const int64_t tile = int64_t(ok ? phys : 0) * H + ip.wr.h;
-    const char* kp = kbase + tile * tile_bytes;
-    const char* vp = vbase + tile * tile_bytes;
-#pragma unroll
-    for (int st = 0; st < T; ++st)
-#pragma unroll
-      for (int i = 0; i < S::KN; ++i)
-        R.k[st][i] = load_stream<KLoad>(kp + koff[st] + i * 64);
-#pragma unroll
-    for (int nc = 0; nc < NC; ++nc) R.v[nc] = load_stream<VLoad>(vp + voff + nc * vstride);
-    if constexpr (Q) {
-      const char* km = reinterpret_cast<const char*>(a.k_meta) + tile * (P * 4);
-      const char* vm = reinterpret_cast<const char*>(a.v_meta) + tile * (P * 4);
-#pragma unroll
-      for (int st = 0; st < T; ++st) {
-        R.km[st] = load_stream<uint4>(km + moff + st * 16);
-        R.vm[st] = load_stream<uint4>(vm + moff + st * 16);
-      }
-    }
-    // advance to the next page of the stream (or stay on the last one)
-    if (!issued_all) {
-      if (++ip.k >= ip.wr.cnt) {
-        StreamPos nx = ip;
-        ++nx.item;
-        stream_seek<P>(a, nx, end, true);
-        if (nx.item < end) ip = nx;
-        else { issued_all = true; ip.k = ip.wr.cnt - 1; }
-      }
-    }
-  };
-
-  // per-item state: q operands, online softmax
-  OpA qop[NT][KK];
-  float qsum[NT];
-  float m[NT], lsum[NT], zacc[NT];
-  f32x4_t acc[NT][NC];
-  auto begin_item = [&](const WorkRange& wr) __attribute__((always_inline)) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int jj = nt * 16 + r;
-      const bool live = jj < g;
-      const uint16_t* qrow =
-          a.q + (int64_t(wr.b) * a.num_q_heads + int64_t(wr.h) * g + (live ? jj : 0)) * D;
-      float qs = 0.0f;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int d0 = S::q_channel(kk, gq);
-        uint4 raw = live ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
-        if constexpr (!Q) {
-          qop[nt][kk] = __builtin_bit_cast(bf16x8_t, raw);
-        } else {
-          const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-          f16x8_t v;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float f = bf16_to_f32((w4[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-            v[e] = (_Float16)f;
-            qs += f;
-          }
-          qop[nt][kk] = v;
-        }
-      }
-      qsum[nt] = ZP ? group4_sum(qs) : 0.0f;
-      m[nt] = -INFINITY;
-      lsum[nt] = 0.0f;
-      zacc[nt] = 0.0f;
-#pragma unroll
-      for (int nc = 0; nc < NC; ++nc) acc[nt][nc] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-  };
-  // the item's result: o / l (and m, l for a partial), straight from registers
-  auto finish_item = [&](const WorkRange& wr) __attribute__((always_inline)) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const float lt = group4_sum(lsum[nt]);
-      const float zt = ZP ? group4_sum(zacc[nt]) : 0.0f;
-      const int jj = nt * 16 + r;
-      if (jj < g) {
-        const int64_t row = int64_t(wr.b) * a.num_q_heads + int64_t(wr.h) * g + jj;
-        const int64_t pr = int64_t(wr.slot) * g + jj;
-#pragma unroll
-        for (int nc = 0; nc < NC; ++nc) {
-          f32x4_t v = acc[nt][nc];
-          if constexpr (ZP) v += zt;
-          const int d = 16 * nc + 4 * gq;
-          if (wr.slot < 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              a.out[row * D + d + i] = f32_to_bf16_rne(lt > 0.0f ? v[i] / lt : 0.0f);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a.part_o[pr * D + d + i] = lt > 0.0f ? v[i] / lt : 0.0f;
-          }
-        }
-        if (wr.slot >= 0 && gq == 0) {
-          a.part_ml[pr * 2] = m[nt];
-          a.part_ml[pr * 2 + 1] = lt;
-        }
-      }
-    }
-  };
-
-  auto compute = [&](const PageRegs<F, P, D>& R, const WorkRange& wr,
-                     int k) __attribute__((always_inline)) {
-    if (R.phys < 0) return;  // absent page: its tokens do not take part
-    const PageMask pm = page_mask<P>(wr, wr.logical(wr.kb0 + k));
-    const bool tail = pm.partial;
-
-    // K operands for all sub-tiles (shared by every head tile).
-    OpA kop[T][KK];
-#pragma unroll
-    for (int st = 0; st < T; ++st) {
-      if constexpr (!Q) {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kop[st][kk] = __builtin_bit_cast(bf16x8_t, R.k[st][kk]);
-      } else {
-        uint32_t w[KB / 4];
-        __builtin_memcpy(w, R.k[st], KB);
-        constexpr int DW = F == kI4 ? 1 : 2;  // dwords per 8 channels
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kop[st][kk] = codes8_to_f16x8<F>(w + DW * kk);
-      }
-    }
-    // V^T operands.
-    OpPV vop[NC];
-#pragma unroll
-    for (int nc = 0; nc < NC; ++nc) {
-      if constexpr (!Q) {
-        VLoad raw = R.v[nc];
-        if (tail) {
-          // rows past the sequence may hold anything (NaN): zero them so 0*x stays 0
-          uint32_t wv[EV / 2];
-          __builtin_memcpy(wv, &raw, sizeof(raw));
-#pragma unroll
-          for (int e = 0; e < EV; ++e) {
-            if (!pm.valid(EV * gq + e)) wv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          }
-          __builtin_memcpy(&raw, wv, sizeof(raw));
-        }
-        vop[nc] = __builtin_bit_cast(OpPV, raw);
-      } else {
-        uint32_t wv[EV / 4];
-        __builtin_memcpy(wv, &R.v[nc], sizeof(R.v[nc]));
-        OpPV v;
-#pragma unroll
-        for (int i = 0; i < EV / 4; ++i) {
-          f16x2_t lo, hi;
-          if constexpr (F == kI8)
-            i8x4_to_f16x4(wv[i], lo, hi);
-          else if constexpr (F == kFP8)
-            fp8x4_to_f16x4(wv[i], lo, hi);
-          else
-            i4sel4_to_f16x4(wv[i], (r & 1) != 0, lo, hi);
-          v[4 * i + 0] = lo[0];
-          v[4 * i + 1] = lo[1];
-          v[4 * i + 2] = hi[0];
-          v[4 * i + 3] = hi[1];
-        }
-        vop[nc] = v;
-      }
-    }
-    // Per-token scale (and zero point) of this lane's rows.
-    float ks[T][4], kz[T][4], vs[T][4], vz[T][4];
-    if constexpr (Q) {
-#pragma unroll
-      for (int st = 0; st < T; ++st) {
-        const uint32_t kw[4] = {R.km[st].x, R.km[st].y, R.km[st].z, R.km[st].w};
-        const uint32_t vw[4] = {R.vm[st].x, R.vm[st].y, R.vm[st].z, R.vm[st].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ks[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] & 0xffffu)) * FI::scale_mul;
-          kz[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] >> 16));
-          vs[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(vw[i] & 0xffffu)) * FI::scale_mul;
-          vz[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(vw[i] >> 16));
-        }
-      }
-    }
-
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float x[T][4];
-#pragma unroll
-      for (int st = 0; st < T; ++st) {
-        f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) sc = mfma_16x16x32(kop[st][kk], qop[nt][kk], sc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (ZP)
-            x[st][i] = (ks[st][i] * sc[i] + kz[st][i] * qsum[nt]) * a.scale_log2;
-          else if constexpr (Q)
-            x[st][i] = ks[st][i] * sc[i] * a.scale_log2;
-          else
-            x[st][i] = sc[i] * a.scale_log2;
-        }
-      }
-      if (tail) {
-#pragma unroll
-        for (int st = 0; st < T; ++st)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (!pm.valid(EV * gq + 4 * st + i)) x[st][i] = -INFINITY;
-      }
-      float mloc = x[0][0];
-#pragma unroll
-      for (int st = 0; st < T; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, x[st][i]);
-      mloc = group4_max(mloc);
-      const float mnew = fmaxf(m[nt], mloc);
-      const float al = fast_exp2(m[nt] - mnew);
-      m[nt] = mnew;
-      float p[T][4];
-      float ps = 0.0f;
-#pragma unroll
-      for (int st = 0; st < T; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[st][i] = fast_exp2(x[st][i] - mnew);
-          ps += p[st][i];
-        }
-      lsum[nt] = lsum[nt] * al + ps;
-      // once the running maximum settles, al is exactly 1 for every head:
-      // skip the (identity) rescale of the accumulators
-      if (wave_any(al != 1.0f)) {
-#pragma unroll
-        for (int nc = 0; nc < NC; ++nc) acc[nt][nc] *= al;
-      }
-      OpPV pop;
-      if constexpr (Q) {
-        float zs = 0.0f;
-#pragma unroll
-        for (int st = 0; st < T; ++st)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool valid = !tail || pm.valid(EV * gq + 4 * st + i);
-            const float pv = valid ? p[st][i] * vs[st][i] : 0.0f;
-            if constexpr (ZP) zs += valid ? p[st][i] * vz[st][i] : 0.0f;
-            pop[4 * st + i] = (_Float16)pv;
-          }
-        zacc[nt] = zacc[nt] * al + zs;
-      } else {
-#pragma unroll
-        for (int st = 0; st < T; ++st)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pop[4 * st + i] = (__bf16)p[st][i];
-      }
-#pragma unroll
-      for (int nc = 0; nc < NC; ++nc) {
-        if constexpr (T == 1)
-          acc[nt][nc] = mfma_16x16x16(vop[nc], pop, acc[nt][nc]);
-        else
-          acc[nt][nc] = mfma_16x16x32(vop[nc], pop, acc[nt][nc]);
-      }
-    }
-  };
-
-
-  // compute side: every valid item in order (empty ones give 0 or an empty
-  // partial right away); pages in the order they were issued.  Each item's
-  // pages run through a loop whose ring slots are compile-time constants
-  // (like the uniform kernel's), so the load counter waits stay those of a
-  // steady stream; the item's start and end (q loads, result stores) sit
-  // outside that loop.
-  static_assert(DEPTH >= 1 && DEPTH <= 4, "stream ring of one to four pages");
-  StreamPos cp;
-  cp.item = i_begin;
-  stream_seek<P>(a, cp, end, false);
-  if (issued_all) {  // no pages at all: only empty items
-    for (; cp.item < end; ++cp.item, stream_seek<P>(a, cp, end, false)) {
-      begin_item(cp.wr);
-      finish_item(cp.wr);
-    }
-    return;
-  }
-  PageRegs<F, P, D> ring[DEPTH];
-#pragma unroll
-  for (int s = 0; s < DEPTH; ++s) issue(ring[s]);
-  // pages of the current item, its first page in ring slot S0
-  auto item_pages = [&](auto s0_tag) __attribute__((always_inline)) {
-    constexpr int S0 = decltype(s0_tag)::value;
-    const int cnt = cp.wr.cnt;
-    int k = 0;
-    for (; k + DEPTH <= cnt; k += DEPTH) {
-#pragma unroll
-      for (int s = 0; s < DEPTH; ++s) {
-        compute(ring[(S0 + s) % DEPTH], cp.wr, k + s);
-        issue(ring[(S0 + s) % DEPTH]);
-      }
-    }
-    // fewer than DEPTH pages left, from slot S0 on
-#pragma unroll
-    for (int s = 0; s < DEPTH - 1; ++s) {
-      if (k + s < cnt) {
-        compute(ring[(S0 + s) % DEPTH], cp.wr, k + s);
-        issue(ring[(S0 + s) % DEPTH]);
-      }
-    }
-  };
-  auto pages_from_slot = [&](int s0) __attribute__((always_inline)) {
-    if (s0 == 0) {
-      item_pages(std::integral_constant<int, 0>{});
-    } else if constexpr (DEPTH > 1) {
-      if (s0 == 1) {
-        item_pages(std::integral_constant<int, 1>{});
-      } else if constexpr (DEPTH > 2) {
-        if (s0 == 2)
-          item_pages(std::integral_constant<int, 2>{});
-        else if constexpr (DEPTH > 3)
-          item_pages(std::integral_constant<int, 3>{});
-      }
-    }
-  };
-  int slot0 = 0;
-  for (; cp.item < end; ++cp.item, stream_seek<P>(a, cp, end, false)) {
-    begin_item(cp.wr);
-    if (cp.wr.cnt > 0) {
-      pages_from_slot(slot0);
-      slot0 = (slot0 + cp.wr.cnt) % DEPTH;
-    }
-    finish_item(cp.wr);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Vector-ALU kernel for g < 4.  Lane l: token row tr = l/4 (+16 per extra
-// sub-tile), channel quarter c = l%4 for q.k; output channels l*D/64.. for P.V.
-template <int F>
-__device__ __forceinline__ float code_to_f32(uint32_t byte_or_nibble) {
-  if constexpr (F == kI8) {
-    return float(int8_t(byte_or_nibble & 0xffu));
-  } else if constexpr (F == kI4) {
-    return float(int(byte_or_nibble & 0xfu) - 8);
-  } else {  // e4m3 value times 2^-8 (the scale carries 2^8)
-    const uint32_t b = byte_or_nibble & 0xffu;
-    return (float)__builtin_bit_cast(_Float16, uint16_t(((b & 0x80u) << 8) | ((b & 0x7fu) << 7)));
-  }
-}
-
-template <int F, int P, int D, int G, int DEPTH, bool SCHED>
-__device__ __forceinline__ void valu_item(const DecodeArgs& a, const WorkRange& wr, float* smem) {
-  using FI = FmtInfo<F>;
-  constexpr bool Q = FI::quant, ZP = FI::zero;
-  constexpr int TPL = P / 16;             // token rows per lane
-  constexpr int DQ = D / 4;               // channels per lane for q.k
-  constexpr int DV = D / 64;              // output channels per lane
-  constexpr int RB = D * FI::bits / 8;    // bytes of a stored token row
-  constexpr int KB = DQ * FI::bits / 8;   // K bytes per lane per token row
-  constexpr int KLB = KB >= 16 ? 16 : KB;
-  constexpr int KN = KB / KLB;
-  // V^T bytes per lane: its DV channels over P tokens ([D][P] elements; for
-  // INT4 the P bytes of the channel pair holding them)
-  constexpr int VBT = F == kI4 ? P : DV * P * FI::bits / 8;
-  constexpr int VL = VBT / 16;
-  using KLoad = typename LoadT<KLB>::type;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int W = blockDim.x >> 6;
-  const int tr = lane >> 2, c = lane & 3;
-  const int H = a.num_kv_heads;
-  float* sm_o = smem;                  // [W][G][D]
-  float* sm_m = smem + W * G * D;      // [W][G]
-  float* sm_l = sm_m + W * G;          // [W][G]
-  float* pbuf = sm_l + W * G + wave * G * P;  // this wave's [G][P] probabilities
-
-  float qf[G][DQ];
-  float qsum[G];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const uint16_t* qrow = a.q + (int64_t(wr.b) * a.num_q_heads + int64_t(wr.h) * G + j) * D;
-    float qs = 0.0f;
-#pragma unroll
-    for (int e = 0; e < DQ; ++e) {
-      qf[j][e] = bf16_to_f32(qrow[c * DQ + e]);
-      qs += qf[j][e];
-    }
-    qs += __shfl_xor(qs, 1);
-    qs += __shfl_xor(qs, 2);
-    qsum[j] = qs;
-  }
-
-  struct Regs {
-    KLoad k[TPL][KN];
-    uint4 v[VL];
-    uint32_t km[TPL], vm[TPL];
-    int phys;
-  };
-  const size_t tile_bytes = size_t(P) * RB;
-  const char* kbase = static_cast<const char*>(a.k_pool);
-  const char* vbase = static_cast<const char*>(a.v_pool);
-  const int32_t* btrow = a.bt + int64_t(wr.b) * a.max_blocks;
-  const int vrow = F == kI4 ? (DV == 2 ? lane : (lane >> 1)) * P : lane * VBT;
-
-  auto issue = [&](Regs& R, int k) {
-    int phys = btrow[wr.logical(wr.kb0 + k)];
-    const bool ok = unsigned(phys) < unsigned(a.num_pages);
-    R.phys = ok ? phys : -1;
-    const int64_t tile = int64_t(ok ? phys : 0) * H + wr.h;
-    const char* kp = kbase + tile * tile_bytes;
-    const char* vp = vbase + tile * tile_bytes;
-#pragma unroll
-    for (int u = 0; u < TPL; ++u)
-#pragma unroll
-      for (int i = 0; i < KN; ++i)
-        R.k[u][i] = load_stream<KLoad>(kp + (tr + 16 * u) * RB + c * KB + KLB * i);
-#pragma unroll
-    for (int i = 0; i < VL; ++i) R.v[i] = load_stream<uint4>(vp + vrow + 16 * i);
-    if constexpr (Q) {
-      const uint32_t* km = reinterpret_cast<const uint32_t*>(a.k_meta) + tile * P;
-      const uint32_t* vm = reinterpret_cast<const uint32_t*>(a.v_meta) + tile * P;
-#pragma unroll
-      for (int u = 0; u < TPL; ++u) {
-        R.km[u] = load_stream<uint32_t>(km + tr + 16 * u);
-        R.vm[u] = load_stream<uint32_t>(vm + tr + 16 * u);
-      }
-    }
-  };
-
-  float m[G], lsum[G], zacc[G], acc[G][DV];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    m[j] = -INFINITY;
-    lsum[j] = 0.0f;
-    zacc[j] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < DV; ++e) acc[j][e] = 0.0f;
-  }
-
-  auto compute = [&](const Regs& R, int k) {
-    if (R.phys < 0) return;
-    const PageMask pm = page_mask<P>(wr, wr.logical(wr.kb0 + k));
-    const bool tail = pm.partial;
-    float x[TPL][G];
-#pragma unroll
-    for (int u = 0; u < TPL; ++u) {
-      float kv[DQ];
-      uint32_t w[KB / 4];
-      __builtin_memcpy(w, R.k[u], KB);
-#pragma unroll
-      for (int e = 0; e < DQ; ++e) {
-        if constexpr (F == kBF16)
-          kv[e] = bf16_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-        else if constexpr (F == kI4)
-          kv[e] = code_to_f32<F>(w[e >> 3] >> (4 * (e & 7)));
-        else
-          kv[e] = code_to_f32<F>(w[e >> 2] >> (8 * (e & 3)));
-      }
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        float dsum = 0.0f;
-#pragma unroll
-        for (int e = 0; e < DQ; ++e) dsum += qf[j][e] * kv[e];
-        dsum += __shfl_xor(dsum, 1);
-        dsum += __shfl_xor(dsum, 2);
-        float sc = dsum;
-        if constexpr (Q) {
-          const float s =
-              (float)__builtin_bit_cast(_Float16, uint16_t(R.km[u] & 0xffffu)) * FI::scale_mul;
-          sc = s * dsum;
-          if constexpr (ZP) {
-            const float z = (float)__builtin_bit_cast(_Float16, uint16_t(R.km[u] >> 16));
-            sc = s * dsum + z * qsum[j];
-          }
-        }
-        x[u][j] = sc * a.scale_log2;
-        if (tail && !pm.valid(tr + 16 * u)) x[u][j] = -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      float mloc = x[0][j];
-#pragma unroll
-      for (int u = 1; u < TPL; ++u) mloc = fmaxf(mloc, x[u][j]);
-      mloc = wave_max(mloc);
-      const float mnew = fmaxf(m[j], mloc);
-      const float al = fast_exp2(m[j] - mnew);
-      m[j] = mnew;
-      float ps = 0.0f, zs = 0.0f;
-#pragma unroll
-      for (int u = 0; u < TPL; ++u) {
-        const float p = fast_exp2(x[u][j] - mnew);
-        const bool valid = !tail || pm.valid(tr + 16 * u);
-        float pv = p;
-        if constexpr (Q) {
-          const float vs =
-              (float)__builtin_bit_cast(_Float16, uint16_t(R.vm[u] & 0xffffu)) * FI::scale_mul;
-          pv = valid ? p * vs : 0.0f;
-          if constexpr (ZP) {
-            const float vz = (float)__builtin_bit_cast(_Float16, uint16_t(R.vm[u] >> 16));
-            zs += valid ? p * vz : 0.0f;
-          }
-        }
-        ps += p;
-        if (c == 0) pbuf[j * P + tr + 16 * u] = pv;
-      }
-      lsum[j] = lsum[j] * al + (c == 0 ? ps : 0.0f);
-      zacc[j] = zacc[j] * al + (c == 0 ? zs : 0.0f);
-#pragma unroll
-      for (int e = 0; e < DV; ++e) acc[j][e] *= al;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // P.V: this lane's output channels d = lane*DV + e over all P tokens.
-    float vv[DV][P];
-    {
-      uint32_t wv[VL * 4];
-      __builtin_memcpy(wv, R.v, sizeof(R.v));
-#pragma unroll
-      for (int e = 0; e < DV; ++e)
-#pragma unroll
-        for (int t = 0; t < P; ++t) {
-          float f;
-          if constexpr (F == kBF16) {
-            const int idx = e * P + t;
-            f = bf16_to_f32((wv[idx >> 1] >> (16 * (idx & 1))) & 0xffffu);
-            if (tail && !pm.valid(t)) f = 0.0f;
-          } else if constexpr (F == kI4) {
-            // byte t of the pair row; this channel's nibble
-            const int nib = DV == 2 ? e : (lane & 1);
-            f = code_to_f32<F>((wv[t >> 2] >> (8 * (t & 3))) >> (4 * nib));
-          } else {
-            const int idx = e * P + t;
-            f = code_to_f32<F>(wv[idx >> 2] >> (8 * (idx & 3)));
-          }
-          vv[e][t] = f;
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-#pragma unroll
-      for (int t4 = 0; t4 < P / 4; ++t4) {
-        const float4 pp = *reinterpret_cast<const float4*>(pbuf + j * P + 4 * t4);
-#pragma unroll
-        for (int e = 0; e < DV; ++e) {
-          acc[j][e] += pp.x * vv[e][4 * t4] + pp.y * vv[e][4 * t4 + 1] +
-                       pp.z * vv[e][4 * t4 + 2] + pp.w * vv[e][4 * t4 + 3];
-        }
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-  };
-
-  if (wr.cnt > 0) {
-    Regs ring[DEPTH];
-#pragma unroll
-    for (int s = 0; s < DEPTH; ++s) issue(ring[s], min(s, wr.cnt - 1));
-    for (int k0 = 0; k0 < wr.cnt; k0 += DEPTH) {
-#pragma unroll
-      for (int s = 0; s < DEPTH; ++s) {
-        const int k = k0 + s;
-        if (k < wr.cnt) compute(ring[s], k);
-        issue(ring[s], min(k + DEPTH, wr.cnt - 1));
-      }
-    }
-  }
-
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const float lt = wave_sum_f(lsum[j]);
-    const float zt = ZP ? wave_sum_f(zacc[j]) : 0.0f;
-#pragma unroll
-    for (int e = 0; e < DV; ++e) sm_o[(wave * G + j) * D + lane * DV + e] = acc[j][e] + zt;
-    if (lane == 0) {
-      sm_m[wave * G + j] = m[j];
-      sm_l[wave * G + j] = lt;
-    }
-  }
-  __syncthreads();
-  combine_and_store<D, SCHED>(a, wr, sm_o, sm_m, sm_l, W, G);
-}
-
-template <int F, int P, int D, int G, int DEPTH, bool SCHED>
-__global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(DecodeArgs a) {
-  extern __shared__ float smem[];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int W = blockDim.x >> 6;
-  if constexpr (!SCHED) {
-    valu_item<F, P, D, G, DEPTH, false>(a, work_range<P>(a, wave, W), smem);
-  } else {
-    const int i0 = max(a.sched[8 + blockIdx.x], 0);
-    const int i1 = min(a.sched[9 + blockIdx.x], a.num_items);
-    for (int i = i0; i < i1; ++i) {
-      if (!item_valid(a, i)) continue;
-      valu_item<F, P, D, G, DEPTH, true>(a, item_range<P>(a, i, wave, W), smem);
-      __syncthreads();  // the next item reuses the LDS merge and probability buffers
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Log-sum-exp merge of split partials, one wavefront per output row:
-// M = max_s m_s; w_s = l_s 2^(m_s - M); out = sum_s w_s o_s / sum_s w_s.
-// Partial s of the row: o at po + s*so (D floats), (m, l) at pml + s*sml.
-template <int D>
-__device__ __forceinline__ void lse_merge_row(const float* __restrict__ po, int64_t so,
-                                              const float* __restrict__ pml, int64_t sml, int S,
-                                              uint16_t* __restrict__ out_row) {
-  constexpr int E = D / 64;
-  const int lane = threadIdx.x & 63;
-  float M = -INFINITY;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, pml[s * sml]);
-  M = wave_max(M);
-  float o[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.0f;
-  float L = 0.0f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float ms = pml[s * sml], ls = pml[s * sml + 1];
-      if (ls > 0.0f) {
-        const float w = ls * fast_exp2(ms - M);
-        L += w;
-        const float* p = po + s * so + lane * E;
-#pragma unroll
-        for (int e = 0; e < E; ++e) o[e] += w * p[e];
-      }
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e) out_row[lane * E + e] = f32_to_bf16_rne(L > 0.0f ? o[e] / L : 0.0f);
-}
-
-// Uniform plan: row = b*H_q + j holds its S partials at (row*S + s).
-template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
-                                                    const float* __restrict__ part_ml,
-                                                    uint16_t* __restrict__ out, int rows, int S) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  lse_merge_row<D>(part_o + int64_t(row) * S * D, D, part_ml + int64_t(row) * S * 2, 2, S,
-                   out + int64_t(row) * D);
-}
-
-// Balanced schedule: merge entry e = (sequence, KV head, first slot, count);
-// query head j of its group has partial (slot*g + j) for each of its slots.
-template <int D>
-__global__ __launch_bounds__(256) void merge_sched_kernel(const float* __restrict__ part_o,
-                                                          const float* __restrict__ part_ml,
-                                                          const int32_t* __restrict__ entries,
-                                                          uint16_t* __restrict__ out, int rows,
-                                                          int g, int num_q_heads, int num_seqs,
-                                                          int num_slots) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int e = row / g, j = row - e * g;
-  const int32_t* m = entries + int64_t(e) * 4;
-  const int b = m[0], h = m[1], first = m[2], cnt = m[3];
-  // entries that name rows or slots outside this call are skipped
-  if (unsigned(b) >= unsigned(num_seqs) || unsigned(h) >= unsigned(num_q_heads / g) ||
-      first < 0 || cnt < 1 || int64_t(first) + cnt > num_slots)
-    return;
-  const int64_t p0 = int64_t(first) * g + j;
-  lse_merge_row<D>(part_o + p0 * D, int64_t(g) * D, part_ml + p0 * 2, int64_t(g) * 2, cnt,
-                   out + (int64_t(b) * num_q_heads + int64_t(h) * g + j) * D);
-}
-
-// ---------------------------------------------------------------------------
-// Host side.
-constexpr int kDepth = 2;
-// Pages a matrix-core wavefront keeps in flight: INT4 pages are half the
-// bytes of INT8 ones, so it keeps twice as many.
-template <int F> constexpr int mfma_depth() { return F == kI4 ? 4 : kDepth; }
+// Instantiated in the per-format files.
+#define KVP_DECODE_FMT_EXTERN(F)                                                    \
+  extern template hipError_t launch_decode_fmt<F, false>(const DecodeArgs&, int, int, bool, \
+                                                         int, dim3, dim3, size_t,        \
+                                                         hipStream_t);                   \
+  extern template hipError_t launch_decode_fmt<F, true>(const DecodeArgs&, int, int, bool,  \
+                                                        int, dim3, dim3, size_t, hipStream_t);
+KVP_DECODE_FMT_EXTERN(kBF16)
+KVP_DECODE_FMT_EXTERN(kI8)
+KVP_DECODE_FMT_EXTERN(kI4)
+KVP_DECODE_FMT_EXTERN(kFP8)
+#undef KVP_DECODE_FMT_EXTERN
 
 int cu_count_current_device() {
   static int cache[64] = {0};
@@ -1365,61 +32,6 @@ int cu_count_current_device() {
     return -1;
   if (dev < 64) cache[dev] = n;
   return n;
-}
-
-template <int F, int P, int D, bool SCHED>
-hipError_t launch_decode_pd(const DecodeArgs& a, bool mfma, int g, dim3 grid, dim3 block,
-                            size_t lds, hipStream_t s) {
-  discard_stale_error();
-  const int nt = g <= 16 ? 1 : g <= 32 ? 2 : 4;
-  const int max_threads = mfma ? mfma_max_threads(P, D, nt) : valu_max_threads(P, D, g);
-  if (int(block.x) > max_threads) return hipErrorInvalidConfiguration;
-  if (mfma) {
-    // balanced schedule: one stream per wavefront, no LDS
-    if constexpr (SCHED) {
-      if (g <= 16)
-        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 1, mfma_depth<F>()>), grid, block,
-                           0, s, a);
-      else if (g <= 32)
-        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 2, mfma_depth<F>()>), grid, block,
-                           0, s, a);
-      else
-        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 4, mfma_depth<F>()>), grid, block,
-                           0, s, a);
-    } else {
-      if (g <= 16)
-        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 1, mfma_depth<F>()>), grid, block, lds,
-                           s, a);
-      else if (g <= 32)
-        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 2, mfma_depth<F>()>), grid, block, lds,
-                           s, a);
-      else
-        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 4, mfma_depth<F>()>), grid, block, lds,
-                           s, a);
-    }
-  } else {
-    if (g == 1)
-      hipLaunchKernelGGL((decode_valu_kernel<F, P, D, 1, kDepth, SCHED>), grid, block, lds, s,
-                         a);
-    else if (g == 2)
-      hipLaunchKernelGGL((decode_valu_kernel<F, P, D, 2, kDepth, SCHED>), grid, block, lds, s,
-                         a);
-    else
-      hipLaunchKernelGGL((decode_valu_kernel<F, P, D, 3, kDepth, SCHED>), grid, block, lds, s,
-                         a);
-  }
-  return hipGetLastError();
-}
-
-// Instance for the pool's (page size, head dim); the descriptor was validated.
-template <int F, bool SCHED>
-hipError_t launch_decode_fmt(const DecodeArgs& a, int P, int D, bool mfma, int g, dim3 grid,
-                             dim3 block, size_t lds, hipStream_t s) {
-  if (P == 16)
-    return D == 64 ? launch_decode_pd<F, 16, 64, SCHED>(a, mfma, g, grid, block, lds, s)
-                   : launch_decode_pd<F, 16, 128, SCHED>(a, mfma, g, grid, block, lds, s);
-  return D == 64 ? launch_decode_pd<F, 32, 64, SCHED>(a, mfma, g, grid, block, lds, s)
-                 : launch_decode_pd<F, 32, 128, SCHED>(a, mfma, g, grid, block, lds, s);
 }
 
 template <bool SCHED>
