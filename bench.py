@@ -591,6 +591,11 @@ def main(argv=None):
         out["roofline"]["traffic"] = rec["traffic_bytes_per_launch"]
         out["roofline"]["traffic_over_algorithmic"] = round(
             rec["traffic_bytes_per_launch"] / sb["split_kernel_per_launch"], 4)
+        # the same record's cache and ALU counters for this kernel, when taken
+        counters = {k: rec[k] for k in ("l2_hit_rate", "valu_busy_pct", "mfma_util_pct")
+                    if k in rec}
+        if counters:
+            out["roofline"]["counters"] = counters
     out["copy_probe"] = copy_probe(dev)
     hc = None
     if not (args.no_parity and args.no_cpu_baseline):

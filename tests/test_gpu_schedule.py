@@ -13,6 +13,7 @@ import torch
 
 import oracle
 from workloads import INT4_LONG, INT8_LONG, LLAMA3_8B_LAYER, make_case, variant
+from workloads.generate import f32_to_bf16_bits
 
 from .casetools import assert_close, assert_within_one_rounding, layout_of
 from .gpu_harness import GpuCase, dev32, log
@@ -68,6 +69,42 @@ def test_scheduled_decode_lowbit(kvp, cfg):
         out = gc.decode_scheduled(max_bins=bins)
         log(f"[sched lowbit] {cfg.name} bins<={bins} {_info(gc.last_schedule)}")
         assert_close(out, ref, f"{cfg.name} bins<={bins}")
+    gc.close()
+
+
+@pytest.mark.parametrize("name", ["l8b_small", "int8_small", "prefix_small"])
+def test_one_device_schedule_serves_many_calls(kvp, name):
+    """One device copy of a schedule that cuts pairs across bins serves calls
+    in stream order (the layers of a step): four calls with different
+    queries on one copy, each against the oracle; the schedule words are
+    left as they were."""
+    cfg = next(c for c in SMALL if c.name == name)
+    case = _case(cfg)
+    k, v, km, vm, _ = _oracle(case)
+    gc = GpuCase(kvp, case)
+    gc.upload(k, v, km, vm)
+    sched = kvp.kvp_decode_schedule(gc.pool, case.ctx, cfg.num_q_heads,
+                                    int(case.block_tables.shape[1]), 7)
+    i = sched.info
+    log(f"[sched reuse] {name} {_info(sched)}")
+    assert i.num_merge > 0, "the case must cut pairs across bins"
+    sdev = dev32(sched.used)
+    ws = torch.full((i.workspace_bytes // 4 + 1,), float("nan"), dtype=torch.float32,
+                    device="cuda")
+    rng = np.random.default_rng(4650)
+    lay = layout_of(case)
+    for call in range(4):
+        qh = case.q if call == 0 else f32_to_bf16_bits(
+            rng.standard_normal(case.q.shape).astype(np.float32))
+        ref = oracle.paged_decode(lay, qh, k, v, km, vm, case.block_tables, case.ctx, case.scale)
+        q = torch.from_numpy(qh.view(np.int16)).cuda()
+        out = torch.full_like(q, int(np.uint16(0x7FC0).view(np.int16)))
+        kvp.kvp_paged_attention_decode_scheduled(
+            gc.pool, q, gc.k_pool, gc.v_pool, gc.k_meta, gc.v_meta, gc.bt, gc.ctx,
+            int(case.ctx.max()), float(case.scale), sdev, sched, out, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy().view(np.uint16), ref, f"{name} call {call}")
+        assert np.array_equal(sdev.cpu().numpy(), sched.used), f"call {call}: schedule changed"
     gc.close()
 
 
