@@ -62,7 +62,8 @@ def parse_args(argv=None):
                    help="decode work plan: the uniform split plan, a balanced schedule built "
                         "from the host lengths, or auto (balanced when the lengths differ)")
     p.add_argument("--bins", type=int, default=0,
-                   help="most bins of the balanced schedule (0 = four per compute unit)")
+                   help="most bins of the balanced schedule (0 = the library's choice: "
+                        "four per compute unit, eight for INT4)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle sample")
@@ -199,7 +200,7 @@ def run_gpu(args, kvp, cfg, case):
     if balanced:
         # one schedule serves every layer (they share lengths and tables); the
         # bench's lengths are the same every step, so it is built once here
-        cus = args.bins or 4 * torch.cuda.get_device_properties(0).multi_processor_count
+        cus = args.bins or kvp.kvp_decode_schedule_bins(pool, Hq)
         t0 = time.perf_counter()
         reps = 20
         for _ in range(reps):

@@ -367,6 +367,16 @@ kvp_status kvp_decode_schedule_bounds(const kvp_pool* pool, int32_t num_seqs,
                                       int32_t num_q_heads, int32_t max_bins,
                                       size_t* sched_bytes, size_t* workspace_bytes);
 
+/* Bins that keep every compute unit of the current device busy along a
+ * schedule for this pool and num_q_heads: four per compute unit (one
+ * wavefront per SIMD), eight for INT4 pools on the matrix-core path
+ * (g >= 4), whose stream kernel is built for two wavefronts per SIMD.  The
+ * value to pass as max_bins below when there is no reason to pick another.
+ * KVP_E_INVAL for a bad pool, head count or pointer; KVP_E_HIP when the
+ * device cannot be queried. */
+kvp_status kvp_decode_schedule_bins(const kvp_pool* pool, int32_t num_q_heads,
+                                    int32_t* max_bins);
+
 /* Build the schedule (host).  context_lens: host array of the B lengths the
  * device array will hold at decode time (0 <= n <= max_blocks*P, else
  * KVP_E_INVAL); sink_tokens/window_tokens as for the window decode (0, 0 for

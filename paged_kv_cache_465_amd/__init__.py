@@ -392,6 +392,16 @@ def kvp_decode_schedule(pool: Pool, context_lens, num_q_heads: int, max_blocks: 
     return Schedule(words, info)
 
 
+def kvp_decode_schedule_bins(pool: Pool, num_q_heads: int) -> int:
+    """Bins that keep every compute unit of the current device busy along a
+    schedule for this pool (four per compute unit, eight for INT4 pools on
+    the matrix-core path)."""
+    n = ctypes.c_int32()
+    _check(_L.kvp_decode_schedule_bins(pool.handle, int(num_q_heads), ctypes.byref(n)),
+           "kvp_decode_schedule_bins")
+    return int(n.value)
+
+
 def kvp_paged_attention_decode_scheduled(pool: Pool, q, k_pool, v_pool, k_meta, v_meta,
                                          block_tables, context_lens, max_context_len: int,
                                          scale: float, sched_dev, schedule: Schedule, out,
@@ -485,7 +495,8 @@ __all__ = [
     "kvp_pages_free", "kvp_seq_grow", "kvp_seq_share", "kvp_seq_release", "kvp_decode_plan",
     "kvp_kv_append", "kvp_decode_workspace_bytes", "kvp_paged_attention_decode",
     "kvp_decode_partials_bytes", "kvp_paged_attention_decode_partials", "kvp_lse_merge",
-    "kvp_decode_schedule_bounds", "kvp_decode_schedule", "kvp_paged_attention_decode_scheduled",
+    "kvp_decode_schedule_bounds", "kvp_decode_schedule", "kvp_decode_schedule_bins",
+    "kvp_paged_attention_decode_scheduled",
     "Schedule", "ScheduleInfo",
     "kvp_seq_evict_window", "kvp_decode_window_workspace_bytes",
     "kvp_paged_attention_decode_window", "kvp_paged_attention_prefill", "PrefixCache",

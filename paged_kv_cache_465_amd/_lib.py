@@ -95,6 +95,7 @@ PROTOTYPES = {
     "kvp_decode_schedule": (c_int32, [c_void_p, P_int32, c_int32, c_int32, c_int32, c_int32,
                                       c_int32, c_int32, P_int32, c_size_t,
                                       ctypes.POINTER(ScheduleInfo)]),
+    "kvp_decode_schedule_bins": (c_int32, [c_void_p, c_int32, P_int32]),
     "kvp_paged_attention_decode_scheduled": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p,
                                                        c_void_p, c_void_p, c_void_p, c_int32,
                                                        c_void_p, c_int32, c_int32, c_int32,

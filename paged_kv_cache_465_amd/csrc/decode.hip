@@ -334,6 +334,23 @@ extern "C" kvp_status kvp_lse_merge(const void* partials, int32_t rows, int32_t 
              : KVP_E_HIP;
 }
 
+extern "C" kvp_status kvp_decode_schedule_bins(const kvp_pool* pool, int32_t num_q_heads,
+                                               int32_t* max_bins) {
+  kvp_pool_desc d;
+  if (!max_bins || kvp_pool_get_desc(pool, &d) != KVP_OK || num_q_heads <= 0 ||
+      num_q_heads % d.num_kv_heads)
+    return KVP_E_INVAL;
+  const int cus = kvp::cu_count_current_device();
+  if (cus <= 0) return KVP_E_HIP;
+  // the planner's choice of kernel family for this group size
+  kvp_decode_plan_t plan;
+  if (kvp_decode_plan(&d, 1, num_q_heads, d.page_size, 0, cus, &plan) != KVP_OK)
+    return KVP_E_INVAL;
+  const int waves = plan.use_mfma && d.dtype == KVP_INT4 ? 2 : 1;
+  *max_bins = 4 * waves * cus;
+  return KVP_OK;
+}
+
 extern "C" kvp_status kvp_paged_attention_decode_scheduled(
     const kvp_pool* pool, const void* q, const void* k_pool, const void* v_pool,
     const void* k_meta, const void* v_meta, const int32_t* block_tables, int32_t max_blocks,

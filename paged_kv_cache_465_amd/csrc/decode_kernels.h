@@ -642,8 +642,17 @@ __device__ __forceinline__ void stream_seek(const DecodeArgs& a, StreamPos& p, i
   p.k = 0;
 }
 
+// Wavefronts per SIMD the stream kernel is compiled for: INT4 pages carry the
+// most arithmetic per byte, and two wavefronts per SIMD (a two-page ring
+// each, eight bins per compute unit) let one compute while the other waits
+// on memory: 166 -> 142 us on 16 sequences of 16k-32k tokens, although the
+// 256-register budget spills a little.  The other formats measured slower
+// that way (P = 32 spills more) and keep one wavefront with a deeper ring.
+template <int F> constexpr int stream_waves_per_simd() { return F == kI4 ? 2 : 1; }
+
 template <int F, int P, int D, int NT, int DEPTH>
-__global__ __launch_bounds__(256) void decode_mfma_stream_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, stream_waves_per_simd<F>()) void decode_mfma_stream_kernel(
+    DecodeArgs a) {
   using S = MfmaShape<F, P, D>;
   using FI = FmtInfo<F>;
   constexpr bool Q = FI::quant, ZP = FI::zero;
@@ -1360,6 +1369,11 @@ constexpr int kDepth = 2;
 // 172 us on 16 sequences of 16k-32k tokens), while FP8 measured 5% slower
 // with three and bfloat16 within noise.
 template <int F> constexpr int mfma_depth() { return F == kI4 ? 4 : F == kI8 ? 3 : kDepth; }
+// The stream kernel's ring: the split kernel's, except where two wavefronts
+// share a SIMD (each keeps two pages in flight).
+template <int F> constexpr int stream_depth() {
+  return stream_waves_per_simd<F>() > 1 ? 2 : mfma_depth<F>();
+}
 
 int cu_count_current_device();
 
@@ -1374,13 +1388,13 @@ hipError_t launch_decode_pd(const DecodeArgs& a, bool mfma, int g, dim3 grid, di
     // balanced schedule: one stream per wavefront, no LDS
     if constexpr (SCHED) {
       if (g <= 16)
-        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 1, mfma_depth<F>()>), grid, block,
+        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 1, stream_depth<F>()>), grid, block,
                            0, s, a);
       else if (g <= 32)
-        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 2, mfma_depth<F>()>), grid, block,
+        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 2, stream_depth<F>()>), grid, block,
                            0, s, a);
       else
-        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 4, mfma_depth<F>()>), grid, block,
+        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 4, stream_depth<F>()>), grid, block,
                            0, s, a);
     } else {
       if (g <= 16)

@@ -115,12 +115,12 @@ class GpuCase:
                          max_context_len=None) -> np.ndarray:
         """The decode (window decode when window > 0) along a balanced
         schedule built from the host lengths (the case's, or ctx_host); by
-        default four bins per compute unit."""
+        default the bins the library picks for the pool."""
         c = self.case
         q = self.q if q is None else q
         ctx = c.ctx if ctx_host is None else ctx_host
         if max_bins is None:
-            max_bins = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+            max_bins = self.kvp.kvp_decode_schedule_bins(self.pool, c.cfg.num_q_heads)
         mx = int(ctx.max()) if max_context_len is None else int(max_context_len)
         sched = self.kvp.kvp_decode_schedule(self.pool, ctx, c.cfg.num_q_heads,
                                              int(self.bt_host.shape[1]), max_bins, sink, window)

@@ -496,6 +496,19 @@ def test_decode_schedule_equal_lengths_need_no_merge(kvp):
     pool.close()
 
 
+def test_schedule_bins_rejects_bad_arguments(kvp):
+    import ctypes
+    from paged_kv_cache_465_amd import _lib
+    lib = _lib.load()
+    pool = kvp.kvp_pool_create(kvp.make_desc(16, 16, 2, 64, "bf16"))
+    n = ctypes.c_int32()
+    assert lib.kvp_decode_schedule_bins(None, 4, ctypes.byref(n)) == kvp.KVP_E_INVAL
+    assert lib.kvp_decode_schedule_bins(pool.handle, 0, ctypes.byref(n)) == kvp.KVP_E_INVAL
+    assert lib.kvp_decode_schedule_bins(pool.handle, 3, ctypes.byref(n)) == kvp.KVP_E_INVAL
+    assert lib.kvp_decode_schedule_bins(pool.handle, 4, None) == kvp.KVP_E_INVAL
+    pool.close()
+
+
 def test_decode_schedule_rejects_bad_arguments(kvp):
     pool = kvp.kvp_pool_create(kvp.make_desc(16, 16, 2, 64, "bf16"))
     for ctx, mb in (([5, -1], 4), ([5, 65], 4)):
