@@ -63,7 +63,7 @@ def parse_args(argv=None):
                         "from the host lengths, or auto (balanced when the lengths differ)")
     p.add_argument("--bins", type=int, default=0,
                    help="most bins of the balanced schedule (0 = the library's choice: "
-                        "four per compute unit, eight for INT4)")
+                        "four per compute unit, eight for quantized pools)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle sample")

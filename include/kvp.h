@@ -337,7 +337,8 @@ kvp_status kvp_paged_attention_decode_window(
  *     and the window's blocks);
  *   - bin k of num_bins covers blocks [k*T/num_bins, (k+1)*T/num_bins) of
  *     that list (T = all blocks); num_bins = min(max_bins, ceil(T/8)), at
- *     least 1 (4 bins per compute unit keep one wavefront per SIMD busy);
+ *     least 1 (kvp_decode_schedule_bins gives the count that fills the
+ *     device);
  *   - the pieces of pairs a bin covers are its items, processed in order; on
  *     the matrix-core path the items of a wavefront's stream share its
  *     register ring, so the next item's pages load while the current one
@@ -369,8 +370,9 @@ kvp_status kvp_decode_schedule_bounds(const kvp_pool* pool, int32_t num_seqs,
 
 /* Bins that keep every compute unit of the current device busy along a
  * schedule for this pool and num_q_heads: four per compute unit (one
- * wavefront per SIMD), eight for INT4 pools on the matrix-core path
- * (g >= 4), whose stream kernel is built for two wavefronts per SIMD.  The
+ * wavefront per SIMD), eight for quantized pools (INT8, INT4, FP8) on the
+ * matrix-core path (g >= 4), whose stream kernel is built for two
+ * wavefronts per SIMD.  The
  * value to pass as max_bins below when there is no reason to pick another.
  * KVP_E_INVAL for a bad pool, head count or pointer; KVP_E_HIP when the
  * device cannot be queried. */

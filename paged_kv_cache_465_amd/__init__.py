@@ -380,7 +380,8 @@ class Schedule:
 def kvp_decode_schedule(pool: Pool, context_lens, num_q_heads: int, max_blocks: int,
                         max_bins: int, sink_tokens: int = 0, window_tokens: int = 0) -> Schedule:
     """Balanced schedule for host context lengths (numpy int32 array); at most
-    max_bins bins (four per compute unit keep one wavefront per SIMD busy)."""
+    max_bins bins (kvp_decode_schedule_bins gives the count that fills the
+    device)."""
     ctx = _i32(np.ascontiguousarray(context_lens, dtype=np.int32))
     sb, _ = kvp_decode_schedule_bounds(pool, ctx.size, num_q_heads, max_bins)
     words = np.zeros(sb // 4, dtype=np.int32)
@@ -394,8 +395,8 @@ def kvp_decode_schedule(pool: Pool, context_lens, num_q_heads: int, max_blocks: 
 
 def kvp_decode_schedule_bins(pool: Pool, num_q_heads: int) -> int:
     """Bins that keep every compute unit of the current device busy along a
-    schedule for this pool (four per compute unit, eight for INT4 pools on
-    the matrix-core path)."""
+    schedule for this pool (four per compute unit, eight for quantized pools
+    on the matrix-core path)."""
     n = ctypes.c_int32()
     _check(_L.kvp_decode_schedule_bins(pool.handle, int(num_q_heads), ctypes.byref(n)),
            "kvp_decode_schedule_bins")

@@ -346,7 +346,7 @@ extern "C" kvp_status kvp_decode_schedule_bins(const kvp_pool* pool, int32_t num
   kvp_decode_plan_t plan;
   if (kvp_decode_plan(&d, 1, num_q_heads, d.page_size, 0, cus, &plan) != KVP_OK)
     return KVP_E_INVAL;
-  const int waves = plan.use_mfma && d.dtype == KVP_INT4 ? 2 : 1;
+  const int waves = plan.use_mfma && d.dtype != KVP_BF16 ? 2 : 1;
   *max_bins = 4 * waves * cus;
   return KVP_OK;
 }

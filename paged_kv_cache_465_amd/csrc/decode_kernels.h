@@ -642,13 +642,15 @@ __device__ __forceinline__ void stream_seek(const DecodeArgs& a, StreamPos& p, i
   p.k = 0;
 }
 
-// Wavefronts per SIMD the stream kernel is compiled for: INT4 pages carry the
-// most arithmetic per byte, and two wavefronts per SIMD (a two-page ring
-// each, eight bins per compute unit) let one compute while the other waits
-// on memory: 166 -> 142 us on 16 sequences of 16k-32k tokens, although the
-// 256-register budget spills a little.  The other formats measured slower
-// that way (P = 32 spills more) and keep one wavefront with a deeper ring.
-template <int F> constexpr int stream_waves_per_simd() { return F == kI4 ? 2 : 1; }
+// Wavefronts per SIMD the stream kernel is compiled for.  Quantized pages
+// carry much more arithmetic per byte than bfloat16 ones (code conversion,
+// scales, zero points), and with two wavefronts per SIMD (eight bins per
+// compute unit) one computes while the other waits on memory.  Measured on
+// 16 sequences of 16k-32k tokens, P = 32: INT4 166 -> 142 us (two-page rings;
+// the 256-register budget spills a little), INT8 176 -> 166 us and FP8 159 ->
+// 150 us (one-page rings, no spills; two-page rings spill and were slower).
+// bfloat16 keeps one wavefront with a two-page ring (two measured slower).
+template <int F> constexpr int stream_waves_per_simd() { return F == kBF16 ? 1 : 2; }
 
 template <int F, int P, int D, int NT, int DEPTH>
 __global__ __launch_bounds__(256, stream_waves_per_simd<F>()) void decode_mfma_stream_kernel(
@@ -1369,10 +1371,11 @@ constexpr int kDepth = 2;
 // 172 us on 16 sequences of 16k-32k tokens), while FP8 measured 5% slower
 // with three and bfloat16 within noise.
 template <int F> constexpr int mfma_depth() { return F == kI4 ? 4 : F == kI8 ? 3 : kDepth; }
-// The stream kernel's ring: the split kernel's, except where two wavefronts
-// share a SIMD (each keeps two pages in flight).
+// The stream kernel's ring: the split kernel's with one wavefront per SIMD;
+// with two, INT4 (half-size pages) keeps two pages in flight and the 8-bit
+// formats one.
 template <int F> constexpr int stream_depth() {
-  return stream_waves_per_simd<F>() > 1 ? 2 : mfma_depth<F>();
+  return stream_waves_per_simd<F>() == 1 ? mfma_depth<F>() : (F == kI4 ? 2 : 1);
 }
 
 int cu_count_current_device();
