@@ -1303,22 +1303,42 @@ __device__ __forceinline__ void lse_merge_row(const float* __restrict__ po, int6
                                               uint16_t* __restrict__ out_row) {
   constexpr int E = D / 64;
   const int lane = threadIdx.x & 63;
-  float M = -INFINITY;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, pml[s * sml]);
+  // (m, l) of slot `lane` (the first 64 slots), loaded together; M over all
+  float m0 = -INFINITY, l0 = 0.0f;
+  if (lane < S) {
+    m0 = pml[lane * sml];
+    l0 = pml[lane * sml + 1];
+  }
+  float M = m0;
+  for (int s = lane + 64; s < S; s += 64) M = fmaxf(M, pml[s * sml]);
   M = wave_max(M);
   float o[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.0f;
   float L = 0.0f;
   if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float ms = pml[s * sml], ls = pml[s * sml + 1];
-      if (ls > 0.0f) {
-        const float w = ls * fast_exp2(ms - M);
-        L += w;
-        const float* p = po + s * so + lane * E;
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      float ms = m0, ls = l0;
+      if (s0 > 0) {
+        const int s = s0 + lane;
+        ms = s < S ? pml[s * sml] : -INFINITY;
+        ls = s < S ? pml[s * sml + 1] : 0.0f;
+      }
+      // weight of slot s0 + lane; empty slots (l = 0, m = -inf) weigh 0
+      const float w = ls > 0.0f ? ls * fast_exp2(ms - M) : 0.0f;
+      const int n = min(64, S - s0);
+      // the partials' loads do not depend on the weights, so consecutive
+      // slots' loads are in flight together
+#pragma unroll 4
+      for (int i = 0; i < n; ++i) {
+        const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i));
+        L += wi;
+        const float* p = po + (s0 + i) * so + lane * E;
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] += w * p[e];
+        for (int e = 0; e < E; ++e) {
+          const float x = p[e];
+          o[e] += wi > 0.0f ? wi * x : 0.0f;
+        }
       }
     }
   }
