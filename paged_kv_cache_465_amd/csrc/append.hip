@@ -91,21 +91,23 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int H = a.num_kv_heads;
   if (item >= int64_t(a.n_tokens) * H) return;
   const int n = int(item / H), h = int(item % H);
-  const int sq = a.seq_idx[n], ps = a.pos[n];
-  if (sq < 0 || sq >= a.num_seqs || ps < 0 || ps >= a.max_blocks * P) return;
-  const int page = a.bt[int64_t(sq) * a.max_blocks + ps / P];
-  if (page < 0 || page >= a.num_pages) return;
-  const int t = ps % P;
-  const int64_t tile = int64_t(page) * H + h;  // (page, head) tile index
   const int d0 = lane * E;
   const int64_t src = (int64_t(n) * H + h) * D + d0;
-
+  // the new row's values depend only on the row index: load them alongside
+  // the position, ahead of the table lookup, so one memory round trip less
+  // stands between the launch and the stores
   uint32_t kb[E], vb[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     kb[e] = a.k_new[src + e];
     vb[e] = a.v_new[src + e];
   }
+  const int sq = a.seq_idx[n], ps = a.pos[n];
+  if (sq < 0 || sq >= a.num_seqs || ps < 0 || ps >= a.max_blocks * P) return;
+  const int page = a.bt[int64_t(sq) * a.max_blocks + ps / P];
+  if (page < 0 || page >= a.num_pages) return;
+  const int t = ps % P;
+  const int64_t tile = int64_t(page) * H + h;  // (page, head) tile index
   if constexpr (F == kBF16) {
     uint16_t* K = static_cast<uint16_t*>(a.k_pool);
     uint16_t* V = static_cast<uint16_t*>(a.v_pool);
