@@ -44,6 +44,9 @@ KERNEL_SOURCES = ("paged_kv_cache_465_amd/csrc/decode.hip",
                   "paged_kv_cache_465_amd/csrc/decode_bf16_split.hip",
                   "paged_kv_cache_465_amd/csrc/device_common.h",
                   "paged_kv_cache_465_amd/csrc/pool.cpp")
+# sources that decide the multi-query (chunked prefill, verification) kernel
+PREFILL_SOURCES = ("paged_kv_cache_465_amd/csrc/prefill.hip",
+                   "paged_kv_cache_465_amd/csrc/device_common.h")
 MALL_FLUSH_BYTES = 1 << 30      # > 256 MB Infinity Cache
 
 
@@ -308,17 +311,19 @@ def run_gpu(args, kvp, cfg, case):
     return res, (pool, layers, bt, ctx)
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the split kernel's sources (counter readings are tied to it)."""
+def kernel_source_digest(chunked: bool = False) -> str:
+    """sha256 over the measured kernel's sources (counter readings are tied to
+    it): the decode kernels', or the multi-query kernel's for chunked
+    workloads."""
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in (PREFILL_SOURCES if chunked else KERNEL_SOURCES):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def recorded_traffic(workload: str):
+def recorded_traffic(workload: str, chunked: bool = False):
     """HBM bytes per launch of the split kernel from the committed counter
     readings (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads
     for a plain copy of known size), or None when there are none for this
@@ -328,7 +333,7 @@ def recorded_traffic(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256") != kernel_source_digest():
+    if rec.get("kernel_source_sha256") != kernel_source_digest(chunked):
         return None
     return rec
 
@@ -587,7 +592,7 @@ def main(argv=None):
                      "intensity_flop_per_byte": round(intensity, 2),
                      "hbm_GBps": round(achieved, 1)},
     }
-    rec = recorded_traffic(cfg.name)
+    rec = recorded_traffic(cfg.name, is_chunked(cfg))
     if rec is not None:
         out["roofline"]["traffic"] = rec["traffic_bytes_per_launch"]
         out["roofline"]["traffic_over_algorithmic"] = round(
