@@ -371,7 +371,7 @@ kvp_status kvp_decode_schedule_bounds(const kvp_pool* pool, int32_t num_seqs,
 /* Bins that keep every compute unit of the current device busy along a
  * schedule for this pool and num_q_heads: four per compute unit (one
  * wavefront per SIMD), eight for quantized pools (INT8, INT4, FP8) on the
- * matrix-core path (g >= 4), whose stream kernel is built for two
+ * matrix-core path with 4 <= g <= 16, whose stream kernel is built for two
  * wavefronts per SIMD.  The
  * value to pass as max_bins below when there is no reason to pick another.
  * KVP_E_INVAL for a bad pool, head count or pointer; KVP_E_HIP when the

@@ -396,7 +396,7 @@ def kvp_decode_schedule(pool: Pool, context_lens, num_q_heads: int, max_blocks: 
 def kvp_decode_schedule_bins(pool: Pool, num_q_heads: int) -> int:
     """Bins that keep every compute unit of the current device busy along a
     schedule for this pool (four per compute unit, eight for quantized pools
-    on the matrix-core path)."""
+    on the matrix-core path with up to 16 query heads per KV head)."""
     n = ctypes.c_int32()
     _check(_L.kvp_decode_schedule_bins(pool.handle, int(num_q_heads), ctypes.byref(n)),
            "kvp_decode_schedule_bins")

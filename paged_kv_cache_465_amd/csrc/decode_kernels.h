@@ -650,10 +650,14 @@ __device__ __forceinline__ void stream_seek(const DecodeArgs& a, StreamPos& p, i
 // the 256-register budget spills a little), INT8 176 -> 166 us and FP8 159 ->
 // 150 us (one-page rings, no spills; two-page rings spill and were slower).
 // bfloat16 keeps one wavefront with a two-page ring (two measured slower).
-template <int F> constexpr int stream_waves_per_simd() { return F == kBF16 ? 1 : 2; }
+// Only instances for groups of up to 16 query heads (one head tile) fit the
+// 256-register budget without spilling; larger groups keep one wavefront.
+template <int F, int NT> constexpr int stream_waves_per_simd() {
+  return F != kBF16 && NT == 1 ? 2 : 1;
+}
 
 template <int F, int P, int D, int NT, int DEPTH>
-__global__ __launch_bounds__(256, stream_waves_per_simd<F>()) void decode_mfma_stream_kernel(
+__global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_mfma_stream_kernel(
     DecodeArgs a) {
   using S = MfmaShape<F, P, D>;
   using FI = FmtInfo<F>;
@@ -1394,8 +1398,8 @@ template <int F> constexpr int mfma_depth() { return F == kI4 ? 4 : F == kI8 ? 3
 // The stream kernel's ring: the split kernel's with one wavefront per SIMD;
 // with two, INT4 (half-size pages) keeps two pages in flight and the 8-bit
 // formats one.
-template <int F> constexpr int stream_depth() {
-  return stream_waves_per_simd<F>() == 1 ? mfma_depth<F>() : (F == kI4 ? 2 : 1);
+template <int F, int NT> constexpr int stream_depth() {
+  return stream_waves_per_simd<F, NT>() == 1 ? mfma_depth<F>() : (F == kI4 ? 2 : 1);
 }
 
 int cu_count_current_device();
@@ -1411,13 +1415,13 @@ hipError_t launch_decode_pd(const DecodeArgs& a, bool mfma, int g, dim3 grid, di
     // balanced schedule: one stream per wavefront, no LDS
     if constexpr (SCHED) {
       if (g <= 16)
-        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 1, stream_depth<F>()>), grid, block,
+        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 1, stream_depth<F, 1>()>), grid, block,
                            0, s, a);
       else if (g <= 32)
-        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 2, stream_depth<F>()>), grid, block,
+        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 2, stream_depth<F, 2>()>), grid, block,
                            0, s, a);
       else
-        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 4, stream_depth<F>()>), grid, block,
+        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 4, stream_depth<F, 4>()>), grid, block,
                            0, s, a);
     } else {
       if (g <= 16)
