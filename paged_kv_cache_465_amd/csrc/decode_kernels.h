@@ -1395,11 +1395,24 @@ constexpr int kDepth = 2;
 // 172 us on 16 sequences of 16k-32k tokens), while FP8 measured 5% slower
 // with three and bfloat16 within noise.
 template <int F> constexpr int mfma_depth() { return F == kI4 ? 4 : F == kI8 ? 3 : kDepth; }
+// Instances for larger groups hold NT head tiles of accumulators and q
+// operands; for 32-token pages of 128 channels their rings shrink so that
+// they fit the register file (at the depths above, four head tiles spilled
+// 500-1,200 bytes per lane).
+template <int F, int P, int D, int NT> constexpr int mfma_depth_nt() {
+  return (P == 32 && D == 128 && NT == 4) ? 1
+         : (P == 32 && D == 128 && NT == 2) ? (mfma_depth<F>() < 2 ? mfma_depth<F>() : 2)
+                                              : mfma_depth<F>();
+}
 // The stream kernel's ring: the split kernel's with one wavefront per SIMD;
 // with two, INT4 (half-size pages) keeps two pages in flight and the 8-bit
 // formats one.
-template <int F, int NT> constexpr int stream_depth() {
-  return stream_waves_per_simd<F, NT>() == 1 ? mfma_depth<F>() : (F == kI4 ? 2 : 1);
+template <int F, int P, int D, int NT> constexpr int stream_depth() {
+  // (the stream kernel's item bookkeeping costs registers too: four head
+  // tiles of 16-token pages also keep at most two pages)
+  constexpr int d1 = (P == 16 && D == 128 && NT == 4 && mfma_depth_nt<F, P, D, NT>() > 2)
+                         ? 2 : mfma_depth_nt<F, P, D, NT>();
+  return stream_waves_per_simd<F, NT>() == 1 ? d1 : (F == kI4 ? 2 : 1);
 }
 
 int cu_count_current_device();
@@ -1415,23 +1428,23 @@ hipError_t launch_decode_pd(const DecodeArgs& a, bool mfma, int g, dim3 grid, di
     // balanced schedule: one stream per wavefront, no LDS
     if constexpr (SCHED) {
       if (g <= 16)
-        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 1, stream_depth<F, 1>()>), grid, block,
+        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 1, stream_depth<F, P, D, 1>()>), grid, block,
                            0, s, a);
       else if (g <= 32)
-        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 2, stream_depth<F, 2>()>), grid, block,
+        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 2, stream_depth<F, P, D, 2>()>), grid, block,
                            0, s, a);
       else
-        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 4, stream_depth<F, 4>()>), grid, block,
+        hipLaunchKernelGGL((decode_mfma_stream_kernel<F, P, D, 4, stream_depth<F, P, D, 4>()>), grid, block,
                            0, s, a);
     } else {
       if (g <= 16)
-        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 1, mfma_depth<F>()>), grid, block, lds,
+        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 1, mfma_depth_nt<F, P, D, 1>()>), grid, block, lds,
                            s, a);
       else if (g <= 32)
-        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 2, mfma_depth<F>()>), grid, block, lds,
+        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 2, mfma_depth_nt<F, P, D, 2>()>), grid, block, lds,
                            s, a);
       else
-        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 4, mfma_depth<F>()>), grid, block, lds,
+        hipLaunchKernelGGL((decode_mfma_kernel<F, P, D, 4, mfma_depth_nt<F, P, D, 4>()>), grid, block, lds,
                            s, a);
     }
   } else {
