@@ -635,3 +635,61 @@ def test_full_chunked_prefill(kvp):
     """8 sequences taking a 512-token chunk on a Llama-3-8B-shaped layer."""
     from workloads import CHUNKED_PREFILL
     _sampled_check(kvp, CHUNKED_PREFILL, seqs=(0, 5))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("layer", [0, 79])
+def test_full_llama3_70b_layer(kvp, layer):
+    """One layer of the Llama-3-70B-shaped full cache ("Understanding
+    KV-Cache Optimization in Modern LLM Serving", section "Concrete Example:
+    Llama-3-70B": 32 requests of 8,192 tokens, 64 query / 8 KV heads, D = 128),
+    drawn on the device exactly as the benchmark draws that layer, appended
+    through the library and decoded with the plan the benchmark times (the
+    planner's split count and wavefronts).  Every byte of both pools against
+    the oracle's append, and all 32 sequences' outputs against the oracle."""
+    from workloads import POISON_BF16, history_rows_device
+    cfg = LLAMA3_70B_FULL
+    case = make_case(cfg, with_data=False)
+    dev = torch.device("cuda")
+    log(f"[full 70b] layer={layer} seed={cfg.seed * 100 + layer} B={case.B} "
+        f"ctx={int(case.ctx[0])} pages={case.num_pages}")
+    q, hk, hv, hs, hp, nk, nv, npos = history_rows_device(cfg, case, layer, dev)
+    as16 = lambda t: t.view(torch.int16)  # noqa: E731
+    desc = kvp.make_desc(case.num_pages, cfg.page_size, cfg.num_kv_heads, cfg.head_dim, "bf16")
+    pool = kvp.kvp_pool_create(desc)
+    kv_bytes, _ = kvp.kvp_pool_bytes(desc)
+    poison = int(np.uint16(POISON_BF16).view(np.int16))
+    kp = torch.full((kv_bytes // 2,), poison, dtype=torch.int16, device=dev)
+    vp = torch.full_like(kp, poison)
+    bt = dev32(case.block_tables)
+    ctx = dev32(case.ctx)
+    seq = torch.arange(case.B, dtype=torch.int32, device=dev)
+    kvp.kvp_kv_append(pool, kp, vp, None, None, as16(hk), as16(hv), hs, hp, bt)
+    kvp.kvp_kv_append(pool, kp, vp, None, None, as16(nk), as16(nv), seq, npos, bt)
+    mx = int(case.ctx.max())
+    plan = kvp.kvp_decode_plan(desc, case.B, cfg.num_q_heads, mx, 0,
+                               torch.cuda.get_device_properties(0).multi_processor_count)
+    wsb = kvp.kvp_decode_workspace_bytes(pool, case.B, cfg.num_q_heads, mx)
+    ws = torch.full((wsb // 4,), float("nan"), device=dev) if wsb else None
+    out = torch.full_like(as16(q), poison)
+    kvp.kvp_paged_attention_decode(pool, as16(q), kp, vp, None, None, bt, ctx, mx,
+                                   float(case.scale), out, 0, ws)
+    torch.cuda.synchronize()
+    log(f"  plan={plan}")
+    got = out.cpu().numpy().view(np.uint16)
+    host = lambda t: as16(t).cpu().numpy().view(np.uint16)  # noqa: E731
+    qh, hkh, hvh, nkh, nvh = host(q), host(hk), host(hv), host(nk), host(nv)
+    del q, hk, hv, nk, nv
+    lay = layout_of(case)
+    k, v, _, _ = lay.empty_pools(POISON_BF16, 0)
+    oracle.append(lay, k, v, None, None, hkh, hvh, hs.cpu().numpy(), hp.cpu().numpy(),
+                  case.block_tables)
+    oracle.append(lay, k, v, None, None, nkh, nvh, np.arange(case.B), npos.cpu().numpy(),
+                  case.block_tables)
+    del hkh, hvh
+    assert np.array_equal(kp.cpu().numpy().view(np.uint16), k), "K pool differs"
+    assert np.array_equal(vp.cpu().numpy().view(np.uint16), v), "V pool differs"
+    ref = oracle.paged_decode(lay, qh, k, v, None, None, case.block_tables, case.ctx, case.scale)
+    m, r = assert_close(got, ref, f"llama3_70b layer {layer}")
+    log(f"  all 32 sequences: max_abs={m:.2e} rel_l2={r:.2e}")
+    pool.close()
