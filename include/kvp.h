@@ -108,7 +108,8 @@ typedef enum {
   KVP_E_INVAL = 1,        /* bad argument, or a state violation (double free ...) */
   KVP_E_NOPAGES = 2,      /* not enough free pages; nothing was allocated */
   KVP_E_UNSUPPORTED = 3,  /* shape or dtype with no kernel (P, D, g, dtype) */
-  KVP_E_HIP = 4           /* a HIP runtime call failed */
+  KVP_E_HIP = 4,          /* a HIP runtime call failed */
+  KVP_E_SCRATCH = 5       /* needs more scratch than KVP_DECODE_SCRATCH_BYTES (noalloc call) */
 } kvp_status;
 
 typedef enum { KVP_BF16 = 0, KVP_INT8 = 1, KVP_INT4 = 2, KVP_FP8 = 3 } kvp_kv_dtype;
@@ -299,6 +300,29 @@ kvp_status kvp_paged_attention_decode(const kvp_pool* pool, const void* q,
                                       float scale, void* out, int32_t num_splits_req,
                                       void* workspace, size_t workspace_bytes,
                                       kvp_stream_t stream);
+
+/* ---- Decode that allocates nothing (device) ---------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * attention, plan and kernels as kvp_paged_attention_decode, with the split
+ * partials in a fixed device buffer the library holds on each GPU it runs on
+ * (KVP_DECODE_SCRATCH_BYTES, until the process ends) instead of a workspace
+ * argument.  The caller still passes every input and output.  The call makes
+ * no device allocation; a plan whose workspace (kvp_decode_workspace_bytes)
+ * exceeds the buffer returns KVP_E_SCRATCH and queues nothing.  All calls on
+ * one GPU share its buffer: calls that can overlap on one GPU (different
+ * streams, or several threads) race and must be serialized by the caller.
+ * The first call on a device looks up the buffer's address there (KVP_E_HIP
+ * if that fails). */
+#define KVP_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+kvp_status kvp_paged_attention_decode_noalloc(const kvp_pool* pool, const void* q,
+                                              const void* k_pool, const void* v_pool,
+                                              const void* k_meta, const void* v_meta,
+                                              const int32_t* block_tables, int32_t max_blocks,
+                                              const int32_t* context_lens, int32_t num_seqs,
+                                              int32_t num_q_heads, int32_t max_context_len,
+                                              float scale, void* out, int32_t num_splits_req,
+                                              kvp_stream_t stream);
 
 /* ---- Decode over attention sinks and a recent window (device) --------------
  * "KV-Cache Optimization Techniques", section "Token Eviction Strategies",

@@ -18,7 +18,7 @@ from ._lib import DecodePlan, PoolDesc, ScheduleInfo
 
 _L = _lib.load()
 
-KVP_OK, KVP_E_INVAL, KVP_E_NOPAGES, KVP_E_UNSUPPORTED, KVP_E_HIP = range(5)
+KVP_OK, KVP_E_INVAL, KVP_E_NOPAGES, KVP_E_UNSUPPORTED, KVP_E_HIP, KVP_E_SCRATCH = range(6)
 KVP_BF16, KVP_INT8, KVP_INT4, KVP_FP8 = 0, 1, 2, 3
 _DTYPES = {"bf16": KVP_BF16, "int8": KVP_INT8, "int4": KVP_INT4, "fp8": KVP_FP8}
 _DTYPE_NAMES = {v: k for k, v in _DTYPES.items()}
@@ -320,6 +320,26 @@ def kvp_paged_attention_decode(pool: Pool, q, k_pool, v_pool, k_meta, v_meta, bl
         _dev(workspace, "workspace"), ws_bytes, _stream(stream)), "kvp_paged_attention_decode")
 
 
+def kvp_paged_attention_decode_noalloc(pool: Pool, q, k_pool, v_pool, k_meta, v_meta,
+                                       block_tables, context_lens, max_context_len: int,
+                                       scale: float, out, num_splits_req: int = 0,
+                                       stream=None) -> None:
+    """kvp_paged_attention_decode with the split partials in the library's
+    fixed device buffer (no workspace argument, no device allocation)."""
+    eb = pool.elem_bytes
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables/context_lens must cover the batch")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _check(_L.kvp_paged_attention_decode_noalloc(
+        pool.handle, _dev(q, "q", 2), _dev(k_pool, "k_pool", eb), _dev(v_pool, "v_pool", eb),
+        _dev(k_meta, "k_meta", 2), _dev(v_meta, "v_meta", 2), _dev(block_tables, "block_tables", 4),
+        int(block_tables.shape[1]), _dev(context_lens, "context_lens", 4), B, Hq,
+        int(max_context_len), float(scale), _dev(out, "out", 2), int(num_splits_req),
+        _stream(stream)), "kvp_paged_attention_decode_noalloc")
+
+
 def kvp_decode_window_workspace_bytes(pool: Pool, num_seqs: int, num_q_heads: int,
                                       max_context_len: int, sink_tokens: int, window_tokens: int,
                                       num_splits_req: int = 0) -> int:
@@ -489,12 +509,14 @@ def kvp_lse_merge(partials, rows: int, num_splits: int, head_dim: int, out, stre
 
 
 __all__ = [
-    "KVP_OK", "KVP_E_INVAL", "KVP_E_NOPAGES", "KVP_E_UNSUPPORTED", "KVP_E_HIP", "KVP_BF16",
+    "KVP_OK", "KVP_E_INVAL", "KVP_E_NOPAGES", "KVP_E_UNSUPPORTED", "KVP_E_HIP", "KVP_E_SCRATCH",
+    "KVP_BF16",
     "KVP_INT8", "KVP_INT4", "KVP_FP8", "KvpError", "Pool", "PoolDesc", "make_desc", "kvp_status_string",
     "kvp_pool_bytes", "kvp_pool_create", "kvp_pool_destroy", "kvp_pool_get_desc",
     "kvp_pool_free_count", "kvp_pool_refcount", "kvp_pages_alloc", "kvp_pages_ref",
     "kvp_pages_free", "kvp_seq_grow", "kvp_seq_share", "kvp_seq_release", "kvp_decode_plan",
     "kvp_kv_append", "kvp_decode_workspace_bytes", "kvp_paged_attention_decode",
+    "kvp_paged_attention_decode_noalloc",
     "kvp_decode_partials_bytes", "kvp_paged_attention_decode_partials", "kvp_lse_merge",
     "kvp_decode_schedule_bounds", "kvp_decode_schedule", "kvp_decode_schedule_bins",
     "kvp_paged_attention_decode_scheduled",

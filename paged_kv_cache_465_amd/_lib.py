@@ -59,6 +59,10 @@ PROTOTYPES = {
                                              c_void_p, c_void_p, c_int32, c_void_p, c_int32,
                                              c_int32, c_int32, c_float, c_void_p, c_int32,
                                              c_void_p, c_size_t, c_void_p]),
+    "kvp_paged_attention_decode_noalloc": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p,
+                                                     c_void_p, c_void_p, c_void_p, c_int32,
+                                                     c_void_p, c_int32, c_int32, c_int32,
+                                                     c_float, c_void_p, c_int32, c_void_p]),
     "kvp_decode_partials_bytes": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32,
                                             P_int32, ctypes.POINTER(c_size_t)]),
     "kvp_paged_attention_decode_partials": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p,

@@ -4,6 +4,7 @@
 // decode_<format>_split.hip and decode_<format>_sched.hip.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "decode_kernels.h"
 
@@ -245,6 +246,64 @@ extern "C" kvp_status kvp_paged_attention_decode(
   return decode_full(pool, q, k_pool, v_pool, k_meta, v_meta, block_tables, max_blocks,
                      context_lens, num_seqs, num_q_heads, max_context_len, scale, 0, 0, out,
                      num_splits_req, workspace, workspace_bytes, stream);
+}
+
+// ---- Decode without a caller workspace --------------------------------------
+// For callers that cannot allocate device memory: the split partials live in
+// one file-scope device array per GPU, held until the process ends.  Host
+// code never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol): the device address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// used.  Every partial a call reads was written earlier in the same call
+// (empty splits write m = -inf, l = 0), so nothing needs clearing.
+static __device__ __align__(256) unsigned char scratch[KVP_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+kvp_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return KVP_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      kvp::discard_stale_error();
+      return KVP_E_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVP_OK;
+}
+
+}  // namespace
+
+extern "C" kvp_status kvp_paged_attention_decode_noalloc(
+    const kvp_pool* pool, const void* q, const void* k_pool, const void* v_pool,
+    const void* k_meta, const void* v_meta, const int32_t* block_tables, int32_t max_blocks,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    float scale, void* out, int32_t num_splits_req, kvp_stream_t stream) {
+  kvp_pool_desc d;
+  kvp_decode_plan_t plan;
+  bool empty;
+  const kvp_status st = prepare_decode(pool, q, k_pool, v_pool, k_meta, v_meta, block_tables,
+                                       max_blocks, context_lens, num_seqs, num_q_heads,
+                                       max_context_len, scale, num_splits_req, 0, 0, &d, &plan,
+                                       &empty);
+  if (st != KVP_OK || empty) return st;
+  if (plan.workspace_bytes > KVP_DECODE_SCRATCH_BYTES) return KVP_E_SCRATCH;
+  void* ws = nullptr;
+  if (plan.workspace_bytes > 0) {
+    const kvp_status sst = scratch_of_current_device(&ws);
+    if (sst != KVP_OK) return sst;
+  }
+  return decode_full(pool, q, k_pool, v_pool, k_meta, v_meta, block_tables, max_blocks,
+                     context_lens, num_seqs, num_q_heads, max_context_len, scale, 0, 0, out,
+                     num_splits_req, ws, KVP_DECODE_SCRATCH_BYTES, stream);
 }
 
 extern "C" kvp_status kvp_decode_window_workspace_bytes(const kvp_pool* pool, int32_t num_seqs,

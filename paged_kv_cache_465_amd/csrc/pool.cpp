@@ -52,6 +52,7 @@ const char* kvp_status_string(kvp_status s) {
     case KVP_E_NOPAGES: return "not enough free pages";
     case KVP_E_UNSUPPORTED: return "unsupported shape or dtype";
     case KVP_E_HIP: return "HIP runtime error";
+    case KVP_E_SCRATCH: return "the call needs more device scratch than the library's fixed buffer";
   }
   return "unknown status";
 }
