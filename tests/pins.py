@@ -61,28 +61,96 @@ def small_cases():
         variant(TINY, name="tiny_p32_int8", page_size=32, kv_dtype="int8", num_q_heads=8,
                 num_kv_heads=2, head_dim=128, pool_pages=16, outlier_channels=3,
                 outlier_gain=8.0),
+        variant(TINY, name="tiny_p16_int4_h2", kv_dtype="int4", num_q_heads=8,
+                num_kv_heads=2, pool_pages=24, outlier_channels=3, outlier_gain=8.0),
+        variant(TINY, name="tiny_p32_fp8_h2", page_size=32, kv_dtype="fp8", num_q_heads=4,
+                num_kv_heads=2, head_dim=128, pool_pages=16),
     ]
 
 
 # ---------------------------------------------------------------- layout / gather
+_EXACT_MEMO = {}
+
+
+def _memo_exact(fn):
+    """Cache an exact-row-model function by its input bits: the model does not
+    depend on the oracle, so its answers hold across planted oracle mistakes."""
+    def wrapped(rows_bits, dtype="int8"):
+        a = np.ascontiguousarray(rows_bits)
+        key = (fn.__name__, dtype, a.shape, a.tobytes())
+        if key not in _EXACT_MEMO:
+            _EXACT_MEMO[key] = fn(a, dtype)
+        return _EXACT_MEMO[key]
+    return wrapped
+
+
+@_memo_exact
+def _row_codes_exact(row_bits, dtype):
+    """One (token, head) row of D bfloat16 values -> (codes, scale bits, zero
+    bits) by the exact-rational model of the row contract (INT8 / INT4), or
+    the exact scale and torch's e4m3 cast (FP8): independent of the oracle's
+    quantizer."""
+    x = _bf16_f64(np.asarray(row_bits).reshape(-1))
+    if dtype == "fp8":
+        sc = fp8_scale_exact(x.tolist())
+        q = (x.astype(np.float32) / np.float32(float(sc))).astype(np.float32)
+        codes = torch.from_numpy(np.clip(q, -448, 448)).to(torch.float8_e4m3fn) \
+            .view(torch.uint8).numpy().astype(np.int64)
+        return codes, int(np.float16(float(sc)).view(np.uint16)), 0
+    if dtype == "int4":
+        codes, sc, z = quantize_row_exact(x.tolist(), steps=14, lo=-8, hi=7)
+    else:
+        codes, sc, z = quantize_row_exact(x.tolist())
+    return (np.asarray(codes, dtype=np.int64), int(np.float16(float(sc)).view(np.uint16)),
+            int(np.float16(float(z)).view(np.uint16)))
+
+
 def loop_scatter(case):
-    """Pools written one element at a time from the header's index formulas."""
+    """Pools written one element at a time from the header's index formulas:
+    bfloat16 rows, or for the quantized formats each row's codes and its
+    (scale, zero) float16 pair from the exact row model."""
+    from workloads import POISON_F16, POISON_I8
     lay = layout_of(case)
     c = case.cfg
     P, H, D = c.page_size, c.num_kv_heads, c.head_dim
-    assert c.kv_dtype == "bf16"
-    k = np.full(lay.elems, 0x7FC0, dtype=np.uint16)
-    v = np.full(lay.elems, 0x7FC0, dtype=np.uint16)
+    dt = c.kv_dtype
+    km = vm = None
+    if dt == "bf16":
+        k = np.full(lay.elems, 0x7FC0, dtype=np.uint16)
+        v = np.full(lay.elems, 0x7FC0, dtype=np.uint16)
+    else:
+        nbytes = lay.elems // 2 if dt == "int4" else lay.elems
+        k = np.full(nbytes, POISON_I8, dtype=np.uint8)
+        v = np.full(nbytes, POISON_I8, dtype=np.uint8)
+        km = np.full(lay.meta_elems, POISON_F16, dtype=np.uint16)
+        vm = np.full(lay.meta_elems, POISON_F16, dtype=np.uint16)
     for b in range(case.B):
         K, V = logical_rows(case, b)
         for pos in range(int(case.ctx[b])):
             page = int(case.block_tables[b][pos // P])
             t = pos % P
             for h in range(H):
-                for d in range(D):
-                    k[((page * H + h) * P + t) * D + d] = K[pos, h, d]
-                    v[((page * H + h) * D + d) * P + t] = V[pos, h, d]
-    return k, v
+                if dt == "bf16":
+                    for d in range(D):
+                        k[((page * H + h) * P + t) * D + d] = K[pos, h, d]
+                        v[((page * H + h) * D + d) * P + t] = V[pos, h, d]
+                    continue
+                for rows, pool, meta, is_v in ((K, k, km, False), (V, v, vm, True)):
+                    codes, s_bits, z_bits = _row_codes_exact(rows[pos, h], dt)
+                    for d in range(D):
+                        if dt == "int4":
+                            idx = (((page * H + h) * (D // 2) + d // 2) * P + t if is_v
+                                   else ((page * H + h) * P + t) * (D // 2) + d // 2)
+                            sh = 4 * (d % 2)
+                            pool[idx] = (int(pool[idx]) & ~(0xF << sh) & 0xFF) | \
+                                (((int(codes[d]) + 8) & 0xF) << sh)
+                        else:
+                            idx = (((page * H + h) * D + d) * P + t if is_v
+                                   else ((page * H + h) * P + t) * D + d)
+                            pool[idx] = int(codes[d]) & 0xFF
+                    meta[((page * H + h) * P + t) * 2 + 0] = s_bits
+                    meta[((page * H + h) * P + t) * 2 + 1] = z_bits
+    return k, v, km, vm
 
 
 def pin_block_table_worked_example():
@@ -93,18 +161,31 @@ def pin_block_table_worked_example():
 
 
 def pin_append_and_gather_layout(case):
-    """oracle.append writes what the element loop writes; gather returns the rows."""
-    k_loop, v_loop = loop_scatter(case)
-    k, v, _, _ = oracle_pools(case)
-    assert np.array_equal(k, k_loop), "K pool differs from the header layout"
-    assert np.array_equal(v, v_loop), "V pool differs from the header layout"
+    """oracle.append writes, byte for byte, what the element loop writes (codes,
+    scales and zero points included); gather returns the rows (for the
+    quantized formats, the exact row model's dequantized values)."""
+    loop = loop_scatter(case)
+    pools = oracle_pools(case)
+    for name, got, want in zip(("K", "V", "K meta", "V meta"), pools, loop):
+        if want is None:
+            assert got is None, name
+            continue
+        assert np.array_equal(np.asarray(got).view(np.uint8), want.view(np.uint8)), \
+            f"{name} pool differs from the header layout"
+    k, v, km, vm = pools
     lay = layout_of(case)
+    dt = case.cfg.kv_dtype
     for b in range(case.B):
         K, V = logical_rows(case, b)
-        Kg, Vg = oracle.gather_sequence(lay, k, v, None, None, case.block_tables[b],
+        Kg, Vg = oracle.gather_sequence(lay, k, v, km, vm, case.block_tables[b],
                                         int(case.ctx[b]))
-        assert np.array_equal(Kg, _bf16_f64(K).transpose(1, 0, 2)), f"K gather seq {b}"
-        assert np.array_equal(Vg, _bf16_f64(V).transpose(1, 0, 2)), f"V gather seq {b}"
+        if dt == "bf16":
+            Kw, Vw = _bf16_f64(K), _bf16_f64(V)
+        else:
+            Kw = np.stack([_dequant_exact(K[t], dt) for t in range(K.shape[0])])
+            Vw = np.stack([_dequant_exact(V[t], dt) for t in range(V.shape[0])])
+        assert np.array_equal(Kg, Kw.transpose(1, 0, 2)), f"K gather seq {b}"
+        assert np.array_equal(Vg, Vw.transpose(1, 0, 2)), f"V gather seq {b}"
 
 
 # ---------------------------------------------------------------- attention
@@ -138,6 +219,7 @@ def pin_attention_vs_sdpa(case, tol=1e-12):
         assert err <= tol, f"seq {b}: oracle vs sdpa {err:.3e}"
 
 
+@_memo_exact
 def _dequant_exact(rows_bits, dtype="int8"):
     """[H, D] bfloat16 rows -> float64 values after the exact row contract of
     ``dtype`` (exact-rational IEEE steps for INT8/INT4; for FP8 the
@@ -192,7 +274,7 @@ def pin_page_relabel_invariance(case, seed=11):
     def relabel(a, n):
         if a is None:
             return None
-        src = a.reshape(case.num_pages, n)
+        src = a.reshape(case.num_pages, -1)   # one page's bytes per row, any format
         dst = np.empty_like(src)
         dst[perm] = src
         return dst.reshape(-1)
@@ -285,6 +367,15 @@ def pin_memory_closed_forms():
         oracle.prefix_cached_bytes(p["requests"], 2500, p["shared"], c)
     assert saved == (p["requests"] - 1) * p["shared"] * c
     assert saved + p["shared"] * c == p["savings_printed_in_units_of_c"]
+    x2 = g["exercise2"]
+    for own in (0, 1, 500, 4096):   # any per-request suffix length: the saving is the same
+        n = x2["shared"] + own
+        saved = oracle.paged_bytes(x2["requests"], n, 1) - \
+            oracle.prefix_cached_bytes(x2["requests"], n, x2["shared"], 1)
+        assert saved == x2["savings_in_units_of_c"], own
+    c70 = oracle.bytes_per_token(80, 8, 128, 2)
+    assert c70 == x2["llama3_70b_c_bytes"]
+    assert x2["savings_in_units_of_c"] * c70 == x2["llama3_70b_savings_bytes"]
     x1 = g["exercise1"]
     worst = max(oracle.waste(n, x1["page_size"]) for n in range(1, 4 * x1["page_size"] + 1))
     assert worst == x1["max_waste_tokens"]

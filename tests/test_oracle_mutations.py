@@ -38,9 +38,8 @@ def _all_pins():
         ("waste", lambda: pins.pin_waste_bound(_case(TINY))),
     ]
     for c in small:
-        if c.kv_dtype == "bf16":
-            checks.append((f"layout_{c.name}",
-                           lambda c=c: pins.pin_append_and_gather_layout(_case(c))))
+        checks.append((f"layout_{c.name}",
+                       lambda c=c: pins.pin_append_and_gather_layout(_case(c))))
         checks.append((f"sdpa_{c.name}", lambda c=c: pins.pin_attention_vs_sdpa(_case(c))))
     for sink, window in ((4, 16), (0, 7)):
         checks.append((f"window_{sink}_{window}",
@@ -159,6 +158,23 @@ def _append_v_untransposed(layout, k, v, km, vm, k_rows, v_rows, seq_idx, pos, b
     spare_meta = None if vm is None else np.empty_like(vm)
     _ORIG_APPEND(layout, k, np.empty_like(v), km, spare_meta, k_rows, v_rows, seq_idx, pos, bt)
     _ORIG_APPEND(layout, v, np.empty_like(v), vm, spare_meta, v_rows, v_rows, seq_idx, pos, bt)
+
+
+def _append_meta_swapped(layout, k, v, km, vm, k_rows, v_rows, seq_idx, pos, bt):
+    # mistake: the zero point stored in the scale's slot and the scale in the
+    # zero's (paired with _dequant_swapped this stays self-consistent)
+    if km is None:
+        return _ORIG_APPEND(layout, k, v, km, vm, k_rows, v_rows, seq_idx, pos, bt)
+    tk, tv = km.copy(), vm.copy()
+    _ORIG_APPEND(layout, k, v, tk, tv, k_rows, v_rows, seq_idx, pos, bt)
+    P, H = layout.page_size, layout.num_kv_heads
+    seq_idx, pos = np.asarray(seq_idx, np.int64), np.asarray(pos, np.int64)
+    pages = np.asarray(bt, np.int64)[seq_idx, pos // P]
+    rows = ((pages[:, None] * H + np.arange(H)[None, :]) * P + (pos % P)[:, None]).reshape(-1)
+    for dst, src in ((km, tk), (vm, tv)):
+        d2, s2 = dst.reshape(-1, 2), src.reshape(-1, 2)
+        d2[rows, 0] = s2[rows, 1]
+        d2[rows, 1] = s2[rows, 0]
 
 
 def _kv_bytes_missing_two(layers, kv_heads, head_dim, tokens, elem_bytes):
@@ -286,6 +302,10 @@ MUTANTS = {
     "zero_point_at_min": [(oq, "quantize_rows", _quant_zero_at_min),
                           (opa, "quantize_rows", _quant_zero_at_min)],
     "dequant_swapped": [(oq, "dequantize", _dequant_swapped), (opa, "dequantize", _dequant_swapped)],
+    "meta_pair_misplaced": [(opa, "append", _append_meta_swapped),
+                            (oracle, "append", _append_meta_swapped),
+                            (oq, "dequantize", _dequant_swapped),
+                            (opa, "dequantize", _dequant_swapped)],
     "append_v_untransposed": [(opa, "append", _append_v_untransposed),
                               (oracle, "append", _append_v_untransposed)],
     "memory_missing_factor_two": [(oacc, "kv_bytes", _kv_bytes_missing_two),

@@ -18,8 +18,6 @@ def test_block_table_worked_example():
 
 
 def test_append_and_gather_follow_layout(small_case):
-    if small_case.cfg.kv_dtype != "bf16":
-        pytest.skip("element-loop layout check is written for bfloat16 pools")
     pins.pin_append_and_gather_layout(small_case)
 
 
