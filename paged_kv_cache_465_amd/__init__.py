@@ -238,6 +238,7 @@ def kvp_copy_pages(pool: Pool, k_pool, v_pool, k_meta, v_meta, src_dst, stream=N
     n = int(src_dst.shape[0]) if src_dst.dim() == 2 else 0
     if src_dst.dim() != 2 or src_dst.shape[1] != 2:
         raise ValueError("src_dst must be [n, 2]")
+    _check_pools(pool, k_pool, v_pool, k_meta, v_meta, "kvp_copy_pages")
     _check(_L.kvp_copy_pages(pool.handle, _dev(k_pool, "k_pool", eb), _dev(v_pool, "v_pool", eb),
                              _dev(k_meta, "k_meta", 2), _dev(v_meta, "v_meta", 2),
                              _dev(src_dst, "src_dst", 4), n, _stream(stream)), "kvp_copy_pages")
@@ -268,6 +269,40 @@ def _dev(t, name, elem_size=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _nbytes(t) -> int:
+    return 0 if t is None else int(t.numel()) * int(t.element_size())
+
+
+def _check_pools(pool: Pool, k_pool, v_pool, k_meta, v_meta, where: str) -> None:
+    """The K/V (and metadata) tensors hold at least one layer's pool bytes."""
+    kv_bytes, meta_bytes = kvp_pool_bytes(pool.desc)
+    for name, t in (("k_pool", k_pool), ("v_pool", v_pool)):
+        if t is None or _nbytes(t) < kv_bytes:
+            raise ValueError(f"{where}: {name} must hold the pool's {kv_bytes} bytes")
+    for name, t in (("k_meta", k_meta), ("v_meta", v_meta)):
+        if meta_bytes and (t is None or _nbytes(t) < meta_bytes):
+            raise ValueError(f"{where}: {name} must hold the pool's {meta_bytes} metadata bytes")
+        if not meta_bytes and t is not None:
+            raise ValueError(f"{where}: bfloat16 pools take no {name}")
+
+
+def _check_queries(pool: Pool, q, out, where: str) -> None:
+    """q and out are [rows, H_q, D] with the pool's head dim and whole groups."""
+    D, Hkv = pool.desc.head_dim, pool.desc.num_kv_heads
+    if q.dim() != 3 or int(q.shape[2]) != D:
+        raise ValueError(f"{where}: q must be [rows, H_q, {D}]")
+    if int(q.shape[1]) % Hkv:
+        raise ValueError(f"{where}: H_q must be a multiple of the pool's {Hkv} KV heads")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"{where}: out must have q's shape")
+
+
+def _check_batch(block_tables, context_lens, B: int, where: str) -> None:
+    if block_tables.dim() != 2 or int(block_tables.shape[0]) != B or context_lens.numel() != B:
+        raise ValueError(f"{where}: block_tables [B, max_blocks] and context_lens [B] "
+                         "must cover the batch")
+
+
 def _stream(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -279,10 +314,12 @@ def kvp_kv_append(pool: Pool, k_pool, v_pool, k_meta, v_meta, k_new, v_new, seq_
     """Write k_new/v_new [N, H_kv, D] (bf16) into the slots the tables name."""
     eb = pool.elem_bytes
     n = int(seq_idx.numel())
-    if pos.numel() != n or k_new.shape[0] != n or v_new.shape[0] != n:
-        raise ValueError("seq_idx, pos, k_new and v_new must agree in length")
+    rows = (n, pool.desc.num_kv_heads, pool.desc.head_dim)
+    if pos.numel() != n or tuple(k_new.shape) != rows or tuple(v_new.shape) != rows:
+        raise ValueError(f"kvp_kv_append: seq_idx and pos [N], k_new and v_new {list(rows)}")
     if block_tables.dim() != 2:
         raise ValueError("block_tables must be [num_seqs, max_blocks]")
+    _check_pools(pool, k_pool, v_pool, k_meta, v_meta, "kvp_kv_append")
     _check(_L.kvp_kv_append(pool.handle, _dev(k_pool, "k_pool", eb), _dev(v_pool, "v_pool", eb),
                             _dev(k_meta, "k_meta", 2), _dev(v_meta, "v_meta", 2),
                             _dev(k_new, "k_new", 2), _dev(v_new, "v_new", 2),
@@ -306,11 +343,10 @@ def kvp_paged_attention_decode(pool: Pool, q, k_pool, v_pool, k_meta, v_meta, bl
                                stream=None) -> None:
     """out[b, j] = softmax(scale * q[b, j] K_b^T) V_b over the sequence's pages."""
     eb = pool.elem_bytes
+    _check_queries(pool, q, out, "decode")
     B, Hq = int(q.shape[0]), int(q.shape[1])
-    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
-        raise ValueError("block_tables/context_lens must cover the batch")
-    if out.shape != q.shape:
-        raise ValueError("out must have q's shape")
+    _check_batch(block_tables, context_lens, B, "decode")
+    _check_pools(pool, k_pool, v_pool, k_meta, v_meta, "decode")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_L.kvp_paged_attention_decode(
         pool.handle, _dev(q, "q", 2), _dev(k_pool, "k_pool", eb), _dev(v_pool, "v_pool", eb),
@@ -327,11 +363,10 @@ def kvp_paged_attention_decode_noalloc(pool: Pool, q, k_pool, v_pool, k_meta, v_
     """kvp_paged_attention_decode with the split partials in the library's
     fixed device buffer (no workspace argument, no device allocation)."""
     eb = pool.elem_bytes
+    _check_queries(pool, q, out, "decode")
     B, Hq = int(q.shape[0]), int(q.shape[1])
-    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
-        raise ValueError("block_tables/context_lens must cover the batch")
-    if out.shape != q.shape:
-        raise ValueError("out must have q's shape")
+    _check_batch(block_tables, context_lens, B, "decode")
+    _check_pools(pool, k_pool, v_pool, k_meta, v_meta, "decode")
     _check(_L.kvp_paged_attention_decode_noalloc(
         pool.handle, _dev(q, "q", 2), _dev(k_pool, "k_pool", eb), _dev(v_pool, "v_pool", eb),
         _dev(k_meta, "k_meta", 2), _dev(v_meta, "v_meta", 2), _dev(block_tables, "block_tables", 4),
@@ -359,11 +394,10 @@ def kvp_paged_attention_decode_window(pool: Pool, q, k_pool, v_pool, k_meta, v_m
                                       stream=None) -> None:
     """Decode attending only to the first sink_tokens and the last window_tokens tokens."""
     eb = pool.elem_bytes
+    _check_queries(pool, q, out, "decode")
     B, Hq = int(q.shape[0]), int(q.shape[1])
-    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
-        raise ValueError("block_tables/context_lens must cover the batch")
-    if out.shape != q.shape:
-        raise ValueError("out must have q's shape")
+    _check_batch(block_tables, context_lens, B, "decode")
+    _check_pools(pool, k_pool, v_pool, k_meta, v_meta, "decode")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_L.kvp_paged_attention_decode_window(
         pool.handle, _dev(q, "q", 2), _dev(k_pool, "k_pool", eb), _dev(v_pool, "v_pool", eb),
@@ -430,11 +464,10 @@ def kvp_paged_attention_decode_scheduled(pool: Pool, q, k_pool, v_pool, k_meta, 
     """Decode along a balanced schedule; sched_dev is the device copy (int32)
     of schedule.used."""
     eb = pool.elem_bytes
+    _check_queries(pool, q, out, "decode")
     B, Hq = int(q.shape[0]), int(q.shape[1])
-    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
-        raise ValueError("block_tables/context_lens must cover the batch")
-    if out.shape != q.shape:
-        raise ValueError("out must have q's shape")
+    _check_batch(block_tables, context_lens, B, "decode")
+    _check_pools(pool, k_pool, v_pool, k_meta, v_meta, "decode")
     if sched_dev.numel() < schedule.info.sched_words:
         raise ValueError("sched_dev must hold the schedule's used words")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -456,8 +489,8 @@ def kvp_paged_attention_prefill(pool: Pool, q, q_start, k_pool, v_pool, k_meta, 
     B = int(context_lens.numel())
     if q_start.numel() != B + 1 or block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("q_start must have B+1 entries and block_tables B rows")
-    if out.shape != q.shape or q.dim() != 3:
-        raise ValueError("q and out must be [N, H_q, D]")
+    _check_queries(pool, q, out, "prefill")
+    _check_pools(pool, k_pool, v_pool, k_meta, v_meta, "prefill")
     _check(_L.kvp_paged_attention_prefill(
         pool.handle, _dev(q, "q", 2), _dev(q_start, "q_start", 4), _dev(k_pool, "k_pool", eb),
         _dev(v_pool, "v_pool", eb), _dev(k_meta, "k_meta", 2), _dev(v_meta, "v_meta", 2),
@@ -485,9 +518,11 @@ def kvp_paged_attention_decode_partials(pool: Pool, q, k_pool, v_pool, k_meta, v
                                         stream=None) -> int:
     """Split kernel only: per-split (o, m, l) partials into ``partials``; returns S."""
     eb = pool.elem_bytes
+    if q.dim() != 3 or int(q.shape[2]) != pool.desc.head_dim:
+        raise ValueError(f"decode partials: q must be [B, H_q, {pool.desc.head_dim}]")
     B, Hq = int(q.shape[0]), int(q.shape[1])
-    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
-        raise ValueError("block_tables/context_lens must cover the batch")
+    _check_batch(block_tables, context_lens, B, "decode partials")
+    _check_pools(pool, k_pool, v_pool, k_meta, v_meta, "decode partials")
     nbytes = partials.numel() * partials.element_size()
     s = ctypes.c_int32()
     _check(_L.kvp_paged_attention_decode_partials(
@@ -503,6 +538,10 @@ def kvp_lse_merge(partials, rows: int, num_splits: int, head_dim: int, out, stre
     """Merge per-split partials by log-sum-exp into ``out`` ([rows, D] bfloat16 bits)."""
     if out.numel() != int(rows) * int(head_dim):
         raise ValueError("out must hold rows * head_dim elements")
+    parts = int(rows) * int(num_splits)
+    need = (parts * int(head_dim) * 4 + 255) // 256 * 256 + parts * 2 * 4
+    if parts > 0 and _nbytes(partials) < need:
+        raise ValueError(f"partials must hold {need} bytes for {rows} rows x {num_splits} splits")
     _check(_L.kvp_lse_merge(_dev(partials, "partials"), int(rows), int(num_splits),
                             int(head_dim), _dev(out, "out", 2), _stream(stream)),
            "kvp_lse_merge")

@@ -156,7 +156,9 @@ kvp_status launch_split_kernel(const kvp_pool_desc& d, const kvp_decode_plan_t& 
   a.sched = sched;
   a.items_off = sched ? sched_info->items_offset : 0;
   a.num_items = sched ? sched_info->num_items : 0;
-  a.num_slots = sched ? sched_info->num_slots : 0;
+  // partial slots exist only with a partials buffer: without one, an item
+  // naming a slot is skipped instead of writing through a null pointer
+  a.num_slots = sched && part_o ? sched_info->num_slots : 0;
   a.num_bins = sched ? sched_info->num_bins : 0;
 
   const int W = plan.waves_per_group;
@@ -419,6 +421,17 @@ extern "C" kvp_status kvp_paged_attention_decode_scheduled(
     float scale, const int32_t* sched, const kvp_schedule_info* info, void* out,
     void* workspace, size_t workspace_bytes, kvp_stream_t stream) {
   if (!info) return KVP_E_INVAL;
+  // the schedule's header first (host only): a schedule that cuts pairs has
+  // partial slots and merge entries, and one that cuts none has neither, so
+  // an info with slots but no merge entries (or the reverse) is not one
+  // kvp_decode_schedule built; refusing it keeps partial writes behind a
+  // workspace the call has checked
+  const int64_t bins = info->num_bins, items = info->num_items;
+  if (bins < 1 || items < 0 || info->num_merge < 0 || info->num_slots < 0 ||
+      (info->num_merge == 0) != (info->num_slots == 0) ||
+      info->items_offset < 8 + bins + 1 ||
+      int64_t(info->merge_offset) != info->items_offset + 8 * items)
+    return KVP_E_INVAL;
   kvp_pool_desc d;
   kvp_decode_plan_t plan;
   bool empty;
@@ -428,11 +441,6 @@ extern "C" kvp_status kvp_paged_attention_decode_scheduled(
                                  info->window_tokens, &d, &plan, &empty);
   if (st != KVP_OK || empty) return st;
   if (!out || !sched) return KVP_E_INVAL;
-  const int64_t bins = info->num_bins, items = info->num_items;
-  if (bins < 1 || items < 0 || info->num_merge < 0 || info->num_slots < 0 ||
-      info->items_offset < 8 + bins + 1 ||
-      int64_t(info->merge_offset) != info->items_offset + 8 * items)
-    return KVP_E_INVAL;
   const int g = num_q_heads / d.num_kv_heads;
   const size_t slots = size_t(info->num_slots);
   float* part_o = nullptr;

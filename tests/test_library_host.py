@@ -525,3 +525,68 @@ def test_decode_schedule_rejects_bad_arguments(kvp):
                                ctypes.byref(info))
     assert st == kvp.KVP_E_INVAL
     pool.close()
+
+
+def test_scheduled_decode_rejects_inconsistent_schedule_info(kvp):
+    """A schedule info with partial slots but no merge entries (or merge entries
+    but no slots) is not one kvp_decode_schedule builds: the scheduled decode
+    refuses it on the host, before any device work (the kernels would
+    otherwise be handed slots with no partials buffer behind them)."""
+    import ctypes
+    from paged_kv_cache_465_amd import _lib
+    L = _lib.load()
+    pool = kvp.kvp_pool_create(kvp.make_desc(16, 16, 2, 64, "bf16"))
+    ctx = np.array([50, 100], np.int32)
+    good = kvp.kvp_decode_schedule(pool, ctx, 8, 8, 3)
+    assert good.info.num_merge > 0 and good.info.num_slots > 0
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: the call fails on the host
+    for merge, slots in ((0, good.info.num_slots), (good.info.num_merge, 0)):
+        info = _lib.ScheduleInfo.from_buffer_copy(good.info)
+        info.num_merge, info.num_slots = merge, slots
+        st = L.kvp_paged_attention_decode_scheduled(
+            pool.handle, fake, fake, fake, None, None, fake, 8, fake, 2, 8, 100, 0.125, fake,
+            ctypes.byref(info), fake, None, 0, None)
+        assert st == kvp.KVP_E_INVAL, (merge, slots)
+    pool.close()
+
+
+def test_binding_checks_shapes_before_any_call(kvp):
+    """The Python wrappers compare tensor shapes and byte sizes with the pool
+    descriptor before they reach the C ABI (a tensor of the wrong shape would
+    otherwise let a kernel read or write past it).  CPU tensors suffice: the
+    shape checks come before the device-pointer checks."""
+    import torch
+    desc = kvp.make_desc(8, 16, 2, 64, "int8")
+    pool = kvp.kvp_pool_create(desc)
+    kv_bytes, meta_bytes = kvp.kvp_pool_bytes(desc)
+    kp = torch.zeros(kv_bytes, dtype=torch.int8)
+    km = torch.zeros(meta_bytes // 2, dtype=torch.int16)
+    bt = torch.zeros((3, 4), dtype=torch.int32)
+    ctx = torch.zeros(3, dtype=torch.int32)
+    q = torch.zeros((3, 8, 64), dtype=torch.int16)
+
+    def raises(match, fn, *a):
+        with pytest.raises(ValueError, match=match):
+            fn(*a)
+
+    dec = kvp.kvp_paged_attention_decode
+    raises("q must be", dec, pool, q[..., :32], kp, kp, km, km, bt, ctx, 16, 0.1, q[..., :32])
+    raises("multiple", dec, pool, q[:, :3], kp, kp, km, km, bt, ctx, 16, 0.1, q[:, :3])
+    raises("out must", dec, pool, q, kp, kp, km, km, bt, ctx, 16, 0.1, q[:2])
+    raises("cover the batch", dec, pool, q, kp, kp, km, km, bt[:2], ctx, 16, 0.1, q)
+    raises("k_pool must hold", dec, pool, q, kp[:-1], kp, km, km, bt, ctx, 16, 0.1, q)
+    raises("v_meta must hold", dec, pool, q, kp, kp, km, km[:-1], bt, ctx, 16, 0.1, q)
+    raises("device tensor", dec, pool, q, kp, kp, km, km, bt, ctx, 16, 0.1, q)
+    app = kvp.kvp_kv_append
+    rows = torch.zeros((5, 2, 64), dtype=torch.int16)
+    idx = torch.zeros(5, dtype=torch.int32)
+    raises("k_new and v_new", app, pool, kp, kp, km, km, rows[:, :1], rows, idx, idx, bt)
+    raises("k_new and v_new", app, pool, kp, kp, km, km, rows, rows[..., :32], idx, idx, bt)
+    raises("k_pool must hold", app, pool, kp[:10], kp, km, km, rows, rows, idx, idx, bt)
+    part = torch.zeros(100, dtype=torch.float32)
+    raises("partials must hold", kvp.kvp_lse_merge, part, 3, 2, 64, torch.zeros((3, 64)))
+    bf = kvp.kvp_pool_create(kvp.make_desc(8, 16, 2, 64, "bf16"))
+    kb = torch.zeros(kvp.kvp_pool_bytes(bf.desc)[0] // 2, dtype=torch.int16)
+    raises("take no k_meta", dec, bf, q, kb, kb, km, None, bt, ctx, 16, 0.1, q)
+    bf.close()
+    pool.close()
