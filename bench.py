@@ -19,6 +19,7 @@ Prints ONE JSON line on stdout (progress goes to stderr):
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
     python bench.py --copy-calibration   # plain copy kernel for counter scaling
+    python bench.py --probe-calibration  # streaming-read probe (non-temporal loads), same
 """
 from __future__ import annotations
 
@@ -73,6 +74,9 @@ def parse_args(argv=None):
     p.add_argument("--no-parity", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of known size (for counter scaling)")
+    p.add_argument("--probe-calibration", action="store_true",
+                   help="only run the streaming-read probe (2 GiB of non-temporal chunk reads "
+                        "per launch: counter scaling for the decode kernels' loads)")
     return p.parse_args(argv)
 
 
@@ -358,14 +362,55 @@ def copy_probe(dev, nbytes=1 << 32, reps=5):
             "GBps_read_plus_write": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
+def stream_read_probe(kvp, dev, num_cus, pool_bytes=1 << 30, reps=5):
+    """The rate the decode kernels' access pattern allows with no arithmetic:
+    kvp_probe_read_chunks over two 1 GiB buffers (a K-like and a V-like pool)
+    in shuffled 4 KiB chunks (one (page, KV head) tile of 16 tokens x 128
+    bfloat16 channels), non-temporal 16-byte loads.  Measured with the decode
+    kernel's own shape (two chunks in flight per wavefront, one wavefront per
+    SIMD) and with a few others; the best shuffled rate is the ceiling.  For
+    context, the same buffers read in order in 8 KiB chunks."""
+    import torch
+    a = torch.ones(pool_bytes // 4, dtype=torch.int32, device=dev)
+    b = torch.ones_like(a)
+    g = torch.Generator(device=dev)
+    g.manual_seed(465)
+    ids = {4096: torch.randperm(pool_bytes // 4096, generator=g, device=dev).to(torch.int32),
+           8192: torch.arange(pool_bytes // 8192, dtype=torch.int32, device=dev)}
+    runs = [("decode_shape", 4096, 2, 4), ("shuffled_d1_w8", 4096, 1, 8),
+            ("shuffled_d2_w8", 4096, 2, 8), ("shuffled_d4_w4", 4096, 4, 4),
+            ("linear_8k_d1_w4", 8192, 1, 4)]
+    res = {}
+    for name, chunk, depth, per_cu in runs:
+        waves = per_cu * num_cus
+        sink = torch.empty(waves * 64, dtype=torch.int32, device=dev)
+        kvp.kvp_probe_read_chunks(a, b, ids[chunk], chunk, waves, sink, depth)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            kvp.kvp_probe_read_chunks(a, b, ids[chunk], chunk, waves, sink, depth)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        res[name] = {"chunk_bytes": chunk, "chunks_in_flight": depth, "wavefronts": waves,
+                     "us": round(us, 2), "GBps": round(2 * pool_bytes / (us * 1e-6) / 1e9, 1)}
+    del a, b
+    best = max((v["GBps"] for k, v in res.items() if k != "linear_8k_d1_w4"))
+    return {"pattern": "two 1 GiB buffers, shuffled 4 KiB chunks, non-temporal 16-byte loads "
+                       "(kvp_probe_read_chunks); GBps = best of the shuffled shapes",
+            "bytes_per_launch": 2 * pool_bytes, "GBps": best,
+            "frac_of_peak": round(best / HBM_PEAK_GBPS, 4), "runs": res}
+
+
 # ---- CPU oracle leg ------------------------------------------------------------------
-def host_layer0(cfg, case, dev):
-    """Layer 0's inputs on the host, drawn exactly as the device setup draws them."""
+def host_layer(cfg, case, dev, layer=0):
+    """One layer's inputs on the host, drawn exactly as the device setup draws them."""
     if not cfg.device_data:
         return case
     import copy
     from workloads import history_rows_device
-    q, hk, hv, hs, hp, nk, nv, npos = history_rows_device(cfg, case, 0, dev)
+    q, hk, hv, hs, hp, nk, nv, npos = history_rows_device(cfg, case, layer, dev)
     c = copy.copy(case)
     h = lambda t: t.view(__import__("torch").int16).cpu().numpy().view(np.uint16)  # noqa: E731
     c.q, c.hist_k, c.hist_v, c.new_k, c.new_v = h(q), h(hk), h(hv), h(nk), h(nv)
@@ -433,7 +478,13 @@ def cpu_baseline(cfg, hc, target_s: float):
     sb = step_bytes(dataclasses.replace(cfg, layers=1, batch=n), hc.ctx[seqs], n_rows)
     sample_bytes = (sb["kv"] + sb["q_out"] + sb["table"]) * passes
     gbps = sample_bytes / dt / 1e9
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
     return {"value": gbps, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "blas_threads": int(threads), "os_cpu_count": os.cpu_count(),
+            "affinity_cpus": affinity,
             "sample": f"layer 0, sequences 0..{n - 1} of {hc.B}, {passes} passes (float64 numpy "
                       f"gather + attention, {dt:.1f} s); GB/s of the same algorithmic bytes",
             "seconds": dt, "tokens_per_s_equiv": n * passes / dt / cfg.layers,
@@ -441,13 +492,23 @@ def cpu_baseline(cfg, hc, target_s: float):
 
 
 def _cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it: model name, family, model and
+    stepping (a virtualised host may report a short model name)."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (x.strip() for x in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping") and k not in fields:
+                    fields[k] = v
+            elif fields:
+                break
     except OSError:
         pass
-    return "unknown"
+    if not fields:
+        return "unknown"
+    return (f"{fields.get('model name', 'unknown')} (family {fields.get('cpu family', '?')}, "
+            f"model {fields.get('model', '?')}, stepping {fields.get('stepping', '?')})")
 
 
 def prefix_cache_bench(kvp, dev, n_req=100, prefix=2000, suffix=512, P=16, copies=4096):
@@ -519,6 +580,10 @@ def main(argv=None):
         print(json.dumps({"copy_calibration": r}))
         return
     import paged_kv_cache_465_amd as kvp
+    if args.probe_calibration:
+        r = stream_read_probe(kvp, dev, torch.cuda.get_device_properties(0).multi_processor_count)
+        print(json.dumps({"probe_calibration": r}))
+        return
     if args.config == "prefix_cache":
         print(json.dumps(prefix_cache_bench(kvp, dev)), flush=True)
         return
@@ -603,29 +668,41 @@ def main(argv=None):
         if counters:
             out["roofline"]["counters"] = counters
     out["copy_probe"] = copy_probe(dev)
+    ceiling = stream_read_probe(kvp, dev, torch.cuda.get_device_properties(0).multi_processor_count)
+    out["stream_read_ceiling"] = ceiling
+    if roof["unit"] == "GB/s":
+        out["roofline"]["frac_of_stream_ceiling"] = round(roof["achieved"] / ceiling["GBps"], 4)
     hc = None
     if not (args.no_parity and args.no_cpu_baseline):
-        hc = host_layer0(cfg, case, dev)
+        hc = host_layer(cfg, case, dev, 0)
     if not args.no_parity:
-        out["parity"] = parity_sample(cfg, hc, state)
+        # the first and the last layer of the timed run (inputs of a layer are
+        # drawn from its own seed, so each is checked against its own oracle)
+        checks = [parity_sample(cfg, hc, state, 0)]
+        if cfg.layers > 1:
+            checks.append(parity_sample(cfg, host_layer(cfg, case, dev, cfg.layers - 1), state,
+                                        cfg.layers - 1))
+        out["parity"] = {"layers": [c["layer"] for c in checks], "seqs": checks[0]["seqs"],
+                         "max_abs": max(c["max_abs"] for c in checks),
+                         "rel_l2": max(c["rel_l2"] for c in checks),
+                         "ok": all(c["ok"] for c in checks), "per_layer": checks}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, hc, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
-def parity_sample(cfg, hc, state, seqs=(0, 13, 31)):
-    """Layer 0 output rows of the timed run for a few sequences against the oracle."""
-    import oracle
+def parity_sample(cfg, hc, state, layer=0, seqs=(0, 13, 31)):
+    """One layer's output rows of the timed run for a few sequences against the oracle."""
     pool, layers, bt, ctx = state
     seqs = [s for s in seqs if s < hc.B]
     lay, pools = oracle_layer(cfg, hc, seqs)
     ref = oracle_decode(cfg, lay, hc, pools, seqs)
-    got_bits = layers[0].out.cpu().numpy().view(np.uint16)
+    got_bits = layers[layer].out.cpu().numpy().view(np.uint16)
     got = (got_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     rows = np.concatenate([np.arange(hc.q_start[b], hc.q_start[b + 1]) for b in seqs])
     d = np.abs(got[rows] - ref[rows])
     rel = float(np.linalg.norm(got[rows] - ref[rows]) / np.linalg.norm(ref[rows]))
-    r = {"layer": 0, "seqs": seqs, "max_abs": float(d.max()), "rel_l2": rel,
+    r = {"layer": layer, "seqs": seqs, "max_abs": float(d.max()), "rel_l2": rel,
          "ok": bool(d.max() <= 1e-2 and rel <= 5e-3)}
     log(f"[parity] {r}")
     return r

@@ -492,6 +492,26 @@ kvp_status kvp_paged_attention_decode_partials(
 kvp_status kvp_lse_merge(const void* partials, int32_t rows, int32_t num_splits, int32_t head_dim,
                          void* out, kvp_stream_t stream);
 
+/* ---- Measurement: streaming-read ceiling (device) ---------------------------
+ * Decode reads every (page, KV head) tile of K and V once per step and is
+ * bound by memory bandwidth ("KV Cache Optimization" glossary, section
+ * "Memory-Bound Operation").  This probe reads the same pattern with no
+ * arithmetic: for each of n_chunks entries of chunk_ids (device int32 array),
+ * chunk chunk_ids[i] (chunk_bytes contiguous bytes at chunk_ids[i] *
+ * chunk_bytes) of pool_a and of pool_b, both device buffers of at least
+ * pool_bytes; with the decode kernels' loads (16 bytes per lane, non-temporal
+ * hint), chunks_in_flight (1, 2, 4 or 8; not 8 with 8 KiB chunks) chunks per
+ * wavefront in flight, num_waves wavefronts each taking a contiguous share of
+ * the list (four per workgroup).  An id outside the buffers reads
+ * chunk 0.  sink: device array of num_waves * 64 uint32 that receives a fold
+ * of the bytes read (its value has no meaning).  chunk_bytes is 1024, 2048,
+ * 4096 or 8192 (KVP_E_UNSUPPORTED otherwise).  Bytes read: 2 * n_chunks *
+ * chunk_bytes. */
+kvp_status kvp_probe_read_chunks(const void* pool_a, const void* pool_b, size_t pool_bytes,
+                                 const int32_t* chunk_ids, int32_t n_chunks, int32_t chunk_bytes,
+                                 int32_t chunks_in_flight, int32_t num_waves, uint32_t* sink,
+                                 kvp_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -547,6 +547,21 @@ def kvp_lse_merge(partials, rows: int, num_splits: int, head_dim: int, out, stre
            "kvp_lse_merge")
 
 
+def kvp_probe_read_chunks(pool_a, pool_b, chunk_ids, chunk_bytes: int, num_waves: int, sink,
+                          chunks_in_flight: int = 2, stream=None) -> None:
+    """Read chunk chunk_ids[i] of both device buffers for every i (the decode
+    kernels' page-streaming pattern with no arithmetic); sink receives
+    num_waves * 64 words."""
+    pool_bytes = min(_nbytes(pool_a), _nbytes(pool_b))
+    if _nbytes(sink) < int(num_waves) * 64 * 4:
+        raise ValueError("sink must hold num_waves * 64 uint32 words")
+    _check(_L.kvp_probe_read_chunks(_dev(pool_a, "pool_a"), _dev(pool_b, "pool_b"), pool_bytes,
+                                    _dev(chunk_ids, "chunk_ids", 4), int(chunk_ids.numel()),
+                                    int(chunk_bytes), int(chunks_in_flight), int(num_waves),
+                                    _dev(sink, "sink", 4),
+                                    _stream(stream)), "kvp_probe_read_chunks")
+
+
 __all__ = [
     "KVP_OK", "KVP_E_INVAL", "KVP_E_NOPAGES", "KVP_E_UNSUPPORTED", "KVP_E_HIP", "KVP_E_SCRATCH",
     "KVP_BF16",
@@ -564,4 +579,5 @@ __all__ = [
     "kvp_paged_attention_decode_window", "kvp_paged_attention_prefill", "PrefixCache",
     "kvp_prefix_cache_create", "kvp_prefix_cache_pages", "kvp_prefix_match",
     "kvp_prefix_insert", "kvp_prefix_evict", "kvp_seq_prepare_append", "kvp_copy_pages",
+    "kvp_probe_read_chunks",
 ]

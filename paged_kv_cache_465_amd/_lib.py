@@ -106,6 +106,8 @@ PROTOTYPES = {
                                                        c_float, c_void_p,
                                                        ctypes.POINTER(ScheduleInfo), c_void_p,
                                                        c_void_p, c_size_t, c_void_p]),
+    "kvp_probe_read_chunks": (c_int32, [c_void_p, c_void_p, c_size_t, c_void_p, c_int32, c_int32,
+                                        c_int32, c_int32, c_void_p, c_void_p]),
 }
 
 _lib = None

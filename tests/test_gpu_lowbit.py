@@ -244,7 +244,7 @@ def test_prefill_rejects_lowbit_pools(kvp, kind):
 
 def test_full_int4_long(kvp):
     """16 sequences of 16k-32k tokens, INT4 pool with outlier channels."""
-    _sampled_check(kvp, INT4_LONG, seqs=(0, 7, 15))
+    _sampled_check(kvp, INT4_LONG, seqs=(0, 7, 15), whole_pool=True)
 
 
 def test_full_fp8_long(kvp):

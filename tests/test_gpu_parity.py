@@ -254,7 +254,10 @@ def test_out_of_range_page_ids_are_skipped(kvp):
 
 
 # ---- full-size workloads (sampled oracle checks) ---------------------------------
-def _sampled_check(kvp, cfg, seqs, splits=0):
+def _sampled_check(kvp, cfg, seqs, splits=0, whole_pool=False):
+    """The full-size workload through the library; the sampled sequences'
+    pages (every pool byte with ``whole_pool``) bit for bit against the
+    oracle's append, and the sampled sequences' outputs against the oracle."""
     case = make_case(cfg)
     log(f"[full] {cfg.name} seed={cfg.seed} B={case.B} pages={case.num_pages} "
         f"max_ctx={int(case.ctx.max())} sampled={list(seqs)}")
@@ -280,14 +283,25 @@ def _sampled_check(kvp, cfg, seqs, splits=0):
     lay = layout_of(case)
     from workloads import POISON_BF16, POISON_F16, POISON_I8
     k, v, km, vm = lay.empty_pools(POISON_BF16 if lay.dtype == "bf16" else POISON_I8, POISON_F16)
-    need = set(seqs) | ({0} if cfg.shared_prefix else set())
-    sel = np.isin(case.hist_seq, list(need))
-    oracle.append(lay, k, v, km, vm, case.hist_k[sel], case.hist_v[sel], case.hist_seq[sel],
-                  case.hist_pos[sel], case.block_tables)
+    need = set(range(case.B)) if whole_pool else \
+        set(seqs) | ({0} if cfg.shared_prefix else set())
+    sel = np.nonzero(np.isin(case.hist_seq, list(need)))[0]
+    for r0 in range(0, sel.size, 65536):     # in chunks: bounded host memory
+        c = sel[r0:r0 + 65536]
+        oracle.append(lay, k, v, km, vm, case.hist_k[c], case.hist_v[c], case.hist_seq[c],
+                      case.hist_pos[c], case.block_tables)
     nsel = np.isin(case.new_seq, list(need))
     oracle.append(lay, k, v, km, vm, case.new_k[nsel], case.new_v[nsel], case.new_seq[nsel],
                   case.new_pos[nsel], case.block_tables)
     gk, gv, gkm, gvm = gc.pools_host()
+    if whole_pool:
+        # every byte of the code and metadata pools, free pages and tails too
+        for name, g, r in (("K", gk, k), ("V", gv, v), ("Km", gkm, km), ("Vm", gvm, vm)):
+            if r is None:
+                continue
+            bad = np.count_nonzero(g.reshape(-1).view(np.uint8) != r.reshape(-1).view(np.uint8))
+            assert bad == 0, f"{name} pool differs at {bad} bytes"
+        log(f"  whole pools bit-exact ({gk.nbytes + gv.nbytes} code bytes)")
     for b in seqs:
         pages = case.block_tables[b][: -(-int(case.ctx[b]) // cfg.page_size)]
         pages = pages[pages >= 0]
@@ -323,7 +337,9 @@ def test_full_llama3_8b_layer(kvp):
 
 
 def test_full_int8_long(kvp):
-    _sampled_check(kvp, INT8_LONG, seqs=(0, 5, 11, 15))
+    """16 sequences of 16k-32k tokens: every byte of the INT8 code and (scale,
+    zero) pools kv_append wrote (and left poisoned) against the oracle."""
+    _sampled_check(kvp, INT8_LONG, seqs=(0, 5, 11, 15), whole_pool=True)
 
 
 def test_full_shared_prefix(kvp):
@@ -693,3 +709,24 @@ def test_full_llama3_70b_layer(kvp, layer):
     m, r = assert_close(got, ref, f"llama3_70b layer {layer}")
     log(f"  all 32 sequences: max_abs={m:.2e} rel_l2={r:.2e}")
     pool.close()
+
+
+def test_read_probe_runs_every_shape(kvp):
+    """The streaming-read probe the benchmark's ceiling comes from runs at every
+    chunk size and ring depth it accepts (ids outside the buffers included)
+    and writes its whole sink."""
+    a = torch.ones(1 << 18, dtype=torch.int32, device="cuda")
+    b = torch.full_like(a, 3)
+    for chunk in (1024, 2048, 4096, 8192):
+        n = a.numel() * 4 // chunk
+        ids = torch.randperm(n, device="cuda").to(torch.int32)
+        ids[0] = n + 5   # outside: reads chunk 0
+        for depth in (1, 2, 4, 8):
+            if chunk == 8192 and depth == 8:
+                continue
+            waves = 7
+            sink = torch.full((waves * 64,), -1, dtype=torch.int32, device="cuda")
+            kvp.kvp_probe_read_chunks(a, b, ids, chunk, waves, sink, depth)
+            torch.cuda.synchronize()
+            # every lane folds an even or odd number of (1 ^ 3) words: never the fill -1
+            assert (sink != -1).all(), (chunk, depth)

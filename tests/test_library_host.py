@@ -590,3 +590,20 @@ def test_binding_checks_shapes_before_any_call(kvp):
     raises("take no k_meta", dec, bf, q, kb, kb, km, None, bt, ctx, 16, 0.1, q)
     bf.close()
     pool.close()
+
+
+def test_read_probe_argument_checks(kvp):
+    """The streaming-read probe refuses chunk sizes and ring depths it has no
+    instance for, and bad counts, on the host (nothing is launched)."""
+    import ctypes
+    from paged_kv_cache_465_amd import _lib
+    L = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    call = lambda n, chunk, depth, waves: L.kvp_probe_read_chunks(  # noqa: E731
+        fake, fake, 1 << 20, fake, n, chunk, depth, waves, fake, None)
+    assert call(4, 3000, 2, 4) == kvp.KVP_E_UNSUPPORTED
+    assert call(4, 4096, 3, 4) == kvp.KVP_E_UNSUPPORTED
+    assert call(4, 8192, 8, 4) == kvp.KVP_E_UNSUPPORTED
+    assert call(-1, 4096, 2, 4) == kvp.KVP_E_INVAL
+    assert call(4, 4096, 2, 0) == kvp.KVP_E_INVAL
+    assert call(0, 4096, 2, 4) == kvp.KVP_OK
