@@ -285,6 +285,15 @@ kvp_status kvp_decode_workspace_bytes(const kvp_pool* pool, int32_t num_seqs,
  * b (ctx_b = context_lens[b]) through KV head j/g, as eq. 1 above, scores
  * multiplied by `scale` (normally 1/sqrt(D)).  Scores, softmax and the
  * weighted sum are accumulated in float32; out is rounded to bfloat16 (RNE).
+ * Matrix-core operands (g >= 4): for bfloat16 pools q and K are used as
+ * stored and the softmax weights p are rounded to bfloat16 before P.V.  For
+ * INT8, INT4 and FP8 pools the codes convert to float16 exactly, q is rounded
+ * to float16 (so |q| <= 65504 is a precondition, and elements below 2^-14
+ * keep fewer bits), and each weight times the row's V scale, p * s, is
+ * rounded to float16 before P.V (products below 2^-14 keep fewer bits, so
+ * rows with tiny V scales lose relative precision; FP8 rows whose scale
+ * times 2^8 exceeds 65504, i.e. max|v| beyond about 114,000, overflow).  The
+ * vector-ALU path (g < 4) computes in float32 throughout. */
  * ctx_b == 0 gives out = 0.  max_context_len is a host-side upper bound of
  * context_lens (1 .. max_blocks*P), used to plan the split.  workspace must
  * be a device buffer of at least kvp_decode_workspace_bytes (may be NULL when
@@ -450,7 +459,8 @@ kvp_status kvp_paged_attention_decode_scheduled(
  *   max_context_len  host bound on context_lens, as for decode.
  * A row whose position would be negative (q_len_b > n_b) gives 0.  Scores,
  * softmax and sums are float32; out is rounded to bfloat16.  No workspace.
- * Reads KVP_BF16 and KVP_INT8 pools; KVP_E_UNSUPPORTED for INT4 and FP8. */
+ * Reads every pool format (quantized pools as for decode, with the same
+ * float16 operands). */
 kvp_status kvp_paged_attention_prefill(
     const kvp_pool* pool, const void* q, const int32_t* q_start, const void* k_pool,
     const void* v_pool, const void* k_meta, const void* v_meta, const int32_t* block_tables,

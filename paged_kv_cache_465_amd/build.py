@@ -24,7 +24,8 @@ ARCH = "gfx950"
 
 # decode kernels: one translation unit per (KV format, plan), so they compile in parallel
 DEVICE_SOURCES = [f"decode_{fmt}_{plan}.hip" for fmt in ("int4", "bf16", "fp8", "int8")
-                  for plan in ("sched", "split")] + ["prefill.hip", "decode.hip", "append.hip", "probe.hip"]
+                  for plan in ("sched", "split")] + [f"prefill_{fmt}.hip" for fmt in ("int4", "bf16", "fp8", "int8")] \
+    + ["prefill.hip", "decode.hip", "append.hip", "probe.hip"]
 HOST_SOURCES = ["pool.cpp", "prefix_cache.cpp", "schedule.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]

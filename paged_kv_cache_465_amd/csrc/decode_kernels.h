@@ -282,25 +282,6 @@ struct PageRegs {
 constexpr int mfma_max_threads(int, int, int) { return 256; }
 constexpr int valu_max_threads(int, int, int) { return 256; }
 
-// Eight consecutive code channels of a lane (starting at dword w[0]) as the
-// float16 matrix-core operand: INT8 and FP8 take two dwords, INT4 one.
-template <int F>
-__device__ __forceinline__ f16x8_t codes8_to_f16x8(const uint32_t* w) {
-  if constexpr (F == kI4) {
-    return i4x8_to_f16x8(w[0]);
-  } else {
-    f16x2_t a0, a1, b0, b1;
-    if constexpr (F == kI8) {
-      i8x4_to_f16x4(w[0], a0, a1);
-      i8x4_to_f16x4(w[1], b0, b1);
-    } else {
-      fp8x4_to_f16x4(w[0], a0, a1);
-      fp8x4_to_f16x4(w[1], b0, b1);
-    }
-    return f16x8_t{a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
-  }
-}
-
 template <int F, int P, int D, int NT, int DEPTH, bool SCHED>
 __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const WorkRange& wr, float* smem) {
   using S = MfmaShape<F, P, D>;

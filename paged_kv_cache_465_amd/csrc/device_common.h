@@ -152,6 +152,39 @@ __device__ __forceinline__ void i4sel4_to_f16x4(uint32_t w, bool hi_nibble, f16x
   hi = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) + off;
 }
 
+// Eight consecutive code channels of a lane (starting at dword w[0]) as the
+// float16 matrix-core operand: INT8 and FP8 take two dwords, INT4 one.
+template <int F>
+__device__ __forceinline__ f16x8_t codes8_to_f16x8(const uint32_t* w) {
+  if constexpr (F == kI4) {
+    return i4x8_to_f16x8(w[0]);
+  } else {
+    f16x2_t a0, a1, b0, b1;
+    if constexpr (F == kI8) {
+      i8x4_to_f16x4(w[0], a0, a1);
+      i8x4_to_f16x4(w[1], b0, b1);
+    } else {
+      fp8x4_to_f16x4(w[0], a0, a1);
+      fp8x4_to_f16x4(w[1], b0, b1);
+    }
+    return f16x8_t{a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
+  }
+}
+
+// Four codes of one channel from one dword (a V^T operand): four INT8 or
+// FP8 bytes, or for INT4 four bytes of a channel pair with this lane's
+// channel in the high nibble when hi_nibble.
+template <int F>
+__device__ __forceinline__ void codes4_to_f16x4(uint32_t w, bool hi_nibble, f16x2_t& lo,
+                                                f16x2_t& hi) {
+  if constexpr (F == kI8)
+    i8x4_to_f16x4(w, lo, hi);
+  else if constexpr (F == kFP8)
+    fp8x4_to_f16x4(w, lo, hi);
+  else
+    i4sel4_to_f16x4(w, hi_nibble, lo, hi);
+}
+
 // float32 -> e4m3 code (OCP e4m3fn: bias 7, 3 mantissa bits, largest finite
 // 448, no infinities), round to nearest with ties to the even code,
 // magnitudes at or beyond 448 saturating to 448; the sign bit follows y.

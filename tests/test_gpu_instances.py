@@ -124,3 +124,49 @@ QGAIN = [_cfg(f, P, 128, g, 467000 + i, suffix="_qgain4", q_gain=4.0)
 @pytest.mark.parametrize("cfg", QGAIN, ids=lambda c: c.name)
 def test_quantized_instances_with_sharp_queries(kvp, cfg):
     _run_matrix_case(kvp, cfg)
+
+
+# ---- multi-query attention (chunked prefill, verification) -----------------------
+# "KV-Cache Optimization Techniques", section "Cache-Aware Scheduling": chunks of
+# q_len new tokens attend causally over the cache.  With g = 4 query heads per
+# KV head, chunks of 3, 6, 20 and 40 tokens give 12, 24, 80 and 160 rows per
+# (sequence, KV head): the page-split kernel with one and two head tiles (rows
+# fit one wavefront) and the row-tiled kernel with one and two tiles per
+# wavefront, for every format, page size and head dim.
+PREFILL_MODES = {3: "split_nt1", 6: "split_nt2", 20: "tiled_nt1", 40: "tiled_nt2"}
+
+
+def _prefill_cfg(fmt, P, D, q_len, seed):
+    ctx = (9 * P + 5, 50, 2 * P + 40, 13 * P - 1)
+    quant = fmt != "bf16"
+    return variant(TINY, name=f"{fmt}_p{P}_d{D}_{PREFILL_MODES[q_len]}", batch=len(ctx),
+                   ctx_fixed=ctx, num_q_heads=8, num_kv_heads=2, head_dim=D, page_size=P,
+                   kv_dtype=fmt, pool_pages=None, outlier_channels=3 if quant else 0,
+                   outlier_gain=8.0 if quant else 1.0, q_len=q_len, seed=seed)
+
+
+PREFILL_MATRIX = [_prefill_cfg(f, P, D, L, 469000 + i) for i, (f, P, D, L) in
+                  enumerate(itertools.product(FORMATS, PAGES, DIMS, sorted(PREFILL_MODES)))]
+
+
+@pytest.mark.parametrize("cfg", PREFILL_MATRIX, ids=lambda c: c.name)
+def test_every_prefill_instance(kvp, cfg):
+    case = make_case(cfg)
+    log(f"[prefill instance] {cfg.name} seed={cfg.seed} ctx={case.ctx.tolist()} "
+        f"q_len={cfg.q_len}")
+    k, v, km, vm = oracle_pools(case)
+    ref = oracle.paged_prefill(layout_of(case), case.q, case.q_start, k, v, km, vm,
+                               case.block_tables, case.ctx, case.scale)
+    gc = GpuCase(kvp, case)
+    gc.append_history()
+    gc.append_new()
+    torch.cuda.synchronize()
+    _pools_equal(gc.pools_host(), (k, v, km, vm), cfg.name)
+    out = torch.full_like(gc.q, int(np.uint16(0x7FC0).view(np.int16)))
+    kvp.kvp_paged_attention_prefill(gc.pool, gc.q, dev32(case.q_start), gc.k_pool, gc.v_pool,
+                                    gc.k_meta, gc.v_meta, gc.bt, gc.ctx, cfg.q_len,
+                                    int(case.ctx.max()), float(case.scale), out)
+    torch.cuda.synchronize()
+    m, r = assert_close(out.cpu().numpy().view(np.uint16), ref, cfg.name)
+    log(f"  max_abs={m:.2e} rel_l2={r:.2e}")
+    gc.close()

@@ -226,20 +226,62 @@ def test_append_special_rows_lowbit(kvp, kind):
     pool.close()
 
 
-@pytest.mark.parametrize("kind", ["int4", "fp8"])
-def test_prefill_rejects_lowbit_pools(kvp, kind):
-    """The multi-query kernel reads bfloat16 and INT8 pools only: an INT4 or
-    FP8 pool is refused before any launch."""
-    cfg = variant(TINY, name=f"tiny_chunk_{kind}", kv_dtype=kind, q_len=3)
-    case = make_case(cfg)
+LOWBIT_PREFILL = [
+    variant(TINY, name=f"tiny_chunk5_{f}", kv_dtype=f, q_len=5) for f in ("int4", "fp8")
+] + [
+    variant(base, name=f"{base.name}_chunk{L}", batch=3, ctx_lo=200, ctx_hi=900, q_len=L,
+            q_len_hi=L + 30)
+    for base in (INT4_LONG, FP8_LONG) for L in (4, 64)
+]
+
+
+@pytest.mark.parametrize("cfg", LOWBIT_PREFILL, ids=lambda c: c.name)
+def test_prefill_lowbit_matches_oracle(kvp, cfg):
+    """Chunked prefill over INT4 and FP8 pools: append bit-exact, outputs
+    against the oracle (ragged chunk lengths, both kernel modes)."""
+    case = _case(cfg)
+    k, v, km, vm = oracle_pools(case)
+    ref = oracle.paged_prefill(layout_of(case), case.q, case.q_start, k, v, km, vm,
+                               case.block_tables, case.ctx, case.scale)
+    log(f"[prefill lowbit] {cfg.name} q_len={np.diff(case.q_start).tolist()}")
     gc = GpuCase(kvp, case)
-    out = torch.empty_like(gc.q)
-    with pytest.raises(kvp.KvpError) as e:
-        kvp.kvp_paged_attention_prefill(gc.pool, gc.q, dev32(case.q_start), gc.k_pool, gc.v_pool,
-                                        gc.k_meta, gc.v_meta, gc.bt, gc.ctx, 3,
-                                        int(case.ctx.max()), float(case.scale), out)
-    assert e.value.status == kvp.KVP_E_UNSUPPORTED
+    gc.append_history()
+    gc.append_new()
+    torch.cuda.synchronize()
+    _pools_equal(gc.pools_host(), (k, v, km, vm))
+    from .test_gpu_parity import _run_prefill
+    out = _run_prefill(kvp, gc, case)
+    m, r = assert_close(out, ref, cfg.name)
+    log(f"  max_abs={m:.2e} rel_l2={r:.2e}")
     gc.close()
+
+
+@pytest.mark.parametrize("cfg", [c for c in LOWBIT if c.name.startswith(("tiny_int4", "tiny_fp8",
+                                                                         "int4_small",
+                                                                         "fp8_small"))],
+                         ids=lambda c: c.name)
+def test_prefill_one_token_equals_decode_lowbit(kvp, cfg):
+    """A one-token chunk per sequence is the decode step on INT4 and FP8 pools."""
+    case = _case(cfg)
+    k, v, km, vm, ref = _oracle(case)
+    log(f"[prefill=decode lowbit] {cfg.name}")
+    gc = GpuCase(kvp, case)
+    gc.upload(k, v, km, vm)
+    from .test_gpu_parity import _run_prefill
+    a = _run_prefill(kvp, gc, case)
+    d = gc.decode(num_splits=1)
+    assert_within_one_rounding(a, d, f"{cfg.name} prefill vs decode")
+    assert_close(a, ref, cfg.name)
+    gc.close()
+
+
+def test_full_chunked_prefill_lowbit(kvp):
+    """The chunked-prefill workload (8 sequences, 512-token chunks) over INT4
+    and FP8 pools, sampled against the oracle."""
+    from workloads import CHUNKED_PREFILL
+    for f in ("int4", "fp8"):
+        _sampled_check(kvp, variant(CHUNKED_PREFILL, name=f"chunked_prefill_{f}", kv_dtype=f,
+                                    outlier_channels=10, outlier_gain=8.0), seqs=(0, 5))
 
 
 def test_full_int4_long(kvp):
