@@ -293,7 +293,7 @@ kvp_status kvp_decode_workspace_bytes(const kvp_pool* pool, int32_t num_seqs,
  * rounded to float16 before P.V (products below 2^-14 keep fewer bits, so
  * rows with tiny V scales lose relative precision; FP8 rows whose scale
  * times 2^8 exceeds 65504, i.e. max|v| beyond about 114,000, overflow).  The
- * vector-ALU path (g < 4) computes in float32 throughout. */
+ * vector-ALU path (g < 4) computes in float32 throughout.
  * ctx_b == 0 gives out = 0.  max_context_len is a host-side upper bound of
  * context_lens (1 .. max_blocks*P), used to plan the split.  workspace must
  * be a device buffer of at least kvp_decode_workspace_bytes (may be NULL when

@@ -515,6 +515,364 @@ prefill_mfma_kernel(PrefillArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row-tiled mode, K/V shared through LDS.
+//
+// A workgroup of four wavefronts owns 128 consecutive rows of one (sequence,
+// KV head); each wavefront owns 32.  The key axis is walked in blocks of 64
+// keys (four 16-token pages or two 32-token pages): all 256 threads load a
+// block's K rows and V^T rows once into LDS (double-buffered: the next
+// block's loads are in flight while the current one is computed) and every
+// wavefront reads its matrix-core operands from there, so each page is read
+// once per workgroup instead of once per wavefront.  This mode serves
+// bfloat16 pools.  (Quantized pools keep the register-streaming tiled kernel
+// above: rounding their dequantized K rows to a 16-bit operand moved scores
+// by up to 1e-3 in log units at the workloads' x8 outlier channels, enough
+// to push outputs past 1e-2; that kernel applies the per-token scales in
+// float32 to exact codes.)
+//
+// Tiles are 32x32x16 matrix-core steps: S^T (64 keys x 32 rows) = K Q^T in two
+// 32-key tiles, then O^T (D x 32 rows) += V^T P^T in four 16-key steps.  A
+// lane owns one row (column n = lane % 32 of every accumulator), so the
+// online softmax is lane-local but for one exchange with lane n + 32, which
+// holds the row's other keys.  The score tile's row r of tile t is fed by key
+// 32t + 16(j/2) + 8h + 4(j%2) + i (r = 8j + 4h + i), so that a lane's
+// accumulator holds, for P.V step s, the 8 consecutive keys 16s + 8h .. + 7
+// that its P^T operand needs: the V^T operand is then one 16-byte LDS read.
+// Rows of LDS are padded by 16 bytes so the wavefront's reads of 32 different
+// rows at one column spread over the banks.
+template <int D>
+struct FaTile {
+  static constexpr int KEYS = 64;                 // keys per block
+  static constexpr int W = D / 8;                 // 16-byte chunks of one K row (8 values)
+  static constexpr int KROW = (W + 1) * 16;       // LDS bytes per K row (padded)
+  static constexpr int VROW = (KEYS / 8 + 1) * 16;  // LDS bytes per V^T row (padded)
+  static constexpr int KBLK = KEYS * KROW;
+  static constexpr int STAGE = KBLK + D * VROW;   // one block of K and V^T
+  static constexpr int KCH = KEYS * W / 256;      // K chunks each thread stages per block
+  static constexpr int VCH = D * (KEYS / 8) / 256;  // V^T chunks each thread stages
+  static constexpr int KS = D / 16;               // 32x32x16 steps over the head dim
+  static constexpr int DT = D / 32;               // 32-channel output tiles
+};
+
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16(const bf16x8_t& a, const bf16x8_t& b,
+                                                  const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// max(x, x of lane n ^ 32): lanes n and n + 32 hold two halves of one row.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int P, int D>
+__global__ __launch_bounds__(256, 2) void prefill_fa_kernel(PrefillArgs a) {
+  using TL = FaTile<D>;
+  constexpr int KEYS = TL::KEYS, W = TL::W, KS = TL::KS, DT = TL::DT;
+  constexpr int RB = D * 2;                       // bytes of one stored token row
+  constexpr int PPB = KEYS / P;                   // pages per block
+  using Op = bf16x8_t;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * TL::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hh = lane >> 5;
+  const int H = a.num_kv_heads, g = a.group;
+
+  // Grid as the tiled kernel: all tiles of an item on one XCD.
+  const int per_group = 8 * a.tiles;
+  const int grp = blockIdx.x / per_group;
+  const int within = blockIdx.x - grp * per_group;
+  const int tile = within >> 3;
+  const int item = grp * 8 + (within & 7);
+  if (item >= a.num_seqs * H) return;
+  const int b = item / H, h = item - b * H;
+  const int q0 = a.q_start[b];
+  const int qlen = a.q_start[b + 1] - q0;
+  const int ctx = min(max(a.ctx_lens[b], 0), a.ctx_cap);
+  const int rows = qlen * g;
+  const int wg_row0 = tile * 128;
+  if (qlen <= 0 || wg_row0 >= rows) return;       // the whole workgroup: no barrier reached
+  const int first_pos = ctx - qlen;
+  const int wg_row_last = min(wg_row0 + 127, rows - 1);
+  const int wg_pos_last = min(first_pos + wg_row_last / g, ctx - 1);
+  const int nblk = wg_pos_last >= 0 ? wg_pos_last / KEYS + 1 : 0;
+
+  // this wavefront's rows
+  const int row0 = wg_row0 + wave * 32;
+  const bool wave_live = row0 < rows;
+  const int row_last = wave_live ? min(row0 + 31, rows - 1) : wg_row_last;
+  const int wpos_min = first_pos + (wave_live ? row0 : wg_row_last) / g;
+  const int wpos_max = first_pos + row_last / g;
+  const int m_row = row0 + n;
+  const int mm = m_row < rows ? m_row : row_last;      // rows past the end mirror the last one
+  const int qi = mm / g, qj = mm - (mm / g) * g;
+  const int lim = first_pos + qi;                       // keys <= lim take part (< ctx)
+
+  // Q^T as the B operand of S^T = K Q^T: lane (n, hh) holds channels 16ks + 8hh .. + 7.
+  // A negative scale is applied as |scale| on -q (exact), so that the running
+  // maximum of the raw scores is the maximum of the scaled ones.
+  const float cs = fabsf(a.scale_log2);
+  const uint32_t qflip = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
+  Op qop[KS];
+  {
+    const uint16_t* qrow = a.q + ((int64_t(q0) + qi) * a.num_q_heads + int64_t(h) * g + qj) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 raw = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hh);
+      raw.x ^= qflip;
+      raw.y ^= qflip;
+      raw.z ^= qflip;
+      raw.w ^= qflip;
+      qop[ks] = __builtin_bit_cast(bf16x8_t, raw);
+    }
+  }
+
+  // LDS read bases: K row of score-tile row r = n for tile t; V^T row d = n of tile dt.
+  int kread[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int j = n >> 3, ih = (n >> 2) & 1, i = n & 3;
+    const int key = 32 * t + 16 * (j >> 1) + 8 * ih + 4 * (j & 1) + i;
+    kread[t] = key * TL::KROW + hh * 16;
+  }
+  const int vread = TL::KBLK + n * TL::VROW + hh * 16;
+  // key offsets (within a block) of this lane's score values, tile t, value r
+  auto key_of = [&](int t, int r) {
+    return 32 * t + 16 * (r >> 3) + 8 * hh + 4 * ((r >> 2) & 1) + (r & 3);
+  };
+
+  // ---- staging: this thread's K chunks (key, column chunk) and V^T chunks
+  // (channel, 8-key group); the column / key group is the same for all of them
+  const int kcc = tid % W;
+  const int vkc = tid & 7;
+  const char* kbase = static_cast<const char*>(a.k_pool);
+  const char* vbase = static_cast<const char*>(a.v_pool);
+  const int32_t* btrow = a.bt + int64_t(b) * a.max_blocks;
+  const size_t tile_bytes = size_t(P) * RB;
+  const int npages_seq = (ctx + P - 1) / P;
+  uint4 kraw[TL::KCH], vraw[TL::VCH];
+  int vphys;
+  // Page ids of a block's PPB pages, loaded one block ahead of its staging
+  // (raw table words, uniform in-range index) so that no load waits on a
+  // table entry; validated (-1: absent, past the sequence or past the last
+  // block) when the block is staged.
+  struct PageTab { int raw[PPB]; int blk; };
+  auto load_tab = [&](int blk) {
+    PageTab t;
+    t.blk = blk;
+#pragma unroll
+    for (int pi = 0; pi < PPB; ++pi) {
+      const int lb = __builtin_amdgcn_readfirstlane(min(blk * PPB + pi, npages_seq - 1));
+      t.raw[pi] = btrow[max(lb, 0)];
+    }
+    return t;
+  };
+  struct PageIds { int id[PPB]; bool clean; };  // clean: every page present, every key < ctx
+  auto validate = [&](const PageTab& t) {
+    PageIds v;
+    v.clean = t.blk < nblk && (t.blk + 1) * KEYS <= ctx;
+#pragma unroll
+    for (int pi = 0; pi < PPB; ++pi) {
+      const int lb = t.blk * PPB + pi;
+      const bool ok = t.blk < nblk && lb < npages_seq && unsigned(t.raw[pi]) < unsigned(a.num_pages);
+      v.id[pi] = __builtin_amdgcn_readfirstlane(ok ? t.raw[pi] : -1);
+      v.clean = v.clean && ok;
+    }
+    return v;
+  };
+  // block-local page of this thread's K chunk c (the same for every lane when
+  // a chunk round covers at most one page)
+  auto kpage = [&](int c) {
+    constexpr int KPR = 256 / W;   // keys per chunk round
+    return KPR <= P ? (c * KPR) / P : (c * KPR + tid / W) / P;
+  };
+  auto sel = [](const PageIds& v, int pi) {
+    int r = v.id[0];
+#pragma unroll
+    for (int q = 1; q < PPB; ++q) r = pi == q ? v.id[q] : r;
+    return r;
+  };
+  auto stage_load = [&](const PageIds& ids) {
+#pragma unroll
+    for (int c = 0; c < TL::KCH; ++c) {
+      const int key = (c * 256 + tid) / W;
+      const int phys = sel(ids, kpage(c));
+      const int64_t t = int64_t(phys < 0 ? 0 : phys) * H + h;
+      kraw[c] = *reinterpret_cast<const uint4*>(kbase + t * tile_bytes + (key % P) * RB + kcc * 16);
+    }
+    const int phys = sel(ids, (8 * vkc) / P);
+    vphys = phys;
+    const int64_t t = int64_t(phys < 0 ? 0 : phys) * H + h;
+    const int tok0 = (8 * vkc) % P;
+#pragma unroll
+    for (int c = 0; c < TL::VCH; ++c) {
+      const int d = (c * 256 + tid) >> 3;
+      vraw[c] = *reinterpret_cast<const uint4*>(vbase + t * tile_bytes + (d * P + tok0) * 2);
+    }
+  };
+  auto stage_store = [&](int blk, const PageIds& ids, unsigned char* st) {
+    if (ids.clean) {   // wave-uniform: no key of the block needs zeroing
+#pragma unroll
+      for (int c = 0; c < TL::KCH; ++c)
+        *reinterpret_cast<uint4*>(st + ((c * 256 + tid) / W) * TL::KROW + kcc * 16) = kraw[c];
+#pragma unroll
+      for (int c = 0; c < TL::VCH; ++c)
+        *reinterpret_cast<uint4*>(st + TL::KBLK + ((c * 256 + tid) >> 3) * TL::VROW + vkc * 16) =
+            vraw[c];
+      return;
+    }
+    const int key0 = blk * KEYS;
+#pragma unroll
+    for (int c = 0; c < TL::KCH; ++c) {
+      const int key = (c * 256 + tid) / W;
+      const bool ok = sel(ids, kpage(c)) >= 0 && key0 + key < ctx;
+      *reinterpret_cast<uint4*>(st + key * TL::KROW + kcc * 16) =
+          ok ? kraw[c] : make_uint4(0, 0, 0, 0);
+    }
+    // V^T: keys 8 vkc .. + 7 of channel d; keys past the sequence (or on an
+    // absent page) are zero so that their zero weights never meet NaN
+    const int kv0 = key0 + 8 * vkc;
+#pragma unroll
+    for (int c = 0; c < TL::VCH; ++c) {
+      const int d = (c * 256 + tid) >> 3;
+      uint32_t w[4];
+      __builtin_memcpy(w, &vraw[c], 16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool keep = vphys >= 0 && kv0 + e < ctx;
+        w[e >> 1] &= keep ? 0xffffffffu : ((e & 1) ? 0x0000ffffu : 0xffff0000u);
+      }
+      uint4 v;
+      __builtin_memcpy(&v, w, 16);
+      *reinterpret_cast<uint4*>(st + TL::KBLK + d * TL::VROW + vkc * 16) = v;
+    }
+  };
+
+  // ---- online softmax state (this lane's row, its half of each block's keys)
+  float m = -INFINITY, lsum = 0.0f;
+  f32x16_t acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16_t{};
+
+  auto compute = [&](int blk, const PageIds& ids, const unsigned char* st) {
+    const int key0 = blk * KEYS;
+    if (!wave_live || key0 > wpos_max) return;   // wave-uniform: nothing of this block is seen
+    // pages of the block present? (wave-uniform)
+    uint32_t pmask = 0;
+#pragma unroll
+    for (int pi = 0; pi < PPB; ++pi) pmask |= (ids.id[pi] >= 0 ? 1u : 0u) << pi;
+    const bool unmasked = pmask == (1u << PPB) - 1 && key0 + KEYS - 1 <= wpos_min;
+    f32x16_t sc[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const Op kop = *reinterpret_cast<const Op*>(st + kread[t] + 32 * ks);
+        sc[t] = mfma_32x32x16(kop, qop[ks], sc[t]);
+      }
+    }
+    if (!unmasked) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = key_of(t, r);
+          const bool ok = key0 + kk <= lim && ((pmask >> (kk / P)) & 1u);
+          if (!ok) sc[t][r] = -INFINITY;
+        }
+    }
+    float mx = sc[0][0];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
+    mx = pair_max(mx) * cs;
+    // The softmax reference m only moves when a score exceeds it by more than
+    // 2^8 (log2 units): weights stay <= 256 (exact enough in bfloat16, no
+    // float32 overflow in the sums) and the accumulators are rescaled rarely.
+    const float mnew = mx > m + 8.0f ? mx : m;
+    // a row that has seen no key yet keeps m = -inf: use 0 as the reference
+    const float mref = mnew == -INFINITY ? 0.0f : mnew;
+    const float al = fast_exp2(m - mref);
+    m = mnew;
+    float ps = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(sc[t][r] * cs - mref);
+        sc[t][r] = p;
+        ps += p;
+      }
+    lsum = lsum * al + ps;
+    if (wave_any(al != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= al;
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      Op pop;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pop[e] = (__bf16)sc[s >> 1][8 * (s & 1) + e];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const Op vop = *reinterpret_cast<const Op*>(st + vread + dt * 32 * TL::VROW + 32 * s);
+        acc[dt] = mfma_32x32x16(vop, pop, acc[dt]);
+      }
+    }
+  };
+
+  if (nblk > 0) {
+    PageIds ids_cur = validate(load_tab(0));
+    PageTab tab_next = load_tab(1);
+    stage_load(ids_cur);
+    stage_store(0, ids_cur, lds);
+    __syncthreads();
+    for (int blk = 0; blk < nblk; ++blk) {
+      unsigned char* cur = lds + (blk & 1) * TL::STAGE;
+      unsigned char* nxt = lds + ((blk + 1) & 1) * TL::STAGE;
+      const bool more = blk + 1 < nblk;
+      const PageIds ids_next = validate(tab_next);
+      if (more) stage_load(ids_next);
+      compute(blk, ids_cur, cur);
+      // (issued after the compute: its wait would otherwise share the LDS
+      // reads' counter at the first matrix-core step)
+      tab_next = load_tab(blk + 2);
+      if (more) stage_store(blk + 1, ids_next, nxt);
+      __syncthreads();
+      ids_cur = ids_next;
+    }
+  }
+
+  // ---- finalize: out = acc / l, bfloat16
+  if (!wave_live || m_row >= rows) return;
+  const float lt = pair_sum(lsum);
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  uint16_t* orow = a.out + ((int64_t(q0) + qi) * a.num_q_heads + int64_t(h) * g + qj) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x16_t& v = acc[dt];
+      const uint32_t lo = uint32_t(f32_to_bf16_rne(v[4 * j + 0] * inv)) |
+                          (uint32_t(f32_to_bf16_rne(v[4 * j + 1] * inv)) << 16);
+      const uint32_t hi = uint32_t(f32_to_bf16_rne(v[4 * j + 2] * inv)) |
+                          (uint32_t(f32_to_bf16_rne(v[4 * j + 3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * j + 4 * hh) = make_uint2(lo, hi);
+    }
+}
+
 constexpr int kPrefillDepth = 2;  // split mode
 
 template <int F, int P, int D>
@@ -527,6 +885,8 @@ hipError_t launch_prefill_pd(const PrefillArgs& a, int nt, bool split, dim3 grid
     else
       hipLaunchKernelGGL((prefill_mfma_kernel<F, P, D, 2, kPrefillDepth, true>), grid,
                          dim3(256), 0, s, a);
+  } else if constexpr (F == kBF16) {
+    hipLaunchKernelGGL((prefill_fa_kernel<P, D>), grid, dim3(256), 0, s, a);
   } else {
     if (nt == 1)
       hipLaunchKernelGGL((prefill_mfma_kernel<F, P, D, 1, prefill_tiled_depth(P, D), false>), grid,
