@@ -46,7 +46,7 @@ extern "C" kvp_status kvp_paged_attention_prefill(
   // quantized pools: 32 rows per wavefront when the longest chunk has at least
   // 128 rows, else 16)
   const int nt = split ? (max_rows > 16 ? 2 : 1) : (max_rows >= 32 * 4 || !quant ? 2 : 1);
-  const int64_t rows_wg = split ? 16 * nt : 4 * 16 * nt;
+  const int64_t rows_wg = split ? 16 * nt : (quant ? 4 * 16 * nt : 32 * kFaWaves * kFaRowTiles);
   const int64_t tiles = (max_rows + rows_wg - 1) / rows_wg;
   const int64_t items = int64_t(num_seqs) * d.num_kv_heads;
   const int64_t wgs = (items + 7) / 8 * 8 * tiles;

@@ -518,8 +518,8 @@ prefill_mfma_kernel(PrefillArgs a) {
 // ---------------------------------------------------------------------------
 // Row-tiled mode, K/V shared through LDS.
 //
-// A workgroup of four wavefronts owns 128 consecutive rows of one (sequence,
-// KV head); each wavefront owns 32.  The key axis is walked in blocks of 64
+// A workgroup of WAVES wavefronts owns 32 RT WAVES consecutive rows of one
+// (sequence, KV head); each wavefront owns RT tiles of 32 rows.  The key axis is walked in blocks of 64
 // keys (four 16-token pages or two 32-token pages): all 256 threads load a
 // block's K rows and V^T rows once into LDS (double-buffered: the next
 // block's loads are in flight while the current one is computed) and every
@@ -541,16 +541,17 @@ prefill_mfma_kernel(PrefillArgs a) {
 // that its P^T operand needs: the V^T operand is then one 16-byte LDS read.
 // Rows of LDS are padded by 16 bytes so the wavefront's reads of 32 different
 // rows at one column spread over the banks.
-template <int D>
+template <int D, int WAVES>
 struct FaTile {
+  static constexpr int NT = 64 * WAVES;           // threads of a workgroup
   static constexpr int KEYS = 64;                 // keys per block
   static constexpr int W = D / 8;                 // 16-byte chunks of one K row (8 values)
   static constexpr int KROW = (W + 1) * 16;       // LDS bytes per K row (padded)
   static constexpr int VROW = (KEYS / 8 + 1) * 16;  // LDS bytes per V^T row (padded)
   static constexpr int KBLK = KEYS * KROW;
   static constexpr int STAGE = KBLK + D * VROW;   // one block of K and V^T
-  static constexpr int KCH = KEYS * W / 256;      // K chunks each thread stages per block
-  static constexpr int VCH = D * (KEYS / 8) / 256;  // V^T chunks each thread stages
+  static constexpr int KCH = KEYS * W / NT;       // K chunks each thread stages per block
+  static constexpr int VCH = D * (KEYS / 8) / NT;  // V^T chunks each thread stages
   static constexpr int KS = D / 16;               // 32x32x16 steps over the head dim
   static constexpr int DT = D / 32;               // 32-channel output tiles
 };
@@ -574,9 +575,11 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int P, int D>
-__global__ __launch_bounds__(256, 2) void prefill_fa_kernel(PrefillArgs a) {
-  using TL = FaTile<D>;
+template <int P, int D, int WAVES, int RT>
+__global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && RT == 1) ? 2 : 1) void prefill_fa_kernel(
+    PrefillArgs a) {
+  using TL = FaTile<D, WAVES>;
+  constexpr int NT = TL::NT;
   constexpr int KEYS = TL::KEYS, W = TL::W, KS = TL::KS, DT = TL::DT;
   constexpr int RB = D * 2;                       // bytes of one stored token row
   constexpr int PPB = KEYS / P;                   // pages per block
@@ -601,32 +604,40 @@ __global__ __launch_bounds__(256, 2) void prefill_fa_kernel(PrefillArgs a) {
   const int qlen = a.q_start[b + 1] - q0;
   const int ctx = min(max(a.ctx_lens[b], 0), a.ctx_cap);
   const int rows = qlen * g;
-  const int wg_row0 = tile * 128;
+  constexpr int WROWS = 32 * RT;                  // rows of one wavefront
+  const int wg_row0 = tile * WROWS * WAVES;
   if (qlen <= 0 || wg_row0 >= rows) return;       // the whole workgroup: no barrier reached
   const int first_pos = ctx - qlen;
-  const int wg_row_last = min(wg_row0 + 127, rows - 1);
+  const int wg_row_last = min(wg_row0 + WROWS * WAVES - 1, rows - 1);
   const int wg_pos_last = min(first_pos + wg_row_last / g, ctx - 1);
   const int nblk = wg_pos_last >= 0 ? wg_pos_last / KEYS + 1 : 0;
 
-  // this wavefront's rows
-  const int row0 = wg_row0 + wave * 32;
+  // this wavefront's rows: tile rt holds rows row0 + 32 rt .. + 31
+  const int row0 = wg_row0 + wave * WROWS;
   const bool wave_live = row0 < rows;
-  const int row_last = wave_live ? min(row0 + 31, rows - 1) : wg_row_last;
+  const int row_last = wave_live ? min(row0 + WROWS - 1, rows - 1) : wg_row_last;
   const int wpos_min = first_pos + (wave_live ? row0 : wg_row_last) / g;
   const int wpos_max = first_pos + row_last / g;
-  const int m_row = row0 + n;
-  const int mm = m_row < rows ? m_row : row_last;      // rows past the end mirror the last one
-  const int qi = mm / g, qj = mm - (mm / g) * g;
-  const int lim = first_pos + qi;                       // keys <= lim take part (< ctx)
+  int m_row[RT], qi[RT], qj[RT], lim[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m_row[rt] = row0 + 32 * rt + n;
+    const int mm = m_row[rt] < rows ? m_row[rt] : row_last;  // rows past the end mirror the last
+    qi[rt] = mm / g;
+    qj[rt] = mm - qi[rt] * g;
+    lim[rt] = first_pos + qi[rt];                            // keys <= lim take part (< ctx)
+  }
 
   // Q^T as the B operand of S^T = K Q^T: lane (n, hh) holds channels 16ks + 8hh .. + 7.
   // A negative scale is applied as |scale| on -q (exact), so that the running
   // maximum of the raw scores is the maximum of the scaled ones.
   const float cs = fabsf(a.scale_log2);
   const uint32_t qflip = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
-  Op qop[KS];
-  {
-    const uint16_t* qrow = a.q + ((int64_t(q0) + qi) * a.num_q_heads + int64_t(h) * g + qj) * D;
+  Op qop[RT][KS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const uint16_t* qrow =
+        a.q + ((int64_t(q0) + qi[rt]) * a.num_q_heads + int64_t(h) * g + qj[rt]) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 raw = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hh);
@@ -634,7 +645,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fa_kernel(PrefillArgs a) {
       raw.y ^= qflip;
       raw.z ^= qflip;
       raw.w ^= qflip;
-      qop[ks] = __builtin_bit_cast(bf16x8_t, raw);
+      qop[rt][ks] = __builtin_bit_cast(bf16x8_t, raw);
     }
   }
 
@@ -678,7 +689,10 @@ __global__ __launch_bounds__(256, 2) void prefill_fa_kernel(PrefillArgs a) {
     }
     return t;
   };
-  struct PageIds { int id[PPB]; bool clean; };  // clean: every page present, every key < ctx
+  // (a vector, not an array: a lane-dependent pick among the ids is then an
+  // in-register selection, never a stack slot)
+  typedef int PageVec __attribute__((ext_vector_type(PPB)));
+  struct PageIds { PageVec id; bool clean; };  // clean: every page present, every key < ctx
   auto validate = [&](const PageTab& t) {
     PageIds v;
     v.clean = t.blk < nblk && (t.blk + 1) * KEYS <= ctx;
@@ -694,19 +708,16 @@ __global__ __launch_bounds__(256, 2) void prefill_fa_kernel(PrefillArgs a) {
   // block-local page of this thread's K chunk c (the same for every lane when
   // a chunk round covers at most one page)
   auto kpage = [&](int c) {
-    constexpr int KPR = 256 / W;   // keys per chunk round
+    constexpr int KPR = NT / W;    // keys per chunk round
     return KPR <= P ? (c * KPR) / P : (c * KPR + tid / W) / P;
   };
   auto sel = [](const PageIds& v, int pi) {
-    int r = v.id[0];
-#pragma unroll
-    for (int q = 1; q < PPB; ++q) r = pi == q ? v.id[q] : r;
-    return r;
+    return v.id[pi];
   };
   auto stage_load = [&](const PageIds& ids) {
 #pragma unroll
     for (int c = 0; c < TL::KCH; ++c) {
-      const int key = (c * 256 + tid) / W;
+      const int key = (c * NT + tid) / W;
       const int phys = sel(ids, kpage(c));
       const int64_t t = int64_t(phys < 0 ? 0 : phys) * H + h;
       kraw[c] = *reinterpret_cast<const uint4*>(kbase + t * tile_bytes + (key % P) * RB + kcc * 16);
@@ -717,7 +728,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fa_kernel(PrefillArgs a) {
     const int tok0 = (8 * vkc) % P;
 #pragma unroll
     for (int c = 0; c < TL::VCH; ++c) {
-      const int d = (c * 256 + tid) >> 3;
+      const int d = (c * NT + tid) >> 3;
       vraw[c] = *reinterpret_cast<const uint4*>(vbase + t * tile_bytes + (d * P + tok0) * 2);
     }
   };
@@ -725,17 +736,17 @@ __global__ __launch_bounds__(256, 2) void prefill_fa_kernel(PrefillArgs a) {
     if (ids.clean) {   // wave-uniform: no key of the block needs zeroing
 #pragma unroll
       for (int c = 0; c < TL::KCH; ++c)
-        *reinterpret_cast<uint4*>(st + ((c * 256 + tid) / W) * TL::KROW + kcc * 16) = kraw[c];
+        *reinterpret_cast<uint4*>(st + ((c * NT + tid) / W) * TL::KROW + kcc * 16) = kraw[c];
 #pragma unroll
       for (int c = 0; c < TL::VCH; ++c)
-        *reinterpret_cast<uint4*>(st + TL::KBLK + ((c * 256 + tid) >> 3) * TL::VROW + vkc * 16) =
+        *reinterpret_cast<uint4*>(st + TL::KBLK + ((c * NT + tid) >> 3) * TL::VROW + vkc * 16) =
             vraw[c];
       return;
     }
     const int key0 = blk * KEYS;
 #pragma unroll
     for (int c = 0; c < TL::KCH; ++c) {
-      const int key = (c * 256 + tid) / W;
+      const int key = (c * NT + tid) / W;
       const bool ok = sel(ids, kpage(c)) >= 0 && key0 + key < ctx;
       *reinterpret_cast<uint4*>(st + key * TL::KROW + kcc * 16) =
           ok ? kraw[c] : make_uint4(0, 0, 0, 0);
@@ -745,7 +756,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fa_kernel(PrefillArgs a) {
     const int kv0 = key0 + 8 * vkc;
 #pragma unroll
     for (int c = 0; c < TL::VCH; ++c) {
-      const int d = (c * 256 + tid) >> 3;
+      const int d = (c * NT + tid) >> 3;
       uint32_t w[4];
       __builtin_memcpy(w, &vraw[c], 16);
 #pragma unroll
@@ -759,11 +770,16 @@ __global__ __launch_bounds__(256, 2) void prefill_fa_kernel(PrefillArgs a) {
     }
   };
 
-  // ---- online softmax state (this lane's row, its half of each block's keys)
-  float m = -INFINITY, lsum = 0.0f;
-  f32x16_t acc[DT];
+  // ---- online softmax state (this lane's rows, its half of each block's keys)
+  float m[RT], lsum[RT];
+  f32x16_t acc[RT][DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16_t{};
+  for (int rt = 0; rt < RT; ++rt) {
+    m[rt] = -INFINITY;
+    lsum[rt] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[rt][dt] = f32x16_t{};
+  }
 
   auto compute = [&](int blk, const PageIds& ids, const unsigned char* st) {
     const int key0 = blk * KEYS;
@@ -773,62 +789,77 @@ __global__ __launch_bounds__(256, 2) void prefill_fa_kernel(PrefillArgs a) {
 #pragma unroll
     for (int pi = 0; pi < PPB; ++pi) pmask |= (ids.id[pi] >= 0 ? 1u : 0u) << pi;
     const bool unmasked = pmask == (1u << PPB) - 1 && key0 + KEYS - 1 <= wpos_min;
-    f32x16_t sc[2] = {f32x16_t{}, f32x16_t{}};
+    // All score tiles' matrix-core steps are issued first (each K operand read
+    // from LDS feeds the RT row tiles); the softmax of one tile then runs on
+    // the vector ALU while later tiles' steps execute.  Each 32-key tile is
+    // one step of the online softmax; its P.V steps read each V^T operand
+    // once for the RT row tiles.
+    f32x16_t sc[RT][2];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int rt = 0; rt < RT; ++rt) sc[rt][t] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
         const Op kop = *reinterpret_cast<const Op*>(st + kread[t] + 32 * ks);
-        sc[t] = mfma_32x32x16(kop, qop[ks], sc[t]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) sc[rt][t] = mfma_32x32x16(kop, qop[rt][ks], sc[rt][t]);
       }
     }
-    if (!unmasked) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      Op pop[RT][2];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x16_t& x = sc[rt][t];
+        if (!unmasked) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = key_of(t, r);
+            const bool ok = key0 + kk <= lim[rt] && ((pmask >> (kk / P)) & 1u);
+            x[r] = ok ? x[r] : -INFINITY;
+          }
+        }
+        float mx = x[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+        mx = pair_max(mx) * cs;
+        // The softmax reference m only moves when a score exceeds it by more
+        // than 2^8 (log2 units): weights stay <= 256 (exact enough in
+        // bfloat16, no float32 overflow in the sums) and the accumulators are
+        // rescaled rarely.
+        const float mnew = mx > m[rt] + 8.0f ? mx : m[rt];
+        // a row that has seen no key yet keeps m = -inf: use 0 as the reference
+        const float mref = mnew == -INFINITY ? 0.0f : mnew;
+        const float al = fast_exp2(m[rt] - mref);
+        m[rt] = mnew;
+        float ps = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kk = key_of(t, r);
-          const bool ok = key0 + kk <= lim && ((pmask >> (kk / P)) & 1u);
-          if (!ok) sc[t][r] = -INFINITY;
+          const float p = fast_exp2(x[r] * cs - mref);
+          x[r] = p;
+          ps += p;
         }
-    }
-    float mx = sc[0][0];
+        lsum[rt] = lsum[rt] * al + ps;
+        if (wave_any(al != 1.0f)) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+          for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= al;
+        }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
-    mx = pair_max(mx) * cs;
-    // The softmax reference m only moves when a score exceeds it by more than
-    // 2^8 (log2 units): weights stay <= 256 (exact enough in bfloat16, no
-    // float32 overflow in the sums) and the accumulators are rescaled rarely.
-    const float mnew = mx > m + 8.0f ? mx : m;
-    // a row that has seen no key yet keeps m = -inf: use 0 as the reference
-    const float mref = mnew == -INFINITY ? 0.0f : mnew;
-    const float al = fast_exp2(m - mref);
-    m = mnew;
-    float ps = 0.0f;
+        for (int half = 0; half < 2; ++half)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(sc[t][r] * cs - mref);
-        sc[t][r] = p;
-        ps += p;
+          for (int e = 0; e < 8; ++e) pop[rt][half][e] = (__bf16)x[8 * half + e];
       }
-    lsum = lsum * al + ps;
-    if (wave_any(al != 1.0f)) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] *= al;
-    }
+      for (int half = 0; half < 2; ++half) {
+        const int step = 2 * t + half;   // keys 16 step .. + 15
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      Op pop;
+        for (int dt = 0; dt < DT; ++dt) {
+          const Op vop =
+              *reinterpret_cast<const Op*>(st + vread + dt * 32 * TL::VROW + 32 * step);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pop[e] = (__bf16)sc[s >> 1][8 * (s & 1) + e];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const Op vop = *reinterpret_cast<const Op*>(st + vread + dt * 32 * TL::VROW + 32 * s);
-        acc[dt] = mfma_32x32x16(vop, pop, acc[dt]);
+          for (int rt = 0; rt < RT; ++rt) acc[rt][dt] = mfma_32x32x16(vop, pop[rt][half], acc[rt][dt]);
+        }
       }
     }
   };
@@ -856,24 +887,37 @@ __global__ __launch_bounds__(256, 2) void prefill_fa_kernel(PrefillArgs a) {
   }
 
   // ---- finalize: out = acc / l, bfloat16
-  if (!wave_live || m_row >= rows) return;
-  const float lt = pair_sum(lsum);
-  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  uint16_t* orow = a.out + ((int64_t(q0) + qi) * a.num_q_heads + int64_t(h) * g + qj) * D;
+  if (!wave_live) return;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int rt = 0; rt < RT; ++rt) {
+    const float lt = pair_sum(lsum[rt]);
+    if (m_row[rt] >= rows) continue;
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    uint16_t* orow =
+        a.out + ((int64_t(q0) + qi[rt]) * a.num_q_heads + int64_t(h) * g + qj[rt]) * D;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x16_t& v = acc[dt];
-      const uint32_t lo = uint32_t(f32_to_bf16_rne(v[4 * j + 0] * inv)) |
-                          (uint32_t(f32_to_bf16_rne(v[4 * j + 1] * inv)) << 16);
-      const uint32_t hi = uint32_t(f32_to_bf16_rne(v[4 * j + 2] * inv)) |
-                          (uint32_t(f32_to_bf16_rne(v[4 * j + 3] * inv)) << 16);
-      *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * j + 4 * hh) = make_uint2(lo, hi);
-    }
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x16_t& v = acc[rt][dt];
+        const uint32_t lo = uint32_t(f32_to_bf16_rne(v[4 * j + 0] * inv)) |
+                            (uint32_t(f32_to_bf16_rne(v[4 * j + 1] * inv)) << 16);
+        const uint32_t hi = uint32_t(f32_to_bf16_rne(v[4 * j + 2] * inv)) |
+                            (uint32_t(f32_to_bf16_rne(v[4 * j + 3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * j + 4 * hh) = make_uint2(lo, hi);
+      }
+  }
 }
 
 constexpr int kPrefillDepth = 2;  // split mode
+// wavefronts per workgroup of the LDS-staged kernel (32 rows each): four,
+// two workgroups per compute unit (eight, one per compute unit, measured
+// 25% slower on 512-token chunks)
+constexpr int kFaWaves = 4;
+// 32-row tiles per wavefront: one.  (Two, with one wavefront per SIMD for
+// the registers, measured 38% slower on 512-token chunks: a lone wavefront
+// does not overlap its softmax with its matrix-core steps.)
+constexpr int kFaRowTiles = 1;
 
 template <int F, int P, int D>
 hipError_t launch_prefill_pd(const PrefillArgs& a, int nt, bool split, dim3 grid, hipStream_t s) {
@@ -886,7 +930,8 @@ hipError_t launch_prefill_pd(const PrefillArgs& a, int nt, bool split, dim3 grid
       hipLaunchKernelGGL((prefill_mfma_kernel<F, P, D, 2, kPrefillDepth, true>), grid,
                          dim3(256), 0, s, a);
   } else if constexpr (F == kBF16) {
-    hipLaunchKernelGGL((prefill_fa_kernel<P, D>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_fa_kernel<P, D, kFaWaves, kFaRowTiles>), grid, dim3(64 * kFaWaves),
+                       0, s, a);
   } else {
     if (nt == 1)
       hipLaunchKernelGGL((prefill_mfma_kernel<F, P, D, 1, prefill_tiled_depth(P, D), false>), grid,
