@@ -282,38 +282,61 @@ struct PageRegs {
 constexpr int mfma_max_threads(int, int, int) { return 256; }
 constexpr int valu_max_threads(int, int, int) { return 256; }
 
-template <int F, int P, int D, int NT, int DEPTH, bool SCHED>
-__device__ __forceinline__ void mfma_item(const DecodeArgs& a, const WorkRange& wr, float* smem) {
+// Operand types of the matrix-core path: q^T and K as float16 (quantized
+// pools: exact code values) or bfloat16; P.V operands are four-wide for
+// 16-token pages.
+template <int F, int P, int D>
+struct MfmaOps {
+  static constexpr bool Q = FmtInfo<F>::quant;
+  using A = typename std::conditional<Q, f16x8_t, bf16x8_t>::type;
+  using PV = typename std::conditional<
+      MfmaShape<F, P, D>::T == 1, typename std::conditional<Q, f16x4_t, bf16x4_t>::type,
+      A>::type;
+};
+
+// Per-lane byte offsets inside a (page, head) tile: K rows of each 16-token
+// sub-tile, the V^T row, the metadata of the lane's tokens.
+template <int F, int P, int D>
+struct MfmaLaneOffsets {
+  int koff[MfmaShape<F, P, D>::T];
+  int voff, moff;
+};
+template <int F, int P, int D>
+__device__ __forceinline__ MfmaLaneOffsets<F, P, D> mfma_lane_offsets(int r, int gq) {
   using S = MfmaShape<F, P, D>;
-  using FI = FmtInfo<F>;
-  constexpr bool Q = FI::quant, ZP = FI::zero;
-  constexpr int T = S::T, KK = S::KK, NC = S::NC, EV = S::EV, RB = S::RB, KB = S::KB;
-  constexpr int HP = NT * 16;
-  using OpA = typename std::conditional<Q, f16x8_t, bf16x8_t>::type;
-  using OpPV = typename std::conditional<
-      T == 1, typename std::conditional<Q, f16x4_t, bf16x4_t>::type, OpA>::type;
-  using KLoad = typename LoadT<S::KLB>::type;
-  using VLoad = typename LoadT<S::VB>::type;
+  MfmaLaneOffsets<F, P, D> o;
+#pragma unroll
+  for (int st = 0; st < S::T; ++st) {
+    // sub-tile st, MFMA row r -> token; with two sub-tiles the rows are
+    // interleaved so a lane's eight P.V tokens are contiguous.
+    const int tok = (S::T == 1) ? r : 8 * (r >> 2) + 4 * st + (r & 3);
+    o.koff[st] = tok * S::RB + S::k_lane_offset(gq);
+  }
+  // V^T tile: [D][P] elements, or [D/2][P] bytes for INT4 (channel pairs)
+  o.voff = F == kBF16 ? (r * P + S::EV * gq) * 2 : (F == kI4 ? (r >> 1) * P : r * P) + S::EV * gq;
+  o.moff = S::EV * gq * 4;
+  return o;
+}
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int W = blockDim.x >> 6;
-  const int r = lane & 15, gq = lane >> 4;
+// q^T of an item as the B operand of S^T = K q^T: lane (r, gq) holds head
+// nt*16 + r (zero past the group), the 8 channels q_channel(kk, gq) of each
+// k-step; for quantized pools float16 values and, for the zero-point term,
+// qsum = the sum of the head's channels (float32, from the bfloat16 values).
+template <int F, int P, int D, int NT>
+__device__ __forceinline__ void mfma_load_q(const DecodeArgs& a, int b, int h, int r, int gq,
+                                            typename MfmaOps<F, P, D>::A (&qop)[NT][MfmaShape<F, P, D>::KK],
+                                            float (&qsum)[NT]) {
+  using S = MfmaShape<F, P, D>;
+  constexpr bool Q = FmtInfo<F>::quant, ZP = FmtInfo<F>::zero;
   const int g = a.group;
-  const int H = a.num_kv_heads;
-
-  // q^T as the B operand of S^T = K q^T: lane holds head nt*16 + r, 8 channels.
-  OpA qop[NT][KK];
-  float qsum[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int jj = nt * 16 + r;
     const bool live = jj < g;
-    const uint16_t* qrow =
-        a.q + (int64_t(wr.b) * a.num_q_heads + int64_t(wr.h) * g + (live ? jj : 0)) * D;
+    const uint16_t* qrow = a.q + (int64_t(b) * a.num_q_heads + int64_t(h) * g + (live ? jj : 0)) * D;
     float qs = 0.0f;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+    for (int kk = 0; kk < S::KK; ++kk) {
       const int d0 = S::q_channel(kk, gq);
       uint4 raw = live ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
       if constexpr (!Q) {
@@ -332,50 +355,235 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const WorkRange& 
     }
     qsum[nt] = ZP ? group4_sum(qs) : 0.0f;
   }
+}
 
-  // Per-lane byte offsets inside a (page, head) tile.
-  int koff[T];
+// Issue the loads of one (page, head) tile into a ring slot.  phys is the raw
+// table entry: out of range -> the slot is marked absent (phys = -1) and
+// page 0 is read in its place, so the load pattern stays fixed.
+template <int F, int P, int D>
+__device__ __forceinline__ void mfma_load_page(const DecodeArgs& a, int phys, int h,
+                                               const MfmaLaneOffsets<F, P, D>& o,
+                                               PageRegs<F, P, D>& R) {
+  using S = MfmaShape<F, P, D>;
+  using KLoad = typename LoadT<S::KLB>::type;
+  using VLoad = typename LoadT<S::VB>::type;
+  constexpr int vstride = F == kBF16 ? 16 * P * 2 : (F == kI4 ? 8 * P : 16 * P);
+  const bool ok = unsigned(phys) < unsigned(a.num_pages);
+  R.phys = ok ? phys : -1;
+  const int64_t tile = int64_t(ok ? phys : 0) * a.num_kv_heads + h;
+  const size_t tile_bytes = size_t(P) * S::RB;
+  const char* kp = static_cast<const char*>(a.k_pool) + tile * tile_bytes;
+  const char* vp = static_cast<const char*>(a.v_pool) + tile * tile_bytes;
+#pragma unroll
+  for (int st = 0; st < S::T; ++st)
+#pragma unroll
+    for (int i = 0; i < S::KN; ++i) R.k[st][i] = load_stream<KLoad>(kp + o.koff[st] + i * 64);
+#pragma unroll
+  for (int nc = 0; nc < S::NC; ++nc) R.v[nc] = load_stream<VLoad>(vp + o.voff + nc * vstride);
+  if constexpr (FmtInfo<F>::quant) {
+    const char* km = reinterpret_cast<const char*>(a.k_meta) + tile * (P * 4);
+    const char* vm = reinterpret_cast<const char*>(a.v_meta) + tile * (P * 4);
+#pragma unroll
+    for (int st = 0; st < S::T; ++st) {
+      R.km[st] = load_stream<uint4>(km + o.moff + st * 16);
+      R.vm[st] = load_stream<uint4>(vm + o.moff + st * 16);
+    }
+  }
+}
+
+// Page k of range wr (its loads in R): S^T = K q^T per head tile, online
+// softmax, O^T += V^T P^T, for the lane's item state (q operands qop, q
+// channel sum qsum for the zero-point term, running max m, sum lsum,
+// zero-point sum zacc, accumulators acc).  Absent pages are skipped; on a
+// partial page (some token past the sequence or outside the window) those
+// tokens' scores are -inf and their V^T values (or V scales) 0.
+template <int F, int P, int D, int NT>
+__device__ __forceinline__ void mfma_page(const DecodeArgs& a, const PageRegs<F, P, D>& R,
+                                          const WorkRange& wr, int k, int r, int gq,
+                                          const typename MfmaOps<F, P, D>::A (&qop)[NT][MfmaShape<F, P, D>::KK],
+                                          const float (&qsum)[NT], float (&m)[NT], float (&lsum)[NT],
+                                          float (&zacc)[NT], f32x4_t (&acc)[NT][MfmaShape<F, P, D>::NC]) {
+  using S = MfmaShape<F, P, D>;
+  using FI = FmtInfo<F>;
+  constexpr bool Q = FI::quant, ZP = FI::zero;
+  constexpr int T = S::T, KK = S::KK, NC = S::NC, EV = S::EV, KB = S::KB;
+  using OpA = typename MfmaOps<F, P, D>::A;
+  using OpPV = typename MfmaOps<F, P, D>::PV;
+  using VLoad = typename LoadT<S::VB>::type;
+
+  if (R.phys < 0) return;  // absent page: its tokens do not take part
+  const PageMask pm = page_mask<P>(wr, wr.logical(wr.kb0 + k));
+  const bool tail = pm.partial;
+
+  // K operands for all sub-tiles (shared by every head tile).
+  OpA kop[T][KK];
 #pragma unroll
   for (int st = 0; st < T; ++st) {
-    // sub-tile st, MFMA row r -> token; with two sub-tiles the rows are
-    // interleaved so a lane's eight P.V tokens are contiguous.
-    const int tok = (T == 1) ? r : 8 * (r >> 2) + 4 * st + (r & 3);
-    koff[st] = tok * RB + S::k_lane_offset(gq);
+    if constexpr (!Q) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kop[st][kk] = __builtin_bit_cast(bf16x8_t, R.k[st][kk]);
+    } else {
+      uint32_t w[KB / 4];
+      __builtin_memcpy(w, R.k[st], KB);
+      constexpr int DW = F == kI4 ? 1 : 2;  // dwords per 8 channels
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kop[st][kk] = codes8_to_f16x8<F>(w + DW * kk);
+    }
   }
-  // V^T tile: [D][P] elements, or [D/2][P] bytes for INT4 (channel pairs)
-  const int voff = F == kBF16 ? (r * P + EV * gq) * 2
-                              : (F == kI4 ? (r >> 1) * P : r * P) + EV * gq;
-  constexpr int vstride = F == kBF16 ? 16 * P * 2 : (F == kI4 ? 8 * P : 16 * P);
-  const int moff = EV * gq * 4;
+  // V^T operands.
+  OpPV vop[NC];
+#pragma unroll
+  for (int nc = 0; nc < NC; ++nc) {
+    if constexpr (!Q) {
+      VLoad raw = R.v[nc];
+      if (tail) {
+        // rows past the sequence may hold anything (NaN): zero them so 0*x stays 0
+        uint32_t wv[EV / 2];
+        __builtin_memcpy(wv, &raw, sizeof(raw));
+#pragma unroll
+        for (int e = 0; e < EV; ++e) {
+          if (!pm.valid(EV * gq + e)) wv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+        }
+        __builtin_memcpy(&raw, wv, sizeof(raw));
+      }
+      vop[nc] = __builtin_bit_cast(OpPV, raw);
+    } else {
+      uint32_t wv[EV / 4];
+      __builtin_memcpy(wv, &R.v[nc], sizeof(R.v[nc]));
+      OpPV v;
+#pragma unroll
+      for (int i = 0; i < EV / 4; ++i) {
+        f16x2_t lo, hi;
+        codes4_to_f16x4<F>(wv[i], (r & 1) != 0, lo, hi);
+        v[4 * i + 0] = lo[0];
+        v[4 * i + 1] = lo[1];
+        v[4 * i + 2] = hi[0];
+        v[4 * i + 3] = hi[1];
+      }
+      vop[nc] = v;
+    }
+  }
+  // Per-token scale (and zero point) of this lane's rows.
+  float ks[T][4], kz[T][4], vs[T][4], vz[T][4];
+  if constexpr (Q) {
+#pragma unroll
+    for (int st = 0; st < T; ++st) {
+      const uint32_t kw[4] = {R.km[st].x, R.km[st].y, R.km[st].z, R.km[st].w};
+      const uint32_t vw[4] = {R.vm[st].x, R.vm[st].y, R.vm[st].z, R.vm[st].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ks[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] & 0xffffu)) * FI::scale_mul;
+        kz[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] >> 16));
+        vs[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(vw[i] & 0xffffu)) * FI::scale_mul;
+        vz[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(vw[i] >> 16));
+      }
+    }
+  }
 
-  const size_t tile_bytes = size_t(P) * RB;
-  const char* kbase = static_cast<const char*>(a.k_pool);
-  const char* vbase = static_cast<const char*>(a.v_pool);
-  const int32_t* btrow = a.bt + int64_t(wr.b) * a.max_blocks;
-
-  auto issue = [&](PageRegs<F, P, D>& R, int k) {
-    int phys = btrow[wr.logical(wr.kb0 + k)];
-    const bool ok = unsigned(phys) < unsigned(a.num_pages);
-    R.phys = ok ? phys : -1;
-    const int64_t tile = int64_t(ok ? phys : 0) * H + wr.h;
-    const char* kp = kbase + tile * tile_bytes;
-    const char* vp = vbase + tile * tile_bytes;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float x[T][4];
+#pragma unroll
+    for (int st = 0; st < T; ++st) {
+      f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) sc = mfma_16x16x32(kop[st][kk], qop[nt][kk], sc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (ZP)
+          x[st][i] = (ks[st][i] * sc[i] + kz[st][i] * qsum[nt]) * a.scale_log2;
+        else if constexpr (Q)
+          x[st][i] = ks[st][i] * sc[i] * a.scale_log2;
+        else
+          x[st][i] = sc[i] * a.scale_log2;
+      }
+    }
+    if (tail) {
+#pragma unroll
+      for (int st = 0; st < T; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!pm.valid(EV * gq + 4 * st + i)) x[st][i] = -INFINITY;
+    }
+    float mloc = x[0][0];
 #pragma unroll
     for (int st = 0; st < T; ++st)
 #pragma unroll
-      for (int i = 0; i < S::KN; ++i)
-        R.k[st][i] = load_stream<KLoad>(kp + koff[st] + i * 64);
+      for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, x[st][i]);
+    mloc = group4_max(mloc);
+    const float mnew = fmaxf(m[nt], mloc);
+    const float al = fast_exp2(m[nt] - mnew);
+    m[nt] = mnew;
+    float p[T][4];
+    float ps = 0.0f;
 #pragma unroll
-    for (int nc = 0; nc < NC; ++nc) R.v[nc] = load_stream<VLoad>(vp + voff + nc * vstride);
-    if constexpr (Q) {
-      const char* km = reinterpret_cast<const char*>(a.k_meta) + tile * (P * 4);
-      const char* vm = reinterpret_cast<const char*>(a.v_meta) + tile * (P * 4);
+    for (int st = 0; st < T; ++st)
 #pragma unroll
-      for (int st = 0; st < T; ++st) {
-        R.km[st] = load_stream<uint4>(km + moff + st * 16);
-        R.vm[st] = load_stream<uint4>(vm + moff + st * 16);
+      for (int i = 0; i < 4; ++i) {
+        p[st][i] = fast_exp2(x[st][i] - mnew);
+        ps += p[st][i];
       }
+    lsum[nt] = lsum[nt] * al + ps;
+    // once the running maximum settles, al is exactly 1 for every head:
+    // skip the (identity) rescale of the accumulators
+    if (wave_any(al != 1.0f)) {
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc) acc[nt][nc] *= al;
     }
+    OpPV pop;
+    if constexpr (Q) {
+      float zs = 0.0f;
+#pragma unroll
+      for (int st = 0; st < T; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool valid = !tail || pm.valid(EV * gq + 4 * st + i);
+          const float pv = valid ? p[st][i] * vs[st][i] : 0.0f;
+          if constexpr (ZP) zs += valid ? p[st][i] * vz[st][i] : 0.0f;
+          pop[4 * st + i] = (_Float16)pv;
+        }
+      zacc[nt] = zacc[nt] * al + zs;
+    } else {
+#pragma unroll
+      for (int st = 0; st < T; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pop[4 * st + i] = (__bf16)p[st][i];
+    }
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc) {
+      if constexpr (T == 1)
+        acc[nt][nc] = mfma_16x16x16(vop[nc], pop, acc[nt][nc]);
+      else
+        acc[nt][nc] = mfma_16x16x32(vop[nc], pop, acc[nt][nc]);
+    }
+  }
+  }
+
+template <int F, int P, int D, int NT, int DEPTH, bool SCHED>
+__device__ __forceinline__ void mfma_item(const DecodeArgs& a, const WorkRange& wr, float* smem) {
+  using S = MfmaShape<F, P, D>;
+  using FI = FmtInfo<F>;
+  constexpr bool ZP = FI::zero;
+  constexpr int KK = S::KK, NC = S::NC;
+  constexpr int HP = NT * 16;
+  using OpA = typename MfmaOps<F, P, D>::A;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
+  const int r = lane & 15, gq = lane >> 4;
+  const int g = a.group;
+
+  // q^T as the B operand of S^T = K q^T
+  OpA qop[NT][KK];
+  float qsum[NT];
+  mfma_load_q<F, P, D, NT>(a, wr.b, wr.h, r, gq, qop, qsum);
+
+  const int32_t* btrow = a.bt + int64_t(wr.b) * a.max_blocks;
+
+  const MfmaLaneOffsets<F, P, D> lo = mfma_lane_offsets<F, P, D>(r, gq);
+  auto issue = [&](PageRegs<F, P, D>& R, int k) {
+    mfma_load_page<F, P, D>(a, btrow[wr.logical(wr.kb0 + k)], wr.h, lo, R);
   };
 
   float m[NT], lsum[NT], zacc[NT];
@@ -390,159 +598,8 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const WorkRange& 
   }
 
   auto compute = [&](const PageRegs<F, P, D>& R, int k) {
-    if (R.phys < 0) return;  // absent page: its tokens do not take part
-    const PageMask pm = page_mask<P>(wr, wr.logical(wr.kb0 + k));
-    const bool tail = pm.partial;
-
-    // K operands for all sub-tiles (shared by every head tile).
-    OpA kop[T][KK];
-#pragma unroll
-    for (int st = 0; st < T; ++st) {
-      if constexpr (!Q) {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kop[st][kk] = __builtin_bit_cast(bf16x8_t, R.k[st][kk]);
-      } else {
-        uint32_t w[KB / 4];
-        __builtin_memcpy(w, R.k[st], KB);
-        constexpr int DW = F == kI4 ? 1 : 2;  // dwords per 8 channels
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kop[st][kk] = codes8_to_f16x8<F>(w + DW * kk);
-      }
-    }
-    // V^T operands.
-    OpPV vop[NC];
-#pragma unroll
-    for (int nc = 0; nc < NC; ++nc) {
-      if constexpr (!Q) {
-        VLoad raw = R.v[nc];
-        if (tail) {
-          // rows past the sequence may hold anything (NaN): zero them so 0*x stays 0
-          uint32_t wv[EV / 2];
-          __builtin_memcpy(wv, &raw, sizeof(raw));
-#pragma unroll
-          for (int e = 0; e < EV; ++e) {
-            if (!pm.valid(EV * gq + e)) wv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          }
-          __builtin_memcpy(&raw, wv, sizeof(raw));
-        }
-        vop[nc] = __builtin_bit_cast(OpPV, raw);
-      } else {
-        uint32_t wv[EV / 4];
-        __builtin_memcpy(wv, &R.v[nc], sizeof(R.v[nc]));
-        OpPV v;
-#pragma unroll
-        for (int i = 0; i < EV / 4; ++i) {
-          f16x2_t lo, hi;
-          if constexpr (F == kI8)
-            i8x4_to_f16x4(wv[i], lo, hi);
-          else if constexpr (F == kFP8)
-            fp8x4_to_f16x4(wv[i], lo, hi);
-          else
-            i4sel4_to_f16x4(wv[i], (r & 1) != 0, lo, hi);
-          v[4 * i + 0] = lo[0];
-          v[4 * i + 1] = lo[1];
-          v[4 * i + 2] = hi[0];
-          v[4 * i + 3] = hi[1];
-        }
-        vop[nc] = v;
-      }
-    }
-    // Per-token scale (and zero point) of this lane's rows.
-    float ks[T][4], kz[T][4], vs[T][4], vz[T][4];
-    if constexpr (Q) {
-#pragma unroll
-      for (int st = 0; st < T; ++st) {
-        const uint32_t kw[4] = {R.km[st].x, R.km[st].y, R.km[st].z, R.km[st].w};
-        const uint32_t vw[4] = {R.vm[st].x, R.vm[st].y, R.vm[st].z, R.vm[st].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ks[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] & 0xffffu)) * FI::scale_mul;
-          kz[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] >> 16));
-          vs[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(vw[i] & 0xffffu)) * FI::scale_mul;
-          vz[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(vw[i] >> 16));
-        }
-      }
-    }
-
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float x[T][4];
-#pragma unroll
-      for (int st = 0; st < T; ++st) {
-        f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) sc = mfma_16x16x32(kop[st][kk], qop[nt][kk], sc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (ZP)
-            x[st][i] = (ks[st][i] * sc[i] + kz[st][i] * qsum[nt]) * a.scale_log2;
-          else if constexpr (Q)
-            x[st][i] = ks[st][i] * sc[i] * a.scale_log2;
-          else
-            x[st][i] = sc[i] * a.scale_log2;
-        }
-      }
-      if (tail) {
-#pragma unroll
-        for (int st = 0; st < T; ++st)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (!pm.valid(EV * gq + 4 * st + i)) x[st][i] = -INFINITY;
-      }
-      float mloc = x[0][0];
-#pragma unroll
-      for (int st = 0; st < T; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, x[st][i]);
-      mloc = group4_max(mloc);
-      const float mnew = fmaxf(m[nt], mloc);
-      const float al = fast_exp2(m[nt] - mnew);
-      m[nt] = mnew;
-      float p[T][4];
-      float ps = 0.0f;
-#pragma unroll
-      for (int st = 0; st < T; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[st][i] = fast_exp2(x[st][i] - mnew);
-          ps += p[st][i];
-        }
-      lsum[nt] = lsum[nt] * al + ps;
-      // once the running maximum settles, al is exactly 1 for every head:
-      // skip the (identity) rescale of the accumulators
-      if (wave_any(al != 1.0f)) {
-#pragma unroll
-        for (int nc = 0; nc < NC; ++nc) acc[nt][nc] *= al;
-      }
-      OpPV pop;
-      if constexpr (Q) {
-        float zs = 0.0f;
-#pragma unroll
-        for (int st = 0; st < T; ++st)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool valid = !tail || pm.valid(EV * gq + 4 * st + i);
-            const float pv = valid ? p[st][i] * vs[st][i] : 0.0f;
-            if constexpr (ZP) zs += valid ? p[st][i] * vz[st][i] : 0.0f;
-            pop[4 * st + i] = (_Float16)pv;
-          }
-        zacc[nt] = zacc[nt] * al + zs;
-      } else {
-#pragma unroll
-        for (int st = 0; st < T; ++st)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pop[4 * st + i] = (__bf16)p[st][i];
-      }
-#pragma unroll
-      for (int nc = 0; nc < NC; ++nc) {
-        if constexpr (T == 1)
-          acc[nt][nc] = mfma_16x16x16(vop[nc], pop, acc[nt][nc]);
-        else
-          acc[nt][nc] = mfma_16x16x32(vop[nc], pop, acc[nt][nc]);
-      }
-    }
+    mfma_page<F, P, D, NT>(a, R, wr, k, r, gq, qop, qsum, m, lsum, zacc, acc);
   };
-
   if (wr.cnt > 0) {
     PageRegs<F, P, D> ring[DEPTH];
 #pragma unroll
@@ -642,13 +699,9 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
     DecodeArgs a) {
   using S = MfmaShape<F, P, D>;
   using FI = FmtInfo<F>;
-  constexpr bool Q = FI::quant, ZP = FI::zero;
-  constexpr int T = S::T, KK = S::KK, NC = S::NC, EV = S::EV, RB = S::RB, KB = S::KB;
-  using OpA = typename std::conditional<Q, f16x8_t, bf16x8_t>::type;
-  using OpPV = typename std::conditional<
-      T == 1, typename std::conditional<Q, f16x4_t, bf16x4_t>::type, OpA>::type;
-  using KLoad = typename LoadT<S::KLB>::type;
-  using VLoad = typename LoadT<S::VB>::type;
+  constexpr bool ZP = FI::zero;
+  constexpr int KK = S::KK, NC = S::NC;
+  using OpA = typename MfmaOps<F, P, D>::A;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -656,23 +709,8 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
   if (bin >= a.num_bins) return;  // the whole wavefront; nothing here waits on the others
   const int r = lane & 15, gq = lane >> 4;
   const int g = a.group;
-  const int H = a.num_kv_heads;
   const int i_begin = max(a.sched[8 + bin], 0);
   const int end = min(a.sched[9 + bin], a.num_items);
-
-  int koff[T];
-#pragma unroll
-  for (int st = 0; st < T; ++st) {
-    const int tok = (T == 1) ? r : 8 * (r >> 2) + 4 * st + (r & 3);
-    koff[st] = tok * RB + S::k_lane_offset(gq);
-  }
-  const int voff = F == kBF16 ? (r * P + EV * gq) * 2
-                              : (F == kI4 ? (r >> 1) * P : r * P) + EV * gq;
-  constexpr int vstride = F == kBF16 ? 16 * P * 2 : (F == kI4 ? 8 * P : 16 * P);
-  const int moff = EV * gq * 4;
-  const size_t tile_bytes = size_t(P) * RB;
-  const char* kbase = static_cast<const char*>(a.k_pool);
-  const char* vbase = static_cast<const char*>(a.v_pool);
 
   // issue side: loads page ip.k of item ip.item; once the stream's pages are
   // all issued it repeats the last page (a cache hit) so the ring's load
@@ -681,30 +719,10 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
   ip.item = i_begin;
   stream_seek<P>(a, ip, end, true);
   bool issued_all = ip.item >= end;
+  const MfmaLaneOffsets<F, P, D> lo = mfma_lane_offsets<F, P, D>(r, gq);
   auto issue = [&](PageRegs<F, P, D>& R) __attribute__((always_inline)) {
     const int32_t* btrow = a.bt + int64_t(ip.wr.b) * a.max_blocks;
-    int phys = btrow[ip.wr.logical(ip.wr.kb0 + ip.k)];
-    const bool ok = unsigned(phys) < unsigned(a.num_pages);
-    R.phys = ok ? phys : -1;
-    const int64_t tile = int64_t(ok ? phys : 0) * H + ip.wr.h;
-    const char* kp = kbase + tile * tile_bytes;
-    const char* vp = vbase + tile * tile_bytes;
-#pragma unroll
-    for (int st = 0; st < T; ++st)
-#pragma unroll
-      for (int i = 0; i < S::KN; ++i)
-        R.k[st][i] = load_stream<KLoad>(kp + koff[st] + i * 64);
-#pragma unroll
-    for (int nc = 0; nc < NC; ++nc) R.v[nc] = load_stream<VLoad>(vp + voff + nc * vstride);
-    if constexpr (Q) {
-      const char* km = reinterpret_cast<const char*>(a.k_meta) + tile * (P * 4);
-      const char* vm = reinterpret_cast<const char*>(a.v_meta) + tile * (P * 4);
-#pragma unroll
-      for (int st = 0; st < T; ++st) {
-        R.km[st] = load_stream<uint4>(km + moff + st * 16);
-        R.vm[st] = load_stream<uint4>(vm + moff + st * 16);
-      }
-    }
+    mfma_load_page<F, P, D>(a, btrow[ip.wr.logical(ip.wr.kb0 + ip.k)], ip.wr.h, lo, R);
     // advance to the next page of the stream (or stay on the last one)
     if (!issued_all) {
       if (++ip.k >= ip.wr.cnt) {
@@ -723,32 +741,9 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
   float m[NT], lsum[NT], zacc[NT];
   f32x4_t acc[NT][NC];
   auto begin_item = [&](const WorkRange& wr) __attribute__((always_inline)) {
+    mfma_load_q<F, P, D, NT>(a, wr.b, wr.h, r, gq, qop, qsum);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int jj = nt * 16 + r;
-      const bool live = jj < g;
-      const uint16_t* qrow =
-          a.q + (int64_t(wr.b) * a.num_q_heads + int64_t(wr.h) * g + (live ? jj : 0)) * D;
-      float qs = 0.0f;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int d0 = S::q_channel(kk, gq);
-        uint4 raw = live ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
-        if constexpr (!Q) {
-          qop[nt][kk] = __builtin_bit_cast(bf16x8_t, raw);
-        } else {
-          const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-          f16x8_t v;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float f = bf16_to_f32((w4[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-            v[e] = (_Float16)f;
-            qs += f;
-          }
-          qop[nt][kk] = v;
-        }
-      }
-      qsum[nt] = ZP ? group4_sum(qs) : 0.0f;
       m[nt] = -INFINITY;
       lsum[nt] = 0.0f;
       zacc[nt] = 0.0f;
@@ -790,159 +785,8 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
 
   auto compute = [&](const PageRegs<F, P, D>& R, const WorkRange& wr,
                      int k) __attribute__((always_inline)) {
-    if (R.phys < 0) return;  // absent page: its tokens do not take part
-    const PageMask pm = page_mask<P>(wr, wr.logical(wr.kb0 + k));
-    const bool tail = pm.partial;
-
-    // K operands for all sub-tiles (shared by every head tile).
-    OpA kop[T][KK];
-#pragma unroll
-    for (int st = 0; st < T; ++st) {
-      if constexpr (!Q) {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kop[st][kk] = __builtin_bit_cast(bf16x8_t, R.k[st][kk]);
-      } else {
-        uint32_t w[KB / 4];
-        __builtin_memcpy(w, R.k[st], KB);
-        constexpr int DW = F == kI4 ? 1 : 2;  // dwords per 8 channels
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kop[st][kk] = codes8_to_f16x8<F>(w + DW * kk);
-      }
-    }
-    // V^T operands.
-    OpPV vop[NC];
-#pragma unroll
-    for (int nc = 0; nc < NC; ++nc) {
-      if constexpr (!Q) {
-        VLoad raw = R.v[nc];
-        if (tail) {
-          // rows past the sequence may hold anything (NaN): zero them so 0*x stays 0
-          uint32_t wv[EV / 2];
-          __builtin_memcpy(wv, &raw, sizeof(raw));
-#pragma unroll
-          for (int e = 0; e < EV; ++e) {
-            if (!pm.valid(EV * gq + e)) wv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          }
-          __builtin_memcpy(&raw, wv, sizeof(raw));
-        }
-        vop[nc] = __builtin_bit_cast(OpPV, raw);
-      } else {
-        uint32_t wv[EV / 4];
-        __builtin_memcpy(wv, &R.v[nc], sizeof(R.v[nc]));
-        OpPV v;
-#pragma unroll
-        for (int i = 0; i < EV / 4; ++i) {
-          f16x2_t lo, hi;
-          if constexpr (F == kI8)
-            i8x4_to_f16x4(wv[i], lo, hi);
-          else if constexpr (F == kFP8)
-            fp8x4_to_f16x4(wv[i], lo, hi);
-          else
-            i4sel4_to_f16x4(wv[i], (r & 1) != 0, lo, hi);
-          v[4 * i + 0] = lo[0];
-          v[4 * i + 1] = lo[1];
-          v[4 * i + 2] = hi[0];
-          v[4 * i + 3] = hi[1];
-        }
-        vop[nc] = v;
-      }
-    }
-    // Per-token scale (and zero point) of this lane's rows.
-    float ks[T][4], kz[T][4], vs[T][4], vz[T][4];
-    if constexpr (Q) {
-#pragma unroll
-      for (int st = 0; st < T; ++st) {
-        const uint32_t kw[4] = {R.km[st].x, R.km[st].y, R.km[st].z, R.km[st].w};
-        const uint32_t vw[4] = {R.vm[st].x, R.vm[st].y, R.vm[st].z, R.vm[st].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ks[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] & 0xffffu)) * FI::scale_mul;
-          kz[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] >> 16));
-          vs[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(vw[i] & 0xffffu)) * FI::scale_mul;
-          vz[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(vw[i] >> 16));
-        }
-      }
-    }
-
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float x[T][4];
-#pragma unroll
-      for (int st = 0; st < T; ++st) {
-        f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) sc = mfma_16x16x32(kop[st][kk], qop[nt][kk], sc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (ZP)
-            x[st][i] = (ks[st][i] * sc[i] + kz[st][i] * qsum[nt]) * a.scale_log2;
-          else if constexpr (Q)
-            x[st][i] = ks[st][i] * sc[i] * a.scale_log2;
-          else
-            x[st][i] = sc[i] * a.scale_log2;
-        }
-      }
-      if (tail) {
-#pragma unroll
-        for (int st = 0; st < T; ++st)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (!pm.valid(EV * gq + 4 * st + i)) x[st][i] = -INFINITY;
-      }
-      float mloc = x[0][0];
-#pragma unroll
-      for (int st = 0; st < T; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, x[st][i]);
-      mloc = group4_max(mloc);
-      const float mnew = fmaxf(m[nt], mloc);
-      const float al = fast_exp2(m[nt] - mnew);
-      m[nt] = mnew;
-      float p[T][4];
-      float ps = 0.0f;
-#pragma unroll
-      for (int st = 0; st < T; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[st][i] = fast_exp2(x[st][i] - mnew);
-          ps += p[st][i];
-        }
-      lsum[nt] = lsum[nt] * al + ps;
-      // once the running maximum settles, al is exactly 1 for every head:
-      // skip the (identity) rescale of the accumulators
-      if (wave_any(al != 1.0f)) {
-#pragma unroll
-        for (int nc = 0; nc < NC; ++nc) acc[nt][nc] *= al;
-      }
-      OpPV pop;
-      if constexpr (Q) {
-        float zs = 0.0f;
-#pragma unroll
-        for (int st = 0; st < T; ++st)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool valid = !tail || pm.valid(EV * gq + 4 * st + i);
-            const float pv = valid ? p[st][i] * vs[st][i] : 0.0f;
-            if constexpr (ZP) zs += valid ? p[st][i] * vz[st][i] : 0.0f;
-            pop[4 * st + i] = (_Float16)pv;
-          }
-        zacc[nt] = zacc[nt] * al + zs;
-      } else {
-#pragma unroll
-        for (int st = 0; st < T; ++st)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pop[4 * st + i] = (__bf16)p[st][i];
-      }
-#pragma unroll
-      for (int nc = 0; nc < NC; ++nc) {
-        if constexpr (T == 1)
-          acc[nt][nc] = mfma_16x16x16(vop[nc], pop, acc[nt][nc]);
-        else
-          acc[nt][nc] = mfma_16x16x32(vop[nc], pop, acc[nt][nc]);
-      }
-    }
+    mfma_page<F, P, D, NT>(a, R, wr, k, r, gq, qop, qsum, m, lsum, zacc, acc);
   };
-
 
   // compute side: every valid item in order (empty ones give 0 or an empty
   // partial right away); pages in the order they were issued.  Each item's
