@@ -403,9 +403,9 @@ kvp_status kvp_decode_schedule_bounds(const kvp_pool* pool, int32_t num_seqs,
 
 /* Bins that keep every compute unit of the current device busy along a
  * schedule for this pool and num_q_heads: four per compute unit (one
- * wavefront per SIMD), eight for quantized pools (INT8, INT4, FP8) on the
- * matrix-core path with 4 <= g <= 16, whose stream kernel is built for two
- * wavefronts per SIMD.  The
+ * wavefront per SIMD), eight for INT8 and FP8 pools and twelve for INT4
+ * pools on the matrix-core path with 4 <= g <= 16, whose stream kernel is
+ * built for two (INT4: three) wavefronts per SIMD.  The
  * value to pass as max_bins below when there is no reason to pick another.
  * KVP_E_INVAL for a bad pool, head count or pointer; KVP_E_HIP when the
  * device cannot be queried. */

@@ -407,9 +407,11 @@ extern "C" kvp_status kvp_decode_schedule_bins(const kvp_pool* pool, int32_t num
   kvp_decode_plan_t plan;
   if (kvp_decode_plan(&d, 1, num_q_heads, d.page_size, 0, cus, &plan) != KVP_OK)
     return KVP_E_INVAL;
-  // two wavefronts per SIMD: quantized pools, one head tile (g <= 16)
+  // wavefronts per SIMD of the stream kernel: quantized pools with one head
+  // tile (g <= 16) run two (INT4: three)
   const int g = num_q_heads / d.num_kv_heads;
-  const int waves = plan.use_mfma && d.dtype != KVP_BF16 && g <= 16 ? 2 : 1;
+  const int waves =
+      plan.use_mfma && d.dtype != KVP_BF16 && g <= 16 ? (d.dtype == KVP_INT4 ? 3 : 2) : 1;
   *max_bins = 4 * waves * cus;
   return KVP_OK;
 }

@@ -463,13 +463,20 @@ __device__ __forceinline__ void mfma_page(const DecodeArgs& a, const PageRegs<F,
       vop[nc] = v;
     }
   }
-  // Per-token scale (and zero point) of this lane's rows.
+  // Per-token scale (and zero point) of this lane's rows.  The V metadata of
+  // tokens not kept may hold anything (NaN): it is zeroed, so that their zero
+  // weights give exact zeros below.
   float ks[T][4], kz[T][4], vs[T][4], vz[T][4];
   if constexpr (Q) {
 #pragma unroll
     for (int st = 0; st < T; ++st) {
       const uint32_t kw[4] = {R.km[st].x, R.km[st].y, R.km[st].z, R.km[st].w};
-      const uint32_t vw[4] = {R.vm[st].x, R.vm[st].y, R.vm[st].z, R.vm[st].w};
+      uint32_t vw[4] = {R.vm[st].x, R.vm[st].y, R.vm[st].z, R.vm[st].w};
+      if (tail) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!pm.valid(EV * gq + 4 * st + i)) vw[i] = 0u;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         ks[st][i] = (float)__builtin_bit_cast(_Float16, uint16_t(kw[i] & 0xffffu)) * FI::scale_mul;
@@ -537,9 +544,9 @@ __device__ __forceinline__ void mfma_page(const DecodeArgs& a, const PageRegs<F,
       for (int st = 0; st < T; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool valid = !tail || pm.valid(EV * gq + 4 * st + i);
-          const float pv = valid ? p[st][i] * vs[st][i] : 0.0f;
-          if constexpr (ZP) zs += valid ? p[st][i] * vz[st][i] : 0.0f;
+          // (a token not kept has weight 0 and zeroed V metadata)
+          const float pv = p[st][i] * vs[st][i];
+          if constexpr (ZP) zs += p[st][i] * vz[st][i];
           pop[4 * st + i] = (_Float16)pv;
         }
       zacc[nt] = zacc[nt] * al + zs;
@@ -682,16 +689,18 @@ __device__ __forceinline__ void stream_seek(const DecodeArgs& a, StreamPos& p, i
 
 // Wavefronts per SIMD the stream kernel is compiled for.  Quantized pages
 // carry much more arithmetic per byte than bfloat16 ones (code conversion,
-// scales, zero points), and with two wavefronts per SIMD (eight bins per
-// compute unit) one computes while the other waits on memory.  Measured on
-// 16 sequences of 16k-32k tokens, P = 32: INT4 166 -> 142 us (two-page rings;
-// the 256-register budget spills a little), INT8 176 -> 166 us and FP8 159 ->
-// 150 us (one-page rings, no spills; two-page rings spill and were slower).
-// bfloat16 keeps one wavefront with a two-page ring (two measured slower).
-// Only instances for groups of up to 16 query heads (one head tile) fit the
-// 256-register budget without spilling; larger groups keep one wavefront.
+// scales, zero points), and with several wavefronts per SIMD one computes
+// while the others wait on memory.  Measured on 16 sequences of 16k-32k
+// tokens, P = 32: INT8 176 -> 166 us and FP8 159 -> 150 us with two (and
+// one-page rings: two-page rings spill and were slower; three wavefronts
+// measured 2-6% slower); INT4, whose pages are half the bytes, 166 -> 142 us
+// with two and two-page rings, and 139 -> 121 us from there with three
+// wavefronts and one-page rings (168 registers, no spills).  bfloat16 keeps
+// one wavefront with a two-page ring (two measured slower).  Only instances
+// for groups of up to 16 query heads (one head tile) fit those register
+// budgets; larger groups keep one wavefront.
 template <int F, int NT> constexpr int stream_waves_per_simd() {
-  return F != kBF16 && NT == 1 ? 2 : 1;
+  return F == kBF16 || NT != 1 ? 1 : (F == kI4 ? 3 : 2);
 }
 
 template <int F, int P, int D, int NT, int DEPTH>
@@ -1229,15 +1238,14 @@ template <int F, int P, int D, int NT> constexpr int mfma_depth_nt() {
          : (P == 32 && D == 128 && NT == 2) ? (mfma_depth<F>() < 2 ? mfma_depth<F>() : 2)
                                               : mfma_depth<F>();
 }
-// The stream kernel's ring: the split kernel's with one wavefront per SIMD;
-// with two, INT4 (half-size pages) keeps two pages in flight and the 8-bit
-// formats one.
+// The stream kernel's ring: the split kernel's with one wavefront per SIMD,
+// one page with more.
 template <int F, int P, int D, int NT> constexpr int stream_depth() {
   // (the stream kernel's item bookkeeping costs registers too: four head
   // tiles of 16-token pages also keep at most two pages)
   constexpr int d1 = (P == 16 && D == 128 && NT == 4 && mfma_depth_nt<F, P, D, NT>() > 2)
                          ? 2 : mfma_depth_nt<F, P, D, NT>();
-  return stream_waves_per_simd<F, NT>() == 1 ? d1 : (F == kI4 ? 2 : 1);
+  return stream_waves_per_simd<F, NT>() == 1 ? d1 : 1;
 }
 
 int cu_count_current_device();

@@ -109,12 +109,12 @@ def test_one_device_schedule_serves_many_calls(kvp, name):
 
 
 def test_schedule_bins_fill_the_device(kvp):
-    """Four bins per compute unit (one wavefront per SIMD); eight for
-    quantized pools on the matrix-core path with g <= 16, whose stream
-    kernel runs two wavefronts per SIMD; the vector path (g < 4) and larger
-    groups keep four."""
+    """Four bins per compute unit (one wavefront per SIMD); eight for INT8
+    and FP8 pools and twelve for INT4 pools on the matrix-core path with
+    g <= 16, whose stream kernel runs two (INT4: three) wavefronts per SIMD;
+    the vector path (g < 4) and larger groups keep four."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    for dtype, hq, want in (("bf16", 32, 4), ("int8", 32, 8), ("fp8", 32, 8), ("int4", 32, 8),
+    for dtype, hq, want in (("bf16", 32, 4), ("int8", 32, 8), ("fp8", 32, 8), ("int4", 32, 12),
                             ("int4", 16, 4), ("bf16", 8, 4), ("int8", 128, 8), ("int8", 256, 4),
                             ("int4", 512, 4)):
         pool = kvp.kvp_pool_create(kvp.make_desc(64, 32, 8, 128, dtype))
