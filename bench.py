@@ -42,11 +42,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 # sources that decide the split kernel's code and launch shape
 KERNEL_SOURCES = ("paged_kv_cache_465_amd/csrc/decode.hip",
                   "paged_kv_cache_465_amd/csrc/decode_kernels.h",
-                  "paged_kv_cache_465_amd/csrc/decode_bf16_split.hip",
+                  *(f"paged_kv_cache_465_amd/csrc/decode_{f}_{p}.hip"
+                    for f in ("bf16", "int8", "int4", "fp8") for p in ("split", "sched")),
                   "paged_kv_cache_465_amd/csrc/device_common.h",
                   "paged_kv_cache_465_amd/csrc/pool.cpp")
 # sources that decide the multi-query (chunked prefill, verification) kernel
 PREFILL_SOURCES = ("paged_kv_cache_465_amd/csrc/prefill.hip",
+                   "paged_kv_cache_465_amd/csrc/prefill_kernels.h",
+                   *(f"paged_kv_cache_465_amd/csrc/prefill_{f}.hip"
+                     for f in ("bf16", "int8", "int4", "fp8")),
                    "paged_kv_cache_465_amd/csrc/device_common.h")
 MALL_FLUSH_BYTES = 1 << 30      # > 256 MB Infinity Cache
 
@@ -607,7 +611,11 @@ def main(argv=None):
     intensity = flops_launch / sb["split_kernel_per_launch"]
     mfma_bound = intensity > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     if is_chunked(cfg):
-        kernel_name = "prefill_mfma_kernel"
+        # bfloat16 pools with more than 32 rows per (sequence, KV head): the
+        # LDS-staged kernel; otherwise the register-streaming one
+        rows = int(np.diff(case.q_start).max()) * (cfg.num_q_heads // cfg.num_kv_heads)
+        kernel_name = ("prefill_fa_kernel" if cfg.kv_dtype == "bf16" and rows > 32
+                       else "prefill_mfma_kernel")
     elif res["plan"]["use_mfma"]:
         kernel_name = "decode_mfma_stream_kernel" if res["balanced"] else "decode_mfma_kernel"
     else:
