@@ -140,17 +140,25 @@ __device__ __forceinline__ void fp8x4_to_f16x4(uint32_t w, f16x2_t& lo, f16x2_t&
 
 // Eight 4-bit codes (one dword; byte j holds channel 2j in its low nibble and
 // 2j+1 in its high nibble, each as code + 8) -> eight exact float16 codes in
-// channel order: interleave the nibbles into bytes, then 0x6400|u = 1024 + u.
+// the slot order of kI4KSlot: each mask-and-or places two nibbles under the
+// float16 exponent of 1024 (low nibbles: 1024 + u; high nibbles: 1024 + 16 u),
+// and one packed add or fma per pair removes the offsets.
 __device__ __forceinline__ f16x8_t i4x8_to_f16x8(uint32_t w) {
-  const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
-  const uint32_t c0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // ch0 ch1 ch2 ch3
-  const uint32_t c1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // ch4 ch5 ch6 ch7
+  const uint32_t w8 = w >> 8;
+  const f16x2_t a = __builtin_bit_cast(f16x2_t, (w & 0x000f000fu) | 0x64006400u);   // ch 0, 4
+  const f16x2_t b = __builtin_bit_cast(f16x2_t, (w & 0x00f000f0u) | 0x64006400u);   // ch 1, 5
+  const f16x2_t c = __builtin_bit_cast(f16x2_t, (w8 & 0x000f000fu) | 0x64006400u);  // ch 2, 6
+  const f16x2_t d = __builtin_bit_cast(f16x2_t, (w8 & 0x00f000f0u) | 0x64006400u);  // ch 3, 7
   const f16x2_t off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const f16x2_t p0 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, c0, 0x04010400u)) + off;
-  const f16x2_t p1 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, c0, 0x04030402u)) + off;
-  const f16x2_t p2 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, c1, 0x04010400u)) + off;
-  const f16x2_t p3 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, c1, 0x04030402u)) + off;
+  const f16x2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const f16x2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const f16x2_t p0 = a + off, p2 = c + off;
+  const f16x2_t p1 = b * sixteenth + off16, p3 = d * sixteenth + off16;
   return f16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+// Channel (of the dword's eight) in slot e of i4x8_to_f16x8's result.
+__device__ __forceinline__ constexpr int kI4KSlot(int e) {
+  return (e & 1) * 4 + (e >> 1);
 }
 
 // Four bytes, each holding this lane's channel in one nibble (the high one

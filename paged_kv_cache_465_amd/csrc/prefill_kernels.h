@@ -167,7 +167,8 @@ prefill_mfma_kernel(PrefillArgs a) {
         f16x8_t v;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float f = bf16_to_f32((w4[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+          const int c = F == kI4 ? kI4KSlot(e) : e;  // the K operand's channel order
+          const float f = bf16_to_f32((w4[c >> 1] >> (16 * (c & 1))) & 0xffffu);
           v[e] = (_Float16)f;
           qs += f;
         }
