@@ -545,9 +545,11 @@ __device__ __forceinline__ void mfma_page(const DecodeArgs& a, const PageRegs<F,
       for (int st = 0; st < T; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          // (a token not kept has weight 0 and zeroed V metadata)
-          const float pv = p[st][i] * vs[st][i];
-          if constexpr (ZP) zs += p[st][i] * vz[st][i];
+          // (a token not kept has weight 0 and zeroed V metadata); slot i
+          // holds token kV4Slot(i), the V^T operand's order
+          const int t = kV4Slot<F>(i);
+          const float pv = p[st][t] * vs[st][t];
+          if constexpr (ZP) zs += p[st][t] * vz[st][t];
           pop[4 * st + i] = (_Float16)pv;
         }
       zacc[nt] = zacc[nt] * al + zs;

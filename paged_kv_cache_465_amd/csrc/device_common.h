@@ -162,13 +162,22 @@ __device__ __forceinline__ constexpr int kI4KSlot(int e) {
 }
 
 // Four bytes, each holding this lane's channel in one nibble (the high one
-// when hi_nibble) -> four exact float16 codes.
+// when hi_nibble) -> four exact float16 codes, in the token order of
+// kV4Slot: lo = tokens (0, 2), hi = tokens (1, 3).  One mask-and-or per pair
+// places the nibbles under the float16 exponent of 1024 (a low nibble as
+// 1024 + u, a high one as 1024 + 16 u) and one packed fma removes the offset
+// (x 1 - 1032, or x 1/16 - 72): exact.
 __device__ __forceinline__ void i4sel4_to_f16x4(uint32_t w, bool hi_nibble, f16x2_t& lo,
                                                 f16x2_t& hi) {
-  const uint32_t u = (hi_nibble ? (w >> 4) : w) & 0x0f0f0f0fu;
-  const f16x2_t off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  lo = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) + off;
-  hi = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) + off;
+  const uint32_t mask = hi_nibble ? 0x00f000f0u : 0x000f000fu;
+  const f16x2_t mul = hi_nibble ? f16x2_t{(_Float16)0.0625f, (_Float16)0.0625f}
+                                : f16x2_t{(_Float16)1.0f, (_Float16)1.0f};
+  const f16x2_t off = hi_nibble ? f16x2_t{(_Float16)-72.0f, (_Float16)-72.0f}
+                                : f16x2_t{(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const f16x2_t a = __builtin_bit_cast(f16x2_t, (w & mask) | 0x64006400u);         // tokens 0, 2
+  const f16x2_t b = __builtin_bit_cast(f16x2_t, ((w >> 8) & mask) | 0x64006400u);  // tokens 1, 3
+  lo = a * mul + off;
+  hi = b * mul + off;
 }
 
 // Eight consecutive code channels of a lane (starting at dword w[0]) as the
@@ -192,7 +201,12 @@ __device__ __forceinline__ f16x8_t codes8_to_f16x8(const uint32_t* w) {
 
 // Four codes of one channel from one dword (a V^T operand): four INT8 or
 // FP8 bytes, or for INT4 four bytes of a channel pair with this lane's
-// channel in the high nibble when hi_nibble.
+// channel in the high nibble when hi_nibble.  Result slot s (lo[0], lo[1],
+// hi[0], hi[1]) holds token kV4Slot<F>(s) of the four.
+template <int F>
+__device__ __forceinline__ constexpr int kV4Slot(int s) {
+  return F == kI4 ? ((s & 1) << 1) | (s >> 1) : s;
+}
 template <int F>
 __device__ __forceinline__ void codes4_to_f16x4(uint32_t w, bool hi_nibble, f16x2_t& lo,
                                                 f16x2_t& hi) {

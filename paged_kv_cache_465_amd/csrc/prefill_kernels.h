@@ -401,9 +401,10 @@ prefill_mfma_kernel(PrefillArgs a) {
         for (int st = 0; st < T; ++st)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const bool valid = EV * gq + 4 * st + i < rem && page_ok;
-            const float pv = valid ? p[st][i] * vs[st][i] : 0.0f;
-            if constexpr (ZP) zs += valid ? p[st][i] * vz[st][i] : 0.0f;
+            const int t = kV4Slot<F>(i);  // slot i holds token t, the V^T operand's order
+            const bool valid = EV * gq + 4 * st + t < rem && page_ok;
+            const float pv = valid ? p[st][t] * vs[st][t] : 0.0f;
+            if constexpr (ZP) zs += valid ? p[st][t] * vz[st][t] : 0.0f;
             pop[4 * st + i] = (_Float16)pv;
           }
         if constexpr (ZP) zacc[nt] = zacc[nt] * al + zs;
