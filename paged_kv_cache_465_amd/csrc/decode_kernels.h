@@ -773,18 +773,20 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
       if (jj < g) {
         const int64_t row = int64_t(wr.b) * a.num_q_heads + int64_t(wr.h) * g + jj;
         const int64_t pr = int64_t(wr.slot) * g + jj;
+        // one reciprocal per head (o * (1/l): within an ulp of o / l in float32)
+        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
 #pragma unroll
         for (int nc = 0; nc < NC; ++nc) {
           f32x4_t v = acc[nt][nc];
           if constexpr (ZP) v += zt;
+          v *= inv;
           const int d = 16 * nc + 4 * gq;
           if (wr.slot < 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              a.out[row * D + d + i] = f32_to_bf16_rne(lt > 0.0f ? v[i] / lt : 0.0f);
+            for (int i = 0; i < 4; ++i) a.out[row * D + d + i] = f32_to_bf16_rne(v[i]);
           } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a.part_o[pr * D + d + i] = lt > 0.0f ? v[i] / lt : 0.0f;
+            for (int i = 0; i < 4; ++i) a.part_o[pr * D + d + i] = v[i];
           }
         }
         if (wr.slot >= 0 && gq == 0) {
