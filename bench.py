@@ -63,7 +63,9 @@ def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed warmup steps (default: at least 5 and at least half a second "
+                        "of steps, so that the clocks have settled before the timed steps)")
     p.add_argument("--config", default="llama3_70b_full_cache")
     p.add_argument("--splits", type=int, default=0, help="forced split count (0 = planner)")
     p.add_argument("--plan", choices=("auto", "uniform", "balanced"), default="auto",
@@ -230,6 +232,22 @@ def run_gpu(args, kvp, cfg, case):
         log(f"[plan] balanced schedule {plan}")
     q_start = torch.from_numpy(case.q_start.astype(np.int32)).to(dev)
     max_q_len = int(np.diff(case.q_start).max())
+    prefill_order = None
+    prefill_plan = {"plan": "grid order"}
+    if chunked and args.plan != "uniform":
+        # longest-first workgroup order for the multi-query call, built once
+        # from the host lengths (the same every step)
+        t0 = time.perf_counter()
+        reps = 20
+        for _ in range(reps):
+            order = kvp.kvp_prefill_schedule(pool, case.q_start, case.ctx, Hq,
+                                             int(case.block_tables.shape[1]), max_q_len, max_ctx)
+        sched_host_us = (time.perf_counter() - t0) / reps * 1e6
+        prefill_order = torch.from_numpy(order).to(dev)
+        prefill_plan = {"plan": "longest-first", "order_entries": int(order.size),
+                        "order_padding": int(np.count_nonzero(order < 0)),
+                        "schedule_host_us": round(sched_host_us, 1)}
+        log(f"[plan] multi-query order {prefill_plan}")
     if windowed:
         wsb = kvp.kvp_decode_window_workspace_bytes(pool, B, Hq, max_ctx, cfg.sink_tokens,
                                                     cfg.window_tokens, args.splits)
@@ -244,7 +262,13 @@ def run_gpu(args, kvp, cfg, case):
             timed = probe is not None and probe[0] == i
             if timed:
                 probe[1].record()
-            if chunked:
+            if chunked and prefill_order is not None:
+                kvp.kvp_paged_attention_prefill_scheduled(pool, L.q, q_start, L.k, L.v, L.km,
+                                                          L.vm, bt, ctx, max_q_len, max_ctx,
+                                                          scale, prefill_order, L.out)
+                if timed:
+                    probe[2].record()
+            elif chunked:
                 kvp.kvp_paged_attention_prefill(pool, L.q, q_start, L.k, L.v, L.km, L.vm, bt, ctx,
                                                 max_q_len, max_ctx, scale, L.out)
                 if timed:
@@ -277,8 +301,21 @@ def run_gpu(args, kvp, cfg, case):
     if cfg.layers == 1:
         flush = torch.empty(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
 
-    for _ in range(args.warmup):
-        one_step()
+    if args.warmup is None:
+        # short steps: a few of them leave the device below its working clock,
+        # so warm up for at least half a second (and at least five steps)
+        n, t0 = 0, time.perf_counter()
+        while n < 5 or (time.perf_counter() - t0 < 0.5 and n < 20000):
+            if flush is not None:
+                flush.fill_(float(n))
+            one_step()
+            n += 1
+            if n >= 5:
+                torch.cuda.synchronize()
+        args.warmup = n
+    else:
+        for _ in range(args.warmup):
+            one_step()
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
 
@@ -314,7 +351,7 @@ def run_gpu(args, kvp, cfg, case):
         f"mean={step_ms.mean():.3f} min={step_ms.min():.3f}; split kernel mean "
         f"{kern_ms.mean() * 1e3:.1f} us min {kern_ms.min() * 1e3:.1f} us")
     res = {"ms_per_step": ms_per_step, "step_ms_events": step_ms, "kernel_ms": kern_ms,
-           "plan": plan, "num_splits": S, "balanced": balanced,
+           "plan": plan, "prefill_plan": prefill_plan, "num_splits": S, "balanced": balanced,
            "merge_launched": bool(balanced and sched.info.num_merge > 0)}
     return res, (pool, layers, bt, ctx)
 
@@ -642,7 +679,10 @@ def main(argv=None):
                    "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads,
                    "head_dim": cfg.head_dim, "page_size": cfg.page_size,
                    "kv_dtype": cfg.kv_dtype,
-                   **({"plan": "balanced", "num_bins": res["plan"]["num_bins"],
+                   **({"plan": res["prefill_plan"]["plan"],
+                       "order_entries": res["prefill_plan"].get("order_entries")}
+                      if is_chunked(cfg) else
+                      {"plan": "balanced", "num_bins": res["plan"]["num_bins"],
                        "num_merge": res["plan"]["num_merge"]} if res["balanced"]
                       else {"plan": "uniform", "num_splits": res["num_splits"]}),
                    **({"sink_tokens": cfg.sink_tokens, "window_tokens": cfg.window_tokens}
@@ -655,7 +695,8 @@ def main(argv=None):
         "bytes_per_step": {k: int(v) for k, v in sb.items()},
         "roofline": {**roof, "traffic": None, "kernel": kernel_name,
                      "kernel_us_mean": round(kern_us, 2),
-                     "timed": ("decode call (split kernel + merge kernel)"
+                     "timed": ("multi-query call (one kernel)" if is_chunked(cfg) else
+                               "decode call (split kernel + merge kernel)"
                                if res["merge_launched"] else
                                "window decode call (split kernel, + merge when split)"
                                if cfg.window_tokens > 0 and not res["balanced"]

@@ -467,6 +467,51 @@ kvp_status kvp_paged_attention_prefill(
     int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
     int32_t max_q_len, int32_t max_context_len, float scale, void* out, kvp_stream_t stream);
 
+/* ---- Multi-query attention along a longest-first order (host + device) ----
+ * The same section ("Cache-Aware Scheduling"): the chunks of one batch see
+ * caches of very different lengths, so the workgroups of the call above run
+ * for very different times, and in grid order the longest can start last
+ * and leave the device idle at the end.  A caller who knows the lengths on
+ * the host can build an order that starts the costliest workgroups first:
+ *   - the call's workgroups (units) are those of kvp_paged_attention_prefill
+ *     for the same pool, num_seqs, num_q_heads, max_blocks, max_q_len and
+ *     max_context_len; a unit's cost is the number of 64-key blocks its last
+ *     query row sees, plus one; units with no query row are left out;
+ *   - (sequence, KV head) items go to the eight XCDs (workgroup position
+ *     i runs on XCD i mod 8), costliest item first, each to the XCD with the
+ *     least cost so far, so that all units of an item share one L2;
+ *   - each XCD runs its units costliest first: entry 8r + x of the order is
+ *     the r-th unit of XCD x, or -1 when XCD x has fewer than r + 1 units.
+ * Results are bit-identical to the unordered call: each unit computes the
+ * same rows the same way. */
+
+/* Upper bound of the order's length (entries) for these arguments, any lengths. */
+kvp_status kvp_prefill_schedule_bound(const kvp_pool* pool, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t max_blocks, int32_t max_q_len,
+                                      int32_t max_context_len, int64_t* max_entries);
+/* Build the order (host).  q_start: host copy of the B + 1 chunk offsets
+ * (q_start[0] = 0, nondecreasing); context_lens: host copy of the B lengths
+ * (>= 0); the other arguments as the call will get them (KVP_E_INVAL /
+ * KVP_E_UNSUPPORTED as for that call).  *entries receives the order's length
+ * (a multiple of 8); sched is a host buffer of capacity int32 entries, and
+ * KVP_E_INVAL with *entries set is returned when that is too few. */
+kvp_status kvp_prefill_schedule(const kvp_pool* pool, const int32_t* q_start,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_q_heads, int32_t max_blocks, int32_t max_q_len,
+                                int32_t max_context_len, int32_t* sched, int64_t capacity,
+                                int64_t* entries);
+/* kvp_paged_attention_prefill with its workgroups in a built order: sched is
+ * a device copy of the entries entries (entries = 0 launches nothing).
+ * Entries outside [0, units) are skipped; an order built for other lengths
+ * or arguments still reads and writes only in bounds, but rows of units it
+ * does not name are not written. */
+kvp_status kvp_paged_attention_prefill_scheduled(
+    const kvp_pool* pool, const void* q, const int32_t* q_start, const void* k_pool,
+    const void* v_pool, const void* k_meta, const void* v_meta, const int32_t* block_tables,
+    int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+    int32_t max_q_len, int32_t max_context_len, float scale, const int32_t* sched,
+    int64_t entries, void* out, kvp_stream_t stream);
+
 /* ---- Decode in two phases (device) -----------------------------------------
  * The same attention as kvp_paged_attention_decode, with its two kernels
  * exposed separately: the split kernel writes one normalized partial per

@@ -500,6 +500,55 @@ def kvp_paged_attention_prefill(pool: Pool, q, q_start, k_pool, v_pool, k_meta, 
         "kvp_paged_attention_prefill")
 
 
+def kvp_prefill_schedule_bound(pool: Pool, num_seqs: int, num_q_heads: int, max_blocks: int,
+                               max_q_len: int, max_context_len: int) -> int:
+    """Upper bound of a multi-query order's length for these arguments."""
+    n = ctypes.c_int64()
+    _check(_L.kvp_prefill_schedule_bound(pool.handle, int(num_seqs), int(num_q_heads),
+                                         int(max_blocks), int(max_q_len), int(max_context_len),
+                                         ctypes.byref(n)), "kvp_prefill_schedule_bound")
+    return int(n.value)
+
+
+def kvp_prefill_schedule(pool: Pool, q_start, context_lens, num_q_heads: int, max_blocks: int,
+                         max_q_len: int, max_context_len: int) -> np.ndarray:
+    """Longest-first workgroup order (int32 host array, -1 = padding) of the
+    multi-query call for these host chunk offsets and lengths."""
+    qs = _i32(np.ascontiguousarray(q_start, dtype=np.int32))
+    ctx = _i32(np.ascontiguousarray(context_lens, dtype=np.int32))
+    if qs.size != ctx.size + 1:
+        raise ValueError("q_start must have B+1 entries")
+    cap = kvp_prefill_schedule_bound(pool, ctx.size, num_q_heads, max_blocks, max_q_len,
+                                     max_context_len)
+    buf = np.zeros(max(cap, 1), dtype=np.int32)
+    n = ctypes.c_int64()
+    _check(_L.kvp_prefill_schedule(pool.handle, _ptr(qs), _ptr(ctx), ctx.size, int(num_q_heads),
+                                   int(max_blocks), int(max_q_len), int(max_context_len),
+                                   _ptr(buf), cap, ctypes.byref(n)), "kvp_prefill_schedule")
+    return buf[: n.value].copy()
+
+
+def kvp_paged_attention_prefill_scheduled(pool: Pool, q, q_start, k_pool, v_pool, k_meta, v_meta,
+                                          block_tables, context_lens, max_q_len: int,
+                                          max_context_len: int, scale: float, sched_dev, out,
+                                          stream=None) -> None:
+    """kvp_paged_attention_prefill with its workgroups in the order sched_dev
+    (device int32 copy of kvp_prefill_schedule's result)."""
+    eb = pool.elem_bytes
+    B = int(context_lens.numel())
+    if q_start.numel() != B + 1 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("q_start must have B+1 entries and block_tables B rows")
+    _check_queries(pool, q, out, "prefill")
+    _check_pools(pool, k_pool, v_pool, k_meta, v_meta, "prefill")
+    _check(_L.kvp_paged_attention_prefill_scheduled(
+        pool.handle, _dev(q, "q", 2), _dev(q_start, "q_start", 4), _dev(k_pool, "k_pool", eb),
+        _dev(v_pool, "v_pool", eb), _dev(k_meta, "k_meta", 2), _dev(v_meta, "v_meta", 2),
+        _dev(block_tables, "block_tables", 4), int(block_tables.shape[1]),
+        _dev(context_lens, "context_lens", 4), B, int(q.shape[1]), int(max_q_len),
+        int(max_context_len), float(scale), _dev(sched_dev, "sched", 4), int(sched_dev.numel()),
+        _dev(out, "out", 2), _stream(stream)), "kvp_paged_attention_prefill_scheduled")
+
+
 def kvp_decode_partials_bytes(pool: Pool, num_seqs: int, num_q_heads: int,
                               max_context_len: int, num_splits_req: int = 0):
     """(num_splits, bytes) of the partials buffer the split kernel writes."""
@@ -576,7 +625,9 @@ __all__ = [
     "kvp_paged_attention_decode_scheduled",
     "Schedule", "ScheduleInfo",
     "kvp_seq_evict_window", "kvp_decode_window_workspace_bytes",
-    "kvp_paged_attention_decode_window", "kvp_paged_attention_prefill", "PrefixCache",
+    "kvp_paged_attention_decode_window", "kvp_paged_attention_prefill",
+    "kvp_prefill_schedule_bound", "kvp_prefill_schedule", "kvp_paged_attention_prefill_scheduled",
+    "PrefixCache",
     "kvp_prefix_cache_create", "kvp_prefix_cache_pages", "kvp_prefix_match",
     "kvp_prefix_insert", "kvp_prefix_evict", "kvp_seq_prepare_append", "kvp_copy_pages",
     "kvp_probe_read_chunks",

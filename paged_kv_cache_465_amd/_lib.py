@@ -8,6 +8,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvp.so")
 
 c_int32 = ctypes.c_int32
+c_int64 = ctypes.c_int64
 c_size_t = ctypes.c_size_t
 c_void_p = ctypes.c_void_p
 c_float = ctypes.c_float
@@ -75,6 +76,16 @@ PROTOTYPES = {
                                               c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                               c_int32, c_int32, c_int32, c_int32, c_float,
                                               c_void_p, c_void_p]),
+    "kvp_prefill_schedule_bound": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                             c_int32, ctypes.POINTER(c_int64)]),
+    "kvp_prefill_schedule": (c_int32, [c_void_p, P_int32, P_int32, c_int32, c_int32, c_int32,
+                                       c_int32, c_int32, P_int32, c_int64,
+                                       ctypes.POINTER(c_int64)]),
+    "kvp_paged_attention_prefill_scheduled": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p,
+                                                        c_void_p, c_void_p, c_void_p, c_void_p,
+                                                        c_int32, c_void_p, c_int32, c_int32,
+                                                        c_int32, c_int32, c_float, c_void_p,
+                                                        c_int64, c_void_p, c_void_p]),
     "kvp_prefix_cache_create": (c_int32, [c_void_p, ctypes.POINTER(c_void_p)]),
     "kvp_prefix_cache_destroy": (None, [c_void_p]),
     "kvp_prefix_cache_pages": (c_int32, [c_void_p]),

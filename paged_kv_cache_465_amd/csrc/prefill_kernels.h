@@ -49,7 +49,16 @@ struct PrefillArgs {
   int32_t num_seqs, max_blocks, num_kv_heads, num_q_heads, group, num_pages, tiles;
   int32_t ctx_cap;
   float scale_log2;
+  const int32_t* order;  // nullptr: natural grid order; else the unit of each workgroup
+  int32_t units;         // workgroups of the natural grid
 };
+
+// Index, in the natural grid, of the unit this workgroup computes: its own
+// position, or the entry a host-built schedule puts there.  Entries outside
+// [0, units) are padding (nothing to do).
+__device__ __forceinline__ int prefill_unit(const PrefillArgs& a) {
+  return a.order ? a.order[blockIdx.x] : int(blockIdx.x);
+}
 
 // Tiled mode is bound by instruction issue.  Two workgroups per CU (two
 // wavefronts per SIMD, <= 256 registers each) hide each other's dependency
@@ -112,10 +121,13 @@ prefill_mfma_kernel(PrefillArgs a) {
 
   // Grid: groups of eight (sequence, KV head) items; within a group the index
   // runs tile-major, so workgroup i goes to XCD i mod 8 = item mod 8 and all
-  // tiles of an item share one XCD (and its L2).
+  // tiles of an item share one XCD (and its L2).  A schedule permutes the
+  // units and keeps each item's tiles on one XCD.
+  const int unit = prefill_unit(a);
+  if (unit < 0 || unit >= a.units) return;   // the whole workgroup: no barrier reached
   const int per_group = 8 * a.tiles;
-  const int grp = blockIdx.x / per_group;
-  const int within = blockIdx.x - grp * per_group;
+  const int grp = unit / per_group;
+  const int within = unit - grp * per_group;
   const int tile = within >> 3;
   const int item = grp * 8 + (within & 7);
   if (item >= a.num_seqs * H) return;
@@ -595,9 +607,11 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && RT == 1) ? 2 : 1) void p
   const int H = a.num_kv_heads, g = a.group;
 
   // Grid as the tiled kernel: all tiles of an item on one XCD.
+  const int unit = prefill_unit(a);
+  if (unit < 0 || unit >= a.units) return;   // the whole workgroup: no barrier reached
   const int per_group = 8 * a.tiles;
-  const int grp = blockIdx.x / per_group;
-  const int within = blockIdx.x - grp * per_group;
+  const int grp = unit / per_group;
+  const int within = unit - grp * per_group;
   const int tile = within >> 3;
   const int item = grp * 8 + (within & 7);
   if (item >= a.num_seqs * H) return;

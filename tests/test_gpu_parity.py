@@ -265,7 +265,8 @@ def _sampled_check(kvp, cfg, seqs, splits=0, whole_pool=False):
     gc.append_history()
     gc.append_new()
     if cfg.q_len > 1 or cfg.q_len_hi > 1:
-        out = _run_prefill(kvp, gc, case)
+        # the launch the benchmark times: workgroups in the longest-first order
+        out = _run_prefill(kvp, gc, case, order=True)
     elif cfg.window_tokens > 0:
         mx = int(case.ctx.max())
         wsb = kvp.kvp_decode_window_workspace_bytes(gc.pool, case.B, cfg.num_q_heads, mx,
@@ -588,13 +589,23 @@ def _prefill_oracle(case):
     return _CACHE[key]
 
 
-def _run_prefill(kvp, gc, case, max_q_len=None):
-    c = case.cfg
+def _run_prefill(kvp, gc, case, max_q_len=None, order=None):
+    """The multi-query call in grid order, or along ``order`` (host int32
+    array, as kvp_prefill_schedule builds it; True: build it here)."""
     qs = dev32(case.q_start)
     out = torch.full_like(gc.q, int(np.uint16(0x7FC0).view(np.int16)))
     mq = int(np.diff(case.q_start).max()) if max_q_len is None else max_q_len
-    kvp.kvp_paged_attention_prefill(gc.pool, gc.q, qs, gc.k_pool, gc.v_pool, gc.k_meta, gc.v_meta,
-                                    gc.bt, gc.ctx, mq, int(case.ctx.max()), float(case.scale), out)
+    mx = int(case.ctx.max())
+    if order is None:
+        kvp.kvp_paged_attention_prefill(gc.pool, gc.q, qs, gc.k_pool, gc.v_pool, gc.k_meta,
+                                        gc.v_meta, gc.bt, gc.ctx, mq, mx, float(case.scale), out)
+    else:
+        if order is True:
+            order = kvp.kvp_prefill_schedule(gc.pool, case.q_start, case.ctx,
+                                             case.cfg.num_q_heads, int(gc.bt.shape[1]), mq, mx)
+        kvp.kvp_paged_attention_prefill_scheduled(gc.pool, gc.q, qs, gc.k_pool, gc.v_pool,
+                                                  gc.k_meta, gc.v_meta, gc.bt, gc.ctx, mq, mx,
+                                                  float(case.scale), dev32(order), out)
     torch.cuda.synchronize()
     return out.cpu().numpy().view(np.uint16)
 
@@ -622,6 +633,32 @@ def test_prefill_matches_oracle(kvp, cfg):
     # instance (another compilation of the same arithmetic): still within tolerance
     big = _run_prefill(kvp, gc, case, max_q_len=int(np.diff(case.q_start).max()) + 40)
     assert_close(big, ref, cfg.name + " generous max_q_len")
+    gc.close()
+
+
+@pytest.mark.parametrize("cfg", PREFILL, ids=lambda c: c.name)
+def test_prefill_scheduled_bit_identical(kvp, cfg):
+    """Along the longest-first order every workgroup computes the same rows
+    the same way, only at another time: outputs bit-identical to the grid
+    order (and so within tolerance of the oracle).  Padding (-1) and entries
+    past the grid are skipped; an order naming each unit twice writes the
+    same bits twice."""
+    case = _case(cfg)
+    k, v, km, vm, ref = _prefill_oracle(case)
+    mq = int(np.diff(case.q_start).max())
+    gc = GpuCase(kvp, case)
+    gc.upload(k, v, km, vm)
+    order = kvp.kvp_prefill_schedule(gc.pool, case.q_start, case.ctx, cfg.num_q_heads,
+                                     int(gc.bt.shape[1]), mq, int(case.ctx.max()))
+    log(f"[prefill scheduled] {cfg.name} entries={order.size} "
+        f"padding={int(np.count_nonzero(order < 0))}")
+    base = _run_prefill(kvp, gc, case)
+    got = _run_prefill(kvp, gc, case, order=order)
+    assert np.array_equal(got, base)
+    assert_close(got, ref, cfg.name + " scheduled")
+    stray = np.concatenate([np.full(8, -1), order, np.full(8, 1 << 30)]).astype(np.int32)
+    assert np.array_equal(_run_prefill(kvp, gc, case, order=stray), base)
+    assert np.array_equal(_run_prefill(kvp, gc, case, order=np.concatenate([order, order])), base)
     gc.close()
 
 

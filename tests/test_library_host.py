@@ -607,3 +607,143 @@ def test_read_probe_argument_checks(kvp):
     assert call(-1, 4096, 2, 4) == kvp.KVP_E_INVAL
     assert call(4, 4096, 2, 0) == kvp.KVP_E_INVAL
     assert call(0, 4096, 2, 4) == kvp.KVP_OK
+
+
+# ---- longest-first order of the multi-query call -------------------------------------------
+def _prefill_units(dtype, B, Hkv, Hq, max_q_len, q_start, ctx):
+    """The multi-query call's natural grid, as its header states it: workgroups
+    of 128 rows (bfloat16), 64 or 32 rows (quantized, by chunk size) or one
+    per (sequence, KV head) when every chunk's rows fit 32; groups of eight
+    items, tile-major.  Returns {unit: (item, cost)} for units with rows."""
+    g = Hq // Hkv
+    max_rows = max_q_len * g
+    split = max_rows <= 32
+    quant = dtype != "bf16"
+    nt = (2 if max_rows > 16 else 1) if split else (2 if max_rows >= 128 or not quant else 1)
+    rows_wg = 16 * nt if split else (64 * nt if quant else 128)
+    tiles = -(-max_rows // rows_wg)
+    items = B * Hkv
+    wgs = -(-items // 8) * 8 * tiles
+    units = {}
+    for u in range(wgs):
+        grp, within = divmod(u, 8 * tiles)
+        tile, item = within >> 3, grp * 8 + (within & 7)
+        if item >= items:
+            continue
+        b = item // Hkv
+        qlen = int(q_start[b + 1] - q_start[b])
+        rows, row0 = qlen * g, 0 if split else tile * rows_wg
+        if qlen <= 0 or row0 >= rows:
+            continue
+        n = int(ctx[b])
+        pos_last = min(n - qlen + (min(row0 + rows_wg, rows) - 1) // g, n - 1)
+        units[u] = (item, (pos_last // 64 + 1 if pos_last >= 0 else 0) + 1)
+    return units, wgs
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_prefill_schedule_is_a_longest_first_permutation(kvp, seed):
+    """Every unit with rows appears once; the length is a multiple of 8 with
+    -1 padding; all units of an item sit in one XCD class (position mod 8);
+    each class runs its units costliest first; class costs differ by at most
+    the costliest item (greedy assignment, costliest item first)."""
+    rng = np.random.default_rng(500 + seed)
+    dtype = ("bf16", "int8", "int4", "fp8")[seed % 4]
+    Hkv = (1, 2, 8)[seed % 3]
+    Hq = Hkv * int(rng.choice([1, 4, 8]))
+    B = int(rng.integers(1, 40))
+    P = (16, 32)[seed % 2]
+    qlen = rng.integers(0, (600, 40, 4)[seed % 3] + 1, B)
+    ctx = qlen + rng.integers(0, 5000, B)
+    q_start = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
+    max_q_len = max(int(qlen.max()), 1)
+    max_blocks = int(-(-int(ctx.max()) // P)) + 1
+    pool = kvp.kvp_pool_create(kvp.make_desc(16, P, Hkv, 128, dtype))
+    order = kvp.kvp_prefill_schedule(pool, q_start, ctx.astype(np.int32), Hq, max_blocks,
+                                     max_q_len, int(ctx.max()))
+    units, wgs = _prefill_units(dtype, B, Hkv, Hq, max_q_len, q_start, ctx)
+    assert order.size % 8 == 0
+    assert order.size <= kvp.kvp_prefill_schedule_bound(pool, B, Hq, max_blocks, max_q_len,
+                                                        int(ctx.max()))
+    named = order[order >= 0]
+    assert sorted(named.tolist()) == sorted(units)
+    assert (order[order < 0] == -1).all()
+    cls = {}
+    for pos, u in enumerate(order.tolist()):
+        if u >= 0:
+            assert cls.setdefault(units[u][0], pos % 8) == pos % 8, "an item split over XCDs"
+    load = np.zeros(8, np.int64)
+    for x in range(8):
+        col = order[x::8]
+        col = col[col >= 0]
+        costs = [units[u][1] for u in col.tolist()]
+        assert costs == sorted(costs, reverse=True)
+        # padding only after the class's last unit
+        assert (order[x::8][: len(col)] >= 0).all()
+        load[x] = sum(costs)
+    item_cost = {}
+    for it, c in units.values():
+        item_cost[it] = item_cost.get(it, 0) + c
+    if item_cost:
+        assert load.max() - load.min() <= max(item_cost.values())
+    pool.close()
+
+
+def test_prefill_schedule_shortens_the_chunked_prefill_tail(kvp):
+    """The chunked-prefill workload (8 sequences, 512-token chunks on 1.5k-7.5k
+    cached tokens, Llama-3-8B-shaped layer): simulated as greedy list
+    scheduling over 64 workgroup slots per XCD, the order finishes sooner than
+    the grid order."""
+    from workloads import CHUNKED_PREFILL
+    cfg = CHUNKED_PREFILL
+    case = make_case(cfg, with_data=False)
+    mq = int(np.diff(case.q_start).max())
+    mb = case.block_tables.shape[1]
+    pool = kvp.kvp_pool_create(kvp.make_desc(16, cfg.page_size, cfg.num_kv_heads, cfg.head_dim,
+                                             "bf16"))
+    order = kvp.kvp_prefill_schedule(pool, case.q_start, case.ctx, cfg.num_q_heads, mb, mq,
+                                     int(case.ctx.max()))
+    units, wgs = _prefill_units("bf16", case.B, cfg.num_kv_heads, cfg.num_q_heads, mq,
+                                case.q_start, case.ctx)
+
+    def makespan(seq):
+        import heapq
+        h = [0] * 64
+        for u in seq:
+            if u in units:
+                heapq.heappush(h, heapq.heappop(h) + units[u][1])
+        return max(h)
+    grid = max(makespan(range(x, wgs, 8)) for x in range(8))
+    ordered = max(makespan(order[x::8].tolist()) for x in range(8))
+    assert ordered < grid
+    pool.close()
+
+
+def test_prefill_schedule_rejects_bad_arguments(kvp):
+    import ctypes
+    from paged_kv_cache_465_amd import _lib
+    lib = _lib.load()
+    pool = kvp.kvp_pool_create(kvp.make_desc(16, 16, 2, 64, "bf16"))
+    n = ctypes.c_int64()
+    buf = np.zeros(1024, np.int32)
+    P = lambda a: a.ctypes.data_as(_lib.P_int32)  # noqa: E731
+    ok_qs, ok_ctx = np.array([0, 3, 5], np.int32), np.array([10, 20], np.int32)
+    assert lib.kvp_prefill_schedule(pool.handle, P(ok_qs), P(ok_ctx), 2, 8, 4, 3, 20, P(buf),
+                                    buf.size, ctypes.byref(n)) == kvp.KVP_OK
+    assert n.value > 0 and n.value % 8 == 0
+    for qs, ctx in (([1, 3, 5], [10, 20]), ([0, 3, 2], [10, 20]), ([0, 3, 5], [10, -1])):
+        qs, ctx = np.array(qs, np.int32), np.array(ctx, np.int32)
+        assert lib.kvp_prefill_schedule(pool.handle, P(qs), P(ctx), 2, 8, 4, 3, 20, P(buf),
+                                        buf.size, ctypes.byref(n)) == kvp.KVP_E_INVAL
+    # too small a buffer: KVP_E_INVAL with the needed length reported
+    assert lib.kvp_prefill_schedule(pool.handle, P(ok_qs), P(ok_ctx), 2, 8, 4, 3, 20, P(buf), 1,
+                                    ctypes.byref(n)) == kvp.KVP_E_INVAL
+    assert n.value > 1
+    # max_context_len beyond the table, heads not a multiple of the KV heads
+    assert lib.kvp_prefill_schedule(pool.handle, P(ok_qs), P(ok_ctx), 2, 8, 1, 3, 20, P(buf),
+                                    buf.size, ctypes.byref(n)) == kvp.KVP_E_INVAL
+    assert lib.kvp_prefill_schedule(pool.handle, P(ok_qs), P(ok_ctx), 2, 3, 4, 3, 20, P(buf),
+                                    buf.size, ctypes.byref(n)) == kvp.KVP_E_INVAL
+    assert lib.kvp_prefill_schedule_bound(None, 2, 8, 4, 3, 20, ctypes.byref(n)) == \
+        kvp.KVP_E_INVAL
+    pool.close()
