@@ -1139,13 +1139,26 @@ __global__ __launch_bounds__(valu_max_threads(P, D, G)) void decode_valu_kernel(
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of split partials, one wavefront per output row:
 // M = max_s m_s; w_s = l_s 2^(m_s - M); out = sum_s w_s o_s / sum_s w_s.
-// Partial s of the row: o at po + s*so (D floats), (m, l) at pml + s*sml.
-template <int D>
-__device__ __forceinline__ void lse_merge_row(const float* __restrict__ po, int64_t so,
-                                              const float* __restrict__ pml, int64_t sml, int S,
-                                              uint16_t* __restrict__ out_row) {
+// Partial s of the row: o at po + s*so (D floats), (m, l) at pml + s*sml;
+// S >= 1.
+template <int D, int kPre>
+__device__ __forceinline__ void lse_merge_row_pre(const float* __restrict__ po, int64_t so,
+                                                  const float* __restrict__ pml, int64_t sml,
+                                                  int S, uint16_t* __restrict__ out_row) {
   constexpr int E = D / 64;
   const int lane = threadIdx.x & 63;
+  // The first kPre slots' partials are loaded before anything else: they do
+  // not depend on the weights, so their loads, those of (m, l) and the
+  // maximum's exchange all overlap and the row pays one memory latency.
+  // (Slots past S reload slot S - 1; their weights are 0, and adding the
+  // zero terms leaves L and o unchanged.)
+  float pre[kPre][E];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int64_t si = min(i, S - 1);
+#pragma unroll
+    for (int e = 0; e < E; ++e) pre[i][e] = po[si * so + lane * E + e];
+  }
   // (m, l) of slot `lane` (the first 64 slots), loaded together; M over all
   float m0 = -INFINITY, l0 = 0.0f;
   if (lane < S) {
@@ -1160,6 +1173,15 @@ __device__ __forceinline__ void lse_merge_row(const float* __restrict__ po, int6
   for (int e = 0; e < E; ++e) o[e] = 0.0f;
   float L = 0.0f;
   if (M != -INFINITY) {
+    // weight of slot `lane`; empty slots (l = 0, m = -inf) weigh 0
+    const float w0 = l0 > 0.0f ? l0 * fast_exp2(m0 - M) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w0), i));
+      L += wi;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] += wi > 0.0f ? wi * pre[i][e] : 0.0f;
+    }
     for (int s0 = 0; s0 < S; s0 += 64) {
       float ms = m0, ls = l0;
       if (s0 > 0) {
@@ -1173,7 +1195,7 @@ __device__ __forceinline__ void lse_merge_row(const float* __restrict__ po, int6
       // the partials' loads do not depend on the weights, so consecutive
       // slots' loads are in flight together
 #pragma unroll 4
-      for (int i = 0; i < n; ++i) {
+      for (int i = s0 == 0 ? kPre : 0; i < n; ++i) {
         const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i));
         L += wi;
         const float* p = po + (s0 + i) * so + lane * E;
@@ -1187,6 +1209,20 @@ __device__ __forceinline__ void lse_merge_row(const float* __restrict__ po, int6
   }
 #pragma unroll
   for (int e = 0; e < E; ++e) out_row[lane * E + e] = f32_to_bf16_rne(L > 0.0f ? o[e] / L : 0.0f);
+}
+// Sixteen slots' partials loaded ahead, thirty-two for rows with more slots.
+// Measured, the whole scheduled decode call (stream kernel + merge): 16
+// sequences of 16k-32k INT4 tokens (about 24 slots per merged row) 107.4 us
+// loading 4 slots ahead, 104.5 with 16, 101.4 with 32; a ragged Llama-3-8B
+// bfloat16 layer (2-3 slots per row) 119.0, 118.4 and 119.8.
+template <int D>
+__device__ __forceinline__ void lse_merge_row(const float* __restrict__ po, int64_t so,
+                                              const float* __restrict__ pml, int64_t sml, int S,
+                                              uint16_t* __restrict__ out_row) {
+  if (S > 16)
+    lse_merge_row_pre<D, 32>(po, so, pml, sml, S, out_row);
+  else
+    lse_merge_row_pre<D, 16>(po, so, pml, sml, S, out_row);
 }
 
 // Uniform plan: row = b*H_q + j holds its S partials at (row*S + s).
