@@ -479,7 +479,10 @@ kvp_status kvp_paged_attention_prefill(
  *     query row sees, plus one; units with no query row are left out;
  *   - (sequence, KV head) items go to the eight XCDs (workgroup position
  *     i runs on XCD i mod 8), costliest item first, each to the XCD with the
- *     least cost so far, so that all units of an item share one L2;
+ *     least cost so far, so that all units of an item share one L2; when
+ *     that would leave one XCD more than 1.2 times the mean cost (fewer items
+ *     than XCDs, or a few dominant ones), the units are shared out the same
+ *     way instead, costliest first;
  *   - each XCD runs its units costliest first: entry 8r + x of the order is
  *     the r-th unit of XCD x, or -1 when XCD x has fewer than r + 1 units.
  * Results are bit-identical to the unordered call: each unit computes the

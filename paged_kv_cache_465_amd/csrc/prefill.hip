@@ -141,8 +141,9 @@ extern "C" kvp_status kvp_prefill_schedule_bound(const kvp_pool* pool, int32_t n
 
 // Longest-first order of the natural grid's units (see the header): a unit's
 // cost is the number of 64-key blocks its last row sees, plus one; items go to
-// the XCD with the least cost so far (costliest item first), and each XCD
-// runs its units costliest first.
+// the XCD with the least cost so far (costliest item first), or, when that
+// leaves one XCD more than 1.2x the mean, the units do; each XCD runs its
+// units costliest first.
 extern "C" kvp_status kvp_prefill_schedule(const kvp_pool* pool, const int32_t* q_start,
                                            const int32_t* context_lens, int32_t num_seqs,
                                            int32_t num_q_heads, int32_t max_blocks,
@@ -182,20 +183,43 @@ extern "C" kvp_status kvp_prefill_schedule(const kvp_pool* pool, const int32_t* 
   std::stable_sort(items.begin(), items.end(), [&](int64_t x, int64_t y) {
     return item_cost[size_t(x)] > item_cost[size_t(y)];
   });
-  std::vector<int> xcd_of(size_t(geo.items), 0);
-  int64_t load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int64_t it : items) {
+  auto least_loaded = [](const int64_t* load) {
     int x = 0;
     for (int k = 1; k < 8; ++k)
       if (load[k] < load[x]) x = k;
+    return x;
+  };
+  std::vector<int> xcd_of(size_t(geo.items), 0);
+  int64_t load[8] = {0, 0, 0, 0, 0, 0, 0, 0}, total = 0;
+  for (int64_t it : items) {
+    const int x = least_loaded(load);
     xcd_of[size_t(it)] = x;
     load[x] += item_cost[size_t(it)];
+    total += item_cost[size_t(it)];
   }
+  // Too few (or too uneven) items to share out whole: one XCD would carry
+  // more than 1.2x the mean.  Then the units themselves are shared out,
+  // costliest first, and an item's tiles no longer share one L2.
+  const bool by_unit = 10 * 8 * *std::max_element(load, load + 8) > 12 * total;
   std::vector<int64_t> lists[8];
-  for (int64_t u = 0; u < geo.wgs; ++u) {
-    if (cost[size_t(u)] == 0) continue;
-    const int64_t grp = u / per_group, within = u - grp * per_group;
-    lists[xcd_of[size_t(grp * 8 + (within & 7))]].push_back(u);
+  if (by_unit) {
+    std::vector<int64_t> order_u;
+    for (int64_t u = 0; u < geo.wgs; ++u)
+      if (cost[size_t(u)] > 0) order_u.push_back(u);
+    std::stable_sort(order_u.begin(), order_u.end(),
+                     [&](int64_t x, int64_t y) { return cost[size_t(x)] > cost[size_t(y)]; });
+    std::fill(load, load + 8, 0);
+    for (int64_t u : order_u) {
+      const int x = least_loaded(load);
+      lists[x].push_back(u);
+      load[x] += cost[size_t(u)];
+    }
+  } else {
+    for (int64_t u = 0; u < geo.wgs; ++u) {
+      if (cost[size_t(u)] == 0) continue;
+      const int64_t grp = u / per_group, within = u - grp * per_group;
+      lists[xcd_of[size_t(grp * 8 + (within & 7))]].push_back(u);
+    }
   }
   size_t longest = 0;
   for (auto& l : lists) {
