@@ -289,11 +289,14 @@ kvp_status kvp_decode_workspace_bytes(const kvp_pool* pool, int32_t num_seqs,
  * stored and the softmax weights p are rounded to bfloat16 before P.V.  For
  * INT8, INT4 and FP8 pools the codes convert to float16 exactly, q is rounded
  * to float16 (so |q| <= 65504 is a precondition, and elements below 2^-14
- * keep fewer bits), and each weight times the row's V scale, p * s, is
- * rounded to float16 before P.V (products below 2^-14 keep fewer bits, so
- * rows with tiny V scales lose relative precision; FP8 rows whose scale
- * times 2^8 exceeds 65504, i.e. max|v| beyond about 114,000, overflow).  The
- * vector-ALU path (g < 4) computes in float32 throughout.
+ * keep fewer bits), and each weight times the token's V scale, p * s, is
+ * rounded to float16 before P.V.  The weights carry a power of two chosen
+ * from the largest V scale seen so far in the sequence (raised, with the
+ * running sums rescaled exactly, when a page brings a larger one), so these
+ * operands stay below 2^15 and above float16's subnormals for V scales from
+ * about 2^-85 to the largest float16 (tested with V rows 1e-4 and 3e4 times
+ * unit draws); only products p * s below about 2^-28 times the largest V
+ * scale lose bits.  The vector-ALU path (g < 4) computes in float32 throughout.
  * ctx_b == 0 gives out = 0.  max_context_len is a host-side upper bound of
  * context_lens (1 .. max_blocks*P), used to plan the split.  workspace must
  * be a device buffer of at least kvp_decode_workspace_bytes (may be NULL when

@@ -322,6 +322,8 @@ __device__ __forceinline__ MfmaLaneOffsets<F, P, D> mfma_lane_offsets(int r, int
 // nt*16 + r (zero past the group), the 8 channels q_channel(kk, gq) of each
 // k-step; for quantized pools float16 values and, for the zero-point term,
 // qsum = the sum of the head's channels (float32, from the bfloat16 values).
+// A negative scale is applied as |scale| on -q (exact), so that scores are
+// always |scale| times a raw dot product and their maximum is the raw one's.
 template <int F, int P, int D, int NT>
 __device__ __forceinline__ void mfma_load_q(const DecodeArgs& a, int b, int h, int r, int gq,
                                             typename MfmaOps<F, P, D>::A (&qop)[NT][MfmaShape<F, P, D>::KK],
@@ -329,6 +331,7 @@ __device__ __forceinline__ void mfma_load_q(const DecodeArgs& a, int b, int h, i
   using S = MfmaShape<F, P, D>;
   constexpr bool Q = FmtInfo<F>::quant, ZP = FmtInfo<F>::zero;
   const int g = a.group;
+  const uint32_t qflip = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int jj = nt * 16 + r;
@@ -339,6 +342,10 @@ __device__ __forceinline__ void mfma_load_q(const DecodeArgs& a, int b, int h, i
     for (int kk = 0; kk < S::KK; ++kk) {
       const int d0 = S::q_channel(kk, gq);
       uint4 raw = live ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
+      raw.x ^= qflip;
+      raw.y ^= qflip;
+      raw.z ^= qflip;
+      raw.w ^= qflip;
       if constexpr (!Q) {
         qop[nt][kk] = __builtin_bit_cast(bf16x8_t, raw);
       } else {
@@ -375,35 +382,49 @@ __device__ __forceinline__ void mfma_load_page(const DecodeArgs& a, int phys, in
   const size_t tile_bytes = size_t(P) * S::RB;
   const char* kp = static_cast<const char*>(a.k_pool) + tile * tile_bytes;
   const char* vp = static_cast<const char*>(a.v_pool) + tile * tile_bytes;
+  // the per-token metadata first: the V scales decide the page's operand
+  // offset before its scores are computed, and waiting for them then does
+  // not wait for the page's codes
+  if constexpr (FmtInfo<F>::quant) {
+    const char* km = reinterpret_cast<const char*>(a.k_meta) + tile * (P * 4);
+    const char* vm = reinterpret_cast<const char*>(a.v_meta) + tile * (P * 4);
+#pragma unroll
+    for (int st = 0; st < S::T; ++st) {
+      R.vm[st] = load_stream<uint4>(vm + o.moff + st * 16);
+      R.km[st] = load_stream<uint4>(km + o.moff + st * 16);
+    }
+  }
 #pragma unroll
   for (int st = 0; st < S::T; ++st)
 #pragma unroll
     for (int i = 0; i < S::KN; ++i) R.k[st][i] = load_stream<KLoad>(kp + o.koff[st] + i * 64);
 #pragma unroll
   for (int nc = 0; nc < S::NC; ++nc) R.v[nc] = load_stream<VLoad>(vp + o.voff + nc * vstride);
-  if constexpr (FmtInfo<F>::quant) {
-    const char* km = reinterpret_cast<const char*>(a.k_meta) + tile * (P * 4);
-    const char* vm = reinterpret_cast<const char*>(a.v_meta) + tile * (P * 4);
-#pragma unroll
-    for (int st = 0; st < S::T; ++st) {
-      R.km[st] = load_stream<uint4>(km + o.moff + st * 16);
-      R.vm[st] = load_stream<uint4>(vm + o.moff + st * 16);
-    }
-  }
 }
 
 // Page k of range wr (its loads in R): S^T = K q^T per head tile, online
 // softmax, O^T += V^T P^T, for the lane's item state (q operands qop, q
 // channel sum qsum for the zero-point term, running max m, sum lsum,
-// zero-point sum zacc, accumulators acc).  Absent pages are skipped; on a
-// partial page (some token past the sequence or outside the window) those
-// tokens' scores are -inf and their V^T values (or V scales) 0.
+// zero-point sum zacc, accumulators acc, V-scale exponent vexp).  Absent
+// pages are skipped; on a partial page (some token past the sequence or
+// outside the window) those tokens' scores are -inf and their V^T values (or
+// V scales) 0.
+//
+// Quantized pools: a token's P.V operand is its weight times its V scale,
+// rounded to float16.  Small V scales would put it among float16's
+// subnormals, large ones (FP8 codes carry 2^8) past its range, so the
+// weights carry a power of two 2^c: vexp is the largest (biased float32)
+// exponent of a V scale the item has seen and c = vexp_offset(vexp), which
+// keeps every operand below 2^15.  lsum, zacc and acc are all in units of
+// 2^c (their ratio, the output, does not depend on it); when a page raises
+// vexp, c drops and the running sums are rescaled with the softmax factor.
 template <int F, int P, int D, int NT>
 __device__ __forceinline__ void mfma_page(const DecodeArgs& a, const PageRegs<F, P, D>& R,
                                           const WorkRange& wr, int k, int r, int gq,
                                           const typename MfmaOps<F, P, D>::A (&qop)[NT][MfmaShape<F, P, D>::KK],
                                           const float (&qsum)[NT], float (&m)[NT], float (&lsum)[NT],
-                                          float (&zacc)[NT], f32x4_t (&acc)[NT][MfmaShape<F, P, D>::NC]) {
+                                          float (&zacc)[NT], f32x4_t (&acc)[NT][MfmaShape<F, P, D>::NC],
+                                          int& vexp) {
   using S = MfmaShape<F, P, D>;
   using FI = FmtInfo<F>;
   constexpr bool Q = FI::quant, ZP = FI::zero;
@@ -487,6 +508,27 @@ __device__ __forceinline__ void mfma_page(const DecodeArgs& a, const PageRegs<F,
       }
     }
   }
+  // the offset c, raised only when some V scale of the page (tokens not kept
+  // have 0) has a larger exponent than any before in the item (wave-uniform)
+  int cnew = vexp_offset(vexp), cdelta = 0;
+  if constexpr (Q) {
+    float vmax = 0.0f;
+#pragma unroll
+    for (int st = 0; st < T; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vmax = fmaxf(vmax, vs[st][i]);
+    if (wave_any(__float_as_uint(vmax) >= uint32_t(vexp + 1) << 23)) {
+      vmax = group4_max(vmax);
+      const int e = __builtin_amdgcn_readfirstlane(int(__float_as_uint(vmax) >> 23));
+      const int cold = cnew;
+      vexp = max(vexp, e);
+      cnew = vexp_offset(vexp);
+      cdelta = cnew - cold;
+    }
+  }
+  // scores are cs times a raw dot product; the multiply rides in the
+  // exponent's fma (cs > 0 keeps masked scores at -inf)
+  const float cs = fmaxf(fabsf(a.scale_log2), 1e-30f);
 
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -499,11 +541,11 @@ __device__ __forceinline__ void mfma_page(const DecodeArgs& a, const PageRegs<F,
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (ZP)
-          x[st][i] = (ks[st][i] * sc[i] + kz[st][i] * qsum[nt]) * a.scale_log2;
+          x[st][i] = ks[st][i] * sc[i] + kz[st][i] * qsum[nt];
         else if constexpr (Q)
-          x[st][i] = ks[st][i] * sc[i] * a.scale_log2;
+          x[st][i] = ks[st][i] * sc[i];
         else
-          x[st][i] = sc[i] * a.scale_log2;
+          x[st][i] = sc[i];
       }
     }
     if (tail) {
@@ -519,16 +561,19 @@ __device__ __forceinline__ void mfma_page(const DecodeArgs& a, const PageRegs<F,
 #pragma unroll
       for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, x[st][i]);
     mloc = group4_max(mloc);
-    const float mnew = fmaxf(m[nt], mloc);
-    const float al = fast_exp2(m[nt] - mnew);
+    // m: the running maximum of the scaled scores (base-2 units)
+    const float mnew = fmaxf(m[nt], mloc * cs);
+    const float al = fast_exp2(Q ? (m[nt] - mnew) + float(cdelta) : m[nt] - mnew);
     m[nt] = mnew;
+    // weights 2^(score - m + c)
+    const float mref = Q ? mnew - float(cnew) : mnew;
     float p[T][4];
     float ps = 0.0f;
 #pragma unroll
     for (int st = 0; st < T; ++st)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[st][i] = fast_exp2(x[st][i] - mnew);
+        p[st][i] = fast_exp2(fmaf(x[st][i], cs, -mref));
         ps += p[st][i];
       }
     lsum[nt] = lsum[nt] * al + ps;
@@ -598,6 +643,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const WorkRange& 
 
   float m[NT], lsum[NT], zacc[NT];
   f32x4_t acc[NT][NC];
+  int vexp = 0;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     m[nt] = -INFINITY;
@@ -608,7 +654,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const WorkRange& 
   }
 
   auto compute = [&](const PageRegs<F, P, D>& R, int k) {
-    mfma_page<F, P, D, NT>(a, R, wr, k, r, gq, qop, qsum, m, lsum, zacc, acc);
+    mfma_page<F, P, D, NT>(a, R, wr, k, r, gq, qop, qsum, m, lsum, zacc, acc, vexp);
   };
   if (wr.cnt > 0) {
     PageRegs<F, P, D> ring[DEPTH];
@@ -626,13 +672,14 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const WorkRange& 
     }
   }
 
-  // Wavefront partials -> LDS.
+  // Wavefront partials -> LDS, in plain units (each wavefront has its own 2^c).
   float* sm_o = smem;                 // [W][g][D]
   float* sm_m = smem + W * g * D;     // [W][HP]
   float* sm_l = sm_m + W * HP;        // [W][HP]
+  const float unc = exp2_int(-vexp_offset(vexp));
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const float lt = group4_sum(lsum[nt]);
+    const float lt = group4_sum(lsum[nt]) * unc;
     const float zt = ZP ? group4_sum(zacc[nt]) : 0.0f;
     const int jj = nt * 16 + r;
     if (jj < g) {
@@ -640,6 +687,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const WorkRange& 
       for (int nc = 0; nc < NC; ++nc) {
         f32x4_t v = acc[nt][nc];
         if constexpr (ZP) v += zt;
+        v *= unc;
         *reinterpret_cast<f32x4_t*>(sm_o + (wave * g + jj) * D + 16 * nc + 4 * gq) = v;
       }
       if (gq == 0) {
@@ -752,8 +800,10 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
   float qsum[NT];
   float m[NT], lsum[NT], zacc[NT];
   f32x4_t acc[NT][NC];
+  int vexp = 0;
   auto begin_item = [&](const WorkRange& wr) __attribute__((always_inline)) {
     mfma_load_q<F, P, D, NT>(a, wr.b, wr.h, r, gq, qop, qsum);
+    vexp = 0;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       m[nt] = -INFINITY;
@@ -791,7 +841,7 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
         }
         if (wr.slot >= 0 && gq == 0) {
           a.part_ml[pr * 2] = m[nt];
-          a.part_ml[pr * 2 + 1] = lt;
+          a.part_ml[pr * 2 + 1] = lt * exp2_int(-vexp_offset(vexp));  // plain units
         }
       }
     }
@@ -799,7 +849,7 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
 
   auto compute = [&](const PageRegs<F, P, D>& R, const WorkRange& wr,
                      int k) __attribute__((always_inline)) {
-    mfma_page<F, P, D, NT>(a, R, wr, k, r, gq, qop, qsum, m, lsum, zacc, acc);
+    mfma_page<F, P, D, NT>(a, R, wr, k, r, gq, qop, qsum, m, lsum, zacc, acc, vexp);
   };
 
   // compute side: every valid item in order (empty ones give 0 or an empty
@@ -1283,9 +1333,13 @@ template <int F, int P, int D, int NT> constexpr int mfma_depth_nt() {
 // one page with more.
 template <int F, int P, int D, int NT> constexpr int stream_depth() {
   // (the stream kernel's item bookkeeping costs registers too: four head
-  // tiles of 16-token pages also keep at most two pages)
-  constexpr int d1 = (P == 16 && D == 128 && NT == 4 && mfma_depth_nt<F, P, D, NT>() > 2)
+  // tiles of 16-token pages also keep at most two pages, and quantized ones
+  // with four head tiles one page (INT4 with 32-token pages of 64 channels:
+  // two), which keeps them free of spills)
+  constexpr bool q4 = F != kBF16 && NT == 4;
+  constexpr int d0 = (P == 16 && D == 128 && NT == 4 && mfma_depth_nt<F, P, D, NT>() > 2)
                          ? 2 : mfma_depth_nt<F, P, D, NT>();
+  constexpr int d1 = q4 ? (d0 < (F == kI4 ? 2 : 1) ? d0 : (F == kI4 ? 2 : 1)) : d0;
   return stream_waves_per_simd<F, NT>() == 1 ? d1 : 1;
 }
 

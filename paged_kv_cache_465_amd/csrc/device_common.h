@@ -115,6 +115,16 @@ __device__ __forceinline__ float group4_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Power-of-two exponent c for the float16 P.V operands of quantized pools,
+// from the largest biased float32 exponent e of the V scales seen so far (0:
+// none yet).  V scales are below 2^(e - 126) and softmax weights at most 1,
+// so weight * 2^c * scale stays below 2^15 (inside float16, and above its
+// subnormals unless the weight itself is tiny) with c = 141 - e; c is capped
+// at 100 so that sums of weights times 2^c stay far inside float32's range.
+__device__ __forceinline__ int vexp_offset(int e) { return e == 0 ? 0 : min(141 - e, 100); }
+// 2^n as a float32 (-126 <= n <= 127)
+__device__ __forceinline__ float exp2_int(int n) { return __uint_as_float(uint32_t(n + 127) << 23); }
+
 // Four signed int8 codes (one dword) -> four exact float16 values.
 // fp16 bits 0x6400|u are 1024 + u for u < 1024; with u = code + 128 (the
 // sign bit flipped) subtracting 1152 gives the code exactly.

@@ -235,6 +235,17 @@ prefill_mfma_kernel(PrefillArgs a) {
     const char* kps[T];
 #pragma unroll
     for (int st = 0; st < T; ++st) kps[st] = kbase + tile_of(ksub[st]) * tile_bytes;
+    // the per-token metadata first: the V scales decide the step's operand
+    // offset before its scores, and waiting for them does not wait for codes
+    if constexpr (Q) {
+      const char* km = reinterpret_cast<const char*>(a.k_meta) + t * (P * 4);
+      const char* vm = reinterpret_cast<const char*>(a.v_meta) + t * (P * 4);
+#pragma unroll
+      for (int st = 0; st < T; ++st) {
+        R.vm[st] = *reinterpret_cast<const uint4*>(vm + moff + st * 16);
+        R.km[st] = *reinterpret_cast<const uint4*>(km + moff + st * 16);
+      }
+    }
     // tiled: the workgroup's wavefronts share each page through L2 (ordinary
     // loads); split: each page is read once (non-temporal loads)
     if constexpr (!SPLIT) {
@@ -254,19 +265,14 @@ prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
       for (int nc = 0; nc < NC; ++nc) R.v[nc] = load_stream<VLoad>(vp + voff + nc * vstride);
     }
-    if constexpr (Q) {
-      const char* km = reinterpret_cast<const char*>(a.k_meta) + t * (P * 4);
-      const char* vm = reinterpret_cast<const char*>(a.v_meta) + t * (P * 4);
-#pragma unroll
-      for (int st = 0; st < T; ++st) {
-        R.km[st] = *reinterpret_cast<const uint4*>(km + moff + st * 16);
-        R.vm[st] = *reinterpret_cast<const uint4*>(vm + moff + st * 16);
-      }
-    }
   };
 
   float m[NT], lsum[NT], zacc[NT];
   f32x4_t acc[NT][NC];
+  // quantized pools: the largest V-scale exponent seen, which sets the
+  // power-of-two offset 2^c the weights carry (vexp_offset); lsum, zacc and
+  // acc are in units of 2^c
+  int vexp = 0;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     m[nt] = -INFINITY;
@@ -352,6 +358,28 @@ prefill_mfma_kernel(PrefillArgs a) {
         }
       }
     }
+    // the offset c, raised only when a V scale of this step's tokens (those
+    // inside the sequence, on present pages) has a larger exponent than any
+    // before (wave-uniform)
+    int cnew = vexp_offset(vexp), cdelta = 0;
+    if constexpr (Q) {
+      float vmax = 0.0f;
+#pragma unroll
+      for (int st = 0; st < T; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool valid = unmasked || (EV * gq + 4 * st + i < rem && page_ok);
+          vmax = fmaxf(vmax, valid ? vs[st][i] : 0.0f);
+        }
+      if (wave_any(__float_as_uint(vmax) >= uint32_t(vexp + 1) << 23)) {
+        vmax = group4_max(vmax);
+        const int e = __builtin_amdgcn_readfirstlane(int(__float_as_uint(vmax) >> 23));
+        const int cold = cnew;
+        vexp = max(vexp, e);
+        cnew = vexp_offset(vexp);
+        cdelta = cnew - cold;
+      }
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float x[T][4];
@@ -388,15 +416,17 @@ prefill_mfma_kernel(PrefillArgs a) {
       // a row none of whose positions has been seen yet keeps m = -inf: use 0
       // as the reference so that no (-inf) - (-inf) arises
       const float mref = mnew == -INFINITY ? 0.0f : mnew;
-      const float al = fast_exp2(m[nt] - mref);
+      const float al = fast_exp2(Q ? (m[nt] - mref) + float(cdelta) : m[nt] - mref);
       m[nt] = mnew;
+      // weights 2^(score - m + c)
+      const float mref_c = Q ? mref - float(cnew) : mref;
       float p[T][4];
       float ps = 0.0f;
 #pragma unroll
       for (int st = 0; st < T; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[st][i] = fast_exp2(x[st][i] - mref);
+          p[st][i] = fast_exp2(x[st][i] - mref_c);
           ps += p[st][i];
         }
       lsum[nt] = lsum[nt] * al + ps;
@@ -455,16 +485,18 @@ prefill_mfma_kernel(PrefillArgs a) {
     // register layout; wave 0 merges them into its own and writes the rows
     __shared__ f32x4_t sm_o[3][NT][NC][64];
     __shared__ float sm_m[3][NT][64], sm_l[3][NT][64];
+    // each wavefront's sums in plain units (their offsets 2^c differ)
+    const float unc = exp2_int(-vexp_offset(vexp));
     if (wave > 0) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const float lt = group4_sum(lsum[nt]);
+        const float lt = group4_sum(lsum[nt]) * unc;
         const float zt = ZP ? group4_sum(zacc[nt]) : 0.0f;
 #pragma unroll
         for (int nc = 0; nc < NC; ++nc) {
           f32x4_t v = acc[nt][nc];
           if constexpr (ZP) v += zt;
-          sm_o[wave - 1][nt][nc][lane] = v;
+          sm_o[wave - 1][nt][nc][lane] = v * unc;
         }
         sm_m[wave - 1][nt][lane] = m[nt];
         sm_l[wave - 1][nt][lane] = lt;
@@ -474,7 +506,7 @@ prefill_mfma_kernel(PrefillArgs a) {
     if (wave > 0) return;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const float l0 = group4_sum(lsum[nt]);
+      const float l0 = group4_sum(lsum[nt]) * unc;
       const float z0 = ZP ? group4_sum(zacc[nt]) : 0.0f;
       float M = m[nt];
 #pragma unroll
@@ -494,7 +526,7 @@ prefill_mfma_kernel(PrefillArgs a) {
       for (int nc = 0; nc < NC; ++nc) {
         f32x4_t v = acc[nt][nc];
         if constexpr (ZP) v += z0;
-        v *= f[0];
+        v *= f[0] * unc;
 #pragma unroll
         for (int w = 0; w < 3; ++w) v += sm_o[w][nt][nc][lane] * f[w + 1];
         acc[nt][nc] = v;

@@ -13,8 +13,8 @@ import pytest
 import torch
 
 import oracle
-from workloads import (FP8_LONG, INT4_LONG, LLAMA3_8B_LAYER, POISON_F16, POISON_I8, TINY,
-                       f32_to_bf16_bits, make_case, variant)
+from workloads import (FP8_LONG, INT4_LONG, INT8_LONG, LLAMA3_8B_LAYER, POISON_F16, POISON_I8,
+                       TINY, f32_to_bf16_bits, make_case, variant)
 
 from .casetools import assert_close, assert_within_one_rounding, layout_of, oracle_pools
 from .gpu_harness import GpuCase, dev16, dev32, log
@@ -292,3 +292,66 @@ def test_full_int4_long(kvp):
 def test_full_fp8_long(kvp):
     """16 sequences of 16k-32k tokens, FP8 pool with outlier channels."""
     _sampled_check(kvp, FP8_LONG, seqs=(0, 7, 15))
+
+
+# ---- V scales far from 1 (every quantized format) -----------------------------------------
+def _vgain(f, gain, tag, **kw):
+    return variant(INT8_LONG, name=f"{f}_v{tag}", kv_dtype=f, batch=4, ctx_lo=300, ctx_hi=2500,
+                   v_gain=gain, outlier_channels=0, seed=468000 + len(tag) + ord(f[-1]), **kw)
+
+
+VGAIN = [_vgain(f, g, t) for f in ("int8", "int4", "fp8")
+         for g, t in ((1e-4, "1e-4"), (3e4, "3e4"))]
+VGAIN_PREFILL = [_vgain(f, g, t + f"_q{L}", q_len=L) for f in ("int8", "fp8")
+                 for g, t in ((1e-4, "1e-4"), (3e4, "3e4")) for L in (4, 64)]
+
+
+def _assert_close_gain(out_bits, ref, gain, what):
+    """The attention bar scaled with V: outputs are linear in V, so a run whose
+    V rows are gain times unit-variance draws is held to rel-L2 5e-3 and to
+    max-abs 1e-2 * gain."""
+    from .casetools import MAX_ABS_TOL, REL_L2_TOL
+    got = (np.asarray(out_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    got = got.astype(np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite outputs"
+    d = np.abs(got - ref)
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    assert rel <= REL_L2_TOL and float(d.max()) <= MAX_ABS_TOL * gain, \
+        f"{what}: max_abs={float(d.max()):.3e} (bar {MAX_ABS_TOL * gain:.1e}) rel_l2={rel:.3e}"
+    return float(d.max()), rel
+
+
+@pytest.mark.parametrize("cfg", VGAIN, ids=lambda c: c.name)
+def test_decode_v_scale_range(kvp, cfg):
+    """V rows 1e-4 or 3e4 times unit draws (INT8 scales near 2^-20, FP8
+    scales past 2^8): the matrix-core kernels carry a power-of-two offset on
+    the weights, so the float16 P.V operands neither fall among float16's
+    subnormals nor overflow.  Every plan against the oracle, the bar scaled
+    with V."""
+    case = _case(cfg)
+    k, v, km, vm, ref = _oracle(case)
+    gc = GpuCase(kvp, case)
+    gc.upload(k, v, km, vm)
+    for name, out in (("S=1", gc.decode(num_splits=1)), ("S=3", gc.decode(num_splits=3)),
+                      ("balanced", gc.decode_scheduled())):
+        m, r = _assert_close_gain(out, ref, cfg.v_gain, f"{cfg.name} {name}")
+        log(f"[v scale] {cfg.name} {name} max_abs={m:.2e} rel_l2={r:.2e}")
+    gc.close()
+
+
+@pytest.mark.parametrize("cfg", VGAIN_PREFILL, ids=lambda c: c.name)
+def test_prefill_v_scale_range(kvp, cfg):
+    """The same V ranges through the multi-query kernel (4-token chunks: pages
+    split across the wavefronts; 64-token chunks: row tiles)."""
+    case = _case(cfg)
+    k, v, km, vm = oracle_pools(case)
+    ref = oracle.paged_prefill(layout_of(case), case.q, case.q_start, k, v, km, vm,
+                               case.block_tables, case.ctx, case.scale)
+    gc = GpuCase(kvp, case)
+    gc.upload(k, v, km, vm)
+    from .test_gpu_parity import _run_prefill
+    for name, order in (("grid", None), ("ordered", True)):
+        m, r = _assert_close_gain(_run_prefill(kvp, gc, case, order=order), ref, cfg.v_gain,
+                                  f"{cfg.name} {name}")
+        log(f"[v scale prefill] {cfg.name} {name} max_abs={m:.2e} rel_l2={r:.2e}")
+    gc.close()

@@ -40,6 +40,7 @@ class DecodeConfig:
     outlier_channels: int = 0       # channels (of H_kv*D) scaled by outlier_gain, K and V drawn separately
     outlier_gain: float = 1.0
     q_gain: float = 1.0
+    v_gain: float = 1.0             # V rows (history and new) times v_gain (small or large V scales)
     q_len: int = 1                  # new query tokens per sequence (chunked prefill / verification)
     q_len_hi: int = 0               # > q_len: per-sequence chunk lengths ~ U{q_len..q_len_hi}
     sink_tokens: int = 0            # with window_tokens > 0: the cache holds only positions

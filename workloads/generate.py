@@ -15,6 +15,7 @@ draws taken in this order:
 5. history K rows then history V rows: standard normal ``[T, H_kv, D]``, drawn
    in chunks of 65,536 rows in order, outlier channels times ``outlier_gain``;
 6. the new token's K then V rows: standard normal ``[B, H_kv, D]`` (outliers too).
+   V rows (history and new) are multiplied by ``v_gain`` before the outliers.
 
 Every float32 draw is rounded to bfloat16 (round to nearest even) and kept as
 its raw 16-bit pattern.  The config with ``device_data`` draws q and K/V on the
@@ -185,9 +186,11 @@ def make_case(cfg: DecodeConfig, with_data: bool = True) -> DecodeCase:
     case.hist_pos = np.concatenate(poss) if poss else np.zeros(0, np.int32)
     T = int(case.hist_pos.shape[0])
     case.hist_k = _normal_bf16(rng, (T, Hkv, D), outliers=out_k, gain_out=cfg.outlier_gain)
-    case.hist_v = _normal_bf16(rng, (T, Hkv, D), outliers=out_v, gain_out=cfg.outlier_gain)
+    case.hist_v = _normal_bf16(rng, (T, Hkv, D), gain=cfg.v_gain, outliers=out_v,
+                               gain_out=cfg.outlier_gain)
     case.new_k = _normal_bf16(rng, (N, Hkv, D), outliers=out_k, gain_out=cfg.outlier_gain)
-    case.new_v = _normal_bf16(rng, (N, Hkv, D), outliers=out_v, gain_out=cfg.outlier_gain)
+    case.new_v = _normal_bf16(rng, (N, Hkv, D), gain=cfg.v_gain, outliers=out_v,
+                              gain_out=cfg.outlier_gain)
     return case
 
 
