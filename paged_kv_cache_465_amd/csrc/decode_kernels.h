@@ -324,32 +324,45 @@ __device__ __forceinline__ MfmaLaneOffsets<F, P, D> mfma_lane_offsets(int r, int
 // qsum = the sum of the head's channels (float32, from the bfloat16 values).
 // A negative scale is applied as |scale| on -q (exact), so that scores are
 // always |scale| times a raw dot product and their maximum is the raw one's.
+// In two steps: the loads (raw bfloat16 words), then the conversion.
 template <int F, int P, int D, int NT>
-__device__ __forceinline__ void mfma_load_q(const DecodeArgs& a, int b, int h, int r, int gq,
-                                            typename MfmaOps<F, P, D>::A (&qop)[NT][MfmaShape<F, P, D>::KK],
-                                            float (&qsum)[NT]) {
+__device__ __forceinline__ void mfma_q_raw(const DecodeArgs& a, int b, int h, int r, int gq,
+                                           uint4 (&raw)[NT][MfmaShape<F, P, D>::KK]) {
   using S = MfmaShape<F, P, D>;
-  constexpr bool Q = FmtInfo<F>::quant, ZP = FmtInfo<F>::zero;
   const int g = a.group;
-  const uint32_t qflip = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int jj = nt * 16 + r;
     const bool live = jj < g;
     const uint16_t* qrow = a.q + (int64_t(b) * a.num_q_heads + int64_t(h) * g + (live ? jj : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < S::KK; ++kk)
+      raw[nt][kk] = live ? *reinterpret_cast<const uint4*>(qrow + S::q_channel(kk, gq))
+                         : make_uint4(0, 0, 0, 0);
+  }
+}
+template <int F, int P, int D, int NT>
+__device__ __forceinline__ void mfma_q_convert(const DecodeArgs& a,
+                                               const uint4 (&raw)[NT][MfmaShape<F, P, D>::KK],
+                                               typename MfmaOps<F, P, D>::A (&qop)[NT][MfmaShape<F, P, D>::KK],
+                                               float (&qsum)[NT]) {
+  using S = MfmaShape<F, P, D>;
+  constexpr bool Q = FmtInfo<F>::quant, ZP = FmtInfo<F>::zero;
+  const uint32_t qflip = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
     float qs = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < S::KK; ++kk) {
-      const int d0 = S::q_channel(kk, gq);
-      uint4 raw = live ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
-      raw.x ^= qflip;
-      raw.y ^= qflip;
-      raw.z ^= qflip;
-      raw.w ^= qflip;
+      uint4 w = raw[nt][kk];
+      w.x ^= qflip;
+      w.y ^= qflip;
+      w.z ^= qflip;
+      w.w ^= qflip;
       if constexpr (!Q) {
-        qop[nt][kk] = __builtin_bit_cast(bf16x8_t, raw);
+        qop[nt][kk] = __builtin_bit_cast(bf16x8_t, w);
       } else {
-        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+        const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
         f16x8_t v;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -363,6 +376,14 @@ __device__ __forceinline__ void mfma_load_q(const DecodeArgs& a, int b, int h, i
     }
     qsum[nt] = ZP ? group4_sum(qs) : 0.0f;
   }
+}
+template <int F, int P, int D, int NT>
+__device__ __forceinline__ void mfma_load_q(const DecodeArgs& a, int b, int h, int r, int gq,
+                                            typename MfmaOps<F, P, D>::A (&qop)[NT][MfmaShape<F, P, D>::KK],
+                                            float (&qsum)[NT]) {
+  uint4 raw[NT][MfmaShape<F, P, D>::KK];
+  mfma_q_raw<F, P, D, NT>(a, b, h, r, gq, raw);
+  mfma_q_convert<F, P, D, NT>(a, raw, qop, qsum);
 }
 
 // Issue the loads of one (page, head) tile into a ring slot.  phys is the raw
@@ -801,8 +822,28 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
   float m[NT], lsum[NT], zacc[NT];
   f32x4_t acc[NT][NC];
   int vexp = 0;
-  auto begin_item = [&](const WorkRange& wr) __attribute__((always_inline)) {
-    mfma_load_q<F, P, D, NT>(a, wr.b, wr.h, r, gq, qop, qsum);
+  // One head tile (NT = 1, and two wavefronts per SIMD at most: INT4's three
+  // have no registers to spare): the next item with pages has its q loaded
+  // while the current one is computed, so an item's first page does not wait
+  // on the q loads issued behind the ring's pages.
+  constexpr bool QPRE = NT == 1 && stream_waves_per_simd<F, NT>() <= 2;
+  uint4 qnext[NT][KK];
+  auto prefetch_q = [&](int from) __attribute__((always_inline)) {
+    StreamPos qp;
+    qp.item = from;
+    stream_seek<P>(a, qp, end, true);
+    if (qp.item < end) mfma_q_raw<F, P, D, NT>(a, qp.wr.b, qp.wr.h, r, gq, qnext);
+  };
+  auto begin_item = [&](const WorkRange& wr, int item) __attribute__((always_inline)) {
+    if constexpr (QPRE) {
+      // items with pages come in the same order as the prefetches
+      if (wr.cnt > 0) {
+        mfma_q_convert<F, P, D, NT>(a, qnext, qop, qsum);
+        prefetch_q(item + 1);
+      }
+    } else {
+      mfma_load_q<F, P, D, NT>(a, wr.b, wr.h, r, gq, qop, qsum);
+    }
     vexp = 0;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -864,11 +905,12 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
   stream_seek<P>(a, cp, end, false);
   if (issued_all) {  // no pages at all: only empty items
     for (; cp.item < end; ++cp.item, stream_seek<P>(a, cp, end, false)) {
-      begin_item(cp.wr);
+      begin_item(cp.wr, cp.item);
       finish_item(cp.wr);
     }
     return;
   }
+  if constexpr (QPRE) prefetch_q(cp.item);
   PageRegs<F, P, D> ring[DEPTH];
 #pragma unroll
   for (int s = 0; s < DEPTH; ++s) issue(ring[s]);
@@ -909,7 +951,7 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
   };
   int slot0 = 0;
   for (; cp.item < end; ++cp.item, stream_seek<P>(a, cp, end, false)) {
-    begin_item(cp.wr);
+    begin_item(cp.wr, cp.item);
     if (cp.wr.cnt > 0) {
       pages_from_slot(slot0);
       slot0 = (slot0 + cp.wr.cnt) % DEPTH;
@@ -1334,9 +1376,10 @@ template <int F, int P, int D, int NT> constexpr int mfma_depth_nt() {
 template <int F, int P, int D, int NT> constexpr int stream_depth() {
   // (the stream kernel's item bookkeeping costs registers too: four head
   // tiles of 16-token pages also keep at most two pages, and quantized ones
-  // with four head tiles one page (INT4 with 32-token pages of 64 channels:
-  // two), which keeps them free of spills)
-  constexpr bool q4 = F != kBF16 && NT == 4;
+  // with four head tiles, and bfloat16 ones of 16-token pages of 128
+  // channels, one page (INT4 with 32-token pages of 64 channels: two), which
+  // keeps them free of spills)
+  constexpr bool q4 = NT == 4 && (F != kBF16 || (P == 16 && D == 128));
   constexpr int d0 = (P == 16 && D == 128 && NT == 4 && mfma_depth_nt<F, P, D, NT>() > 2)
                          ? 2 : mfma_depth_nt<F, P, D, NT>();
   constexpr int d1 = q4 ? (d0 < (F == kI4 ? 2 : 1) ? d0 : (F == kI4 ? 2 : 1)) : d0;
