@@ -296,7 +296,13 @@ kvp_status kvp_decode_workspace_bytes(const kvp_pool* pool, int32_t num_seqs,
  * operands stay below 2^15 and above float16's subnormals for V scales from
  * about 2^-85 to the largest float16 (tested with V rows 1e-4 and 3e4 times
  * unit draws); only products p * s below about 2^-28 times the largest V
- * scale lose bits.  The vector-ALU path (g < 4) computes in float32 throughout.
+ * scale lose bits.  INT4 K codes enter as code + 1032 (exact in float16) and
+ * 1032 times the sum of q's float16 values starts each score's float32
+ * accumulation at the negated offset, so the accumulator holds values of
+ * about 1032 |sum of q| and its roundings are relative to that (for unit q,
+ * about 1e-3 absolute on raw dot products of ~50, below the float16
+ * rounding of q and p * s).  The vector-ALU path (g < 4) computes in float32
+ * throughout.
  * ctx_b == 0 gives out = 0.  max_context_len is a host-side upper bound of
  * context_lens (1 .. max_blocks*P), used to plan the split.  workspace must
  * be a device buffer of at least kvp_decode_workspace_bytes (may be NULL when

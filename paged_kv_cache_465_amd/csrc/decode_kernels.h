@@ -321,7 +321,8 @@ __device__ __forceinline__ MfmaLaneOffsets<F, P, D> mfma_lane_offsets(int r, int
 // q^T of an item as the B operand of S^T = K q^T: lane (r, gq) holds head
 // nt*16 + r (zero past the group), the 8 channels q_channel(kk, gq) of each
 // k-step; for quantized pools float16 values and, for the zero-point term,
-// qsum = the sum of the head's channels (float32, from the bfloat16 values).
+// qsum = the sum of the head's channels (float32, from the bfloat16 values;
+// for INT4 from their float16 operand values).
 // A negative scale is applied as |scale| on -q (exact), so that scores are
 // always |scale| times a raw dot product and their maximum is the raw one's.
 // In two steps: the loads (raw bfloat16 words), then the conversion.
@@ -369,7 +370,9 @@ __device__ __forceinline__ void mfma_q_convert(const DecodeArgs& a,
           const int c = F == kI4 ? kI4KSlot(e) : e;  // the K operand's channel order
           const float f = bf16_to_f32((w4[c >> 1] >> (16 * (c & 1))) & 0xffffu);
           v[e] = (_Float16)f;
-          qs += f;
+          // INT4: the sum of the operand's own values, which the K codes'
+          // offset is removed with (the same as f's unless q is tiny)
+          qs += F == kI4 ? float(v[e]) : f;
         }
         qop[nt][kk] = v;
       }
@@ -439,13 +442,14 @@ __device__ __forceinline__ void mfma_load_page(const DecodeArgs& a, int phys, in
 // keeps every operand below 2^15.  lsum, zacc and acc are all in units of
 // 2^c (their ratio, the output, does not depend on it); when a page raises
 // vexp, c drops and the running sums are rescaled with the softmax factor.
-template <int F, int P, int D, int NT>
+struct PageVInRegs {};  // mfma_page's default: the V^T bytes are in R.v
+template <int F, int P, int D, int NT, typename VFetch = PageVInRegs>
 __device__ __forceinline__ void mfma_page(const DecodeArgs& a, const PageRegs<F, P, D>& R,
                                           const WorkRange& wr, int k, int r, int gq,
                                           const typename MfmaOps<F, P, D>::A (&qop)[NT][MfmaShape<F, P, D>::KK],
                                           const float (&qsum)[NT], float (&m)[NT], float (&lsum)[NT],
                                           float (&zacc)[NT], f32x4_t (&acc)[NT][MfmaShape<F, P, D>::NC],
-                                          int& vexp) {
+                                          int& vexp, const VFetch& vfetch = VFetch{}) {
   using S = MfmaShape<F, P, D>;
   using FI = FmtInfo<F>;
   constexpr bool Q = FI::quant, ZP = FI::zero;
@@ -470,15 +474,18 @@ __device__ __forceinline__ void mfma_page(const DecodeArgs& a, const PageRegs<F,
       __builtin_memcpy(w, R.k[st], KB);
       constexpr int DW = F == kI4 ? 1 : 2;  // dwords per 8 channels
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kop[st][kk] = codes8_to_f16x8<F>(w + DW * kk);
+      for (int kk = 0; kk < KK; ++kk) kop[st][kk] = codes8_to_f16x8_offset<F>(w + DW * kk);
     }
   }
-  // V^T operands.
+  // V^T operands: from R.v, or (late_v) from vfetch right before P.V, so
+  // that the V^T bytes do not hold registers while the scores are computed
+  constexpr bool late_v = !std::is_same<VFetch, PageVInRegs>::value;
   OpPV vop[NC];
+  auto build_vop = [&](const VLoad (&vraw)[NC]) __attribute__((always_inline)) {
 #pragma unroll
   for (int nc = 0; nc < NC; ++nc) {
     if constexpr (!Q) {
-      VLoad raw = R.v[nc];
+      VLoad raw = vraw[nc];
       if (tail) {
         // rows past the sequence may hold anything (NaN): zero them so 0*x stays 0
         uint32_t wv[EV / 2];
@@ -492,7 +499,7 @@ __device__ __forceinline__ void mfma_page(const DecodeArgs& a, const PageRegs<F,
       vop[nc] = __builtin_bit_cast(OpPV, raw);
     } else {
       uint32_t wv[EV / 4];
-      __builtin_memcpy(wv, &R.v[nc], sizeof(R.v[nc]));
+      __builtin_memcpy(wv, &vraw[nc], sizeof(vraw[nc]));
       OpPV v;
 #pragma unroll
       for (int i = 0; i < EV / 4; ++i) {
@@ -506,6 +513,8 @@ __device__ __forceinline__ void mfma_page(const DecodeArgs& a, const PageRegs<F,
       vop[nc] = v;
     }
   }
+  };
+  if constexpr (!late_v) build_vop(R.v);
   // Per-token scale (and zero point) of this lane's rows.  The V metadata of
   // tokens not kept may hold anything (NaN): it is zeroed, so that their zero
   // weights give exact zeros below.
@@ -557,6 +566,11 @@ __device__ __forceinline__ void mfma_page(const DecodeArgs& a, const PageRegs<F,
 #pragma unroll
     for (int st = 0; st < T; ++st) {
       f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (FI::koff != 0.0f) {
+        // sum over channels of q (code + koff), minus koff sum(q): q . code
+        const float c0 = -FI::koff * qsum[nt];
+        sc = f32x4_t{c0, c0, c0, c0};
+      }
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) sc = mfma_16x16x32(kop[st][kk], qop[nt][kk], sc);
 #pragma unroll
@@ -624,6 +638,13 @@ __device__ __forceinline__ void mfma_page(const DecodeArgs& a, const PageRegs<F,
       for (int st = 0; st < T; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i) pop[4 * st + i] = (__bf16)p[st][i];
+    }
+    if constexpr (late_v) {
+      if (nt == 0) {
+        VLoad vraw[NC];
+        vfetch(vraw);
+        build_vop(vraw);
+      }
     }
 #pragma unroll
     for (int nc = 0; nc < NC; ++nc) {
@@ -775,6 +796,141 @@ template <int F, int NT> constexpr int stream_waves_per_simd() {
   return F == kBF16 || NT != 1 ? 1 : (F == kI4 ? 3 : 2);
 }
 
+// LDS page ring.  A wavefront's page loads are bounded by the registers they
+// land in: three INT4 wavefronts per SIMD with one page each keep about 13 MB
+// in flight on the chip, and at the loaded latency that sustains ~4.5 TB/s.
+// The loads can land in LDS instead (global_load_lds: each lane's 4 or 16
+// bytes go to the LDS base in m0 plus lane * size), where a wavefront keeps
+// several pages in flight for no registers; the page being computed is read
+// from its slot into the same registers the register ring would hold.  Used
+// by the stream kernel for INT4 pools with 32-token pages of 128 channels
+// (one head tile): 16 sequences of 16k-32k tokens measured 100.5 -> 96.4 us
+// for the whole decode call, and 94.6 with the K codes' offset left in (the
+// ring moved the limit to the vector ALUs).  The same ring measured 3-5%
+// slower for INT8, FP8 (two wavefronts per SIMD, two slots) and bfloat16
+// (one wavefront per SIMD, four slots): fewer wavefronts leave the slot
+// reads' latency exposed.
+template <int F, int P, int D, int NT> constexpr bool stream_lds_ring() {
+  return F == kI4 && P == 32 && D == 128 && NT == 1;
+}
+template <int F, int P, int D> struct LdsSlot {
+  static constexpr int TB = P * MfmaShape<F, P, D>::RB;     // one K (or V) tile
+  static constexpr int MB = FmtInfo<F>::quant ? P * 4 : 0;  // its (scale, zero) pairs
+  static constexpr int SB = 2 * TB + 2 * MB;                // K, V, K meta, V meta
+  // pages in flight per wavefront: the slots of a compute unit's twelve
+  // INT4 wavefronts (three per SIMD) fill 153 of its 160 KiB of LDS
+  static constexpr int depth = 3;
+  static constexpr int k_loads = TB / 1024, v_loads = TB / 1024;
+  static constexpr int loads = (MB ? 1 : 0) + k_loads + v_loads;  // copies per page
+};
+// One copy instruction: `bytes` (4 or 16) per lane from the lane's global
+// address to LDS byte m0 + lane * bytes, with the streaming cache policy.
+// The copies and the slot reads below are asm statements that are not
+// volatile (the compiler treats its own LDS-copy builtin, and any volatile
+// asm, as writing all memory, and would then read the read-only tables with
+// vector loads, whose waits wait for every copy in flight); they are kept in
+// program order by one token that each takes and passes on ("+s"), and the
+// last wait takes it too.  The compiler does not count these copies in its
+// own load-counter waits, which only makes those waits longer (the counter
+// retires loads in order); the slot reads wait for them explicitly.  (An SALU
+// write of m0 needs one wait state before a copy reads it.)
+template <int bytes>
+__device__ __forceinline__ void lds_copy(const void* src, uint32_t lds_addr, uint32_t& tok) {
+  static_assert(bytes == 4 || bytes == 16, "dword or dwordx4 copies");
+  if constexpr (bytes == 16)
+    asm("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off nt"
+        : "+s"(tok)
+        : "s"(lds_addr), "v"(src)
+        : "m0");
+  else
+    asm("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off nt"
+        : "+s"(tok)
+        : "s"(lds_addr), "v"(src)
+        : "m0");
+}
+
+// Copy one (page, head) tile into an LDS slot as flat byte ranges (lane l's
+// bytes at l * size): both metadata rows (K's 128 bytes, then V's), the K
+// tile, the V^T tile.  Out of range table entries read page 0 (the pattern
+// stays fixed) and return -1.
+template <int F, int P, int D>
+__device__ __forceinline__ int lds_load_page(const DecodeArgs& a, int phys, int h, int lane,
+                                             uint32_t slot, uint32_t& tok) {
+  using L = LdsSlot<F, P, D>;
+  static_assert(L::TB % 1024 == 0 && (L::MB == 0 || L::MB == 128),
+                "1 KiB copies and one metadata row");
+  const bool ok = unsigned(phys) < unsigned(a.num_pages);
+  const int64_t tile = int64_t(ok ? phys : 0) * a.num_kv_heads + h;
+  if constexpr (L::MB > 0) {
+    const char* km = reinterpret_cast<const char*>(a.k_meta) + tile * L::MB;
+    const char* vm = reinterpret_cast<const char*>(a.v_meta) + tile * L::MB;
+    const char* mp = lane < 32 ? km + 4 * lane : vm + 4 * (lane - 32);
+    lds_copy<4>(mp, slot + 2 * L::TB, tok);
+  }
+  const char* kp = static_cast<const char*>(a.k_pool) + tile * L::TB + 16 * lane;
+  const char* vp = static_cast<const char*>(a.v_pool) + tile * L::TB + 16 * lane;
+#pragma unroll
+  for (int i = 0; i < L::k_loads; ++i) lds_copy<16>(kp + 1024 * i, slot + 1024 * i, tok);
+#pragma unroll
+  for (int i = 0; i < L::v_loads; ++i)
+    lds_copy<16>(vp + 1024 * i, slot + L::TB + 1024 * i, tok);
+  return ok ? phys : -1;
+}
+
+// Read a slot into a lane's page registers (the register ring's layout), in
+// two parts: K and the metadata when the page is computed, V^T right before
+// its P.V products.  Each part first waits until its copies have landed:
+// `later` copy instructions were issued after them (any other memory
+// operation issued since only makes the wait longer); its reads and both
+// waits sit in one asm block, so no read is in flight when it ends.  Lane
+// addresses: ak = the lane's first K piece, am = its metadata, av = its V^T
+// bytes; the offsets in the reads follow the register ring's loads
+// (mfma_load_page) for each shape.
+template <int F, int P, int D> struct LdsRead;
+// INT4, 32-token pages: K sub-tile 1 is four token rows (256 bytes) past
+// sub-tile 0; V^T chunk nc at nc * 8P = 256 bytes (read2 offsets count 8
+// bytes); metadata: K's rows at 0 and 16, V's 128 bytes later.
+template <> struct LdsRead<kI4, 32, 128> {
+  using S = MfmaShape<kI4, 32, 128>;
+  static_assert(S::T == 2 && S::KN == 1 && S::NC == 8 && S::VB == 8 && S::RB == 64,
+                "32-token INT4 pages of 128 channels");
+  template <int later>
+  __device__ static void k_meta(uint32_t ak, uint32_t am, PageRegs<kI4, 32, 128>& R,
+                                uint32_t& tok) {
+    asm("s_waitcnt vmcnt(%[later])\n\t"
+        "ds_read_b128 %[k0], %[ak]\n\t"
+        "ds_read_b128 %[k1], %[ak] offset:256\n\t"
+        "ds_read_b128 %[km0], %[am]\n\t"
+        "ds_read_b128 %[km1], %[am] offset:16\n\t"
+        "ds_read_b128 %[vm0], %[am] offset:128\n\t"
+        "ds_read_b128 %[vm1], %[am] offset:144\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : [k0] "=&v"(R.k[0][0]), [k1] "=&v"(R.k[1][0]), [km0] "=&v"(R.km[0]),
+          [km1] "=&v"(R.km[1]), [vm0] "=&v"(R.vm[0]), [vm1] "=&v"(R.vm[1]), [tok] "+s"(tok)
+        : [ak] "v"(ak), [am] "v"(am), [later] "n"(later));
+  }
+  template <int later>
+  __device__ static void v(uint32_t av, uint2 (&v)[8], uint32_t& tok) {
+    uint4 v01, v23, v45, v67;
+    asm("s_waitcnt vmcnt(%[later])\n\t"
+        "ds_read2_b64 %[v01], %[av] offset1:32\n\t"
+        "ds_read2_b64 %[v23], %[av] offset0:64 offset1:96\n\t"
+        "ds_read2_b64 %[v45], %[av] offset0:128 offset1:160\n\t"
+        "ds_read2_b64 %[v67], %[av] offset0:192 offset1:224\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : [v01] "=&v"(v01), [v23] "=&v"(v23), [v45] "=&v"(v45), [v67] "=&v"(v67),
+          [tok] "+s"(tok)
+        : [av] "v"(av), [later] "n"(later));
+    v[0] = make_uint2(v01.x, v01.y);
+    v[1] = make_uint2(v01.z, v01.w);
+    v[2] = make_uint2(v23.x, v23.y);
+    v[3] = make_uint2(v23.z, v23.w);
+    v[4] = make_uint2(v45.x, v45.y);
+    v[5] = make_uint2(v45.z, v45.w);
+    v[6] = make_uint2(v67.x, v67.y);
+    v[7] = make_uint2(v67.z, v67.w);
+  }
+};
 template <int F, int P, int D, int NT, int DEPTH>
 __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_mfma_stream_kernel(
     DecodeArgs a) {
@@ -801,9 +957,25 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
   stream_seek<P>(a, ip, end, true);
   bool issued_all = ip.item >= end;
   const MfmaLaneOffsets<F, P, D> lo = mfma_lane_offsets<F, P, D>(r, gq);
-  auto issue = [&](PageRegs<F, P, D>& R) __attribute__((always_inline)) {
+  // the ring: RD pages in registers, or (LR) in this wavefront's LDS slots
+  // with only their page ids in registers
+  constexpr bool LR = stream_lds_ring<F, P, D, NT>();
+  using LS = LdsSlot<F, P, D>;
+  constexpr int RD = LR ? LS::depth : DEPTH;
+  __shared__ __attribute__((aligned(16))) char lds_ring[LR ? 4 * RD * LS::SB : 16];
+  // this wavefront's slots (an LDS byte address: the low half of the generic one)
+  const uint32_t wslots =
+      uint32_t(reinterpret_cast<uintptr_t>(lds_ring)) + (LR ? wave * RD * LS::SB : 0);
+  PageRegs<F, P, D> ring[LR ? 1 : RD];
+  int ring_phys[RD];
+  uint32_t ltok = 0;  // orders the LDS ring's asm statements
+  auto issue = [&](int s) __attribute__((always_inline)) {
     const int32_t* btrow = a.bt + int64_t(ip.wr.b) * a.max_blocks;
-    mfma_load_page<F, P, D>(a, btrow[ip.wr.logical(ip.wr.kb0 + ip.k)], ip.wr.h, lo, R);
+    const int phys = btrow[ip.wr.logical(ip.wr.kb0 + ip.k)];
+    if constexpr (LR)
+      ring_phys[s] = lds_load_page<F, P, D>(a, phys, ip.wr.h, lane, wslots + s * LS::SB, ltok);
+    else
+      mfma_load_page<F, P, D>(a, phys, ip.wr.h, lo, ring[s]);
     // advance to the next page of the stream (or stay on the last one)
     if (!issued_all) {
       if (++ip.k >= ip.wr.cnt) {
@@ -888,9 +1060,31 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
     }
   };
 
-  auto compute = [&](const PageRegs<F, P, D>& R, const WorkRange& wr,
-                     int k) __attribute__((always_inline)) {
-    mfma_page<F, P, D, NT>(a, R, wr, k, r, gq, qop, qsum, m, lsum, zacc, acc, vexp);
+  // lane addresses of the LDS slots' pieces (slot 0; slot s is s * SB on)
+  uint32_t lds_k = 0, lds_v = 0, lds_m = 0;
+  if constexpr (LR) {
+    lds_k = wslots + lo.koff[0];
+    lds_v = wslots + LS::TB + lo.voff;
+    lds_m = wslots + 2 * LS::TB + lo.moff;
+  }
+  auto compute = [&](int s, const WorkRange& wr, int k) __attribute__((always_inline)) {
+    if constexpr (LR) {
+      // the pages issued after this one are later copies still in flight;
+      // this page's own V^T copies come after its K and metadata ones
+      constexpr int later = (RD - 1) * LS::loads;
+      static_assert(later + LS::v_loads <= 63, "load counter range");
+      PageRegs<F, P, D> R;
+      LdsRead<F, P, D>::template k_meta<later + LS::v_loads>(lds_k + s * LS::SB,
+                                                              lds_m + s * LS::SB, R, ltok);
+      R.phys = ring_phys[s];
+      const uint32_t av = lds_v + s * LS::SB;
+      auto vfetch = [av, &ltok](uint2 (&v)[8]) __attribute__((always_inline)) {
+        LdsRead<F, P, D>::template v<later>(av, v, ltok);
+      };
+      mfma_page<F, P, D, NT>(a, R, wr, k, r, gq, qop, qsum, m, lsum, zacc, acc, vexp, vfetch);
+    } else {
+      mfma_page<F, P, D, NT>(a, ring[s], wr, k, r, gq, qop, qsum, m, lsum, zacc, acc, vexp);
+    }
   };
 
   // compute side: every valid item in order (empty ones give 0 or an empty
@@ -899,7 +1093,7 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
   // (like the uniform kernel's), so the load counter waits stay those of a
   // steady stream; the item's start and end (q loads, result stores) sit
   // outside that loop.
-  static_assert(DEPTH >= 1 && DEPTH <= 4, "stream ring of one to four pages");
+  static_assert(RD >= 1 && RD <= 4, "stream ring of one to four pages");
   StreamPos cp;
   cp.item = i_begin;
   stream_seek<P>(a, cp, end, false);
@@ -911,40 +1105,39 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
     return;
   }
   if constexpr (QPRE) prefetch_q(cp.item);
-  PageRegs<F, P, D> ring[DEPTH];
 #pragma unroll
-  for (int s = 0; s < DEPTH; ++s) issue(ring[s]);
+  for (int s = 0; s < RD; ++s) issue(s);
   // pages of the current item, its first page in ring slot S0
   auto item_pages = [&](auto s0_tag) __attribute__((always_inline)) {
     constexpr int S0 = decltype(s0_tag)::value;
     const int cnt = cp.wr.cnt;
     int k = 0;
-    for (; k + DEPTH <= cnt; k += DEPTH) {
+    for (; k + RD <= cnt; k += RD) {
 #pragma unroll
-      for (int s = 0; s < DEPTH; ++s) {
-        compute(ring[(S0 + s) % DEPTH], cp.wr, k + s);
-        issue(ring[(S0 + s) % DEPTH]);
+      for (int s = 0; s < RD; ++s) {
+        compute((S0 + s) % RD, cp.wr, k + s);
+        issue((S0 + s) % RD);
       }
     }
-    // fewer than DEPTH pages left, from slot S0 on
+    // fewer than RD pages left, from slot S0 on
 #pragma unroll
-    for (int s = 0; s < DEPTH - 1; ++s) {
+    for (int s = 0; s < RD - 1; ++s) {
       if (k + s < cnt) {
-        compute(ring[(S0 + s) % DEPTH], cp.wr, k + s);
-        issue(ring[(S0 + s) % DEPTH]);
+        compute((S0 + s) % RD, cp.wr, k + s);
+        issue((S0 + s) % RD);
       }
     }
   };
   auto pages_from_slot = [&](int s0) __attribute__((always_inline)) {
     if (s0 == 0) {
       item_pages(std::integral_constant<int, 0>{});
-    } else if constexpr (DEPTH > 1) {
+    } else if constexpr (RD > 1) {
       if (s0 == 1) {
         item_pages(std::integral_constant<int, 1>{});
-      } else if constexpr (DEPTH > 2) {
+      } else if constexpr (RD > 2) {
         if (s0 == 2)
           item_pages(std::integral_constant<int, 2>{});
-        else if constexpr (DEPTH > 3)
+        else if constexpr (RD > 3)
           item_pages(std::integral_constant<int, 3>{});
       }
     }
@@ -954,10 +1147,12 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
     begin_item(cp.wr, cp.item);
     if (cp.wr.cnt > 0) {
       pages_from_slot(slot0);
-      slot0 = (slot0 + cp.wr.cnt) % DEPTH;
+      slot0 = (slot0 + cp.wr.cnt) % RD;
     }
     finish_item(cp.wr);
   }
+  // the ring's last copies land before the wavefront (and its LDS) ends
+  if constexpr (LR) asm volatile("s_waitcnt vmcnt(0) ; %0" : : "s"(ltok));
 }
 
 // ---------------------------------------------------------------------------
