@@ -824,7 +824,8 @@ template <int F, int P, int D> struct LdsSlot {
   static constexpr int loads = (MB ? 1 : 0) + k_loads + v_loads;  // copies per page
 };
 // One copy instruction: `bytes` (4 or 16) per lane from the lane's global
-// address to LDS byte m0 + lane * bytes, with the streaming cache policy.
+// address to LDS byte m0 + lane * bytes, with the streaming cache policy
+// (page data) or the default one (`cached`).
 // The copies and the slot reads below are asm statements that are not
 // volatile (the compiler treats its own LDS-copy builtin, and any volatile
 // asm, as writing all memory, and would then read the read-only tables with
@@ -834,10 +835,16 @@ template <int F, int P, int D> struct LdsSlot {
 // own load-counter waits, which only makes those waits longer (the counter
 // retires loads in order); the slot reads wait for them explicitly.  (An SALU
 // write of m0 needs one wait state before a copy reads it.)
-template <int bytes>
+template <int bytes, bool cached = false>
 __device__ __forceinline__ void lds_copy(const void* src, uint32_t lds_addr, uint32_t& tok) {
   static_assert(bytes == 4 || bytes == 16, "dword or dwordx4 copies");
-  if constexpr (bytes == 16)
+  if constexpr (cached) {
+    static_assert(bytes == 4, "cached copies are the ring's 4-byte fillers");
+    asm("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off"
+        : "+s"(tok)
+        : "s"(lds_addr), "v"(src)
+        : "m0");
+  } else if constexpr (bytes == 16)
     asm("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off nt"
         : "+s"(tok)
         : "s"(lds_addr), "v"(src)
@@ -875,6 +882,22 @@ __device__ __forceinline__ int lds_load_page(const DecodeArgs& a, int phys, int 
   for (int i = 0; i < L::v_loads; ++i)
     lds_copy<16>(vp + 1024 * i, slot + L::TB + 1024 * i, tok);
   return ok ? phys : -1;
+}
+
+// The ring's filler once a stream's pages are all issued: as many copy
+// instructions as a page (the slot reads' waits count them), each of 256
+// bytes that stay cached (the first q row, 4 bytes per lane), into a slot
+// that is never read again.  Re-issuing the last page instead, as the
+// register ring does, re-read it from HBM: three fillers per bin added 3% to
+// INT4's traffic.
+template <int F, int P, int D>
+__device__ __forceinline__ void lds_load_filler(const DecodeArgs& a, int lane, uint32_t slot,
+                                                uint32_t& tok) {
+  static_assert(D == 128 && LdsSlot<F, P, D>::loads * 256 <= LdsSlot<F, P, D>::SB,
+                "a 256-byte q row, copies within the slot");
+  const char* src = reinterpret_cast<const char*>(a.q) + 4 * lane;
+#pragma unroll
+  for (int i = 0; i < LdsSlot<F, P, D>::loads; ++i) lds_copy<4, true>(src, slot + 256 * i, tok);
 }
 
 // Read a slot into a lane's page registers (the register ring's layout), in
@@ -972,9 +995,12 @@ __global__ __launch_bounds__(256, (stream_waves_per_simd<F, NT>())) void decode_
   auto issue = [&](int s) __attribute__((always_inline)) {
     const int32_t* btrow = a.bt + int64_t(ip.wr.b) * a.max_blocks;
     const int phys = btrow[ip.wr.logical(ip.wr.kb0 + ip.k)];
-    if constexpr (LR)
-      ring_phys[s] = lds_load_page<F, P, D>(a, phys, ip.wr.h, lane, wslots + s * LS::SB, ltok);
-    else
+    if constexpr (LR) {
+      if (issued_all)  // every page is issued: a filler keeps the count of copies
+        lds_load_filler<F, P, D>(a, lane, wslots + s * LS::SB, ltok);
+      else
+        ring_phys[s] = lds_load_page<F, P, D>(a, phys, ip.wr.h, lane, wslots + s * LS::SB, ltok);
+    } else
       mfma_load_page<F, P, D>(a, phys, ip.wr.h, lo, ring[s]);
     // advance to the next page of the stream (or stay on the last one)
     if (!issued_all) {
