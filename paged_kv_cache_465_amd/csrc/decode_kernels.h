@@ -473,8 +473,14 @@ __device__ __forceinline__ void mfma_page(const DecodeArgs& a, const PageRegs<F,
       uint32_t w[KB / 4];
       __builtin_memcpy(w, R.k[st], KB);
       constexpr int DW = F == kI4 ? 1 : 2;  // dwords per 8 channels
+      // INT4: the float16 exponent bits in a register (an empty asm hides
+      // the constant), so that each mask-and-or is one instruction (it cannot
+      // take two literal constants): 16 sequences of 16k-32k tokens, 93.8 ->
+      // 92.9 us for the decode call
+      uint32_t expo = 0x64006400u;
+      if constexpr (F == kI4) asm("" : "+v"(expo));
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kop[st][kk] = codes8_to_f16x8_offset<F>(w + DW * kk);
+      for (int kk = 0; kk < KK; ++kk) kop[st][kk] = codes8_to_f16x8_offset<F>(w + DW * kk, expo);
     }
   }
   // V^T operands: from R.v, or (late_v) from vfetch right before P.V, so

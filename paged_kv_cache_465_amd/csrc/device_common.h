@@ -213,18 +213,19 @@ __device__ __forceinline__ f16x8_t codes8_to_f16x8(const uint32_t* w) {
 
 // Decode's K operand: for INT4 the eight channels of i4x8_to_f16x8 (same
 // slots) as code + 1032, exactly (each nibble u = code + 8 under the float16
-// exponent of 1024, from three shifts and four mask-and-ors): the offset is
-// left in, so the dot product with q carries 1032 sum(q), which the caller
-// removes once per dot product instead of once per code.  Other formats as
-// codes8_to_f16x8.
+// exponent of 1024, `expo`, from three shifts and four mask-and-ors): the
+// offset is left in, so the dot product with q carries 1032 sum(q), which
+// the caller removes once per dot product instead of once per code.  Other
+// formats as codes8_to_f16x8.
 template <int F>
-__device__ __forceinline__ f16x8_t codes8_to_f16x8_offset(const uint32_t* w) {
+__device__ __forceinline__ f16x8_t codes8_to_f16x8_offset(const uint32_t* w,
+                                                         uint32_t expo = 0x64006400u) {
   if constexpr (F == kI4) {
     const uint32_t x = w[0];
-    const f16x2_t a = __builtin_bit_cast(f16x2_t, (x & 0x000f000fu) | 0x64006400u);          // ch 0, 4
-    const f16x2_t b = __builtin_bit_cast(f16x2_t, ((x >> 4) & 0x000f000fu) | 0x64006400u);   // ch 1, 5
-    const f16x2_t c = __builtin_bit_cast(f16x2_t, ((x >> 8) & 0x000f000fu) | 0x64006400u);   // ch 2, 6
-    const f16x2_t d = __builtin_bit_cast(f16x2_t, ((x >> 12) & 0x000f000fu) | 0x64006400u);  // ch 3, 7
+    const f16x2_t a = __builtin_bit_cast(f16x2_t, (x & 0x000f000fu) | expo);          // ch 0, 4
+    const f16x2_t b = __builtin_bit_cast(f16x2_t, ((x >> 4) & 0x000f000fu) | expo);   // ch 1, 5
+    const f16x2_t c = __builtin_bit_cast(f16x2_t, ((x >> 8) & 0x000f000fu) | expo);   // ch 2, 6
+    const f16x2_t d = __builtin_bit_cast(f16x2_t, ((x >> 12) & 0x000f000fu) | expo);  // ch 3, 7
     return f16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
   } else {
     return codes8_to_f16x8<F>(w);

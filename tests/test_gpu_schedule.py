@@ -72,6 +72,31 @@ def test_scheduled_decode_lowbit(kvp, cfg):
     gc.close()
 
 
+def test_int4_lds_ring_short_streams(kvp):
+    """INT4 pools with 32-token pages of 128 channels (g <= 16) stream their
+    pages through a three-slot LDS ring per wavefront, with filler copies once
+    a stream's pages are all issued: sequences of one to three pages and just
+    past them, cut into 1 to 1024 bins (one-page items, bins holding a single
+    page, streams shorter than the ring), against the oracle and within one
+    bfloat16 rounding of the uniform plan."""
+    from .casetools import oracle_pools
+    cfg = variant(INT4_LONG, name="int4_ring", batch=12, ctx_lo=0, ctx_hi=0,
+                  ctx_fixed=(1, 31, 32, 33, 64, 65, 95, 96, 97, 130, 700, 2049))
+    case = make_case(cfg)
+    k, v, km, vm = oracle_pools(case)
+    ref = oracle.paged_decode(layout_of(case), case.q, k, v, km, vm, case.block_tables, case.ctx,
+                              case.scale)
+    gc = GpuCase(kvp, case)
+    gc.upload(k, v, km, vm)
+    uniform = gc.decode()
+    for bins in (1, 2, 7, 64, 1024):
+        out = gc.decode_scheduled(max_bins=bins)
+        log(f"[int4 ring] bins<={bins} {_info(gc.last_schedule)}")
+        assert_close(out, ref, f"int4 ring bins<={bins}")
+        assert_within_one_rounding(out, uniform, f"int4 ring bins<={bins} vs uniform")
+    gc.close()
+
+
 @pytest.mark.parametrize("name", ["l8b_small", "int8_small", "prefix_small"])
 def test_one_device_schedule_serves_many_calls(kvp, name):
     """One device copy of a schedule that cuts pairs across bins serves calls
