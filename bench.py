@@ -609,7 +609,8 @@ def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
-              "has no multi-GPU mode in this build.", file=sys.stderr)
+              "has no multi-GPU mode (the way it would shard across GPUs is documented with the "
+              "design).", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
