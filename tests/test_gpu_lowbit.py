@@ -226,6 +226,27 @@ def test_append_special_rows_lowbit(kvp, kind):
     pool.close()
 
 
+@pytest.mark.parametrize("name", ["int4_small", "fp8_small"])
+@pytest.mark.parametrize("sink,window", [(4, 64), (0, 17), (3, 200)])
+def test_scheduled_window_decode_lowbit(kvp, name, sink, window):
+    """Sinks + window over INT4 and FP8 pools along a schedule built for that
+    selection: INT4's 32-token pages of 128 channels go through the stream
+    kernel's LDS ring, and the sink and window boundaries cut pages in the
+    middle of a stream.  Dropped pages are freed (-1) and poisoned."""
+    cfg = next(c for c in LOWBIT if c.name == name)
+    case = _case(cfg)
+    k, v, km, vm, bt, n_poisoned = _evicted_case(case, sink, window, pools=_oracle(case)[:4])
+    ref = oracle.paged_decode_window(layout_of(case), case.q, k, v, km, vm, bt, case.ctx,
+                                     case.scale, sink, window)
+    log(f"[sched window lowbit] {cfg.name} s={sink} w={window} poisoned_pages={n_poisoned}")
+    gc = GpuCase(kvp, case, block_tables=bt)
+    gc.upload(k, v, km, vm)
+    for bins in (4, 1024):
+        out = gc.decode_scheduled(max_bins=bins, sink=sink, window=window)
+        assert_close(out, ref, f"{cfg.name} s={sink} w={window} bins<={bins}")
+    gc.close()
+
+
 LOWBIT_PREFILL = [
     variant(TINY, name=f"tiny_chunk5_{f}", kv_dtype=f, q_len=5) for f in ("int4", "fp8")
 ] + [
