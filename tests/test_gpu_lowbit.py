@@ -247,6 +247,37 @@ def test_scheduled_window_decode_lowbit(kvp, name, sink, window):
     gc.close()
 
 
+def test_scheduled_out_of_range_page_ids_int4(kvp):
+    """Along a schedule over an INT4 pool (pages through the stream kernel's
+    LDS ring): table entries past each sequence hold garbage ids and are never
+    read; one used entry in the middle of a stream, outside [0, num_pages),
+    drops that block's tokens and is skipped in the ring's order."""
+    cfg = next(c for c in LOWBIT if c.name == "int4_small")
+    case = _case(cfg)
+    k, v, km, vm, ref = _oracle(case)
+    P = cfg.page_size
+    nb = -(-case.ctx // P)
+    b0 = int(np.argmax(nb >= 3))
+    assert nb[b0] >= 3, "a sequence of at least three blocks"
+    bt = case.block_tables.copy()
+    for b in range(case.B):
+        bt[b, nb[b]:] = 1_000_000_000
+    bt[b0, 1] = -5
+    gc = GpuCase(kvp, case, block_tables=bt)
+    gc.upload(k, v, km, vm)
+    lay = layout_of(case)
+    q = (case.q.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    Kf, Vf = oracle.gather_sequence(lay, k, v, km, vm, case.block_tables[b0], int(case.ctx[b0]))
+    keep = np.r_[0:P, 2 * P:int(case.ctx[b0])]
+    ref2 = ref.copy()
+    ref2[b0] = oracle.attend(q[b0], Kf[:, keep], Vf[:, keep], float(np.float32(case.scale)))
+    log(f"[bad ids sched int4] sequence {b0} ctx={int(case.ctx[b0])}")
+    for bins in (3, 1024):
+        out = gc.decode_scheduled(max_bins=bins)
+        assert_close(out, ref2, f"int4 block 1 of sequence {b0} dropped, bins<={bins}")
+    gc.close()
+
+
 LOWBIT_PREFILL = [
     variant(TINY, name=f"tiny_chunk5_{f}", kv_dtype=f, q_len=5) for f in ("int4", "fp8")
 ] + [
